@@ -1,0 +1,203 @@
+/*
+ * zeroshard.h -- C ABI of libzeroshard: the per-rank ZeRO-2 optimizer-shard
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * One call sequence updates this rank's shard of a model trained with
+ * mixed precision under ZeRO stage 2:
+ *   (a) owner's side of the gradient reduce-scatter: W workers' 16-bit
+ *       gradient buffers are summed in fp32, in the order a ring
+ *       scatter-reduce accumulates them, and averaged;
+ *   (b) AdamW on the fp32 partition: unscale by the loss scale, overflow
+ *       check, moments, bias correction, decoupled weight decay;
+ *   (c) cast of the new fp32 master weights to 16 bits, written at this
+ *       rank's offset of the flat all-gather buffer.
+ *
+ * Sources, cited by page title and section:
+ *   [Notes] untitled lecture notes on DP, DDP and DeepSpeed ZeRO
+ *           (gitcode.csdn.net/69c4e349...): "二、DDP" (ring all-reduce,
+ *           bucketing), "三、DeepSpeed ZeRO - 1" (the owner's update
+ *           sequence), "四、DeepSpeed ZeRO - 2 & ZeRO - 3".
+ *   [Intro] "并行训练框架DeepSpeed介绍" (nanhubrain.csdn.net): part 一.3,
+ *           items (1)-(3) mixed precision, BF16 and loss scaling, (12) ZeRO-2.
+ *   [L7]    "第 7 讲：Parallelism（上）" (CS336 lecture 7): "数学等价性",
+ *           "Ring AllReduce 算法", "Gradient Accumulation", "ZeRO Stage 2".
+ *
+ * Conventions for every entry point
+ *   - Device pointers are HIP device (HBM) addresses the caller allocated;
+ *     the library never allocates or frees device memory, never keeps a
+ *     pointer after the call returns and never synchronizes. Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     completes asynchronously; kernel faults surface at the caller's next
+ *     synchronization.
+ *   - Host pointers (arrays of device pointers, hyper-parameter structs,
+ *     outputs of zs_partition) are read or written during the call only.
+ *   - 16-bit values are IEEE binary16 (ZS_FP16) or bfloat16 (ZS_BF16).
+ *   - Any element offset is accepted; 16-byte-aligned operands take the
+ *     widest (8-element) vector path, others a narrower one of the same
+ *     kernel.
+ *   - n == 0 is a no-op that returns ZS_OK.
+ *   - Status codes: ZS_OK on success; ZS_ERR_INVALID_ARG (null pointer,
+ *     world == 0 or > ZS_MAX_WORLD, rank >= world, bad dtype, non-finite or
+ *     zero loss scale, step_t == 0) before anything is enqueued;
+ *     ZS_ERR_ALIAS when zs_step_fused's output set overlaps its input set;
+ *     ZS_ERR_HIP when a launch fails (zs_last_error() has HIP's message).
+ *   - Overflow is data, not an error: it is reported only through the
+ *     uint32 flag, which calls set to 1 and never clear. The caller zeroes it
+ *     before a step; several calls may OR into the same flag.
+ *   - Concurrent calls on different streams are safe if their buffers are
+ *     disjoint.
+ */
+#ifndef ZEROSHARD_H
+#define ZEROSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZS_ABI_VERSION 1
+#define ZS_MAX_WORLD 64
+
+typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
+
+typedef enum {
+  ZS_OK = 0,
+  ZS_ERR_INVALID_ARG = 1,
+  ZS_ERR_UNSUPPORTED = 2,
+  ZS_ERR_ALIAS = 3,
+  ZS_ERR_HIP = 4
+} zs_status;
+
+/* AdamW hyper-parameters of one step. lr, betas, eps and weight_decay are
+ * the usual AdamW settings; loss_scale is the factor the gradients carry
+ * (the update divides it out); step_t is the 1-based index of the step being
+ * attempted, i.e. committed steps + 1 (skipped steps do not advance it). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  float loss_scale;
+  uint32_t step_t;
+} zs_adamw_hparams;
+
+/* ZS_ABI_VERSION of the loaded library. */
+int zs_abi_version(void);
+/* Static string naming a status code. */
+const char *zs_status_string(int status);
+/* Detail of this thread's last non-OK status ("" if none). Thread-local. */
+const char *zs_last_error(void);
+
+/* Partition map ([Notes] 二: each ring chunk is phi/N elements of the flat
+ * buffer; [L7] "Ring AllReduce 算法": the vector is cut into W blocks).
+ * chunk = ceil(phi / world); rank `rank` owns the flat elements
+ * [offset, offset + count) with offset = rank * chunk and
+ * count = min(chunk, max(0, phi - offset)). Host-only. Any output pointer
+ * may be NULL. Errors: ZS_ERR_INVALID_ARG for world == 0 or rank >= world. */
+int zs_partition(uint64_t phi, uint32_t world, uint32_t rank, uint64_t *chunk,
+                 uint64_t *offset, uint64_t *count);
+
+/* Owner's side of the gradient reduce-scatter ([Notes] 二 worked ring
+ * example and 四: the owner collects and averages its part; [Intro] (12);
+ * [L7] "ZeRO Stage 2": ReduceScatter replaces AllReduce).
+ *   worker_grads : host array of `world` device pointers in worker order;
+ *                  worker_grads[k] points at element `offset` of worker k's
+ *                  flat 16-bit gradient buffer (n readable elements).
+ *   For i < n:  s = G[r+1][i] + G[r+2][i] + ... + G[r+W-1][i] + G[r][i]
+ *               (indices mod W, fp32, left to right: the order in which the
+ *               ring's partial sum for chunk r picks up each worker, the
+ *               owner's own term last), a = s / W (IEEE division), then
+ *               grad_part[i] = a             if accumulate == 0,
+ *               grad_part[i] = grad_part[i] + a otherwise (a later
+ *               micro-batch, [L7] "Gradient Accumulation").
+ *   grad_part    : device fp32[n], written (read too when accumulating).
+ *   overflow_flag: device uint32 or NULL; if set, becomes 1 when any
+ *                  grad_part[i] / loss_scale is not finite.
+ *   loss_scale   : used only for the flag. */
+int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
+                          uint32_t world, uint32_t rank, uint64_t n,
+                          float *grad_part, int accumulate,
+                          uint32_t *overflow_flag, float loss_scale,
+                          void *stream);
+
+/* Overflow check of dynamic loss scaling ([Intro] 一.3 items (1) and (3)).
+ * Sets *overflow_flag = 1 when any grad_part[i] / loss_scale (fp32 IEEE
+ * division) is inf or NaN; otherwise leaves it unchanged.
+ * grad_part: device fp32[n]; overflow_flag: device uint32. */
+int zs_check_overflow(const float *grad_part, uint64_t n, float loss_scale,
+                      uint32_t *overflow_flag, void *stream);
+
+/* AdamW on this rank's partition, in place ([Notes] 三: gradients to FP32
+ * and unscaled, moments updated, then the FP32 master; [L7] memory table:
+ * fp32 master, m, v; decoupled decay as in AdamW). With g = grad_part[i] /
+ * loss_scale and the per-step scalars (formed in double, rounded once to
+ * fp32) alpha = lr / (1 - beta1^t), b2 = sqrt(1 - beta2^t),
+ * delta = 1 - lr*weight_decay, c1 = 1 - beta1, c2 = 1 - beta2:
+ *   m' = beta1*m + c1*g;  v' = beta2*v + c2*(g*g);
+ *   d  = sqrt(v')/b2 + eps;  master' = master*delta - alpha*(m'/d)
+ * each operator one fp32 IEEE operation, in this order.
+ *   master, m, v : device fp32[n], updated in place.
+ *   grad_part    : device fp32[n], the averaged (still scaled) gradient.
+ *   overflow_flag: device uint32 or NULL. When non-NULL and the flag is set
+ *                  at kernel start, nothing is written (the step is skipped)
+ *                  -- no host round trip is needed to gate the update. */
+int zs_adamw_step(float *master, float *m, float *v, const float *grad_part,
+                  uint64_t n, const zs_adamw_hparams *hp,
+                  const uint32_t *overflow_flag, void *stream);
+
+/* This rank's contribution to the parameter all-gather ([Notes] 三: the
+ * owner refreshes its 16-bit parameters; [Intro] (12) and [L7] "ZeRO Stage
+ * 1": AllGather of the updated parameters).
+ *   gather_buf[offset + i] = round_to_nearest_even_16(master[i]), i < n.
+ *   master     : device fp32[n].
+ *   gather_buf : device 16-bit flat buffer (world * chunk elements in the
+ *                usual layout); only [offset, offset + n) is written.
+ *   overflow_flag: device uint32 or NULL; when set, nothing is written. */
+int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
+                   uint64_t offset, uint64_t n, const uint32_t *overflow_flag,
+                   void *stream);
+
+/* One whole shard step in a single pass over HBM: reduce-scatter average
+ * (with optional accumulated micro-batches), unscale, overflow check, AdamW
+ * and cast, all with the arithmetic of the calls above, element for element.
+ * The update is written out of place, to an output set that must not
+ * overlap the input set (ZS_ERR_ALIAS), so a step whose flag turns out set
+ * leaves the input set untouched: the caller reads the flag, then either
+ * swaps the sets (flag 0) or keeps the input set (flag 1, step skipped).
+ * gather_buf belongs to the output set too. */
+typedef struct {
+  uint32_t world, rank;
+  uint64_t n;
+  int32_t grad_dtype, param_dtype;
+  const void *const *worker_grads; /* host array [world], as above         */
+  const float *acc_in;             /* NULL, or fp32[n] summed micro-batches */
+  const float *master_in, *m_in, *v_in;  /* fp32[n], read only             */
+  float *master_out, *m_out, *v_out;     /* fp32[n], written               */
+  void *gather_buf;                /* 16-bit flat buffer                    */
+  uint64_t gather_offset;          /* element offset of this rank's slice   */
+  uint32_t *overflow_flag;         /* device uint32, OR-ed                  */
+  zs_adamw_hparams hp;
+} zs_step_args;
+
+int zs_step_fused(const zs_step_args *args, void *stream);
+
+/* Host-side commit/skip bookkeeping of dynamic loss scaling ([Intro] 一.3
+ * items (1) and (3) name it without a rule). With dynamic != 0: on overflow
+ * the scale halves, clean_steps resets and step_t stays; otherwise
+ * step_t += 1 and clean_steps += 1, and when clean_steps reaches
+ * growth_interval the scale doubles for the next step and clean_steps
+ * restarts at 0. With dynamic == 0 the scale never changes. Host-only.
+ * Errors: ZS_ERR_INVALID_ARG for a NULL state. */
+typedef struct {
+  float scale;
+  uint32_t clean_steps;
+  uint32_t growth_interval;
+  uint32_t dynamic;
+  uint64_t step_t;   /* committed steps */
+  uint64_t skipped;  /* skipped steps   */
+} zs_loss_scaler;
+
+int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZEROSHARD_H */

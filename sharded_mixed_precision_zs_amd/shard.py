@@ -1,0 +1,135 @@
+"""Host-side driver of one rank's ZeRO-2 shard step (built on the C ABI only).
+
+`ShardState` owns this rank's optimizer shard in HBM -- two sets of fp32
+(master, m, v) and two 16-bit gather buffers (ping-pong), the overflow flag
+and the loss scaler -- and runs one optimizer step as
+
+    zs_step_fused(in-set -> out-set)    one pass over HBM
+    flag -> host (4 bytes)              the only synchronization
+    flag == 0: swap sets, t += 1        commit
+    flag == 1: keep the in-set          skip (scale halves when dynamic)
+
+which is the owner's update sequence of the DeepSpeed ZeRO notes (section
+三): gradients averaged and unscaled in fp32, moments and master updated, the
+16-bit copy refreshed for the all-gather. Micro-batches before the last are
+reduced into an fp32 accumulator with zs_reduce_scatter_avg (lecture 7,
+"Gradient Accumulation"). All arithmetic runs in libzeroshard's kernels;
+torch only allocates memory and provides the stream.
+"""
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import zeroshard as zs
+
+
+@dataclass
+class AdamW:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+
+class ShardState:
+    """One rank's shard: n parameters at flat offset `offset` of a model with
+    `world` data-parallel ranks; gather buffers hold `gather_len` elements."""
+
+    FLAG_RING = 256  # flags zeroed in bulk, one slot per step
+
+    def __init__(self, n, world, rank, offset, gather_len, param_dtype, grad_dtype,
+                 opt: AdamW, loss_scale, dynamic=False, growth_interval=0,
+                 device="cuda", accumulate=False):
+        self.n, self.world, self.rank, self.offset = n, world, rank, offset
+        self.param_dtype, self.grad_dtype = param_dtype, grad_dtype
+        self.opt = opt
+        f32 = dict(dtype=torch.float32, device=device)
+        self.sets = [[torch.empty(n, **f32) for _ in range(3)] for _ in range(2)]
+        pdt = torch.bfloat16 if param_dtype == zs.ZS_BF16 else torch.float16
+        self.gather = [torch.zeros(gather_len, dtype=pdt, device=device) for _ in range(2)]
+        self.cur = 0
+        self.acc = torch.empty(n, **f32) if accumulate else None
+        self.flags = torch.zeros(self.FLAG_RING, dtype=torch.int32, device=device)
+        self.flag_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+        self.slot = 0
+        self.scaler = zs.zs_loss_scaler(scale=loss_scale, clean_steps=0,
+                                        growth_interval=growth_interval,
+                                        dynamic=1 if dynamic else 0, step_t=0, skipped=0)
+        self.last_flag = 0
+
+    # -- state access -------------------------------------------------------
+    @property
+    def master(self):
+        return self.sets[self.cur][0]
+
+    @property
+    def m(self):
+        return self.sets[self.cur][1]
+
+    @property
+    def v(self):
+        return self.sets[self.cur][2]
+
+    @property
+    def params(self):
+        """This rank's slice of the current 16-bit gather buffer."""
+        return self.gather[self.cur][self.offset:self.offset + self.n]
+
+    @property
+    def t(self):
+        return int(self.scaler.step_t)
+
+    @property
+    def loss_scale(self):
+        return float(self.scaler.scale)
+
+    def hparams(self):
+        o = self.opt
+        return zs.hparams(o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.loss_scale,
+                          self.t + 1)
+
+    # -- flag ring ----------------------------------------------------------
+    def _next_flag(self):
+        if self.slot == self.FLAG_RING:
+            self.flags.zero_()
+            self.slot = 0
+        f = self.flags[self.slot:self.slot + 1]
+        self.slot += 1
+        return f
+
+    # -- micro-batches before the last one ------------------------------------
+    def reduce_micro(self, worker_grads: Sequence[torch.Tensor], first: bool, stream=None):
+        """acc = mean of this micro-batch's worker gradients (first) or
+        acc += that mean (later micro-batches)."""
+        zs.zs_reduce_scatter_avg(worker_grads, self.grad_dtype, self.world, self.rank, self.n,
+                                 self.acc, accumulate=not first, overflow_flag=None,
+                                 loss_scale=self.loss_scale, stream=stream)
+
+    # -- one optimizer step -------------------------------------------------
+    def launch(self, worker_grads: Sequence[torch.Tensor], acc_in: Optional[torch.Tensor] = None,
+               stream=None):
+        """Enqueue the fused step; returns the device flag slot it ORs into."""
+        flag = self._next_flag()
+        src, dst = self.sets[self.cur], self.sets[1 - self.cur]
+        args = zs.StepArgs(worker_grads, self.rank, self.n, src[0], src[1], src[2],
+                           dst[0], dst[1], dst[2], self.gather[1 - self.cur], self.offset,
+                           flag, self.hparams(), acc_in=acc_in, grad_dtype=self.grad_dtype,
+                           param_dtype=self.param_dtype)
+        zs.zs_step_fused(args, stream)
+        return flag
+
+    def finish(self, flag, stream=None):
+        """Read the flag back (the step's only synchronization), then commit or skip."""
+        s = stream if stream is not None else torch.cuda.current_stream()
+        self.flag_host.copy_(flag, non_blocking=True)
+        s.synchronize()
+        self.last_flag = int(self.flag_host[0])
+        zs.zs_scaler_update(self.scaler, self.last_flag)
+        if self.last_flag == 0:
+            self.cur = 1 - self.cur
+        return self.last_flag == 0
+
+    def step(self, worker_grads, acc_in=None, stream=None):
+        return self.finish(self.launch(worker_grads, acc_in, stream), stream)

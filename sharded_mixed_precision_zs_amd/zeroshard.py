@@ -1,0 +1,246 @@
+"""Python binding of libzeroshard (ctypes): argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/zeroshard.h
+documents the semantics and cites the pages). Device buffers are torch CUDA
+tensors (or raw integer device addresses); torch supplies memory and the
+stream, every step of the computation runs in the library's HIP kernels.
+The binding checks that each tensor is a contiguous CUDA tensor of the right
+element size holding at least the elements the kernel will touch, then passes
+plain pointers. There is no fallback: if the library is missing, importing
+this module raises.
+"""
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+from . import build as _build
+
+ZS_ABI_VERSION = 1
+ZS_MAX_WORLD = 64
+ZS_BF16, ZS_FP16 = 0, 1
+ZS_OK, ZS_ERR_INVALID_ARG, ZS_ERR_UNSUPPORTED, ZS_ERR_ALIAS, ZS_ERR_HIP = range(5)
+
+LIB_PATH = _build.LIB
+
+
+class ZsError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn}: {zs_status_string(status)}: {detail}")
+        self.status = status
+
+
+class zs_adamw_hparams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float),
+                ("eps", C.c_float), ("weight_decay", C.c_float),
+                ("loss_scale", C.c_float), ("step_t", C.c_uint32)]
+
+
+class zs_step_args(C.Structure):
+    _fields_ = [("world", C.c_uint32), ("rank", C.c_uint32), ("n", C.c_uint64),
+                ("grad_dtype", C.c_int32), ("param_dtype", C.c_int32),
+                ("worker_grads", C.POINTER(C.c_void_p)),
+                ("acc_in", C.c_void_p),
+                ("master_in", C.c_void_p), ("m_in", C.c_void_p), ("v_in", C.c_void_p),
+                ("master_out", C.c_void_p), ("m_out", C.c_void_p), ("v_out", C.c_void_p),
+                ("gather_buf", C.c_void_p), ("gather_offset", C.c_uint64),
+                ("overflow_flag", C.c_void_p),
+                ("hp", zs_adamw_hparams)]
+
+
+class zs_loss_scaler(C.Structure):
+    _fields_ = [("scale", C.c_float), ("clean_steps", C.c_uint32),
+                ("growth_interval", C.c_uint32), ("dynamic", C.c_uint32),
+                ("step_t", C.c_uint64), ("skipped", C.c_uint64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libzeroshard is not built ({LIB_PATH}); "
+                          "run __graft_entry__.build() -- there is no fallback path")
+    lib = C.CDLL(LIB_PATH)
+    vp, u32, u64, f32, i32 = C.c_void_p, C.c_uint32, C.c_uint64, C.c_float, C.c_int
+    sig = {
+        "zs_abi_version": ([], i32),
+        "zs_status_string": ([i32], C.c_char_p),
+        "zs_last_error": ([], C.c_char_p),
+        "zs_partition": ([u64, u32, u32, C.POINTER(u64), C.POINTER(u64), C.POINTER(u64)], i32),
+        "zs_reduce_scatter_avg": ([C.POINTER(vp), i32, u32, u32, u64, vp, i32, vp, f32, vp], i32),
+        "zs_check_overflow": ([vp, u64, f32, vp, vp], i32),
+        "zs_adamw_step": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, vp], i32),
+        "zs_cast_gather": ([vp, vp, i32, u64, u64, vp, vp], i32),
+        "zs_step_fused": ([C.POINTER(zs_step_args), vp], i32),
+        "zs_scaler_update": ([C.POINTER(zs_loss_scaler), u32], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, res
+    if lib.zs_abi_version() != ZS_ABI_VERSION:
+        raise ImportError("libzeroshard ABI version mismatch")
+    return lib
+
+
+_lib = _load()
+
+
+# ---- marshalling helpers ----------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, explicit):
+    if explicit is not None:
+        return int(explicit)
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ZS_BF16
+    if t.dtype == torch.float16:
+        return ZS_FP16
+    raise TypeError(f"16-bit float tensor expected, got {t.dtype}; pass the dtype explicitly")
+
+
+def _ptr(x, n, elem, what, offset=0):
+    """Device address of x after checking it holds offset+n elements of `elem` bytes."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError(f"{what}: CUDA tensor expected")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: contiguous tensor expected")
+    if x.element_size() != elem:
+        raise ValueError(f"{what}: {elem}-byte elements expected, got {x.element_size()}")
+    if x.numel() < offset + n:
+        raise ValueError(f"{what}: needs {offset + n} elements, has {x.numel()}")
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != ZS_OK:
+        raise ZsError(fn, status, zs_last_error())
+
+
+def hparams(lr, beta1, beta2, eps, weight_decay, loss_scale, step_t):
+    return zs_adamw_hparams(lr, beta1, beta2, eps, weight_decay, loss_scale, step_t)
+
+
+# ---- entry points -----------------------------------------------------------
+
+def zs_abi_version():
+    return _lib.zs_abi_version()
+
+
+def zs_status_string(status):
+    return _lib.zs_status_string(status).decode()
+
+
+def zs_last_error():
+    return _lib.zs_last_error().decode()
+
+
+def zs_partition(phi, world, rank):
+    """Returns (chunk, offset, count)."""
+    p, o, c = C.c_uint64(), C.c_uint64(), C.c_uint64()
+    _check("zs_partition", _lib.zs_partition(phi, world, rank, C.byref(p), C.byref(o), C.byref(c)))
+    return p.value, o.value, c.value
+
+
+def _grad_array(worker_grads, n):
+    ptrs = [_ptr(g, n, 2, f"worker_grads[{k}]") for k, g in enumerate(worker_grads)]
+    return (C.c_void_p * len(ptrs))(*ptrs)
+
+
+def zs_reduce_scatter_avg(worker_grads: Sequence, grad_dtype: Optional[int], world: int,
+                          rank: int, n: int, grad_part, accumulate=False,
+                          overflow_flag=None, loss_scale=1.0, stream=None):
+    if len(worker_grads) != world:
+        raise ValueError("len(worker_grads) must equal world")
+    arr = _grad_array(worker_grads, n)
+    dt = _dtype_code(worker_grads[0], grad_dtype) if world else 0
+    _check("zs_reduce_scatter_avg", _lib.zs_reduce_scatter_avg(
+        arr, dt, world, rank, n, _ptr(grad_part, n, 4, "grad_part"), 1 if accumulate else 0,
+        _ptr(overflow_flag, 1, 4, "overflow_flag"), loss_scale, _stream(stream)))
+
+
+def zs_check_overflow(grad_part, n, loss_scale, overflow_flag, stream=None):
+    _check("zs_check_overflow", _lib.zs_check_overflow(
+        _ptr(grad_part, n, 4, "grad_part"), n, loss_scale,
+        _ptr(overflow_flag, 1, 4, "overflow_flag"), _stream(stream)))
+
+
+def zs_adamw_step(master, m, v, grad_part, n, hp: zs_adamw_hparams, overflow_flag=None,
+                  stream=None):
+    _check("zs_adamw_step", _lib.zs_adamw_step(
+        _ptr(master, n, 4, "master"), _ptr(m, n, 4, "m"), _ptr(v, n, 4, "v"),
+        _ptr(grad_part, n, 4, "grad_part"), n, C.byref(hp),
+        _ptr(overflow_flag, 1, 4, "overflow_flag"), _stream(stream)))
+
+
+def zs_cast_gather(master, gather_buf, param_dtype: Optional[int], offset, n,
+                   overflow_flag=None, stream=None):
+    dt = _dtype_code(gather_buf, param_dtype)
+    _check("zs_cast_gather", _lib.zs_cast_gather(
+        _ptr(master, n, 4, "master"), _ptr(gather_buf, n, 2, "gather_buf", offset), dt,
+        offset, n, _ptr(overflow_flag, 1, 4, "overflow_flag"), _stream(stream)))
+
+
+class StepArgs:
+    """A prepared zs_step_args: built once, re-pointed cheaply between steps
+    (swap() exchanges the input and output sets after a committed step)."""
+
+    def __init__(self, worker_grads, rank, n, master_in, m_in, v_in, master_out, m_out, v_out,
+                 gather_buf, gather_offset, overflow_flag, hp: zs_adamw_hparams,
+                 acc_in=None, grad_dtype=None, param_dtype=None, gather_in=None):
+        world = len(worker_grads)
+        self._grads = _grad_array(worker_grads, n)
+        a = zs_step_args()
+        a.world, a.rank, a.n = world, rank, n
+        a.grad_dtype = _dtype_code(worker_grads[0], grad_dtype)
+        a.param_dtype = _dtype_code(gather_buf, param_dtype)
+        a.worker_grads = C.cast(self._grads, C.POINTER(C.c_void_p))
+        a.acc_in = _ptr(acc_in, n, 4, "acc_in")
+        a.master_in, a.m_in, a.v_in = (_ptr(master_in, n, 4, "master_in"), _ptr(m_in, n, 4, "m_in"),
+                                       _ptr(v_in, n, 4, "v_in"))
+        a.master_out, a.m_out, a.v_out = (_ptr(master_out, n, 4, "master_out"),
+                                          _ptr(m_out, n, 4, "m_out"), _ptr(v_out, n, 4, "v_out"))
+        a.gather_buf = _ptr(gather_buf, n, 2, "gather_buf", gather_offset)
+        # Optional second gather buffer: with one per set, a skipped step also
+        # leaves the current set's 16-bit parameters untouched.
+        self._gather_in = _ptr(gather_in, n, 2, "gather_in", gather_offset)
+        a.gather_offset = gather_offset
+        a.overflow_flag = _ptr(overflow_flag, 1, 4, "overflow_flag")
+        a.hp = hp
+        self.args = a
+
+    def set_grads(self, worker_grads):
+        n = self.args.n
+        for k, g in enumerate(worker_grads):
+            self._grads[k] = _ptr(g, n, 2, f"worker_grads[{k}]")
+
+    def swap(self):
+        a = self.args
+        a.master_in, a.master_out = a.master_out, a.master_in
+        a.m_in, a.m_out = a.m_out, a.m_in
+        a.v_in, a.v_out = a.v_out, a.v_in
+        if self._gather_in is not None:
+            a.gather_buf, self._gather_in = self._gather_in, a.gather_buf
+
+
+def zs_step_fused(args, stream=None):
+    """args: a StepArgs (or a raw zs_step_args)."""
+    raw = args.args if isinstance(args, StepArgs) else args
+    _check("zs_step_fused", _lib.zs_step_fused(C.byref(raw), _stream(stream)))
+
+
+def zs_scaler_update(state: zs_loss_scaler, overflow):
+    _check("zs_scaler_update", _lib.zs_scaler_update(C.byref(state), 1 if overflow else 0))

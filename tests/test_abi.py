@@ -1,0 +1,173 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and its host-only logic (partition, scaler, argument validation
+that returns before any launch) behaves as documented. No GPU work is done.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "zeroshard.h")
+
+
+@pytest.fixture(scope="module")
+def zs(hip_built):
+    from sharded_mixed_precision_zs_amd import zeroshard
+    return zeroshard
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("zs_reduce_scatter_avg", "zs_check_overflow", "zs_adamw_step",
+                     "zs_cast_gather", "zs_step_fused", "zs_partition", "zs_scaler_update",
+                     "zs_abi_version", "zs_status_string", "zs_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(zs):
+    lib = C.CDLL(zs.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 1
+
+
+def test_status_strings(zs):
+    assert zs.zs_status_string(zs.ZS_OK) == "ZS_OK"
+    assert zs.zs_status_string(zs.ZS_ERR_ALIAS) == "ZS_ERR_ALIAS"
+    assert zs.zs_status_string(99) == "ZS_UNKNOWN_STATUS"
+
+
+def test_partition_matches_oracle(zs):
+    for phi in (0, 1, 2, 3, 7, 100, 1001, 2 ** 20, 124_439_808, 7_500_000_000):
+        for w in (1, 2, 3, 4, 7, 8, 64):
+            for r in sorted({0, 1 % w, w // 2, w - 1}):
+                assert zs.zs_partition(phi, w, r) == oracle.partition(phi, w, r)
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_partition(10, 0, 0)
+    assert e.value.status == zs.ZS_ERR_INVALID_ARG
+    with pytest.raises(zs.ZsError):
+        zs.zs_partition(10, 4, 4)
+
+
+def test_scaler_matches_oracle(zs):
+    rng = __import__("numpy").random.default_rng(0)
+    flags = [int(x) for x in rng.random(200) < 0.15]
+    ours = zs.zs_loss_scaler(scale=65536.0, clean_steps=0, growth_interval=4, dynamic=1,
+                             step_t=0, skipped=0)
+    ref = oracle.Scaler(65536.0, 4)
+    for f in flags:
+        zs.zs_scaler_update(ours, f)
+        ref.update(f)
+        assert (ours.scale, ours.clean_steps, ours.step_t, ours.skipped) == \
+            (ref.scale, ref.clean, ref.t, ref.skipped)
+    static = zs.zs_loss_scaler(scale=1024.0, clean_steps=0, growth_interval=0, dynamic=0,
+                               step_t=0, skipped=0)
+    for f in (0, 1, 0, 0, 0, 0, 0):
+        zs.zs_scaler_update(static, f)
+    assert static.scale == 1024.0 and static.step_t == 6 and static.skipped == 1
+
+
+# Raw C calls with fake, never-dereferenced addresses: every case below must
+# be rejected on the host before anything is enqueued.
+FAKE = 0x7F0000000000
+
+
+def _raw(zs):
+    return zs._lib
+
+
+def test_reduce_rejects_bad_arguments(zs):
+    lib = _raw(zs)
+    arr = (C.c_void_p * 3)(FAKE, FAKE + 4096, FAKE + 8192)
+    ok_out = C.c_void_p(FAKE + 65536)
+    cases = [
+        (None, 0, 3, 0, 10, ok_out, 1.0),           # null worker array
+        (arr, 0, 3, 0, 10, None, 1.0),               # null output
+        (arr, 0, 0, 0, 10, ok_out, 1.0),             # world 0
+        (arr, 0, 65, 0, 10, ok_out, 1.0),            # world > 64
+        (arr, 0, 3, 3, 10, ok_out, 1.0),             # rank >= world
+        (arr, 7, 3, 0, 10, ok_out, 1.0),             # bad dtype
+        (arr, 0, 3, 0, 10, ok_out, 0.0),             # zero scale
+        (arr, 0, 3, 0, 10, ok_out, float("inf")),    # inf scale
+        (arr, 0, 3, 0, 10, ok_out, float("nan")),    # nan scale
+    ]
+    for a, dt, w, r, n, out, s in cases:
+        st = lib.zs_reduce_scatter_avg(a, dt, w, r, n, out, 0, None, s, None)
+        assert st == zs.ZS_ERR_INVALID_ARG, (w, r, dt, s)
+        assert zs.zs_last_error()
+    nulls = (C.c_void_p * 3)(FAKE, None, FAKE)
+    assert lib.zs_reduce_scatter_avg(nulls, 0, 3, 0, 10, ok_out, 0, None, 1.0, None) == \
+        zs.ZS_ERR_INVALID_ARG
+    # n == 0 is a no-op
+    assert lib.zs_reduce_scatter_avg(arr, 0, 3, 0, 0, ok_out, 0, None, 1.0, None) == zs.ZS_OK
+
+
+def test_other_entry_points_reject_bad_arguments(zs):
+    lib = _raw(zs)
+    hp = zs.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    bad_t = zs.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 0)
+    p = C.c_void_p(FAKE)
+    E = zs.ZS_ERR_INVALID_ARG
+    assert lib.zs_check_overflow(None, 10, 1.0, p, None) == E
+    assert lib.zs_check_overflow(p, 10, 1.0, None, None) == E
+    assert lib.zs_check_overflow(p, 10, -1.0, p, None) == E
+    assert lib.zs_adamw_step(p, p, None, p, 10, C.byref(hp), None, None) == E
+    assert lib.zs_adamw_step(p, p, p, p, 10, C.byref(bad_t), None, None) == E
+    assert lib.zs_adamw_step(p, p, p, p, 10, None, None, None) == E
+    assert lib.zs_cast_gather(None, p, 0, 0, 10, None, None) == E
+    assert lib.zs_cast_gather(p, p, 5, 0, 10, None, None) == E
+    assert lib.zs_check_overflow(p, 0, 1.0, p, None) == zs.ZS_OK
+    assert lib.zs_adamw_step(p, p, p, p, 0, C.byref(hp), None, None) == zs.ZS_OK
+    assert lib.zs_cast_gather(p, p, 0, 0, 0, None, None) == zs.ZS_OK
+
+
+def _fused_args(zs, n=1000, **over):
+    grads = (C.c_void_p * 2)(FAKE, FAKE + 0x100000)
+    a = zs.zs_step_args()
+    a.world, a.rank, a.n = 2, 0, n
+    a.grad_dtype = a.param_dtype = zs.ZS_BF16
+    a.worker_grads = C.cast(grads, C.POINTER(C.c_void_p))
+    base = FAKE + 0x1000000
+    a.master_in, a.m_in, a.v_in = base, base + 0x100000, base + 0x200000
+    a.master_out, a.m_out, a.v_out = base + 0x300000, base + 0x400000, base + 0x500000
+    a.gather_buf, a.gather_offset = base + 0x600000, 0
+    a.overflow_flag = base + 0x700000
+    a.hp = zs.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, grads
+
+
+def test_fused_rejects_aliasing_and_bad_arguments(zs):
+    lib = _raw(zs)
+    base = FAKE + 0x1000000
+    for field, addr in (("master_out", base), ("m_out", base + 0x100000 + 40),
+                        ("v_out", base + 0x200000 - 8), ("gather_buf", base + 0x100)):
+        a, keep = _fused_args(zs, **{field: addr})
+        assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS, field
+    a, keep = _fused_args(zs, m_out=base + 0x300000 + 100)       # two outputs overlap
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS
+    a, keep = _fused_args(zs, master_out=FAKE + 8)                # output on a gradient
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS
+    a, keep = _fused_args(zs, acc_in=base + 0x400000)             # output on acc_in
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS
+    for field, val in (("world", 0), ("world", 65), ("rank", 2), ("grad_dtype", 3),
+                       ("overflow_flag", None), ("master_in", None)):
+        a, keep = _fused_args(zs, **{field: val})
+        assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_INVALID_ARG, field
+    a, keep = _fused_args(zs)
+    a.hp.step_t = 0
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_INVALID_ARG
+    a, keep = _fused_args(zs, n=0)
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_OK
+    assert lib.zs_step_fused(None, None) == zs.ZS_ERR_INVALID_ARG
