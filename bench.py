@@ -1,0 +1,270 @@
+"""Benchmark of the per-rank ZeRO-2 optimizer-shard step on one MI355X.
+
+One step = one pass of the whole shard step over one batch of synthetic
+gradients already resident in HBM: ring-order W-way fp32 sum, average,
+unscale, overflow check, AdamW, cast into the gather buffer (one
+zs_step_fused launch), plus the 4-byte flag readback and the commit/skip
+bookkeeping on the host. Inputs come from the seeded generator, on the
+device.
+
+Prints ONE JSON line (rank 0). `value` is parameters updated per second of
+the chosen workload; the HBM side of the metric is in `hbm_gbps`,
+`hbm_pct_of_peak` and `roofline`. `roofline.achieved` is the algorithmic
+bytes of one fused launch ((2W + 12) read + 14 written per parameter, plus
+4 read per parameter for an accumulated micro-batch input) divided by that
+launch's average duration measured with HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload NAME] [--also NAME,...] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak (vendor figure)
+DEFAULT_WORKLOAD = "gpt2s-w8"   # GPT-2-small-shaped flat model, W = 8
+DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1"
+KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zeroshard.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.md")
+METRIC = "params updated/sec per ZeRO-2 shard step + achieved HBM GB/s (% of peak)"
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per fused launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def copy_ceiling_gbps(torch, gib=4, reps=10):
+    """Plain device copy (read + write) bandwidth: the practical ceiling."""
+    n = gib * (1 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def replicas_for(wl, bytes_per_step):
+    """Independent shard copies cycled through so a step never finds its
+    inputs in the 256 MB last-level cache (whole working set >= 1 GB)."""
+    return max(1, min(8, -(-(1 << 30) // max(bytes_per_step, 1))))
+
+
+def run_workload(name, steps, warmup, torch):
+    from sharded_mixed_precision_zs_amd import shard, synth
+
+    wl = synth.WORKLOADS[name]
+    n, W, A = wl.n, wl.world, wl.accum
+    rd, wr = wl.bytes_per_param()
+    # bytes of the fused launch alone (the last micro-batch) and of the step
+    fused_rd = 2 * W + 12 + (4 if A > 1 else 0)
+    fused_bytes = (fused_rd + 14) * n
+    step_bytes = (rd + wr) * n
+    R = replicas_for(wl, step_bytes)
+    log(f"{name}: n={n} W={W} A={A} replicas={R} step bytes={step_bytes / 1e9:.3f} GB")
+    opt = shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay)
+    reps = []
+    for r in range(R):
+        st = shard.ShardState(n, W, wl.rank, wl.offset, wl.offset + n, wl.param_dtype,
+                              wl.grad_dtype, opt, wl.loss_scale, dynamic=wl.dynamic_scale,
+                              growth_interval=wl.scale_interval, accumulate=A > 1)
+        synth.dev_state(wl, wl.offset, st.master, st.m, st.v)
+        grads = torch.empty((A, W, n), dtype=torch.int16, device="cuda")
+        for j in range(A):
+            for k in range(W):
+                synth.dev_grad(wl, k, 1 + r, j, wl.offset, grads[j, k], scale=wl.loss_scale)
+        reps.append((st, [[grads[j, k] for k in range(W)] for j in range(A)]))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def one_step(i, events=None):
+        st, g = reps[i % R]
+        for j in range(A - 1):
+            st.reduce_micro(g[j], first=(j == 0))
+        if events is not None:
+            events[0].record(stream)
+        flag = st.launch(g[A - 1], acc_in=st.acc if A > 1 else None)
+        if events is not None:
+            events[1].record(stream)
+        return st.finish(flag)
+
+    for i in range(warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    committed = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        committed += one_step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    ms_per_step = elapsed * 1e3 / steps
+    res = dict(workload=name, n=n, world=W, accum=A, replicas=R,
+               ms_per_step=ms_per_step, params_per_s=n / (ms_per_step * 1e-3),
+               step_bytes=step_bytes, hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9,
+               fused_kernel_ms=kern_avg, fused_bytes=fused_bytes,
+               fused_gbps=fused_bytes / (kern_avg * 1e-3) / 1e9, committed=committed,
+               kernel_ms_min=min(kern_ms), kernel_ms_max=max(kern_ms))
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name, target_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from sharded_mixed_precision_zs_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    threads = min(16, len(os.sched_getaffinity(0)))
+    kw = dict(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+              weight_decay=wl.weight_decay, loss_scale=wl.loss_scale, step_t=1)
+
+    def timed(ns, reps):
+        steps = []
+        for r in range(reps):
+            micro = [[synth.host_grad(wl, k, 1 + r, j, wl.offset, ns) for k in range(wl.world)]
+                     for j in range(wl.accum)]
+            steps.append(micro)
+        master, m, v = synth.host_state(wl, wl.offset, ns)
+        acc = np.empty(ns, np.float32) if wl.accum > 1 else None
+        t0 = time.perf_counter()
+        for micro in steps:
+            for j, parts in enumerate(micro[:-1]):
+                oracle.reduce_avg(parts, wl.rank, wl.grad_dtype, acc, j > 0, wl.loss_scale)
+            oracle.shard_step(micro[-1], wl.rank, wl.grad_dtype, wl.param_dtype, master, m, v,
+                              acc_in=acc, threads=threads, **kw)
+        return time.perf_counter() - t0
+
+    probe = min(wl.n, 1 << 18)
+    dt = timed(probe, 1)
+    # host memory bound on the sample: ~6 GB of generated inputs and state
+    cap = (6 << 30) // (2 * wl.world * wl.accum + 30)
+    want = int(probe * target_s / max(dt, 1e-6))
+    ns = int(min(wl.n, cap, max(probe, want)))
+    reps = max(1, min(wl.steps, int(want // ns)))
+    dt = timed(ns, reps)
+    return dict(value=ns * reps / dt, unit="params/s", cores=threads, kind="oracle",
+                sample=f"{ns} params of the {name} rank-{wl.rank} partition (W={wl.world}, "
+                       f"{wl.accum} micro-batch(es)) x {reps} step(s), {threads} threads, "
+                       f"{dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="comma-separated extra workloads reported under 'other_workloads'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU: the shard step takes one "
+                          "rank's real share on one MI355X; multi-GPU runs are not part of it"}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    from sharded_mixed_precision_zs_amd import synth  # noqa: F401  (fails loudly if unbuilt)
+    from sharded_mixed_precision_zs_amd import zeroshard  # noqa: F401
+
+    ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
+    if ceiling:
+        log(f"plain copy ceiling {ceiling:.0f} GB/s")
+    main_res = run_workload(args.workload, args.steps, args.warmup, torch)
+    log(json.dumps(main_res))
+    others = []
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        r = run_workload(name, max(3, args.steps // 2), 2, torch)
+        log(json.dumps(r))
+        others.append(dict(workload=name, params_per_s=r["params_per_s"],
+                           ms_per_step=r["ms_per_step"], hbm_gbps=r["hbm_gbps"],
+                           fused_kernel_ms=r["fused_kernel_ms"], fused_gbps=r["fused_gbps"],
+                           roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
+
+    from sharded_mixed_precision_zs_amd import synth as s
+    wl = s.WORKLOADS[args.workload]
+    traffic = recorded_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": main_res["params_per_s"],
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator, generated in HBM)",
+        "config": {"workload": args.workload, "description": wl.description,
+                   "phi": wl.phi, "world": wl.world, "rank": wl.rank, "shard_params": wl.n,
+                   "grad_dtype": "bf16" if wl.grad_dtype == 0 else "fp16",
+                   "param_dtype": "bf16" if wl.param_dtype == 0 else "fp16",
+                   "micro_batches": wl.accum, "replicas": main_res["replicas"]},
+        "hbm_gbps": main_res["hbm_gbps"],
+        "hbm_pct_of_peak": 100.0 * main_res["hbm_gbps"] / PEAK_HBM_GBPS,
+        "copy_ceiling_gbps": ceiling,
+        "roofline": {"bound": "hbm", "achieved": main_res["fused_gbps"],
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": main_res["fused_gbps"] / PEAK_HBM_GBPS,
+                     "traffic": traffic,
+                     "kernel": "zs::fused_kernel", "kernel_ms": main_res["fused_kernel_ms"],
+                     "algorithmic_bytes_per_launch": main_res["fused_bytes"]},
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,7 @@
 
 #include "zeroshard.h"
 
-namespace {
+namespace zs {
 
 constexpr int kBlock = 256;     /* threads per workgroup (4 waves of 64)   */
 constexpr int kLoadBatch = 8;   /* gradient vectors in flight per thread   */
@@ -417,6 +417,12 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   }
   flag_or(p.flag, bad);
 }
+
+}  // namespace zs
+
+namespace {
+
+using namespace zs;
 
 /* ------------------------------------------------------------------------
  * Host side: validation, scalar preparation, launch.

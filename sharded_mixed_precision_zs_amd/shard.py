@@ -58,6 +58,7 @@ class ShardState:
                                         growth_interval=growth_interval,
                                         dynamic=1 if dynamic else 0, step_t=0, skipped=0)
         self.last_flag = 0
+        self._prepared = {}
 
     # -- state access -------------------------------------------------------
     @property
@@ -108,15 +109,31 @@ class ShardState:
                                  loss_scale=self.loss_scale, stream=stream)
 
     # -- one optimizer step -------------------------------------------------
+    def _args(self, worker_grads, acc_in):
+        """Prepared zs_step_args for the current direction (cached by pointers)."""
+        key = (self.cur, tuple(g.data_ptr() for g in worker_grads),
+               acc_in.data_ptr() if acc_in is not None else 0)
+        args = self._prepared.get(key)
+        if args is None:
+            src, dst = self.sets[self.cur], self.sets[1 - self.cur]
+            args = zs.StepArgs(worker_grads, self.rank, self.n, src[0], src[1], src[2],
+                               dst[0], dst[1], dst[2], self.gather[1 - self.cur], self.offset,
+                               self.flags[0:1], self.hparams(), acc_in=acc_in,
+                               grad_dtype=self.grad_dtype, param_dtype=self.param_dtype)
+            if len(self._prepared) > 16:
+                self._prepared.clear()
+            self._prepared[key] = args
+        return args
+
     def launch(self, worker_grads: Sequence[torch.Tensor], acc_in: Optional[torch.Tensor] = None,
                stream=None):
         """Enqueue the fused step; returns the device flag slot it ORs into."""
         flag = self._next_flag()
-        src, dst = self.sets[self.cur], self.sets[1 - self.cur]
-        args = zs.StepArgs(worker_grads, self.rank, self.n, src[0], src[1], src[2],
-                           dst[0], dst[1], dst[2], self.gather[1 - self.cur], self.offset,
-                           flag, self.hparams(), acc_in=acc_in, grad_dtype=self.grad_dtype,
-                           param_dtype=self.param_dtype)
+        args = self._args(worker_grads, acc_in)
+        a = args.args
+        a.overflow_flag = flag.data_ptr()
+        a.hp.loss_scale = self.loss_scale
+        a.hp.step_t = self.t + 1
         zs.zs_step_fused(args, stream)
         return flag
 
