@@ -81,6 +81,12 @@ def copy_ceiling_gbps(torch, gib=4, reps=10):
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
+def pad_elems(n, align_bytes=256):
+    """Row length (16-bit elements) rounded up to a multiple of align_bytes."""
+    per = align_bytes // 2
+    return -(-n // per) * per
+
+
 def replicas_for(wl, bytes_per_step):
     """Independent shard copies cycled through so a step never finds its
     inputs in the 256 MB last-level cache (whole working set >= 1 GB)."""
@@ -106,11 +112,13 @@ def run_workload(name, steps, warmup, torch):
                               wl.grad_dtype, opt, wl.loss_scale, dynamic=wl.dynamic_scale,
                               growth_interval=wl.scale_interval, accumulate=A > 1)
         synth.dev_state(wl, wl.offset, st.master, st.m, st.v)
-        grads = torch.empty((A, W, n), dtype=torch.int16, device="cuda")
+        # one row per worker, rows padded to 256 B like separate allocations
+        grads = torch.empty((A, W, pad_elems(n)), dtype=torch.int16, device="cuda")
+        views = [[grads[j, k, :n] for k in range(W)] for j in range(A)]
         for j in range(A):
             for k in range(W):
-                synth.dev_grad(wl, k, 1 + r, j, wl.offset, grads[j, k], scale=wl.loss_scale)
-        reps.append((st, [[grads[j, k] for k in range(W)] for j in range(A)]))
+                synth.dev_grad(wl, k, 1 + r, j, wl.offset, views[j][k], scale=wl.loss_scale)
+        reps.append((st, views))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 

@@ -117,19 +117,29 @@ struct Raw16 {                         /* VEC 16-bit values, as loaded      */
   uint32_t w[VEC / 2 > 0 ? VEC / 2 : 1];
 };
 
-template <int VEC>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+/* NT = true marks the load non-temporal: gradients are read exactly once,
+ * so they should not displace cache lines that are. */
+template <int VEC, bool NT = false>
 __device__ __forceinline__ Raw16<VEC> ld16(const uint16_t *__restrict__ p) {
   Raw16<VEC> r;
   if constexpr (VEC == 8) {
-    uint4 t = *reinterpret_cast<const uint4 *>(p);
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+    u32x4 t;
+    if constexpr (NT) t = __builtin_nontemporal_load(q); else t = *q;
     r.w[0] = t.x; r.w[1] = t.y; r.w[2] = t.z; r.w[3] = t.w;
   } else if constexpr (VEC == 4) {
-    uint2 t = *reinterpret_cast<const uint2 *>(p);
+    const u32x2 *q = reinterpret_cast<const u32x2 *>(p);
+    u32x2 t;
+    if constexpr (NT) t = __builtin_nontemporal_load(q); else t = *q;
     r.w[0] = t.x; r.w[1] = t.y;
   } else if constexpr (VEC == 2) {
-    r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+    if constexpr (NT) r.w[0] = __builtin_nontemporal_load(q); else r.w[0] = *q;
   } else {
-    r.w[0] = *p;
+    if constexpr (NT) r.w[0] = __builtin_nontemporal_load(p); else r.w[0] = *p;
   }
   return r;
 }
@@ -229,6 +239,32 @@ __device__ __forceinline__ void ring_sum(const GradPtrs &g, uint32_t world,
   for (; j < world; ++j) add_up<VEC, DT>(s, ld16<VEC>(g.p[j] + i0));
 }
 
+/* The same ring-order sum for U vectors per thread. Loads are issued
+ * worker-major (all U vectors of one worker back to back, kLoadBatch
+ * workers ahead of the adds) and marked non-temporal. */
+template <int VEC, int U, int DT>
+__device__ __forceinline__ void ring_sum_u(const GradPtrs &g, uint32_t world,
+                                           const uint64_t (&i0)[U],
+                                           float (&s)[U][VEC]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) upcast<VEC, DT>(ld16<VEC, true>(g.p[0] + i0[u]), s[u]);
+  uint32_t j = 1;
+  for (; j + kLoadBatch <= world; j += kLoadBatch) {
+    Raw16<VEC> r[kLoadBatch][U];
+#pragma unroll
+    for (int b = 0; b < kLoadBatch; ++b)
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[b][u] = ld16<VEC, true>(g.p[j + b] + i0[u]);
+#pragma unroll
+    for (int b = 0; b < kLoadBatch; ++b)
+#pragma unroll
+      for (int u = 0; u < U; ++u) add_up<VEC, DT>(s[u], r[b][u]);
+  }
+  for (; j < world; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u) add_up<VEC, DT>(s[u], ld16<VEC, true>(g.p[j] + i0[u]));
+}
+
 /* Wave-level OR of the overflow flag: one vector atomic per wave that saw a
  * non-finite value, issued by its first such lane. */
 __device__ __forceinline__ void flag_or(uint32_t *flag, bool bad) {
@@ -241,7 +277,12 @@ __device__ __forceinline__ void flag_or(uint32_t *flag, bool bad) {
  * Kernels. Thread t of block b owns elements [i0, i0 + VEC) with
  * i0 = (b * kBlock + t) * VEC; the thread holding the ragged end (fewer
  * than VEC elements left) walks them one at a time with VEC = 1 accesses.
+ * The reducing kernels work on tiles of U vectors per thread: vector u of
+ * thread t in block b starts at ((b * U + u) * kBlock + t) * VEC, and only
+ * the last block, when the tile overhangs n, walks its elements one by one.
  * ---------------------------------------------------------------------- */
+
+constexpr int kTileVecs = 2;  /* U: vectors per thread in the reducing kernels */
 
 __device__ __forceinline__ uint64_t first_elem(int vec) {
   return ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * (uint64_t)vec;
@@ -274,15 +315,43 @@ __device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, uint64_t i0) {
   return bad;
 }
 
-template <int VEC, int DT>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
-  uint64_t i0 = first_elem(VEC);
-  if (i0 >= a.n) return;
+template <int VEC, int U, int DT>
+__device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, uint64_t base) {
+  uint64_t i0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
+  float s[U][VEC];
+  ring_sum_u<VEC, U, DT>(a.g, a.world, i0, s);
   bool bad = false;
-  if (i0 + VEC <= a.n) {
-    bad = reduce_vec<VEC, DT>(a, i0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float acc[VEC];
+    if (a.accumulate) ldf<VEC>(a.out + i0[u], acc);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float v = average(s[u][e], a.k);
+      if (a.accumulate) v = acc[e] + v;
+      s[u][e] = v;
+      bad |= !__builtin_isfinite(unscale(v, a.k));
+    }
+    stf<VEC>(a.out + i0[u], s[u]);
+  }
+  return bad;
+}
+
+template <int VEC, int U, int DT>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
+  const uint64_t tile = (uint64_t)kBlock * U * VEC;
+  const uint64_t base = (uint64_t)blockIdx.x * tile;
+  bool bad = false;
+  if (base + tile <= a.n) {
+    bad = reduce_tile<VEC, U, DT>(a, base);
   } else {
-    for (uint64_t i = i0; i < a.n; ++i) bad |= reduce_vec<1, DT>(a, i);
+    /* ragged last tile: element by element (one block; few registers) */
+    for (int u = 0; u < U; ++u) {
+      uint64_t i0 = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
+      for (uint64_t i = i0; i < i0 + VEC && i < a.n; ++i) bad |= reduce_vec<1, DT>(a, i);
+    }
   }
   if (a.flag) flag_or(a.flag, bad);
 }
@@ -405,15 +474,68 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
   return bad;
 }
 
-template <int VEC, int GDT, int PDT>
-__global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
-  uint64_t i0 = first_elem(VEC);
-  if (i0 >= p.n) return;
-  bool bad = false;
-  if (i0 + VEC <= p.n) {
-    bad = fused_vec<VEC, GDT, PDT>(p, i0);
+/* One tile of U vectors per thread. MULTI (W > 1) loads the state after
+ * the gradient sum, which keeps registers (and so waves in flight) for the
+ * gradient streams; with a single worker (W = 1) there is no sum, one
+ * gradient load, and the state loads go first. */
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT>
+__device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
+  uint64_t i0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
+  float th[U][VEC], m[U][VEC], v[U][VEC], acc[U][VEC], s[U][VEC];
+  auto load_state = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ldf<VEC>(p.master_in + i0[u], th[u]);
+      ldf<VEC>(p.m_in + i0[u], m[u]);
+      ldf<VEC>(p.v_in + i0[u], v[u]);
+      if constexpr (ACC) ldf<VEC>(p.acc_in + i0[u], acc[u]);
+    }
+  };
+  if constexpr (MULTI) {
+    ring_sum_u<VEC, U, GDT>(p.g, p.world, i0, s);
+    load_state();
   } else {
-    for (uint64_t i = i0; i < p.n; ++i) bad |= fused_vec<1, GDT, PDT>(p, i);
+    load_state();
+#pragma unroll
+    for (int u = 0; u < U; ++u) upcast<VEC, GDT>(ld16<VEC, true>(p.g.p[0] + i0[u]), s[u]);
+  }
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float a = average(s[u][e], p.k);
+      if constexpr (ACC) a = acc[u][e] + a;
+      float g = unscale(a, p.k);
+      bad |= !__builtin_isfinite(g);
+      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, p.h);
+    }
+    stf<VEC>(p.master_out + i0[u], th[u]);
+    stf<VEC>(p.m_out + i0[u], m[u]);
+    stf<VEC>(p.v_out + i0[u], v[u]);
+    st16<VEC, PDT>(p.param_out + i0[u], th[u]);
+  }
+  return bad;
+}
+
+/* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
+ * added before the unscale; a separate instance so the common case carries
+ * no registers for it. */
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT>
+__global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)kBlock * U * VEC;
+  const uint64_t base = (uint64_t)blockIdx.x * tile;
+  bool bad = false;
+  if (base + tile <= p.n) {
+    bad = fused_tile<VEC, U, MULTI, ACC, GDT, PDT>(p, base);
+  } else {
+    /* ragged last tile: element by element (one block; few registers) */
+    for (int u = 0; u < U; ++u) {
+      uint64_t i0 = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
+      for (uint64_t i = i0; i < i0 + VEC && i < p.n; ++i) bad |= fused_vec<1, GDT, PDT>(p, i);
+    }
   }
   flag_or(p.flag, bad);
 }
@@ -502,13 +624,14 @@ int pick_vec(const void *const *p16, int n16, const void *const *p32, int n32) {
   return 1;
 }
 
-unsigned grid_for(uint64_t n, int vec) {
-  uint64_t per_block = (uint64_t)kBlock * (uint64_t)vec;
+/* Blocks for n elements when every thread covers `per_thread` of them. */
+unsigned grid_for(uint64_t n, int per_thread) {
+  uint64_t per_block = (uint64_t)kBlock * (uint64_t)per_thread;
   return (unsigned)((n + per_block - 1) / per_block);
 }
 
-bool grid_ok(uint64_t n, int vec) {
-  uint64_t per_block = (uint64_t)kBlock * (uint64_t)vec;
+bool grid_ok(uint64_t n, int per_thread) {
+  uint64_t per_block = (uint64_t)kBlock * (uint64_t)per_thread;
   return (n + per_block - 1) / per_block <= 0x7fffffffull;
 }
 
@@ -589,10 +712,12 @@ int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
   a.accumulate = accumulate ? 1 : 0;
   const void *f32[] = {grad_part};
   int vec = pick_vec(reinterpret_cast<const void *const *>(a.g.p), (int)world, f32, 1);
-  if (!grid_ok(n, vec)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
+  const int per_thread = vec * kTileVecs;
+  if (!grid_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(grid_for(n, vec)), block(kBlock);
-#define ZS_LAUNCH_REDUCE(V, D) hipLaunchKernelGGL((reduce_kernel<V, D>), grid, block, 0, s, a)
+  dim3 grid(grid_for(n, per_thread)), block(kBlock);
+#define ZS_LAUNCH_REDUCE(V, D) \
+  hipLaunchKernelGGL((reduce_kernel<V, kTileVecs, D>), grid, block, 0, s, a)
   if (grad_dtype == ZS_BF16) {
     switch (vec) {
       case 8: ZS_LAUNCH_REDUCE(8, ZS_BF16); break;
@@ -760,10 +885,22 @@ int zs_step_fused(const zs_step_args *a, void *stream) {
   const void *f32[] = {a->master_in, a->m_in, a->v_in, a->master_out, a->m_out,
                        a->v_out, a->acc_in ? a->acc_in : a->master_in};
   int vec = pick_vec(p16, (int)a->world + 1, f32, 7);
-  if (!grid_ok(n, vec)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
+  const int per_thread = vec * kTileVecs;
+  if (!grid_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(grid_for(n, vec)), block(kBlock);
-#define ZS_LAUNCH_FUSED(V, G, P) hipLaunchKernelGGL((fused_kernel<V, G, P>), grid, block, 0, s, p)
+  dim3 grid(grid_for(n, per_thread)), block(kBlock);
+  const int mode = (a->world > 1 ? 1 : 0) | (a->acc_in ? 2 : 0);
+#define ZS_FUSED_K(V, L, A, G, P) \
+  hipLaunchKernelGGL((fused_kernel<V, kTileVecs, L, A, G, P>), grid, block, 0, s, p)
+#define ZS_LAUNCH_FUSED(V, G, P)                          \
+  do {                                                    \
+    switch (mode) {                                       \
+      case 0: ZS_FUSED_K(V, false, false, G, P); break;   \
+      case 1: ZS_FUSED_K(V, true, false, G, P); break;    \
+      case 2: ZS_FUSED_K(V, false, true, G, P); break;    \
+      default: ZS_FUSED_K(V, true, true, G, P); break;    \
+    }                                                     \
+  } while (0)
 #define ZS_FUSED_VEC(G, P)                  \
   switch (vec) {                            \
     case 8: ZS_LAUNCH_FUSED(8, G, P); break; \
@@ -782,6 +919,7 @@ int zs_step_fused(const zs_step_args *a, void *stream) {
   }
 #undef ZS_FUSED_VEC
 #undef ZS_LAUNCH_FUSED
+#undef ZS_FUSED_K
   return launch_result();
 }
 

@@ -55,8 +55,10 @@ def run_workload(env, name, windows=None, gather_full=False):
                           wl.loss_scale, dynamic=wl.dynamic_scale,
                           growth_interval=wl.scale_interval, accumulate=A > 1)
     synth.dev_state(wl, off, st.master, st.m, st.v)
-    grads = torch.empty((W, n), dtype=torch.int16, device="cuda")
-    gviews = [grads[k] for k in range(W)]
+    # one row per worker, padded to 256 B like separate allocations
+    row = -(-n // 128) * 128
+    grads = torch.empty((W, row), dtype=torch.int16, device="cuda")
+    gviews = [grads[k, :n] for k in range(W)]
     gdt = wl.grad_dtype
     # host-side oracle state per window
     hs = [list(synth.host_state(wl, off + s, L)) for s, L in wins]
