@@ -33,14 +33,45 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak (vendor figure)
 DEFAULT_WORKLOAD = "gpt2s-w8"   # GPT-2-small-shaped flat model, W = 8
 DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1"
-KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zeroshard.hip")
+KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zs_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.md")
+EVENT_EVERY = 2
 METRIC = "params updated/sec per ZeRO-2 shard step + achieved HBM GB/s (% of peak)"
 
 
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (libamdhip64 through ctypes). The library's
+    zs_step_commit records them on the launch stream immediately before and
+    after the fused kernel."""
+
+    def __init__(self):
+        import ctypes
+        self.C = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.C.c_void_p()
+        if self.lib.hipEventCreate(self.C.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, start, stop):
+        ms = self.C.c_float()
+        if self.lib.hipEventElapsedTime(self.C.byref(ms), start, stop) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
 
 
 def kernel_source_hash():
@@ -119,33 +150,37 @@ def run_workload(name, steps, warmup, torch):
             for k in range(W):
                 synth.dev_grad(wl, k, 1 + r, j, wl.offset, views[j][k], scale=wl.loss_scale)
         reps.append((st, views))
+    for st, g in reps:
+        st.bind(g[A - 1], acc_in=st.acc if A > 1 else None)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    hip = HipEvents()
 
     def one_step(i, events=None):
         st, g = reps[i % R]
         for j in range(A - 1):
             st.reduce_micro(g[j], first=(j == 0))
-        if events is not None:
-            events[0].record(stream)
-        flag = st.launch(g[A - 1], acc_in=st.acc if A > 1 else None)
-        if events is not None:
-            events[1].record(stream)
-        return st.finish(flag)
+        if events is None:
+            return st.step()
+        return st.step(ev_start=events[0], ev_stop=events[1])
 
     for i in range(warmup):
         one_step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    # HIP events bracket the fused kernel on every EVENT_EVERY-th timed step
+    # (recording them costs a few microseconds per step)
+    timed = list(range(0, steps, EVENT_EVERY))
+    evs = {i: (hip.create(), hip.create()) for i in timed}
     committed = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        committed += one_step(warmup + i, evs[i])
+        committed += one_step(warmup + i, evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in evs]
+    kern_ms = [hip.elapsed_ms(*evs[i]) for i in timed]
+    for s, e in evs.values():
+        hip.destroy(s)
+        hip.destroy(e)
     kern_avg = sum(kern_ms) / len(kern_ms)
     ms_per_step = elapsed * 1e3 / steps
     res = dict(workload=name, n=n, world=W, accum=A, replicas=R,
@@ -172,15 +207,17 @@ def cpu_baseline(name, target_s=12.0):
               weight_decay=wl.weight_decay, loss_scale=wl.loss_scale, step_t=1)
 
     def timed(ns, reps):
-        steps = []
-        for r in range(reps):
+        # distinct inputs for up to the workload's step count, then cycled
+        distinct = []
+        for r in range(min(reps, wl.steps)):
             micro = [[synth.host_grad(wl, k, 1 + r, j, wl.offset, ns) for k in range(wl.world)]
                      for j in range(wl.accum)]
-            steps.append(micro)
+            distinct.append(micro)
         master, m, v = synth.host_state(wl, wl.offset, ns)
         acc = np.empty(ns, np.float32) if wl.accum > 1 else None
         t0 = time.perf_counter()
-        for micro in steps:
+        for r in range(reps):
+            micro = distinct[r % len(distinct)]
             for j, parts in enumerate(micro[:-1]):
                 oracle.reduce_avg(parts, wl.rank, wl.grad_dtype, acc, j > 0, wl.loss_scale)
             oracle.shard_step(micro[-1], wl.rank, wl.grad_dtype, wl.param_dtype, master, m, v,
@@ -193,7 +230,7 @@ def cpu_baseline(name, target_s=12.0):
     cap = (6 << 30) // (2 * wl.world * wl.accum + 30)
     want = int(probe * target_s / max(dt, 1e-6))
     ns = int(min(wl.n, cap, max(probe, want)))
-    reps = max(1, min(wl.steps, int(want // ns)))
+    reps = max(1, min(1000, int(want // ns)))
     dt = timed(ns, reps)
     return dict(value=ns * reps / dt, unit="params/s", cores=threads, kind="oracle",
                 sample=f"{ns} params of the {name} rank-{wl.rank} partition (W={wl.world}, "

@@ -197,6 +197,27 @@ typedef struct {
 
 int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow);
 
+/* One committed-or-skipped optimizer step, synchronously: the commit-or-skip
+ * decision of dynamic loss scaling ([Intro] 一.3 items (1) and (3)) taken on
+ * the host right after the fused pass, with one 4-byte device-to-host copy.
+ *   1. zs_step_fused(a) with a->hp.loss_scale and a->hp.step_t replaced by
+ *      scaler->scale and scaler->step_t + 1 (the other fields of a->hp are
+ *      used as given);
+ *   2. the uint32 at a->overflow_flag is copied to *host_flag (host memory;
+ *      page-locked memory avoids a staging copy) and the call waits for it
+ *      (busy-polling the host word and the stream) -- unlike the other
+ *      kernel entry points, this call blocks until the step is done;
+ *   3. zs_scaler_update(scaler, flag); *committed = (flag == 0).
+ * The caller then swaps the input and output sets when *committed is 1.
+ * ev_start / ev_stop: NULL, or hipEvent_t handles recorded on `stream`
+ * immediately before and after the fused kernel (for timing). Errors: as zs_step_fused;
+ * ZS_ERR_INVALID_ARG for a NULL scaler, host_flag or committed, or a
+ * non-finite / non-positive scale; ZS_ERR_HIP if the copy or the
+ * synchronization fails (including an earlier kernel fault on the stream);
+ * on any error the scaler is left unchanged. */
+int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
+                   void *stream, void *ev_start, void *ev_stop, int *committed);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,28 +1,12 @@
 /*
  * zeroshard.hip -- libzeroshard: the per-rank ZeRO-2 optimizer-shard step for
- * AMD Instinct MI355X (gfx950, CDNA4). The C ABI is declared and documented in
- * include/zeroshard.h; the sources it cites are listed there:
- *   [Notes] lecture notes on DP / DDP / DeepSpeed ZeRO (gitcode.csdn.net)
- *   [Intro] "并行训练框架DeepSpeed介绍"
- *   [L7]    "第 7 讲：Parallelism（上）" (CS336 lecture 7)
- *
- * Design (all kernels are HBM-bandwidth bound; nothing here is a dense
- * contraction, so there is no MFMA):
- *   - one 64-bit element index per thread-vector; each thread owns VEC
- *     consecutive elements (VEC = 8 when every operand is 16-byte aligned:
- *     128-bit loads of 16-bit gradients, 2 x 128-bit loads of fp32 state);
- *   - the W-way gradient sum runs in fp32 registers in the fixed ring order,
- *     with loads issued in batches ahead of the in-order adds;
- *   - the overflow flag is a wave ballot, one vector atomic OR per wave that
- *     saw a non-finite value;
- *   - 16-bit outputs use the hardware round-to-nearest-even converts
- *     (v_cvt_pk_bf16_f32, v_cvt_f16_f32);
- *   - built with -ffp-contract=off: every arithmetic operator is one IEEE
- *     binary32 operation; division and square root are the correctly rounded
- *     sequences, denormals are kept.
+ * AMD Instinct MI355X (gfx950, CDNA4). Host side: argument validation,
+ * per-step scalars, vector-width choice, launches and the C ABI declared and
+ * documented in include/zeroshard.h. The device code is in zs_kernels.h.
  */
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -30,517 +14,8 @@
 
 #include "zeroshard.h"
 
-namespace zs {
+#include "zs_kernels.h"
 
-constexpr int kBlock = 256;     /* threads per workgroup (4 waves of 64)   */
-constexpr int kLoadBatch = 8;   /* gradient vectors in flight per thread   */
-
-/* ------------------------------------------------------------------------
- * Per-element arithmetic. Each line is written exactly in the order the
- * header documents; with contraction off, each operator rounds once.
- * ---------------------------------------------------------------------- */
-
-struct AdamK {
-  float alpha, b2, delta, c1, c2, beta1, beta2, eps;
-};
-
-struct Scales {
-  float wf, inv_w;      /* world as float; 2^-k when world = 2^k         */
-  float sf, inv_s;      /* loss scale; 2^-k when it is 2^k               */
-  int w_pow2, s_pow2;   /* multiply by the exact reciprocal instead      */
-};
-
-__device__ __forceinline__ float average(float s, const Scales &k) {
-  /* s / W; for W = 2^k the product with 2^-k is the same correctly
-   * rounded value, without the division sequence. */
-  return k.w_pow2 ? s * k.inv_w : s / k.wf;
-}
-
-__device__ __forceinline__ float unscale(float a, const Scales &k) {
-  return k.s_pow2 ? a * k.inv_s : a / k.sf;
-}
-
-__device__ __forceinline__ float adamw_elem(float theta, float &m, float &v,
-                                            float g, const AdamK &k) {
-  float decayed = theta * k.delta;             /* decoupled weight decay  */
-  float m1 = k.beta1 * m + k.c1 * g;           /* first moment            */
-  float v1 = k.beta2 * v + k.c2 * (g * g);     /* second moment           */
-  float d = sqrtf(v1) / k.b2 + k.eps;          /* bias-corrected rms      */
-  float out = decayed - k.alpha * (m1 / d);    /* alpha = lr / (1-b1^t)   */
-  m = m1;
-  v = v1;
-  return out;
-}
-
-/* ------------------------------------------------------------------------
- * 16-bit formats. A 32-bit word holds elements 2j (low half) and 2j+1.
- * ---------------------------------------------------------------------- */
-
-template <int DT>
-__device__ __forceinline__ float up_lo(uint32_t w) {
-  if constexpr (DT == ZS_BF16) return __uint_as_float(w << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-}
-
-template <int DT>
-__device__ __forceinline__ float up_hi(uint32_t w) {
-  if constexpr (DT == ZS_BF16) return __uint_as_float(w & 0xffff0000u);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-/* Two fp32 -> one word of two 16-bit values, round to nearest even. */
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  f32x2 f = {lo, hi};
-  if constexpr (DT == ZS_BF16)
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-  else
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-}
-
-template <int DT>
-__device__ __forceinline__ uint16_t pack1(float x) {
-  if constexpr (DT == ZS_BF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
-  else return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
-
-/* ------------------------------------------------------------------------
- * Vector loads / stores of VEC elements (VEC in {8, 4, 2, 1}).
- * ---------------------------------------------------------------------- */
-
-template <int VEC>
-struct Raw16 {                         /* VEC 16-bit values, as loaded      */
-  uint32_t w[VEC / 2 > 0 ? VEC / 2 : 1];
-};
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-/* NT = true marks the load non-temporal: gradients are read exactly once,
- * so they should not displace cache lines that are. */
-template <int VEC, bool NT = false>
-__device__ __forceinline__ Raw16<VEC> ld16(const uint16_t *__restrict__ p) {
-  Raw16<VEC> r;
-  if constexpr (VEC == 8) {
-    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
-    u32x4 t;
-    if constexpr (NT) t = __builtin_nontemporal_load(q); else t = *q;
-    r.w[0] = t.x; r.w[1] = t.y; r.w[2] = t.z; r.w[3] = t.w;
-  } else if constexpr (VEC == 4) {
-    const u32x2 *q = reinterpret_cast<const u32x2 *>(p);
-    u32x2 t;
-    if constexpr (NT) t = __builtin_nontemporal_load(q); else t = *q;
-    r.w[0] = t.x; r.w[1] = t.y;
-  } else if constexpr (VEC == 2) {
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-    if constexpr (NT) r.w[0] = __builtin_nontemporal_load(q); else r.w[0] = *q;
-  } else {
-    if constexpr (NT) r.w[0] = __builtin_nontemporal_load(p); else r.w[0] = *p;
-  }
-  return r;
-}
-
-template <int VEC, int DT>
-__device__ __forceinline__ void upcast(const Raw16<VEC> &r, float (&x)[VEC]) {
-  if constexpr (VEC == 1) {
-    x[0] = up_lo<DT>(r.w[0]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < VEC / 2; ++j) {
-      x[2 * j] = up_lo<DT>(r.w[j]);
-      x[2 * j + 1] = up_hi<DT>(r.w[j]);
-    }
-  }
-}
-
-template <int VEC, int DT>
-__device__ __forceinline__ void add_up(float (&s)[VEC], const Raw16<VEC> &r) {
-  float x[VEC];
-  upcast<VEC, DT>(r, x);
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) s[e] = s[e] + x[e];
-}
-
-template <int VEC>
-__device__ __forceinline__ void ldf(const float *__restrict__ p, float (&x)[VEC]) {
-  if constexpr (VEC == 8) {
-    float4 a = *reinterpret_cast<const float4 *>(p);
-    float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  } else if constexpr (VEC == 4) {
-    float4 a = *reinterpret_cast<const float4 *>(p);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  } else if constexpr (VEC == 2) {
-    float2 a = *reinterpret_cast<const float2 *>(p);
-    x[0] = a.x; x[1] = a.y;
-  } else {
-    x[0] = *p;
-  }
-}
-
-template <int VEC>
-__device__ __forceinline__ void stf(float *__restrict__ p, const float (&x)[VEC]) {
-  if constexpr (VEC == 8) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
-  } else if constexpr (VEC == 4) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  } else if constexpr (VEC == 2) {
-    *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
-  } else {
-    *p = x[0];
-  }
-}
-
-template <int VEC, int DT>
-__device__ __forceinline__ void st16(uint16_t *__restrict__ p, const float (&x)[VEC]) {
-  if constexpr (VEC == 8) {
-    *reinterpret_cast<uint4 *>(p) =
-        make_uint4(pack2<DT>(x[0], x[1]), pack2<DT>(x[2], x[3]),
-                   pack2<DT>(x[4], x[5]), pack2<DT>(x[6], x[7]));
-  } else if constexpr (VEC == 4) {
-    *reinterpret_cast<uint2 *>(p) =
-        make_uint2(pack2<DT>(x[0], x[1]), pack2<DT>(x[2], x[3]));
-  } else if constexpr (VEC == 2) {
-    *reinterpret_cast<uint32_t *>(p) = pack2<DT>(x[0], x[1]);
-  } else {
-    *p = pack1<DT>(x[0]);
-  }
-}
-
-/* ------------------------------------------------------------------------
- * Ring-order sum. g.p[j] is worker (rank + 1 + j) mod W, so summing
- * p[0], p[1], ..., p[W-1] left to right adds the owner's term last: the
- * order in which the ring's running partial for this chunk visits the
- * workers ([Notes] 二 three-GPU example; [L7] "Ring AllReduce 算法").
- * ---------------------------------------------------------------------- */
-
-struct GradPtrs {
-  const uint16_t *p[ZS_MAX_WORLD];
-};
-
-template <int VEC, int DT>
-__device__ __forceinline__ void ring_sum(const GradPtrs &g, uint32_t world,
-                                         uint64_t i0, float (&s)[VEC]) {
-  upcast<VEC, DT>(ld16<VEC>(g.p[0] + i0), s);
-  uint32_t j = 1;
-  for (; j + kLoadBatch <= world; j += kLoadBatch) {
-    Raw16<VEC> r[kLoadBatch];
-#pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b) r[b] = ld16<VEC>(g.p[j + b] + i0);
-#pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b) add_up<VEC, DT>(s, r[b]);
-  }
-  for (; j < world; ++j) add_up<VEC, DT>(s, ld16<VEC>(g.p[j] + i0));
-}
-
-/* The same ring-order sum for U vectors per thread. Loads are issued
- * worker-major (all U vectors of one worker back to back, kLoadBatch
- * workers ahead of the adds) and marked non-temporal. */
-template <int VEC, int U, int DT>
-__device__ __forceinline__ void ring_sum_u(const GradPtrs &g, uint32_t world,
-                                           const uint64_t (&i0)[U],
-                                           float (&s)[U][VEC]) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) upcast<VEC, DT>(ld16<VEC, true>(g.p[0] + i0[u]), s[u]);
-  uint32_t j = 1;
-  for (; j + kLoadBatch <= world; j += kLoadBatch) {
-    Raw16<VEC> r[kLoadBatch][U];
-#pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b)
-#pragma unroll
-      for (int u = 0; u < U; ++u) r[b][u] = ld16<VEC, true>(g.p[j + b] + i0[u]);
-#pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b)
-#pragma unroll
-      for (int u = 0; u < U; ++u) add_up<VEC, DT>(s[u], r[b][u]);
-  }
-  for (; j < world; ++j)
-#pragma unroll
-    for (int u = 0; u < U; ++u) add_up<VEC, DT>(s[u], ld16<VEC, true>(g.p[j] + i0[u]));
-}
-
-/* Wave-level OR of the overflow flag: one vector atomic per wave that saw a
- * non-finite value, issued by its first such lane. */
-__device__ __forceinline__ void flag_or(uint32_t *flag, bool bad) {
-  unsigned long long m = __ballot(bad);
-  if (m && bad && (threadIdx.x & 63u) == (unsigned)(__ffsll(m) - 1))
-    atomicOr(flag, 1u);
-}
-
-/* ------------------------------------------------------------------------
- * Kernels. Thread t of block b owns elements [i0, i0 + VEC) with
- * i0 = (b * kBlock + t) * VEC; the thread holding the ragged end (fewer
- * than VEC elements left) walks them one at a time with VEC = 1 accesses.
- * The reducing kernels work on tiles of U vectors per thread: vector u of
- * thread t in block b starts at ((b * U + u) * kBlock + t) * VEC, and only
- * the last block, when the tile overhangs n, walks its elements one by one.
- * ---------------------------------------------------------------------- */
-
-constexpr int kTileVecs = 2;  /* U: vectors per thread in the reducing kernels */
-
-__device__ __forceinline__ uint64_t first_elem(int vec) {
-  return ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * (uint64_t)vec;
-}
-
-struct ReduceArgs {
-  GradPtrs g;
-  uint32_t world;
-  uint64_t n;
-  float *out;
-  uint32_t *flag;  /* may be null */
-  int accumulate;
-  Scales k;
-};
-
-template <int VEC, int DT>
-__device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, uint64_t i0) {
-  float s[VEC], acc[VEC];
-  if (a.accumulate) ldf<VEC>(a.out + i0, acc);
-  ring_sum<VEC, DT>(a.g, a.world, i0, s);
-  bool bad = false;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    float v = average(s[e], a.k);
-    if (a.accumulate) v = acc[e] + v;
-    s[e] = v;
-    bad |= !__builtin_isfinite(unscale(v, a.k));
-  }
-  stf<VEC>(a.out + i0, s);
-  return bad;
-}
-
-template <int VEC, int U, int DT>
-__device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, uint64_t base) {
-  uint64_t i0[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
-  float s[U][VEC];
-  ring_sum_u<VEC, U, DT>(a.g, a.world, i0, s);
-  bool bad = false;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float acc[VEC];
-    if (a.accumulate) ldf<VEC>(a.out + i0[u], acc);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float v = average(s[u][e], a.k);
-      if (a.accumulate) v = acc[e] + v;
-      s[u][e] = v;
-      bad |= !__builtin_isfinite(unscale(v, a.k));
-    }
-    stf<VEC>(a.out + i0[u], s[u]);
-  }
-  return bad;
-}
-
-template <int VEC, int U, int DT>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
-  const uint64_t tile = (uint64_t)kBlock * U * VEC;
-  const uint64_t base = (uint64_t)blockIdx.x * tile;
-  bool bad = false;
-  if (base + tile <= a.n) {
-    bad = reduce_tile<VEC, U, DT>(a, base);
-  } else {
-    /* ragged last tile: element by element (one block; few registers) */
-    for (int u = 0; u < U; ++u) {
-      uint64_t i0 = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
-      for (uint64_t i = i0; i < i0 + VEC && i < a.n; ++i) bad |= reduce_vec<1, DT>(a, i);
-    }
-  }
-  if (a.flag) flag_or(a.flag, bad);
-}
-
-struct CheckArgs {
-  const float *a;
-  uint64_t n;
-  uint32_t *flag;
-  Scales k;
-};
-
-template <int VEC>
-__global__ __launch_bounds__(kBlock) void check_kernel(CheckArgs c) {
-  uint64_t i0 = first_elem(VEC);
-  if (i0 >= c.n) return;
-  bool bad = false;
-  if (i0 + VEC <= c.n) {
-    float x[VEC];
-    ldf<VEC>(c.a + i0, x);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) bad |= !__builtin_isfinite(unscale(x[e], c.k));
-  } else {
-    for (uint64_t i = i0; i < c.n; ++i)
-      bad |= !__builtin_isfinite(unscale(c.a[i], c.k));
-  }
-  flag_or(c.flag, bad);
-}
-
-struct AdamArgs {
-  float *master, *m, *v;
-  const float *a;
-  uint64_t n;
-  const uint32_t *flag;  /* may be null */
-  Scales k;
-  AdamK h;
-};
-
-template <int VEC>
-__device__ __forceinline__ void adam_vec(const AdamArgs &p, uint64_t i0) {
-  float th[VEC], m[VEC], v[VEC], a[VEC];
-  ldf<VEC>(p.master + i0, th);
-  ldf<VEC>(p.m + i0, m);
-  ldf<VEC>(p.v + i0, v);
-  ldf<VEC>(p.a + i0, a);
-#pragma unroll
-  for (int e = 0; e < VEC; ++e)
-    th[e] = adamw_elem(th[e], m[e], v[e], unscale(a[e], p.k), p.h);
-  stf<VEC>(p.master + i0, th);
-  stf<VEC>(p.m + i0, m);
-  stf<VEC>(p.v + i0, v);
-}
-
-template <int VEC>
-__global__ __launch_bounds__(kBlock) void adamw_kernel(AdamArgs p) {
-  if (p.flag && *p.flag) return;  /* overflow: the step is skipped */
-  uint64_t i0 = first_elem(VEC);
-  if (i0 >= p.n) return;
-  if (i0 + VEC <= p.n) {
-    adam_vec<VEC>(p, i0);
-  } else {
-    for (uint64_t i = i0; i < p.n; ++i) adam_vec<1>(p, i);
-  }
-}
-
-struct CastArgs {
-  const float *master;
-  uint16_t *out;  /* already at this rank's offset */
-  uint64_t n;
-  const uint32_t *flag;
-};
-
-template <int VEC, int DT>
-__global__ __launch_bounds__(kBlock) void cast_kernel(CastArgs c) {
-  if (c.flag && *c.flag) return;
-  uint64_t i0 = first_elem(VEC);
-  if (i0 >= c.n) return;
-  if (i0 + VEC <= c.n) {
-    float x[VEC];
-    ldf<VEC>(c.master + i0, x);
-    st16<VEC, DT>(c.out + i0, x);
-  } else {
-    for (uint64_t i = i0; i < c.n; ++i) c.out[i] = pack1<DT>(c.master[i]);
-  }
-}
-
-struct FusedArgs {
-  GradPtrs g;
-  uint32_t world;
-  uint64_t n;
-  const float *acc_in;  /* may be null */
-  const float *master_in, *m_in, *v_in;
-  float *master_out, *m_out, *v_out;
-  uint16_t *param_out;  /* already at this rank's offset */
-  uint32_t *flag;
-  Scales k;
-  AdamK h;
-};
-
-template <int VEC, int GDT, int PDT>
-__device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
-  float th[VEC], m[VEC], v[VEC], acc[VEC], s[VEC];
-  ldf<VEC>(p.master_in + i0, th);
-  ldf<VEC>(p.m_in + i0, m);
-  ldf<VEC>(p.v_in + i0, v);
-  if (p.acc_in) ldf<VEC>(p.acc_in + i0, acc);
-  ring_sum<VEC, GDT>(p.g, p.world, i0, s);
-  bool bad = false;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    float a = average(s[e], p.k);
-    if (p.acc_in) a = acc[e] + a;
-    float g = unscale(a, p.k);
-    bad |= !__builtin_isfinite(g);
-    th[e] = adamw_elem(th[e], m[e], v[e], g, p.h);
-  }
-  stf<VEC>(p.master_out + i0, th);
-  stf<VEC>(p.m_out + i0, m);
-  stf<VEC>(p.v_out + i0, v);
-  st16<VEC, PDT>(p.param_out + i0, th);
-  return bad;
-}
-
-/* One tile of U vectors per thread. MULTI (W > 1) loads the state after
- * the gradient sum, which keeps registers (and so waves in flight) for the
- * gradient streams; with a single worker (W = 1) there is no sum, one
- * gradient load, and the state loads go first. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT>
-__device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
-  uint64_t i0[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
-  float th[U][VEC], m[U][VEC], v[U][VEC], acc[U][VEC], s[U][VEC];
-  auto load_state = [&]() {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ldf<VEC>(p.master_in + i0[u], th[u]);
-      ldf<VEC>(p.m_in + i0[u], m[u]);
-      ldf<VEC>(p.v_in + i0[u], v[u]);
-      if constexpr (ACC) ldf<VEC>(p.acc_in + i0[u], acc[u]);
-    }
-  };
-  if constexpr (MULTI) {
-    ring_sum_u<VEC, U, GDT>(p.g, p.world, i0, s);
-    load_state();
-  } else {
-    load_state();
-#pragma unroll
-    for (int u = 0; u < U; ++u) upcast<VEC, GDT>(ld16<VEC, true>(p.g.p[0] + i0[u]), s[u]);
-  }
-  bool bad = false;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float a = average(s[u][e], p.k);
-      if constexpr (ACC) a = acc[u][e] + a;
-      float g = unscale(a, p.k);
-      bad |= !__builtin_isfinite(g);
-      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, p.h);
-    }
-    stf<VEC>(p.master_out + i0[u], th[u]);
-    stf<VEC>(p.m_out + i0[u], m[u]);
-    stf<VEC>(p.v_out + i0[u], v[u]);
-    st16<VEC, PDT>(p.param_out + i0[u], th[u]);
-  }
-  return bad;
-}
-
-/* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
- * added before the unscale; a separate instance so the common case carries
- * no registers for it. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT>
-__global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
-  const uint64_t tile = (uint64_t)kBlock * U * VEC;
-  const uint64_t base = (uint64_t)blockIdx.x * tile;
-  bool bad = false;
-  if (base + tile <= p.n) {
-    bad = fused_tile<VEC, U, MULTI, ACC, GDT, PDT>(p, base);
-  } else {
-    /* ragged last tile: element by element (one block; few registers) */
-    for (int u = 0; u < U; ++u) {
-      uint64_t i0 = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
-      for (uint64_t i = i0; i < i0 + VEC && i < p.n; ++i) bad |= fused_vec<1, GDT, PDT>(p, i);
-    }
-  }
-  flag_or(p.flag, bad);
-}
-
-}  // namespace zs
 
 namespace {
 
@@ -565,6 +40,9 @@ int launch_result() {
 }
 
 bool valid_dtype(int dt) { return dt == ZS_BF16 || dt == ZS_FP16; }
+
+/* zs_step_commit polls the stream for errors this often while it waits. */
+constexpr int kQueryMicros = 1000;
 
 /* Exact power of two with a normal reciprocal: then x * (1/p) == x / p. */
 bool exact_pow2(float p, float *inv) {
@@ -623,6 +101,17 @@ int pick_vec(const void *const *p16, int n16, const void *const *p32, int n32) {
   }
   return 1;
 }
+
+/* Tiled kernels: floor(n / tile) full tiles plus one block per kBlock
+ * elements of the remainder. */
+uint64_t tiled_blocks(uint64_t n, int per_thread) {
+  uint64_t tile = (uint64_t)kBlock * (uint64_t)per_thread;
+  return n / tile + ((n % tile) + kBlock - 1) / kBlock;
+}
+
+unsigned tiled_grid(uint64_t n, int per_thread) { return (unsigned)tiled_blocks(n, per_thread); }
+
+bool tiled_ok(uint64_t n, int per_thread) { return tiled_blocks(n, per_thread) <= 0x7fffffffull; }
 
 /* Blocks for n elements when every thread covers `per_thread` of them. */
 unsigned grid_for(uint64_t n, int per_thread) {
@@ -713,9 +202,9 @@ int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
   const void *f32[] = {grad_part};
   int vec = pick_vec(reinterpret_cast<const void *const *>(a.g.p), (int)world, f32, 1);
   const int per_thread = vec * kTileVecs;
-  if (!grid_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
+  if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(grid_for(n, per_thread)), block(kBlock);
+  dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
 #define ZS_LAUNCH_REDUCE(V, D) \
   hipLaunchKernelGGL((reduce_kernel<V, kTileVecs, D>), grid, block, 0, s, a)
   if (grad_dtype == ZS_BF16) {
@@ -830,7 +319,10 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
   return launch_result();
 }
 
-int zs_step_fused(const zs_step_args *a, void *stream) {
+/* zs_step_fused with optional start/stop events recorded on the stream
+ * immediately before and after the kernel launch. */
+static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop) {
   if (!a) return fail(ZS_ERR_INVALID_ARG, "null args%s");
   if (!a->worker_grads || !a->master_in || !a->m_in || !a->v_in || !a->master_out ||
       !a->m_out || !a->v_out || !a->gather_buf || !a->overflow_flag)
@@ -886,9 +378,9 @@ int zs_step_fused(const zs_step_args *a, void *stream) {
                        a->v_out, a->acc_in ? a->acc_in : a->master_in};
   int vec = pick_vec(p16, (int)a->world + 1, f32, 7);
   const int per_thread = vec * kTileVecs;
-  if (!grid_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
+  if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(grid_for(n, per_thread)), block(kBlock);
+  dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
   const int mode = (a->world > 1 ? 1 : 0) | (a->acc_in ? 2 : 0);
 #define ZS_FUSED_K(V, L, A, G, P) \
   hipLaunchKernelGGL((fused_kernel<V, kTileVecs, L, A, G, P>), grid, block, 0, s, p)
@@ -908,6 +400,10 @@ int zs_step_fused(const zs_step_args *a, void *stream) {
     case 2: ZS_LAUNCH_FUSED(2, G, P); break; \
     default: ZS_LAUNCH_FUSED(1, G, P); break; \
   }
+  if (ev_start) {
+    hipError_t e = hipEventRecord(ev_start, s);
+    if (e != hipSuccess) return fail(ZS_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  }
   if (a->grad_dtype == ZS_BF16 && a->param_dtype == ZS_BF16) {
     ZS_FUSED_VEC(ZS_BF16, ZS_BF16)
   } else if (a->grad_dtype == ZS_FP16 && a->param_dtype == ZS_FP16) {
@@ -920,7 +416,64 @@ int zs_step_fused(const zs_step_args *a, void *stream) {
 #undef ZS_FUSED_VEC
 #undef ZS_LAUNCH_FUSED
 #undef ZS_FUSED_K
-  return launch_result();
+  int launched = launch_result();
+  if (launched == ZS_OK && ev_stop) {
+    hipError_t e = hipEventRecord(ev_stop, s);
+    if (e != hipSuccess) return fail(ZS_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  }
+  return launched;
+}
+
+int zs_step_fused(const zs_step_args *a, void *stream) {
+  return step_fused_impl(a, stream, nullptr, nullptr);
+}
+
+int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
+                   void *stream, void *ev_start, void *ev_stop, int *committed) {
+  if (!a || !scaler || !host_flag || !committed)
+    return fail(ZS_ERR_INVALID_ARG, "null args, scaler, host_flag or committed%s");
+  if (!(scaler->scale > 0.0f) || !isfinite(scaler->scale))
+    return fail(ZS_ERR_INVALID_ARG, "scaler->scale must be finite and > 0%s");
+  if (scaler->step_t >= 0xffffffffull)
+    return fail(ZS_ERR_UNSUPPORTED, "step count exceeds 32 bits%s");
+  zs_step_args local = *a;
+  local.hp.loss_scale = scaler->scale;
+  local.hp.step_t = (uint32_t)(scaler->step_t + 1);
+  int rc = step_fused_impl(&local, stream, static_cast<hipEvent_t>(ev_start),
+                           static_cast<hipEvent_t>(ev_stop));
+  if (rc != ZS_OK) return rc;
+  if (a->n == 0) {
+    *committed = 1;
+    return zs_scaler_update(scaler, 0);
+  }
+  /* The flag is only ever 0 or 1, so a sentinel in host memory shows when
+   * the 4-byte copy (stream-ordered after the kernel) has landed: the call
+   * spins on that word, which returns sooner than a blocking stream
+   * synchronization, and queries the stream once per kQueryMicros so that
+   * a failed stream ends the wait with an error instead of a hang. */
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  volatile uint32_t *hf = host_flag;
+  const uint32_t kSentinel = 0xffffffffu;
+  *hf = kSentinel;
+  hipError_t e = hipMemcpyAsync(host_flag, a->overflow_flag, sizeof(uint32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return fail(ZS_ERR_HIP, "flag readback failed: %s", hipGetErrorString(e));
+  auto last = std::chrono::steady_clock::now();
+  const auto every = std::chrono::microseconds(kQueryMicros);
+  for (uint32_t spins = 1; *hf == kSentinel; ++spins) {
+    if ((spins & 1023u) != 0) continue;
+    auto now = std::chrono::steady_clock::now();
+    if (now - last < every) continue;
+    last = now;
+    hipError_t q = hipStreamQuery(s);
+    if (q == hipErrorNotReady) continue;
+    if (q != hipSuccess)
+      return fail(ZS_ERR_HIP, "stream failed before the flag arrived: %s", hipGetErrorString(q));
+    if (*hf == kSentinel) return fail(ZS_ERR_HIP, "flag readback did not arrive%s");
+  }
+  uint32_t flag = *hf;
+  *committed = flag == 0;
+  return zs_scaler_update(scaler, flag);
 }
 
 int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow) {

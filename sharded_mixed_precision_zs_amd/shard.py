@@ -59,6 +59,8 @@ class ShardState:
                                         dynamic=1 if dynamic else 0, step_t=0, skipped=0)
         self.last_flag = 0
         self._prepared = {}
+        self._flag_base = self.flags.data_ptr()
+        self._bound = None
 
     # -- state access -------------------------------------------------------
     @property
@@ -92,13 +94,19 @@ class ShardState:
                           self.t + 1)
 
     # -- flag ring ----------------------------------------------------------
-    def _next_flag(self):
+    def _next_flag_addr(self):
+        """Device address of a fresh zeroed uint32 flag slot."""
         if self.slot == self.FLAG_RING:
-            self.flags.zero_()
+            self.flags.zero_()   # stream-ordered before the next launch
             self.slot = 0
-        f = self.flags[self.slot:self.slot + 1]
+        addr = self._flag_base + 4 * self.slot
         self.slot += 1
-        return f
+        return addr
+
+    def _next_flag(self):
+        addr = self._next_flag_addr()
+        i = (addr - self._flag_base) // 4
+        return self.flags[i:i + 1]
 
     # -- micro-batches before the last one ------------------------------------
     def reduce_micro(self, worker_grads: Sequence[torch.Tensor], first: bool, stream=None):
@@ -127,7 +135,8 @@ class ShardState:
 
     def launch(self, worker_grads: Sequence[torch.Tensor], acc_in: Optional[torch.Tensor] = None,
                stream=None):
-        """Enqueue the fused step; returns the device flag slot it ORs into."""
+        """Enqueue the fused step without waiting; returns the device flag
+        slot it ORs into (finish() reads it back)."""
         flag = self._next_flag()
         args = self._args(worker_grads, acc_in)
         a = args.args
@@ -148,5 +157,26 @@ class ShardState:
             self.cur = 1 - self.cur
         return self.last_flag == 0
 
-    def step(self, worker_grads, acc_in=None, stream=None):
-        return self.finish(self.launch(worker_grads, acc_in, stream), stream)
+    def bind(self, worker_grads: Sequence[torch.Tensor], acc_in: Optional[torch.Tensor] = None):
+        """Prepare both directions' arguments once for gradients that stay at
+        the same addresses every step; step() with no gradients uses them."""
+        saved = self.cur
+        pair = []
+        for c in (0, 1):
+            self.cur = c
+            pair.append(self._args(worker_grads, acc_in))
+        self.cur = saved
+        self._bound = pair
+
+    def step(self, worker_grads=None, acc_in=None, stream=None, ev_start=None, ev_stop=None):
+        """One optimizer step through zs_step_commit (launch, flag readback,
+        scaler update in one native call); returns True when committed.
+        ev_start / ev_stop: optional raw hipEvent_t handles around the kernel."""
+        args = (self._bound[self.cur] if worker_grads is None
+                else self._args(worker_grads, acc_in))
+        args.args.overflow_flag = self._next_flag_addr()
+        ok = zs.zs_step_commit(args, self.scaler, self.flag_host, stream, ev_start, ev_stop)
+        self.last_flag = 0 if ok else 1
+        if ok:
+            self.cur = 1 - self.cur
+        return ok

@@ -70,6 +70,8 @@ def _load():
         "zs_cast_gather": ([vp, vp, i32, u64, u64, vp, vp], i32),
         "zs_step_fused": ([C.POINTER(zs_step_args), vp], i32),
         "zs_scaler_update": ([C.POINTER(zs_loss_scaler), u32], i32),
+        "zs_step_commit": ([C.POINTER(zs_step_args), C.POINTER(zs_loss_scaler), vp, vp, vp, vp,
+                            C.POINTER(C.c_int)], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -244,3 +246,16 @@ def zs_step_fused(args, stream=None):
 
 def zs_scaler_update(state: zs_loss_scaler, overflow):
     _check("zs_scaler_update", _lib.zs_scaler_update(C.byref(state), 1 if overflow else 0))
+
+
+def zs_step_commit(args, scaler: zs_loss_scaler, host_flag, stream=None, ev_start=None,
+                   ev_stop=None):
+    """Fused step + flag readback + scaler update (blocks). host_flag: a
+    (pinned) host tensor or address of at least 4 bytes. Returns committed."""
+    raw = args.args if isinstance(args, StepArgs) else args
+    hf = host_flag if isinstance(host_flag, int) else host_flag.data_ptr()
+    committed = C.c_int(0)
+    _check("zs_step_commit", _lib.zs_step_commit(C.byref(raw), C.byref(scaler), hf,
+                                                 _stream(stream), ev_start, ev_stop,
+                                                 C.byref(committed)))
+    return bool(committed.value)

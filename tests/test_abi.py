@@ -171,3 +171,31 @@ def test_fused_rejects_aliasing_and_bad_arguments(zs):
     a, keep = _fused_args(zs, n=0)
     assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_OK
     assert lib.zs_step_fused(None, None) == zs.ZS_ERR_INVALID_ARG
+
+
+def test_step_commit_rejects_bad_arguments(zs):
+    lib = _raw(zs)
+    a, keep = _fused_args(zs)
+    good = zs.zs_loss_scaler(scale=1024.0, clean_steps=0, growth_interval=4, dynamic=1,
+                             step_t=0, skipped=0)
+    hf = C.c_uint32(0)
+    ok = C.c_int(7)
+    E = zs.ZS_ERR_INVALID_ARG
+    assert lib.zs_step_commit(None, C.byref(good), C.byref(hf), None, None, None, C.byref(ok)) == E
+    assert lib.zs_step_commit(C.byref(a), None, C.byref(hf), None, None, None, C.byref(ok)) == E
+    assert lib.zs_step_commit(C.byref(a), C.byref(good), None, None, None, None, C.byref(ok)) == E
+    assert lib.zs_step_commit(C.byref(a), C.byref(good), C.byref(hf), None, None, None, None) == E
+    for bad_scale in (0.0, -1.0, float("inf"), float("nan")):
+        sc = zs.zs_loss_scaler(scale=bad_scale, clean_steps=0, growth_interval=4, dynamic=1,
+                               step_t=0, skipped=0)
+        assert lib.zs_step_commit(C.byref(a), C.byref(sc), C.byref(hf), None, None, None,
+                                  C.byref(ok)) == E
+    alias, keep2 = _fused_args(zs, master_out=FAKE + 0x1000000)
+    assert lib.zs_step_commit(C.byref(alias), C.byref(good), C.byref(hf), None, None, None,
+                              C.byref(ok)) == zs.ZS_ERR_ALIAS
+    # every error left the scaler untouched; n == 0 commits an empty step
+    assert (good.scale, good.step_t, good.skipped) == (1024.0, 0, 0)
+    empty, keep3 = _fused_args(zs, n=0)
+    assert lib.zs_step_commit(C.byref(empty), C.byref(good), C.byref(hf), None, None, None,
+                              C.byref(ok)) == zs.ZS_OK
+    assert ok.value == 1 and good.step_t == 1

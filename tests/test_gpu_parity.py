@@ -293,3 +293,57 @@ def test_step_fused_equals_unfused(zs):
     for a, b in zip(dout, du):
         assert_bits_equal(down32(a), down32(b), "fused vs unfused")
     assert np.array_equal(down16(gf), down16(gu))
+
+
+# ---- zs_step_commit ---------------------------------------------------------------
+
+def test_step_commit_commits_skips_and_times(zs):
+    import ctypes as C
+    rng = np.random.default_rng(8)
+    world, rank, n = 4, 1, 50_000
+    hip = C.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    hip.hipEventDestroy.argtypes = [C.c_void_p]
+    ev = [C.c_void_p(), C.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(C.byref(e)) == 0
+    master = (rng.standard_normal(n) * 0.02).astype(F32)
+    m = np.zeros(n, F32)
+    v = np.zeros(n, F32)
+    sets = [[up32(x) for x in (master, m, v)],
+            [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]]
+    gather = [torch.zeros(n, dtype=torch.float16, device="cuda") for _ in range(2)]
+    flags = torch.zeros(8, dtype=torch.int32, device="cuda")
+    host_flag = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    scaler = zs.zs_loss_scaler(scale=65536.0, clean_steps=0, growth_interval=2, dynamic=1,
+                               step_t=0, skipped=0)
+    ref = oracle.Scaler(65536.0, 2)
+    state = (master, m, v)
+    cur = 0
+    for step, inject in enumerate([False, True, False, False, True], start=1):
+        announce(f"step_commit step {step} inject={inject}")
+        g16 = [rand16(rng, n, 1e-3 * ref.scale, "fp16") for _ in range(world)]
+        if inject:
+            g16[step % world][123 + step] = 0x7C00
+        dg = [up16(g, "fp16") for g in g16]
+        args = zs.StepArgs(dg, rank, n, *sets[cur], *sets[1 - cur], gather[1 - cur], 0,
+                           flags[step:step + 1], zs.hparams(**HP, loss_scale=1.0, step_t=999))
+        ok = zs.zs_step_commit(args, scaler, host_flag, None, ev[0].value, ev[1].value)
+        f, mo, mmo, vo, po = oracle.shard_step(g16, rank, "fp16", "fp16", *state,
+                                               loss_scale=ref.scale, step_t=ref.t + 1, **HP)
+        assert ok == (f == 0) and ok == (not inject)
+        ref.update(f)
+        assert (scaler.scale, scaler.step_t, scaler.skipped, scaler.clean_steps) == \
+            (ref.scale, ref.t, ref.skipped, ref.clean)
+        ms = C.c_float()
+        assert hip.hipEventElapsedTime(C.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 1000.0
+        if ok:
+            cur = 1 - cur
+            state = (mo, mmo, vo)
+            assert assert_ulp16(down16(gather[cur]), po, "fp16", 1, "params") == 0
+        for got, want in zip(sets[cur], state):
+            assert_bits_equal(down32(got), want, f"state after step {step}")
+    for e in ev:
+        hip.hipEventDestroy(e)
