@@ -88,6 +88,27 @@ class ShardState:
     def loss_scale(self):
         return float(self.scaler.scale)
 
+    # -- checkpoint / resume ---------------------------------------------------
+    def state_dict(self):
+        """Host copy of everything the next step depends on: the current fp32
+        set, this rank's 16-bit parameters and the scaler."""
+        sc = self.scaler
+        return {"master": self.master.cpu(), "m": self.m.cpu(), "v": self.v.cpu(),
+                "params": self.params.cpu(),
+                "scaler": {"scale": float(sc.scale), "clean_steps": int(sc.clean_steps),
+                           "growth_interval": int(sc.growth_interval), "dynamic": int(sc.dynamic),
+                           "step_t": int(sc.step_t), "skipped": int(sc.skipped)}}
+
+    def load_state_dict(self, sd):
+        """Restore a state_dict() into the current set (shapes must match)."""
+        for dst, key in ((self.master, "master"), (self.m, "m"), (self.v, "v"),
+                         (self.params, "params")):
+            if dst.shape != sd[key].shape or dst.dtype != sd[key].dtype:
+                raise ValueError(f"state_dict[{key!r}] has the wrong shape or dtype")
+            dst.copy_(sd[key])
+        for k, v in sd["scaler"].items():
+            setattr(self.scaler, k, v)
+
     def hparams(self):
         o = self.opt
         return zs.hparams(o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.loss_scale,

@@ -347,3 +347,36 @@ def test_step_commit_commits_skips_and_times(zs):
             assert_bits_equal(down32(got), want, f"state after step {step}")
     for e in ev:
         hip.hipEventDestroy(e)
+
+
+# ---- exhaustive conversions on the device ------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_cast_all_fp32_patterns(zs, dtype):
+    """Every one of the 2^32 fp32 bit patterns through zs_cast_gather's
+    hardware round-to-nearest-even convert, against the oracle (NaN by class)."""
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.int16, device="cuda")
+    for c in range(1 << 32 >> 28):
+        announce(f"cast all patterns {dtype} chunk {c}")
+        x = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda")
+        x = x.to(torch.int32).view(torch.float32)
+        zs.zs_cast_gather(x, out, DT[dtype], 0, chunk)
+        got = down16(out)
+        del x
+        host = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64).astype(np.uint32).view(F32)
+        want = oracle.float_to_half(host, dtype)
+        assert assert_ulp16(got, want, dtype, 0, f"{dtype} chunk {c}") == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_widen_all_16bit_patterns(zs, dtype):
+    """Every 16-bit pattern widened by the kernels (W = 1: the sum is the
+    value itself, the average divides by 1) against the oracle."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    out = torch.empty(bits.size, dtype=torch.float32, device="cuda")
+    flag = _flag()
+    announce(f"widen all {dtype} patterns")
+    zs.zs_reduce_scatter_avg([up16(bits, dtype)], None, 1, 0, bits.size, out, False, flag, 1.0)
+    assert_bits_equal(down32(out), oracle.half_to_float(bits, dtype), f"widen {dtype}")
+    assert int(flag.item()) == 1  # the NaN and inf patterns raise the flag

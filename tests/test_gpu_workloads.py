@@ -154,3 +154,51 @@ def test_1p3b_w4_acc4_fp16_windows(env):
     st = run_workload(env, wl.name, windows=_windows(wl.n, 6, 4))
     # two injected steps skipped: 2^16 -> 2^15 -> 2^14, eight steps committed
     assert st.loss_scale == 2.0 ** 14 and st.t == 8
+
+
+def test_checkpoint_resume_is_bit_identical(env, tmp_path):
+    """k steps, save, reload into a fresh shard, continue: identical bits to
+    an uninterrupted run (dynamic scaler and skipped steps included)."""
+    zs, synth, shard = env
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["1p3b-w4-acc4-fp16"], phi=4 * 300_007,
+                             inject_steps=(2, 5), steps=7, name="resume-case")
+    n, W, A = wl.n, wl.world, wl.accum
+    opt = shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay)
+
+    def fresh():
+        st = shard.ShardState(n, W, 0, 0, n, wl.param_dtype, wl.grad_dtype, opt, wl.loss_scale,
+                              dynamic=True, growth_interval=2, accumulate=True)
+        synth.dev_state(wl, 0, st.master, st.m, st.v)
+        return st
+
+    grads = torch.empty((W, -(-n // 128) * 128), dtype=torch.int16, device="cuda")
+    g = [grads[k, :n] for k in range(W)]
+
+    def run(st, steps):
+        for step in steps:
+            for j in range(A):
+                for k in range(W):
+                    synth.dev_grad(wl, k, step, j, 0, g[k], scale=st.loss_scale)
+                if j < A - 1:
+                    st.reduce_micro(g, first=(j == 0))
+                else:
+                    st.step(g, acc_in=st.acc)
+
+    announce("checkpoint/resume")
+    ref = fresh()
+    run(ref, range(1, 8))
+    a = fresh()
+    run(a, range(1, 4))
+    path = tmp_path / "shard.pt"
+    torch.save(a.state_dict(), path)
+    del a
+    b = fresh()
+    b.load_state_dict(torch.load(path, weights_only=True))
+    run(b, range(4, 8))
+    for x, y in ((b.master, ref.master), (b.m, ref.m), (b.v, ref.v)):
+        assert_bits_equal(down32(x), down32(y), "resumed state")
+    assert np.array_equal(down16(b.params.view(torch.int16)), down16(ref.params.view(torch.int16)))
+    assert (b.t, b.loss_scale, int(b.scaler.skipped)) == (ref.t, ref.loss_scale,
+                                                          int(ref.scaler.skipped))
+    assert int(ref.scaler.skipped) == 2
