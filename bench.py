@@ -124,7 +124,7 @@ def replicas_for(wl, bytes_per_step):
     return max(1, min(8, -(-(1 << 30) // max(bytes_per_step, 1))))
 
 
-def run_workload(name, steps, warmup, torch):
+def run_workload(name, steps, warmup, torch, wire=0):
     from sharded_mixed_precision_zs_amd import shard, synth
 
     wl = synth.WORKLOADS[name]
@@ -141,7 +141,8 @@ def run_workload(name, steps, warmup, torch):
     for r in range(R):
         st = shard.ShardState(n, W, wl.rank, wl.offset, wl.offset + n, wl.param_dtype,
                               wl.grad_dtype, opt, wl.loss_scale, dynamic=wl.dynamic_scale,
-                              growth_interval=wl.scale_interval, accumulate=A > 1)
+                              growth_interval=wl.scale_interval, accumulate=A > 1,
+                              wire_dtype=wire)
         synth.dev_state(wl, wl.offset, st.master, st.m, st.v)
         # one row per worker, rows padded to 256 B like separate allocations
         grads = torch.empty((A, W, pad_elems(n)), dtype=torch.int16, device="cuda")
@@ -246,6 +247,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="comma-separated extra workloads reported under 'other_workloads'")
+    ap.add_argument("--wire", choices=["fp32", "bf16", "fp16"], default="fp32",
+                    help="precision of the ring's partial sums (default fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     args = ap.parse_args()
@@ -263,11 +266,12 @@ def main():
     ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
     if ceiling:
         log(f"plain copy ceiling {ceiling:.0f} GB/s")
-    main_res = run_workload(args.workload, args.steps, args.warmup, torch)
+    wire = {"fp32": 0, "bf16": 1, "fp16": 2}[args.wire]
+    main_res = run_workload(args.workload, args.steps, args.warmup, torch, wire)
     log(json.dumps(main_res))
     others = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
-        r = run_workload(name, max(3, args.steps // 2), 2, torch)
+        r = run_workload(name, max(3, args.steps // 2), 2, torch, wire)
         log(json.dumps(r))
         others.append(dict(workload=name, params_per_s=r["params_per_s"],
                            ms_per_step=r["ms_per_step"], hbm_gbps=r["hbm_gbps"],
@@ -295,7 +299,8 @@ def main():
                    "phi": wl.phi, "world": wl.world, "rank": wl.rank, "shard_params": wl.n,
                    "grad_dtype": "bf16" if wl.grad_dtype == 0 else "fp16",
                    "param_dtype": "bf16" if wl.param_dtype == 0 else "fp16",
-                   "micro_batches": wl.accum, "replicas": main_res["replicas"]},
+                   "micro_batches": wl.accum, "replicas": main_res["replicas"],
+                   "wire": args.wire},
         "hbm_gbps": main_res["hbm_gbps"],
         "hbm_pct_of_peak": 100.0 * main_res["hbm_gbps"] / PEAK_HBM_GBPS,
         "copy_ceiling_gbps": ceiling,

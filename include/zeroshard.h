@@ -37,7 +37,7 @@
  *     kernel.
  *   - n == 0 is a no-op that returns ZS_OK.
  *   - Status codes: ZS_OK on success; ZS_ERR_INVALID_ARG (null pointer,
- *     world == 0 or > ZS_MAX_WORLD, rank >= world, bad dtype, non-finite or
+ *     world == 0 or > ZS_MAX_WORLD, rank >= world, bad dtype or wire dtype, non-finite or
  *     zero loss scale, step_t == 0) before anything is enqueued;
  *     ZS_ERR_ALIAS when zs_step_fused's output set overlaps its input set;
  *     ZS_ERR_HIP when a launch fails (zs_last_error() has HIP's message).
@@ -56,10 +56,18 @@
 extern "C" {
 #endif
 
-#define ZS_ABI_VERSION 1
+#define ZS_ABI_VERSION 2
 #define ZS_MAX_WORLD 64
 
 typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
+
+/* Precision of the partial sums the ring reduction passes between ranks.
+ * ZS_WIRE_FP32 (0, the default) carries them in fp32 ([Notes] 三: the owner
+ * works in FP32). ZS_WIRE_BF16 / ZS_WIRE_FP16 round every partial, the
+ * owner's final sum included, to nearest-even 16 bits, as a reduction run in
+ * a 16-bit dtype does ([L7] "ZeRO 与 FSDP": MixedPrecision reduce_dtype):
+ *   s = R(G[r+1]);  s = R(s + G[r+s']) for s' = 2..W   (adds in fp32). */
+typedef enum { ZS_WIRE_FP32 = 0, ZS_WIRE_BF16 = 1, ZS_WIRE_FP16 = 2 } zs_wire;
 
 typedef enum {
   ZS_OK = 0,
@@ -108,13 +116,15 @@ int zs_partition(uint64_t phi, uint32_t world, uint32_t rank, uint64_t *chunk,
  *               grad_part[i] = a             if accumulate == 0,
  *               grad_part[i] = grad_part[i] + a otherwise (a later
  *               micro-batch, [L7] "Gradient Accumulation").
+ *   wire_dtype   : zs_wire, the precision of the partial sums (0 = fp32;
+ *                  with a 16-bit wire each partial is rounded as above).
  *   grad_part    : device fp32[n], written (read too when accumulating).
  *   overflow_flag: device uint32 or NULL; if set, becomes 1 when any
  *                  grad_part[i] / loss_scale is not finite.
  *   loss_scale   : used only for the flag. */
 int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
-                          uint32_t world, uint32_t rank, uint64_t n,
-                          float *grad_part, int accumulate,
+                          int wire_dtype, uint32_t world, uint32_t rank,
+                          uint64_t n, float *grad_part, int accumulate,
                           uint32_t *overflow_flag, float loss_scale,
                           void *stream);
 
@@ -175,6 +185,7 @@ typedef struct {
   uint64_t gather_offset;          /* element offset of this rank's slice   */
   uint32_t *overflow_flag;         /* device uint32, OR-ed                  */
   zs_adamw_hparams hp;
+  int32_t wire_dtype;              /* zs_wire; 0 = fp32 partial sums        */
 } zs_step_args;
 
 int zs_step_fused(const zs_step_args *args, void *stream);

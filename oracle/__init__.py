@@ -18,6 +18,8 @@ from . import build as _build
 BF16 = 0
 FP16 = 1
 _DTYPES = {"bf16": BF16, "fp16": FP16, BF16: BF16, FP16: FP16}
+WIRE_FP32, WIRE_BF16, WIRE_FP16 = 0, 1, 2
+_WIRES = {"fp32": 0, "bf16": 1, "fp16": 2, 0: 0, 1: 1, 2: 2, None: 0}
 
 _lib = None
 
@@ -51,6 +53,11 @@ def _load():
     lib.zso_reduce_avg.argtypes = [C.c_uint32, C.c_uint32, C.POINTER(u16p), C.c_int, C.c_uint64,
                                    f32p, C.c_int, C.c_float]
     lib.zso_reduce_avg.restype = C.c_uint32
+    lib.zso_reduce_avg_wire.argtypes = [C.c_uint32, C.c_uint32, C.POINTER(u16p), C.c_int, C.c_int,
+                                        C.c_uint64, f32p, C.c_int, C.c_float]
+    lib.zso_reduce_avg_wire.restype = C.c_uint32
+    lib.zso_ring_chunk_sum_wire.argtypes = [C.c_uint32, C.c_uint32, C.POINTER(u16p), C.c_int,
+                                            C.c_int, C.c_uint64, f32p]
     lib.zso_check_overflow.argtypes = [f32p, C.c_uint64, C.c_float]
     lib.zso_check_overflow.restype = C.c_uint32
     lib.zso_adamw_consts_make.argtypes = [C.c_float] * 5 + [C.c_uint32, C.POINTER(AdamWConsts)]
@@ -87,7 +94,7 @@ class _StepArgs(C.Structure):
                 ("param_out", C.POINTER(C.c_uint16)),
                 ("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float),
                 ("eps", C.c_float), ("weight_decay", C.c_float), ("loss_scale", C.c_float),
-                ("step_t", C.c_uint32)]
+                ("step_t", C.c_uint32), ("wire", C.c_int)]
 
 
 class ScalerState(C.Structure):
@@ -174,27 +181,32 @@ def ring_held_chunk(world, rank, sigma):
     return _load().zso_ring_held_chunk(world, rank, sigma)
 
 
-def ring_chunk_sum(parts, rank, dtype):
-    """fp32 ring-order sum of rank `rank`'s partition; parts in worker order."""
+def ring_chunk_sum(parts, rank, dtype, wire=None):
+    """Ring-order sum of rank `rank`'s partition (parts in worker order), the
+    partials carried in fp32 (default) or rounded to `wire` at every hop."""
     lib = _load()
     keep, arr = _parts(parts)
     n = keep[0].size
     out = np.empty(n, np.float32)
-    lib.zso_ring_chunk_sum(len(keep), rank, arr, dtype_code(dtype), n,
-                           out.ctypes.data_as(C.POINTER(C.c_float)))
+    if _WIRES[wire] == WIRE_FP32:
+        lib.zso_ring_chunk_sum(len(keep), rank, arr, dtype_code(dtype), n,
+                               out.ctypes.data_as(C.POINTER(C.c_float)))
+    else:
+        lib.zso_ring_chunk_sum_wire(len(keep), rank, arr, dtype_code(dtype), _WIRES[wire], n,
+                                    out.ctypes.data_as(C.POINTER(C.c_float)))
     return out
 
 
 # ---- a3-a5 ----------------------------------------------------------------
 
-def reduce_avg(parts, rank, dtype, out, accumulate, loss_scale):
+def reduce_avg(parts, rank, dtype, out, accumulate, loss_scale, wire=None):
     """out = ring_sum/W (or out += ring_sum/W); returns the overflow flag."""
     lib = _load()
     keep, arr = _parts(parts)
     assert out.dtype == np.float32 and out.flags.c_contiguous and out.size == keep[0].size
-    return int(lib.zso_reduce_avg(len(keep), rank, arr, dtype_code(dtype), out.size,
-                                  out.ctypes.data_as(C.POINTER(C.c_float)),
-                                  1 if accumulate else 0, loss_scale))
+    return int(lib.zso_reduce_avg_wire(len(keep), rank, arr, dtype_code(dtype), _WIRES[wire],
+                                       out.size, out.ctypes.data_as(C.POINTER(C.c_float)),
+                                       1 if accumulate else 0, loss_scale))
 
 
 def check_overflow(a, loss_scale):
@@ -227,7 +239,7 @@ def adamw(master, m, v, a, loss_scale, lr, beta1, beta2, eps, weight_decay, t):
 # ---- the whole step -------------------------------------------------------
 
 def shard_step(parts, rank, grad_dtype, param_dtype, master, m, v, *, lr, beta1, beta2,
-               eps, weight_decay, loss_scale, step_t, acc_in=None, threads=1):
+               eps, weight_decay, loss_scale, step_t, acc_in=None, threads=1, wire=None):
     """One shard step; returns (flag, master_out, m_out, v_out, param_out_bits)."""
     lib = _load()
     keep, arr = _parts(parts)
@@ -251,6 +263,7 @@ def shard_step(parts, rank, grad_dtype, param_dtype, master, m, v, *, lr, beta1,
     a.param_out = pout.ctypes.data_as(C.POINTER(C.c_uint16))
     a.lr, a.beta1, a.beta2, a.eps = lr, beta1, beta2, eps
     a.weight_decay, a.loss_scale, a.step_t = weight_decay, loss_scale, step_t
+    a.wire = _WIRES[wire]
     flag = lib.zso_shard_step(C.byref(a), threads)
     if flag == 0xFFFFFFFF:
         raise MemoryError("oracle: thread allocation failed")

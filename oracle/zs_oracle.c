@@ -196,28 +196,55 @@ void zso_ring_chunk_sum(uint32_t world, uint32_t rank,
   }
 }
 
+/* What a 16-bit wire does to a partial sum: round it to the wire type. */
+static float on_wire(float x, int wire) {
+  if (wire == ZSO_WIRE_BF16) return zso_half_to_float(zso_float_to_half(x, ZSO_BF16), ZSO_BF16);
+  if (wire == ZSO_WIRE_FP16) return zso_half_to_float(zso_float_to_half(x, ZSO_FP16), ZSO_FP16);
+  return x;
+}
+
+/* One element of the journey, partials carried in `wire` precision. */
+static float ring_elem(uint32_t world, uint32_t rank, const uint16_t *const *part,
+                       int dtype, int wire, uint64_t i) {
+  float acc = on_wire(zso_half_to_float(part[(rank + 1) % world][i], dtype), wire);
+  for (uint32_t s = 2; s <= world; ++s)
+    acc = on_wire(acc + zso_half_to_float(part[(rank + s) % world][i], dtype), wire);
+  return acc;
+}
+
+void zso_ring_chunk_sum_wire(uint32_t world, uint32_t rank,
+                             const uint16_t *const *part, int dtype, int wire,
+                             uint64_t n, float *sum_out) {
+  for (uint64_t i = 0; i < n; ++i) sum_out[i] = ring_elem(world, rank, part, dtype, wire, i);
+}
+
 /* ---- owner's average, accumulation and overflow check --------------------
  * [Notes] 三 and 四: the owner gathers the W contributions of its part and
  * takes their mean; [L7] "数学等价性": the mean of the W worker gradients
  * is the full-batch gradient. [L7] "Gradient Accumulation": micro-batch
  * gradients are summed before the single update. */
 
-uint32_t zso_reduce_avg(uint32_t world, uint32_t rank,
-                        const uint16_t *const *part, int dtype, uint64_t n,
-                        float *out, int accumulate, float loss_scale) {
+uint32_t zso_reduce_avg_wire(uint32_t world, uint32_t rank,
+                             const uint16_t *const *part, int dtype, int wire,
+                             uint64_t n, float *out, int accumulate,
+                             float loss_scale) {
   uint32_t flag = 0;
   const float wf = (float)world;
   for (uint64_t i = 0; i < n; ++i) {
-    float acc = zso_half_to_float(part[(rank + 1) % world][i], dtype);
-    for (uint32_t s = 2; s <= world; ++s)
-      acc = acc + zso_half_to_float(part[(rank + s) % world][i], dtype);
-    float a = acc / wf;
+    float a = ring_elem(world, rank, part, dtype, wire, i) / wf;
     if (accumulate) a = out[i] + a;
     out[i] = a;
     float g = a / loss_scale;
     if (!isfinite(g)) flag = 1;
   }
   return flag;
+}
+
+uint32_t zso_reduce_avg(uint32_t world, uint32_t rank,
+                        const uint16_t *const *part, int dtype, uint64_t n,
+                        float *out, int accumulate, float loss_scale) {
+  return zso_reduce_avg_wire(world, rank, part, dtype, ZSO_WIRE_FP32, n, out, accumulate,
+                             loss_scale);
 }
 
 uint32_t zso_check_overflow(const float *a, uint64_t n, float loss_scale) {
@@ -285,11 +312,7 @@ static void *step_range(void *arg) {
   const float wf = (float)a->world;
   uint32_t flag = 0;
   for (uint64_t i = job->lo; i < job->hi; ++i) {
-    float s = zso_half_to_float(a->part[(a->rank + 1) % a->world][i],
-                                a->grad_dtype);
-    for (uint32_t j = 2; j <= a->world; ++j)
-      s = s + zso_half_to_float(a->part[(a->rank + j) % a->world][i],
-                                a->grad_dtype);
+    float s = ring_elem(a->world, a->rank, a->part, a->grad_dtype, a->wire, i);
     float avg = s / wf;
     if (a->acc_in) avg = a->acc_in[i] + avg;
     float g = avg / a->loss_scale;

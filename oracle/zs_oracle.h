@@ -48,6 +48,12 @@ extern "C" {
 
 enum { ZSO_BF16 = 0, ZSO_FP16 = 1 };
 
+/* Precision of the partial sums the ring passes between ranks ("on the
+ * wire"): fp32 (the default), or rounded to bf16 / fp16 at every hop, as
+ * when the reduction runs in a 16-bit dtype ([L7] "ZeRO 与 FSDP": the FSDP
+ * example's MixedPrecision reduce_dtype=bfloat16). */
+enum { ZSO_WIRE_FP32 = 0, ZSO_WIRE_BF16 = 1, ZSO_WIRE_FP16 = 2 };
+
 /* Returns 1 when the floating-point environment keeps subnormals and rounds
  * to nearest-even (the oracle's results assume both), else 0. */
 int zso_fp_env_ok(void);
@@ -91,6 +97,14 @@ void zso_ring_chunk_sum(uint32_t world, uint32_t rank,
                         const uint16_t *const *part, int dtype, uint64_t n,
                         float *sum_out);
 
+/* The same journey with a 16-bit wire: every partial the ring sends is
+ * rounded (nearest-even) to the wire type, i.e. acc = R(G[r+1]), then
+ * acc = R(acc + G[r+s]) for s = 2..W, the last (the owner's) included.
+ * wire = ZSO_WIRE_FP32 gives zso_ring_chunk_sum exactly. */
+void zso_ring_chunk_sum_wire(uint32_t world, uint32_t rank,
+                             const uint16_t *const *part, int dtype, int wire,
+                             uint64_t n, float *sum_out);
+
 /* Owner's reduction of one gradient bucket: a = sum / W (ring order), then
  * out = a (accumulate == 0) or out = out + a (accumulate != 0: later
  * micro-batches, [L7] "Gradient Accumulation"). Returns the overflow flag of
@@ -98,6 +112,11 @@ void zso_ring_chunk_sum(uint32_t world, uint32_t rank,
 uint32_t zso_reduce_avg(uint32_t world, uint32_t rank,
                         const uint16_t *const *part, int dtype, uint64_t n,
                         float *out, int accumulate, float loss_scale);
+/* zso_reduce_avg with the partial sums carried in `wire` precision. */
+uint32_t zso_reduce_avg_wire(uint32_t world, uint32_t rank,
+                             const uint16_t *const *part, int dtype, int wire,
+                             uint64_t n, float *out, int accumulate,
+                             float loss_scale);
 
 /* 1 if any (a[i] / loss_scale) is not finite, else 0. */
 uint32_t zso_check_overflow(const float *a, uint64_t n, float loss_scale);
@@ -131,6 +150,7 @@ typedef struct {
   uint16_t *param_out;          /* this rank's slice of the gather buffer      */
   float lr, beta1, beta2, eps, weight_decay, loss_scale;
   uint32_t step_t;
+  int wire;                     /* ZSO_WIRE_*: precision of the ring partials */
 } zso_step_args;
 
 /* One whole shard step (ring sum, average, optional accumulate, unscale,

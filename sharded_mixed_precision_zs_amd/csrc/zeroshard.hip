@@ -41,6 +41,8 @@ int launch_result() {
 
 bool valid_dtype(int dt) { return dt == ZS_BF16 || dt == ZS_FP16; }
 
+bool valid_wire(int w) { return w == ZS_WIRE_FP32 || w == ZS_WIRE_BF16 || w == ZS_WIRE_FP16; }
+
 /* zs_step_commit polls the stream for errors this often while it waits. */
 constexpr int kQueryMicros = 1000;
 
@@ -179,8 +181,8 @@ int zs_partition(uint64_t phi, uint32_t world, uint32_t rank, uint64_t *chunk,
 }
 
 int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
-                          uint32_t world, uint32_t rank, uint64_t n,
-                          float *grad_part, int accumulate,
+                          int wire_dtype, uint32_t world, uint32_t rank,
+                          uint64_t n, float *grad_part, int accumulate,
                           uint32_t *overflow_flag, float loss_scale,
                           void *stream) {
   if (!worker_grads || !grad_part)
@@ -188,7 +190,9 @@ int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
   if (world == 0 || world > ZS_MAX_WORLD || rank >= world)
     return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64 and rank < world%s");
   if (!valid_dtype(grad_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad grad dtype%s");
+  if (!valid_wire(wire_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad wire dtype%s");
   ReduceArgs a;
+  a.wire = wire_dtype;
   if (!make_scales(world, loss_scale, &a.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
   if (n == 0) return ZS_OK;
@@ -205,8 +209,14 @@ int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
   if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
-#define ZS_LAUNCH_REDUCE(V, D) \
-  hipLaunchKernelGGL((reduce_kernel<V, kTileVecs, D>), grid, block, 0, s, a)
+#define ZS_REDUCE_K(V, D, W) \
+  hipLaunchKernelGGL((reduce_kernel<V, kTileVecs, D, W>), grid, block, 0, s, a)
+#define ZS_LAUNCH_REDUCE(V, D)                                  \
+  do {                                                          \
+    if (wire_dtype == ZS_WIRE_BF16) ZS_REDUCE_K(V, D, ZS_WIRE_BF16);      \
+    else if (wire_dtype == ZS_WIRE_FP16) ZS_REDUCE_K(V, D, ZS_WIRE_FP16); \
+    else ZS_REDUCE_K(V, D, ZS_WIRE_FP32);                       \
+  } while (0)
   if (grad_dtype == ZS_BF16) {
     switch (vec) {
       case 8: ZS_LAUNCH_REDUCE(8, ZS_BF16); break;
@@ -223,6 +233,7 @@ int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
     }
   }
 #undef ZS_LAUNCH_REDUCE
+#undef ZS_REDUCE_K
   return launch_result();
 }
 
@@ -331,7 +342,9 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64 and rank < world%s");
   if (!valid_dtype(a->grad_dtype) || !valid_dtype(a->param_dtype))
     return fail(ZS_ERR_INVALID_ARG, "bad grad or param dtype%s");
+  if (!valid_wire(a->wire_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad wire dtype%s");
   FusedArgs p;
+  p.wire = a->wire_dtype;
   if (!make_scales(a->world, a->hp.loss_scale, &p.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
   if (!make_adam(&a->hp, &p.h)) return fail(ZS_ERR_INVALID_ARG, "step_t must be >= 1%s");
@@ -382,8 +395,14 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
   const int mode = (a->world > 1 ? 1 : 0) | (a->acc_in ? 2 : 0);
-#define ZS_FUSED_K(V, L, A, G, P) \
-  hipLaunchKernelGGL((fused_kernel<V, kTileVecs, L, A, G, P>), grid, block, 0, s, p)
+#define ZS_FUSED_KW(V, L, A, G, P, W) \
+  hipLaunchKernelGGL((fused_kernel<V, kTileVecs, L, A, G, P, W>), grid, block, 0, s, p)
+#define ZS_FUSED_K(V, L, A, G, P)                                             \
+  do {                                                                        \
+    if (p.wire == ZS_WIRE_BF16) ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_BF16);     \
+    else if (p.wire == ZS_WIRE_FP16) ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_FP16); \
+    else ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_FP32);                            \
+  } while (0)
 #define ZS_LAUNCH_FUSED(V, G, P)                          \
   do {                                                    \
     switch (mode) {                                       \
@@ -416,6 +435,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
 #undef ZS_FUSED_VEC
 #undef ZS_LAUNCH_FUSED
 #undef ZS_FUSED_K
+#undef ZS_FUSED_KW
   int launched = launch_result();
   if (launched == ZS_OK && ev_stop) {
     hipError_t e = hipEventRecord(ev_stop, s);

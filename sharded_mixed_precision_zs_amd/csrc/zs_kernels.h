@@ -219,36 +219,73 @@ __device__ __forceinline__ void st16(uint16_t *__restrict__ p, const float (&x)[
  * p[0], p[1], ..., p[W-1] left to right adds the owner's term last: the
  * order in which the ring's running partial for this chunk visits the
  * workers ([Notes] 二 three-GPU example; [L7] "Ring AllReduce 算法").
+ *
+ * WIRE is the precision of the partial the ring passes on: ZS_WIRE_FP32
+ * keeps it in fp32; ZS_WIRE_BF16 / ZS_WIRE_FP16 round it to nearest-even
+ * 16 bits at every hop, the last (owner's) one included, as a reduction
+ * run in a 16-bit dtype does ([L7] "ZeRO 与 FSDP", reduce_dtype).
  * ---------------------------------------------------------------------- */
 
 struct GradPtrs {
   const uint16_t *p[ZS_MAX_WORLD];
 };
 
-template <int VEC, int DT>
-__device__ __forceinline__ void ring_sum(const GradPtrs &g, uint32_t world,
-                                         uint64_t i0, float (&s)[VEC]) {
-  upcast<VEC, DT>(ld16<VEC>(g.p[0] + i0), s);
+template <int WIRE>
+__device__ __forceinline__ float on_wire(float x) {
+  if constexpr (WIRE == ZS_WIRE_BF16) return __uint_as_float((uint32_t)pack1<ZS_BF16>(x) << 16);
+  else if constexpr (WIRE == ZS_WIRE_FP16) return (float)(_Float16)x;
+  else return x;
+}
+
+template <int VEC, int DT, int WIRE>
+__device__ __forceinline__ void set_up(float (&s)[VEC], const Raw16<VEC> &r) {
+  upcast<VEC, DT>(r, s);
+  if constexpr (WIRE != ZS_WIRE_FP32) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[e] = on_wire<WIRE>(s[e]);
+  }
+}
+
+template <int VEC, int DT, int WIRE>
+__device__ __forceinline__ void add_wire(float (&s)[VEC], const Raw16<VEC> &r) {
+  float x[VEC];
+  upcast<VEC, DT>(r, x);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = on_wire<WIRE>(s[e] + x[e]);
+}
+
+template <int VEC, int DT, int WIRE>
+__device__ __forceinline__ void ring_sum_w(const GradPtrs &g, uint32_t world, uint64_t i0,
+                                           float (&s)[VEC]) {
+  set_up<VEC, DT, WIRE>(s, ld16<VEC>(g.p[0] + i0));
   uint32_t j = 1;
   for (; j + kLoadBatch <= world; j += kLoadBatch) {
     Raw16<VEC> r[kLoadBatch];
 #pragma unroll
     for (int b = 0; b < kLoadBatch; ++b) r[b] = ld16<VEC>(g.p[j + b] + i0);
 #pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b) add_up<VEC, DT>(s, r[b]);
+    for (int b = 0; b < kLoadBatch; ++b) add_wire<VEC, DT, WIRE>(s, r[b]);
   }
-  for (; j < world; ++j) add_up<VEC, DT>(s, ld16<VEC>(g.p[j] + i0));
+  for (; j < world; ++j) add_wire<VEC, DT, WIRE>(s, ld16<VEC>(g.p[j] + i0));
+}
+
+/* One vector per thread; the wire precision is a uniform runtime choice. */
+template <int VEC, int DT>
+__device__ __forceinline__ void ring_sum(const GradPtrs &g, uint32_t world, int wire,
+                                         uint64_t i0, float (&s)[VEC]) {
+  if (wire == ZS_WIRE_BF16) ring_sum_w<VEC, DT, ZS_WIRE_BF16>(g, world, i0, s);
+  else if (wire == ZS_WIRE_FP16) ring_sum_w<VEC, DT, ZS_WIRE_FP16>(g, world, i0, s);
+  else ring_sum_w<VEC, DT, ZS_WIRE_FP32>(g, world, i0, s);
 }
 
 /* The same ring-order sum for U vectors per thread. Loads are issued
  * worker-major (all U vectors of one worker back to back, kLoadBatch
  * workers ahead of the adds) and marked non-temporal. */
-template <int VEC, int U, int DT>
-__device__ __forceinline__ void ring_sum_u(const GradPtrs &g, uint32_t world,
-                                           const uint64_t (&i0)[U],
-                                           float (&s)[U][VEC]) {
+template <int VEC, int U, int DT, int WIRE>
+__device__ __forceinline__ void ring_sum_uw(const GradPtrs &g, uint32_t world,
+                                            const uint64_t (&i0)[U], float (&s)[U][VEC]) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) upcast<VEC, DT>(ld16<VEC, true>(g.p[0] + i0[u]), s[u]);
+  for (int u = 0; u < U; ++u) set_up<VEC, DT, WIRE>(s[u], ld16<VEC, true>(g.p[0] + i0[u]));
   uint32_t j = 1;
   for (; j + kLoadBatch <= world; j += kLoadBatch) {
     Raw16<VEC> r[kLoadBatch][U];
@@ -259,11 +296,11 @@ __device__ __forceinline__ void ring_sum_u(const GradPtrs &g, uint32_t world,
 #pragma unroll
     for (int b = 0; b < kLoadBatch; ++b)
 #pragma unroll
-      for (int u = 0; u < U; ++u) add_up<VEC, DT>(s[u], r[b][u]);
+      for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], r[b][u]);
   }
   for (; j < world; ++j)
 #pragma unroll
-    for (int u = 0; u < U; ++u) add_up<VEC, DT>(s[u], ld16<VEC, true>(g.p[j] + i0[u]));
+    for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], ld16<VEC, true>(g.p[j] + i0[u]));
 }
 
 /* Wave-level OR of the overflow flag: one vector atomic per wave that saw a
@@ -293,6 +330,7 @@ __device__ __forceinline__ uint64_t first_elem(int vec) {
 struct ReduceArgs {
   GradPtrs g;
   uint32_t world;
+  int wire;        /* ZS_WIRE_*: precision of the ring's partials */
   uint64_t n;
   float *out;
   uint32_t *flag;  /* may be null */
@@ -304,7 +342,7 @@ template <int VEC, int DT>
 __device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, uint64_t i0) {
   float s[VEC], acc[VEC];
   if (a.accumulate) ldf<VEC>(a.out + i0, acc);
-  ring_sum<VEC, DT>(a.g, a.world, i0, s);
+  ring_sum<VEC, DT>(a.g, a.world, a.wire, i0, s);
   bool bad = false;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -317,13 +355,13 @@ __device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, uint64_t i0) {
   return bad;
 }
 
-template <int VEC, int U, int DT>
+template <int VEC, int U, int DT, int WIRE>
 __device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
   float s[U][VEC];
-  ring_sum_u<VEC, U, DT>(a.g, a.world, i0, s);
+  ring_sum_uw<VEC, U, DT, WIRE>(a.g, a.world, i0, s);
   bool bad = false;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -341,13 +379,13 @@ __device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, uint64_t base) 
   return bad;
 }
 
-template <int VEC, int U, int DT>
+template <int VEC, int U, int DT, int WIRE>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
   const uint64_t tile = (uint64_t)kBlock * U * VEC;
   const uint64_t full = a.n / tile;  /* blocks past `full` cover the tail */
   bool bad = false;
   if (blockIdx.x < full) {
-    bad = reduce_tile<VEC, U, DT>(a, (uint64_t)blockIdx.x * tile);
+    bad = reduce_tile<VEC, U, DT, WIRE>(a, (uint64_t)blockIdx.x * tile);
   } else {
     uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * kBlock + threadIdx.x;
     if (i < a.n) bad = reduce_vec<1, DT>(a, i);
@@ -439,6 +477,7 @@ __global__ __launch_bounds__(kBlock) void cast_kernel(CastArgs c) {
 struct FusedArgs {
   GradPtrs g;
   uint32_t world;
+  int wire;        /* ZS_WIRE_*: precision of the ring's partials */
   uint64_t n;
   const float *acc_in;  /* may be null */
   const float *master_in, *m_in, *v_in;
@@ -456,7 +495,7 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
   ldf<VEC>(p.m_in + i0, m);
   ldf<VEC>(p.v_in + i0, v);
   if (p.acc_in) ldf<VEC>(p.acc_in + i0, acc);
-  ring_sum<VEC, GDT>(p.g, p.world, i0, s);
+  ring_sum<VEC, GDT>(p.g, p.world, p.wire, i0, s);
   bool bad = false;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
@@ -477,7 +516,7 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
  * the gradient sum, which keeps registers (and so waves in flight) for the
  * gradient streams; with a single worker (W = 1) there is no sum, one
  * gradient load, and the state loads go first. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT>
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
 __device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
@@ -493,12 +532,11 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
     }
   };
   if constexpr (MULTI) {
-    ring_sum_u<VEC, U, GDT>(p.g, p.world, i0, s);
+    ring_sum_uw<VEC, U, GDT, WIRE>(p.g, p.world, i0, s);
     load_state();
   } else {
     load_state();
-#pragma unroll
-    for (int u = 0; u < U; ++u) upcast<VEC, GDT>(ld16<VEC, true>(p.g.p[0] + i0[u]), s[u]);
+    ring_sum_uw<VEC, U, GDT, WIRE>(p.g, 1, i0, s);  /* one worker: no loop runs */
   }
   bool bad = false;
 #pragma unroll
@@ -522,13 +560,13 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
 /* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
  * added before the unscale; a separate instance so the common case carries
  * no registers for it. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT>
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
 __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   const uint64_t tile = (uint64_t)kBlock * U * VEC;
   const uint64_t full = p.n / tile;  /* blocks past `full` cover the tail */
   bool bad = false;
   if (blockIdx.x < full) {
-    bad = fused_tile<VEC, U, MULTI, ACC, GDT, PDT>(p, (uint64_t)blockIdx.x * tile);
+    bad = fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE>(p, (uint64_t)blockIdx.x * tile);
   } else {
     /* ragged end: one element per thread, spread over enough blocks that
      * no thread walks a chain of them */

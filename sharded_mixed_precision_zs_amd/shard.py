@@ -41,8 +41,9 @@ class ShardState:
 
     def __init__(self, n, world, rank, offset, gather_len, param_dtype, grad_dtype,
                  opt: AdamW, loss_scale, dynamic=False, growth_interval=0,
-                 device="cuda", accumulate=False):
+                 device="cuda", accumulate=False, wire_dtype=zs.ZS_WIRE_FP32):
         self.n, self.world, self.rank, self.offset = n, world, rank, offset
+        self.wire_dtype = wire_dtype  # precision of the ring's partial sums
         self.param_dtype, self.grad_dtype = param_dtype, grad_dtype
         self.opt = opt
         f32 = dict(dtype=torch.float32, device=device)
@@ -135,7 +136,8 @@ class ShardState:
         acc += that mean (later micro-batches)."""
         zs.zs_reduce_scatter_avg(worker_grads, self.grad_dtype, self.world, self.rank, self.n,
                                  self.acc, accumulate=not first, overflow_flag=None,
-                                 loss_scale=self.loss_scale, stream=stream)
+                                 loss_scale=self.loss_scale, stream=stream,
+                                 wire_dtype=self.wire_dtype)
 
     # -- one optimizer step -------------------------------------------------
     def _args(self, worker_grads, acc_in):
@@ -148,7 +150,8 @@ class ShardState:
             args = zs.StepArgs(worker_grads, self.rank, self.n, src[0], src[1], src[2],
                                dst[0], dst[1], dst[2], self.gather[1 - self.cur], self.offset,
                                self.flags[0:1], self.hparams(), acc_in=acc_in,
-                               grad_dtype=self.grad_dtype, param_dtype=self.param_dtype)
+                               grad_dtype=self.grad_dtype, param_dtype=self.param_dtype,
+                               wire_dtype=self.wire_dtype)
             if len(self._prepared) > 16:
                 self._prepared.clear()
             self._prepared[key] = args

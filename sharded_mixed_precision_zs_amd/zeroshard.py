@@ -15,9 +15,10 @@ from typing import Optional, Sequence
 
 from . import build as _build
 
-ZS_ABI_VERSION = 1
+ZS_ABI_VERSION = 2
 ZS_MAX_WORLD = 64
 ZS_BF16, ZS_FP16 = 0, 1
+ZS_WIRE_FP32, ZS_WIRE_BF16, ZS_WIRE_FP16 = 0, 1, 2
 ZS_OK, ZS_ERR_INVALID_ARG, ZS_ERR_UNSUPPORTED, ZS_ERR_ALIAS, ZS_ERR_HIP = range(5)
 
 LIB_PATH = _build.LIB
@@ -44,7 +45,7 @@ class zs_step_args(C.Structure):
                 ("master_out", C.c_void_p), ("m_out", C.c_void_p), ("v_out", C.c_void_p),
                 ("gather_buf", C.c_void_p), ("gather_offset", C.c_uint64),
                 ("overflow_flag", C.c_void_p),
-                ("hp", zs_adamw_hparams)]
+                ("hp", zs_adamw_hparams), ("wire_dtype", C.c_int32)]
 
 
 class zs_loss_scaler(C.Structure):
@@ -64,7 +65,8 @@ def _load():
         "zs_status_string": ([i32], C.c_char_p),
         "zs_last_error": ([], C.c_char_p),
         "zs_partition": ([u64, u32, u32, C.POINTER(u64), C.POINTER(u64), C.POINTER(u64)], i32),
-        "zs_reduce_scatter_avg": ([C.POINTER(vp), i32, u32, u32, u64, vp, i32, vp, f32, vp], i32),
+        "zs_reduce_scatter_avg": ([C.POINTER(vp), i32, i32, u32, u32, u64, vp, i32, vp, f32, vp],
+                                  i32),
         "zs_check_overflow": ([vp, u64, f32, vp, vp], i32),
         "zs_adamw_step": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, vp], i32),
         "zs_cast_gather": ([vp, vp, i32, u64, u64, vp, vp], i32),
@@ -164,14 +166,16 @@ def _grad_array(worker_grads, n):
 
 def zs_reduce_scatter_avg(worker_grads: Sequence, grad_dtype: Optional[int], world: int,
                           rank: int, n: int, grad_part, accumulate=False,
-                          overflow_flag=None, loss_scale=1.0, stream=None):
+                          overflow_flag=None, loss_scale=1.0, stream=None,
+                          wire_dtype=ZS_WIRE_FP32):
     if len(worker_grads) != world:
         raise ValueError("len(worker_grads) must equal world")
     arr = _grad_array(worker_grads, n)
     dt = _dtype_code(worker_grads[0], grad_dtype) if world else 0
     _check("zs_reduce_scatter_avg", _lib.zs_reduce_scatter_avg(
-        arr, dt, world, rank, n, _ptr(grad_part, n, 4, "grad_part"), 1 if accumulate else 0,
-        _ptr(overflow_flag, 1, 4, "overflow_flag"), loss_scale, _stream(stream)))
+        arr, dt, wire_dtype, world, rank, n, _ptr(grad_part, n, 4, "grad_part"),
+        1 if accumulate else 0, _ptr(overflow_flag, 1, 4, "overflow_flag"), loss_scale,
+        _stream(stream)))
 
 
 def zs_check_overflow(grad_part, n, loss_scale, overflow_flag, stream=None):
@@ -202,7 +206,8 @@ class StepArgs:
 
     def __init__(self, worker_grads, rank, n, master_in, m_in, v_in, master_out, m_out, v_out,
                  gather_buf, gather_offset, overflow_flag, hp: zs_adamw_hparams,
-                 acc_in=None, grad_dtype=None, param_dtype=None, gather_in=None):
+                 acc_in=None, grad_dtype=None, param_dtype=None, gather_in=None,
+                 wire_dtype=ZS_WIRE_FP32):
         world = len(worker_grads)
         self._grads = _grad_array(worker_grads, n)
         a = zs_step_args()
@@ -222,6 +227,7 @@ class StepArgs:
         a.gather_offset = gather_offset
         a.overflow_flag = _ptr(overflow_flag, 1, 4, "overflow_flag")
         a.hp = hp
+        a.wire_dtype = wire_dtype
         self.args = a
 
     def set_grads(self, worker_grads):

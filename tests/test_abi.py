@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(zs):
     lib = C.CDLL(zs.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 1
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 2
 
 
 def test_status_strings(zs):
@@ -102,14 +102,17 @@ def test_reduce_rejects_bad_arguments(zs):
         (arr, 0, 3, 0, 10, ok_out, float("nan")),    # nan scale
     ]
     for a, dt, w, r, n, out, s in cases:
-        st = lib.zs_reduce_scatter_avg(a, dt, w, r, n, out, 0, None, s, None)
+        st = lib.zs_reduce_scatter_avg(a, dt, 0, w, r, n, out, 0, None, s, None)
         assert st == zs.ZS_ERR_INVALID_ARG, (w, r, dt, s)
         assert zs.zs_last_error()
     nulls = (C.c_void_p * 3)(FAKE, None, FAKE)
-    assert lib.zs_reduce_scatter_avg(nulls, 0, 3, 0, 10, ok_out, 0, None, 1.0, None) == \
+    assert lib.zs_reduce_scatter_avg(nulls, 0, 0, 3, 0, 10, ok_out, 0, None, 1.0, None) == \
         zs.ZS_ERR_INVALID_ARG
     # n == 0 is a no-op
-    assert lib.zs_reduce_scatter_avg(arr, 0, 3, 0, 0, ok_out, 0, None, 1.0, None) == zs.ZS_OK
+    for wire in (-1, 3):                             # bad wire dtype
+        assert lib.zs_reduce_scatter_avg(arr, 0, wire, 3, 0, 10, ok_out, 0, None, 1.0, None) == \
+            zs.ZS_ERR_INVALID_ARG
+    assert lib.zs_reduce_scatter_avg(arr, 0, 0, 3, 0, 0, ok_out, 0, None, 1.0, None) == zs.ZS_OK
 
 
 def test_other_entry_points_reject_bad_arguments(zs):
@@ -162,7 +165,7 @@ def test_fused_rejects_aliasing_and_bad_arguments(zs):
     a, keep = _fused_args(zs, acc_in=base + 0x400000)             # output on acc_in
     assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS
     for field, val in (("world", 0), ("world", 65), ("rank", 2), ("grad_dtype", 3),
-                       ("overflow_flag", None), ("master_in", None)):
+                       ("overflow_flag", None), ("master_in", None), ("wire_dtype", 5)):
         a, keep = _fused_args(zs, **{field: val})
         assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_INVALID_ARG, field
     a, keep = _fused_args(zs)

@@ -380,3 +380,57 @@ def test_widen_all_16bit_patterns(zs, dtype):
     zs.zs_reduce_scatter_avg([up16(bits, dtype)], None, 1, 0, bits.size, out, False, flag, 1.0)
     assert_bits_equal(down32(out), oracle.half_to_float(bits, dtype), f"widen {dtype}")
     assert int(flag.item()) == 1  # the NaN and inf patterns raise the flag
+
+
+# ---- 16-bit wire mode -------------------------------------------------------------
+
+WIRE = {"fp32": 0, "bf16": 1, "fp16": 2}
+
+
+@pytest.mark.parametrize("world", [2, 3, 8, 64])
+@pytest.mark.parametrize("dtype,wire", [("bf16", "bf16"), ("fp16", "fp16"), ("fp16", "bf16"),
+                                        ("bf16", "fp16")])
+def test_reduce_scatter_avg_wire(zs, world, dtype, wire):
+    rng = np.random.default_rng(world + 10 * WIRE[wire])
+    n = 5000 + 13 * world
+    for off in (0, 1):
+        rank = world - 1 if off else 0
+        announce(f"reduce wire={wire} W={world} {dtype} off={off}")
+        g16 = [rand16(rng, n + off, 1.0, dtype) for _ in range(world)]
+        views = [up16(g, dtype)[off:] for g in g16]
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+        flag = _flag()
+        zs.zs_reduce_scatter_avg(views, None, world, rank, n, out, False, flag, 1.0,
+                                 wire_dtype=WIRE[wire])
+        ref = np.empty(n, F32)
+        rflag = oracle.reduce_avg([g[off:] for g in g16], rank, dtype, ref, False, 1.0, wire=wire)
+        assert_bits_equal(down32(out), ref, f"wire {wire} mean")
+        assert int(flag.item()) == rflag
+
+
+@pytest.mark.parametrize("world", [1, 4, 64])
+@pytest.mark.parametrize("wire", ["bf16", "fp16"])
+def test_step_fused_wire(zs, world, wire):
+    rng = np.random.default_rng(world + 7)
+    gdt = "bf16" if wire == "bf16" else "fp16"
+    for n, with_acc in ((20_011, False), (4099, True)):
+        announce(f"fused wire={wire} W={world} n={n} acc={with_acc}")
+        g16 = [rand16(rng, n, 1e-3 * 1024, gdt) for _ in range(world)]
+        master = (rng.standard_normal(n) * 0.02).astype(F32)
+        m = (rng.standard_normal(n) * 1e-4).astype(F32)
+        v = rng.uniform(0, 1e-6, n).astype(F32)
+        acc = (rng.standard_normal(n) * 1.0).astype(F32) if with_acc else None
+        dout = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+        gather = torch.zeros(n, dtype=torch.int16, device="cuda")
+        flag = _flag()
+        args = zs.StepArgs([up16(g, gdt) for g in g16], 0, n, *[up32(x) for x in (master, m, v)],
+                           *dout, gather, 0, flag, zs.hparams(**HP, loss_scale=1024.0, step_t=2),
+                           acc_in=up32(acc) if with_acc else None, grad_dtype=DT[gdt],
+                           param_dtype=DT[gdt], wire_dtype=WIRE[wire])
+        zs.zs_step_fused(args)
+        f, mo, mmo, vo, po = oracle.shard_step(g16, 0, gdt, gdt, master, m, v, loss_scale=1024.0,
+                                               step_t=2, acc_in=acc, wire=wire, **HP)
+        assert int(flag.item()) == f
+        for got, want, what in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
+            assert assert_rel(down32(got), want, 1e-6, what) == 0
+        assert assert_ulp16(down16(gather), po, gdt, 1, "params") == 0

@@ -452,3 +452,79 @@ def test_ring_time_estimate_matches_the_pages():
         assert round(limit, int(digits)) == float(secs), " ".join(src)
         exact = oracle.ring_allreduce_time(float(msg), float(world), 0.0, float(beta))
         assert exact < limit
+
+
+# ---- 16-bit wire (partials rounded at every hop) ------------------------------------
+
+def test_wire_bf16_witnesses():
+    # W = 2, rank 0: the sum is G1 then + G0 (the owner's term last).
+    one = to_bf16_bits(np.array([1.0, 1.0, 1.0078125, 1.0], F32))
+    tiny = to_bf16_bits(np.array([2.0 ** -8, 3 * 2.0 ** -9, 2.0 ** -8, -2.0 ** -9], F32))
+    parts = [tiny, one]  # worker 0 = owner, worker 1 = successor
+    fp32 = oracle.ring_chunk_sum(parts, 0, "bf16")
+    wire = oracle.ring_chunk_sum(parts, 0, "bf16", wire="bf16")
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even -> 1
+    # 1 + 3*2^-9 is above the tie -> 1 + 2^-7
+    # 1.0078125 + 2^-8 is a tie between 1 + 2^-7 and 1 + 2^-6: even -> 1 + 2^-6
+    # 1 - 2^-9 is a tie between 1 - 2^-8 and 1 (spacing 2^-8 below 1): even -> 1
+    np.testing.assert_array_equal(wire, np.array([1.0, 1.0078125, 1.015625, 1.0], F32))
+    np.testing.assert_array_equal(fp32, np.array([1.00390625, 1.005859375, 1.01171875,
+                                                  0.998046875], F32))
+
+
+@pytest.mark.parametrize("wire,dtype,u", [("bf16", "bf16", 2.0 ** -8), ("fp16", "fp16", 2.0 ** -11)])
+@pytest.mark.parametrize("world", [2, 8, 64])
+def test_wire_rounding_bound_and_format(wire, dtype, u, world):
+    rng = np.random.default_rng(world)
+    n = 20000
+    if dtype == "bf16":
+        parts = [rand_bf16(rng, n, 1.0) for _ in range(world)]
+    else:
+        parts = [(rng.standard_normal(n)).astype(np.float16).view(np.uint16) for _ in range(world)]
+    vals = np.stack([oracle.half_to_float(p, dtype).astype(np.float64) for p in parts])
+    exact = vals.sum(axis=0)                         # |x| <= 2^16 terms: exact in binary64
+    got = oracle.ring_chunk_sum(parts, 0, dtype, wire=wire)
+    # every partial is rounded once (relative error <= u) after one fp32 add
+    # (<= 2^-24): |error| <= W (u + 2^-24)(1 + u) * sum|x|
+    bound = world * (u + 2.0 ** -24) * (1 + u) * np.abs(vals).sum(axis=0)
+    assert np.all(np.abs(got.astype(np.float64) - exact) <= bound)
+    # the result is a value of the wire format
+    assert np.array_equal(oracle.half_to_float(oracle.float_to_half(got, wire), wire), got)
+    # and the rounding is real: most sums differ from the fp32-wire ones
+    fp32 = oracle.ring_chunk_sum(parts, 0, dtype)
+    assert np.mean(got != fp32) > 0.5
+    assert np.array_equal(oracle.ring_chunk_sum(parts, 0, dtype, wire="fp32"), fp32)
+
+
+def test_wire_is_exact_when_every_partial_fits():
+    rng = np.random.default_rng(12)
+    ints = rng.integers(-8, 9, size=(16, 999))   # partial sums stay below 2^7
+    parts = [to_bf16_bits(ints[k].astype(F32)) for k in range(16)]
+    got = oracle.ring_chunk_sum(parts, 3, "bf16", wire="bf16")
+    np.testing.assert_array_equal(got.astype(np.int64), ints.sum(axis=0))
+
+
+def test_fp16_wire_overflow_raises_the_flag():
+    big = np.full(5, 60000.0, np.float16).view(np.uint16)
+    out = np.empty(5, F32)
+    assert oracle.reduce_avg([big, big], 0, "fp16", out, False, 1.0) == 0
+    assert np.all(out == 60000.0)                    # fp32 partials: 120000 / 2
+    assert oracle.reduce_avg([big, big], 0, "fp16", out, False, 1.0, wire="fp16") == 1
+    assert np.all(np.isinf(out))                     # 120000 overflows binary16
+
+
+def test_shard_step_carries_the_wire():
+    rng = np.random.default_rng(31)
+    parts = [rand_bf16(rng, 3000, 1.0) for _ in range(8)]
+    master = (rng.standard_normal(3000) * 0.02).astype(F32)
+    z = np.zeros(3000, F32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, loss_scale=1.0,
+              step_t=1)
+    f, mo, mmo, vo, po = oracle.shard_step(parts, 2, "bf16", "bf16", master, z, z, wire="bf16",
+                                           **hp)
+    a = np.empty(3000, F32)
+    oracle.reduce_avg(parts, 2, "bf16", a, False, 1.0, wire="bf16")
+    m2, mm2, v2 = master.copy(), z.copy(), z.copy()
+    oracle.adamw(m2, mm2, v2, a, 1.0, 1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    np.testing.assert_array_equal(mo, m2)
+    np.testing.assert_array_equal(mmo, mm2)
