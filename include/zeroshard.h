@@ -190,6 +190,24 @@ typedef struct {
 
 int zs_step_fused(const zs_step_args *args, void *stream);
 
+/* One step of the ring all-gather of the 16-bit parameters over `world`
+ * replicas of the flat buffer held on this GPU ([Notes] 二: each GPU passes
+ * the chunk it holds to its successor, and after W-1 steps every GPU holds
+ * every chunk; [Intro] (12) and [L7] "ZeRO Stage 1": AllGather of the
+ * updated parameters). Chunks are the partition of zs_partition:
+ * chunk c = elements [c*P, min(phi, (c+1)*P)), P = ceil(phi / world).
+ * At step s (1 <= s < world) replica k's chunk (k + sigma - s + 1) mod W is
+ * copied into replica (k + 1) mod W at the same offset; with sigma = 0 rank
+ * k starts out holding chunk k (ZeRO's owner layout), sigma = 1 replays the
+ * page's labelling. Running s = 1 .. W-1 in order on one stream completes
+ * the gather.
+ *   replicas: host array of `world` device pointers, each to phi 16-bit
+ *             elements; they must not overlap (ZS_ERR_ALIAS).
+ * Errors: ZS_ERR_INVALID_ARG for null pointers, world == 0 or > 64,
+ * sigma >= world, step outside [1, world). */
+int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint32_t sigma,
+                       uint32_t step, void *stream);
+
 /* Host-side commit/skip bookkeeping of dynamic loss scaling ([Intro] 一.3
  * items (1) and (3) name it without a rule). With dynamic != 0: on overflow
  * the scale halves, clean_steps resets and step_t stays; otherwise

@@ -496,6 +496,43 @@ int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host
   return zs_scaler_update(scaler, flag);
 }
 
+int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint32_t sigma,
+                       uint32_t step, void *stream) {
+  if (!replicas) return fail(ZS_ERR_INVALID_ARG, "null replicas%s");
+  if (world == 0 || world > ZS_MAX_WORLD)
+    return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64%s");
+  if (sigma >= world || step == 0 || step >= world)
+    return fail(ZS_ERR_INVALID_ARG, "need sigma < world and 1 <= step < world%s");
+  GatherArgs g;
+  for (uint32_t k = 0; k < world; ++k) {
+    if (!replicas[k]) return fail(ZS_ERR_INVALID_ARG, "replicas has a null pointer%s");
+    g.r[k] = static_cast<uint16_t *>(replicas[k]);
+  }
+  for (uint32_t k = world; k < ZS_MAX_WORLD; ++k) g.r[k] = nullptr;
+  for (uint32_t i = 0; i < world; ++i)
+    for (uint32_t j = i + 1; j < world; ++j)
+      if (overlaps(g.r[i], 2 * phi, g.r[j], 2 * phi))
+        return fail(ZS_ERR_ALIAS, "zs_all_gather_step: replicas overlap%s");
+  g.world = world;
+  g.sigma = sigma;
+  g.step = step;
+  g.phi = phi;
+  g.chunk = phi / world + (phi % world != 0);
+  if (phi == 0) return ZS_OK;
+  /* 16-byte copies need every replica 16-byte aligned and chunk starts at
+   * multiples of 8 elements. */
+  bool wide = g.chunk % 8 == 0;
+  for (uint32_t k = 0; k < world && wide; ++k) wide = ((uintptr_t)g.r[k] % 16) == 0;
+  const int vec = wide ? 8 : 1;
+  const uint64_t blocks = (g.chunk + (uint64_t)kBlock * vec - 1) / ((uint64_t)kBlock * vec);
+  if (blocks > 0x7fffffffull) return fail(ZS_ERR_UNSUPPORTED, "chunk too large for one launch%s");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 grid((unsigned)blocks, world), block(kBlock);
+  if (wide) hipLaunchKernelGGL(gather_step_kernel<8>, grid, block, 0, s, g);
+  else hipLaunchKernelGGL(gather_step_kernel<1>, grid, block, 0, s, g);
+  return launch_result();
+}
+
 int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow) {
   if (!s) return fail(ZS_ERR_INVALID_ARG, "null scaler%s");
   if (overflow) {

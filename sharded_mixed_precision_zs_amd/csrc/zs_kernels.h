@@ -576,6 +576,45 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   flag_or(p.flag, bad);
 }
 
+/* ------------------------------------------------------------------------
+ * One step of the ring all-gather over W replicas of the flat 16-bit
+ * parameter buffer ([Notes] 二: after the scatter-reduce each GPU passes the
+ * chunk total it holds to its successor; after W-1 such steps every GPU has
+ * every chunk; [L7] "Ring AllReduce 算法", phase two). Rank k sends chunk
+ * c_k = (k + sigma - step + 1) mod W to rank k+1. blockIdx.y is the sender;
+ * each thread copies 8 elements (16 bytes) or, on the ragged end or with
+ * misaligned chunks, one at a time.
+ * ---------------------------------------------------------------------- */
+
+struct GatherArgs {
+  uint16_t *r[ZS_MAX_WORLD];   /* replica k's flat buffer */
+  uint32_t world, sigma, step;
+  uint64_t phi, chunk;
+};
+
+template <int VEC>
+__global__ __launch_bounds__(kBlock) void gather_step_kernel(GatherArgs a) {
+  const uint32_t k = blockIdx.y;
+  const uint32_t c = (uint32_t)(((uint64_t)k + a.sigma + (uint64_t)a.world * a.step - a.step + 1) %
+                                a.world);
+  const uint64_t begin = (uint64_t)c * a.chunk;
+  if (begin >= a.phi) return;
+  const uint64_t len = a.phi - begin < a.chunk ? a.phi - begin : a.chunk;
+  const uint16_t *src = a.r[k] + begin;
+  uint16_t *dst = a.r[(k + 1) % a.world] + begin;
+  const uint64_t i0 = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * VEC;
+  if (i0 >= len) return;
+  if (VEC > 1 && i0 + VEC <= len) {
+    Raw16<VEC> v = ld16<VEC, true>(src + i0);
+    if constexpr (VEC == 8) {
+      u32x4 w = {v.w[0], v.w[1], v.w[2], v.w[3]};
+      *reinterpret_cast<u32x4 *>(dst + i0) = w;
+    }
+  } else {
+    for (uint64_t i = i0; i < len && i < i0 + VEC; ++i) dst[i] = src[i];
+  }
+}
+
 }  // namespace zs
 
 #endif /* ZS_KERNELS_H */

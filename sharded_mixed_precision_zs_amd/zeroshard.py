@@ -74,6 +74,7 @@ def _load():
         "zs_scaler_update": ([C.POINTER(zs_loss_scaler), u32], i32),
         "zs_step_commit": ([C.POINTER(zs_step_args), C.POINTER(zs_loss_scaler), vp, vp, vp, vp,
                             C.POINTER(C.c_int)], i32),
+        "zs_all_gather_step": ([C.POINTER(vp), u32, u64, u32, u32, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -265,3 +266,11 @@ def zs_step_commit(args, scaler: zs_loss_scaler, host_flag, stream=None, ev_star
                                                  _stream(stream), ev_start, ev_stop,
                                                  C.byref(committed)))
     return bool(committed.value)
+
+
+def zs_all_gather_step(replicas: Sequence, phi: int, step: int, sigma: int = 0, stream=None):
+    """One ring all-gather step over len(replicas) flat 16-bit buffers."""
+    ptrs = [_ptr(r, phi, 2, f"replicas[{k}]") for k, r in enumerate(replicas)]
+    arr = (C.c_void_p * len(ptrs))(*ptrs)
+    _check("zs_all_gather_step", _lib.zs_all_gather_step(arr, len(ptrs), phi, sigma, step,
+                                                         _stream(stream)))

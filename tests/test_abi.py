@@ -202,3 +202,20 @@ def test_step_commit_rejects_bad_arguments(zs):
     assert lib.zs_step_commit(C.byref(empty), C.byref(good), C.byref(hf), None, None, None,
                               C.byref(ok)) == zs.ZS_OK
     assert ok.value == 1 and good.step_t == 1
+
+
+def test_all_gather_step_rejects_bad_arguments(zs):
+    lib = _raw(zs)
+    reps = (C.c_void_p * 3)(FAKE, FAKE + 0x100000, FAKE + 0x200000)
+    E = zs.ZS_ERR_INVALID_ARG
+    assert lib.zs_all_gather_step(None, 3, 1000, 0, 1, None) == E
+    assert lib.zs_all_gather_step(reps, 0, 1000, 0, 1, None) == E
+    assert lib.zs_all_gather_step(reps, 65, 1000, 0, 1, None) == E
+    assert lib.zs_all_gather_step(reps, 3, 1000, 3, 1, None) == E    # sigma >= world
+    assert lib.zs_all_gather_step(reps, 3, 1000, 0, 0, None) == E    # step 0
+    assert lib.zs_all_gather_step(reps, 3, 1000, 0, 3, None) == E    # step >= world
+    nul = (C.c_void_p * 3)(FAKE, None, FAKE + 0x200000)
+    assert lib.zs_all_gather_step(nul, 3, 1000, 0, 1, None) == E
+    close = (C.c_void_p * 3)(FAKE, FAKE + 1000, FAKE + 0x200000)  # 2*phi bytes overlap
+    assert lib.zs_all_gather_step(close, 3, 1000, 0, 1, None) == zs.ZS_ERR_ALIAS
+    assert lib.zs_all_gather_step(reps, 3, 0, 0, 1, None) == zs.ZS_OK  # phi == 0

@@ -434,3 +434,85 @@ def test_step_fused_wire(zs, world, wire):
         for got, want, what in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
             assert assert_rel(down32(got), want, 1e-6, what) == 0
         assert assert_ulp16(down16(gather), po, gdt, 1, "params") == 0
+
+
+# ---- ring all-gather of the parameters --------------------------------------------
+
+def test_all_gather_replays_the_three_gpu_example(zs):
+    """[Notes] 二: after the scatter-reduce GPU k holds the total of chunk
+    k+1 (sigma = 1); the golden file lists which totals each GPU holds after
+    each all-gather step."""
+    from conftest import golden_rows
+    L, W = 1000, 3
+    totals = [up16(np.full(L, bits, np.uint16), "bf16") for bits in (0x3F80, 0x4000, 0x4040)]
+    reps = [torch.zeros(W * L, dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    for k in range(W):
+        c = (k + 1) % W
+        reps[k][c * L:(c + 1) * L] = totals[c]
+    names = {"A": 0, "B": 1, "C": 2}
+    for step in (1, 2):
+        announce(f"all-gather example step {step}")
+        zs.zs_all_gather_step(reps, W * L, step, sigma=1)
+        for row in golden_rows("ring_three_gpu_example.txt"):
+            if row[0] == "all_gather" and int(row[1]) == step:
+                gpu, c = int(row[2]), names[row[3]]
+                got = down16(reps[gpu][c * L:(c + 1) * L].view(torch.int16))
+                assert np.all(got == down16(totals[c].view(torch.int16))), (step, row)
+    for k in range(W):  # every GPU holds every total
+        for c in range(W):
+            assert torch.equal(reps[k][c * L:(c + 1) * L], totals[c])
+
+
+@pytest.mark.parametrize("world,phi,sigma", [(2, 100_000, 0), (3, 100_003, 1), (5, 77_777, 0),
+                                             (8, 1 << 20, 0), (64, 1_000_001, 0), (64, 64 * 4096, 1)])
+def test_all_gather_matches_the_oracle(zs, world, phi, sigma):
+    rng = np.random.default_rng(world + phi)
+    P = -(-phi // world)
+    announce(f"all-gather W={world} phi={phi} sigma={sigma}")
+    data = rng.integers(0, 1 << 16, size=(world, phi), dtype=np.uint64).astype(np.uint16)
+    reps = [up16(data[k], "bf16") for k in range(world)]
+
+    def oracle_after(steps):
+        ref = np.zeros((world, world * P), F32)
+        ref[:, :phi] = np.stack([oracle.half_to_float(d, "bf16") for d in data])
+        return oracle.ring_all_gather(np.ascontiguousarray(ref), sigma, steps)[:, :phi]
+
+    for step in range(1, world):
+        zs.zs_all_gather_step(reps, phi, step, sigma=sigma)
+        if step in (1, world // 2, world - 1):
+            got = np.stack([oracle.half_to_float(down16(r.view(torch.int16)), "bf16")
+                            for r in reps])
+            assert_bits_equal(got, oracle_after(step), f"after step {step}")
+
+
+def test_sharded_step_over_all_ranks_then_all_gather(zs):
+    """A whole ZeRO-2 step for W ranks on one GPU: every rank's fused step
+    on its own partition (gradients reduced in that rank's ring order), then
+    the ring all-gather; every replica must hold the oracle's parameters."""
+    rng = np.random.default_rng(77)
+    W, phi = 4, 4 * 50_003 + 3
+    P = -(-phi // W)
+    announce(f"sharded step W={W} phi={phi}")
+    grads = [rand16(rng, phi, 1e-3 * 1024, "bf16") for _ in range(W)]
+    master = (rng.standard_normal(phi) * 0.02).astype(F32)
+    dgrads = [up16(g, "bf16") for g in grads]
+    reps = [torch.zeros(phi, dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    want = np.empty(phi, np.uint16)
+    for r in range(W):
+        p, off, cnt = oracle.partition(phi, W, r)
+        din = [up32(master[off:off + cnt]), up32(np.zeros(cnt, F32)), up32(np.zeros(cnt, F32))]
+        dout = [torch.empty(cnt, dtype=torch.float32, device="cuda") for _ in range(3)]
+        args = zs.StepArgs([g[off:off + cnt] for g in dgrads], r, cnt, *din, *dout, reps[r], off,
+                           flags[r:r + 1], zs.hparams(**HP, loss_scale=1024.0, step_t=1))
+        zs.zs_step_fused(args)
+        f, mo, mmo, vo, po = oracle.shard_step([g[off:off + cnt] for g in grads], r, "bf16",
+                                               "bf16", master[off:off + cnt],
+                                               np.zeros(cnt, F32), np.zeros(cnt, F32),
+                                               loss_scale=1024.0, step_t=1, **HP)
+        want[off:off + cnt] = po
+    for step in range(1, W):
+        zs.zs_all_gather_step(reps, phi, step)
+    assert not flags.any()
+    for k in range(W):
+        assert np.array_equal(down16(reps[k].view(torch.int16)), want), k
