@@ -208,6 +208,25 @@ int zs_step_fused(const zs_step_args *args, void *stream);
 int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint32_t sigma,
                        uint32_t step, void *stream);
 
+/* ZeRO-Offload update on the host ([Intro] 一.3 item (16): the update is
+ * cheap, so optimizer states and gradients live in CPU memory while the
+ * forward and backward stay on the GPU). The reduction stays on the GPU
+ * (zs_reduce_scatter_avg); the caller copies the fp32 averaged gradient
+ * partition to host memory, calls this, and copies the 16-bit parameters
+ * back into the gather buffer.
+ *   Pass 1: *overflow = 1 if any grad_part[i] / loss_scale is not finite;
+ *           then nothing is written (the step is skipped).
+ *   Pass 2: master, m, v updated in place with exactly the arithmetic of
+ *           zs_adamw_step, and params16[i] = RNE16(master'[i]).
+ *   master, m, v, grad_part: host fp32[n]; params16: host 16-bit[n].
+ *   threads: worker threads (<= 0: the machine's hardware threads, at most
+ *            64); every range runs with round-to-nearest, subnormals kept.
+ * Blocks until done. Errors: ZS_ERR_INVALID_ARG for null pointers, a bad
+ * param dtype, a non-finite or non-positive loss scale, step_t == 0. */
+int zs_cpu_step(float *master, float *m, float *v, const float *grad_part, uint64_t n,
+                const zs_adamw_hparams *hp, void *params16, int param_dtype, int threads,
+                uint32_t *overflow);
+
 /* Host-side commit/skip bookkeeping of dynamic loss scaling ([Intro] 一.3
  * items (1) and (3) name it without a rule). With dynamic != 0: on overflow
  * the scale halves, clean_steps resets and step_t stays; otherwise

@@ -1,6 +1,7 @@
 """Build the in-tree shared libraries of the package.
 
   libzeroshard.so        the shard-step library (HIP, gfx950)  <- csrc/zeroshard.hip
+                         + its host-side offload update (gcc) <- csrc/offload_cpu.cpp
   synth/libzssynth_dev.so   device twin of the input generator (HIP, gfx950)
   synth/libzssynth_host.so  host twin of the input generator (gcc)
 
@@ -43,8 +44,18 @@ def _hip_lib(src, out, verbose, extra=()):
     os.replace(tmp, out)
 
 
+# Host half of the library (the ZeRO-Offload update): gcc, no contraction so
+# vector mul/add stay separate IEEE operations; F16C for the fp16 convert.
+CPU_FLAGS = ["-O3", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-mf16c", "-fPIC",
+             "-Wall", "-Wextra", "-pthread"]
+
+
 def build_zeroshard(verbose=False):
-    _hip_lib(os.path.join(PKG, "csrc", "zeroshard.hip"), LIB, verbose)
+    obj = os.path.join(PKG, "csrc", "offload_cpu.o")
+    _run(["g++", *CPU_FLAGS, "-I", INCLUDE, "-c", os.path.join(PKG, "csrc", "offload_cpu.cpp"),
+          "-o", obj], verbose)
+    _hip_lib(os.path.join(PKG, "csrc", "zeroshard.hip"), LIB, verbose, extra=[obj, "-pthread"])
+    os.remove(obj)
     return LIB
 
 

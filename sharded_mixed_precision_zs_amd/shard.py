@@ -204,3 +204,72 @@ class ShardState:
         if ok:
             self.cur = 1 - self.cur
         return ok
+
+
+class OffloadShard:
+    """ZeRO-Offload variant of one rank's shard (the DeepSpeed introduction,
+    item (16)): fp32 master, m and v live in host memory and the update runs
+    on the host (zs_cpu_step); the GPU keeps the W-way ring-order reduction
+    (zs_reduce_scatter_avg) and the 16-bit parameters. Per step, 4 bytes per
+    parameter cross PCIe to the host (the averaged fp32 gradient) and 2 back
+    (the parameters), against the fused GPU step's 12 B/param of optimizer
+    state kept in HBM. The arithmetic is the fused step's, element for
+    element, so both variants produce the same bits."""
+
+    def __init__(self, n, world, rank, offset, gather_len, param_dtype, grad_dtype,
+                 opt: AdamW, loss_scale, dynamic=False, growth_interval=0, device="cuda",
+                 threads=0, wire_dtype=zs.ZS_WIRE_FP32):
+        self.n, self.world, self.rank, self.offset = n, world, rank, offset
+        self.param_dtype, self.grad_dtype, self.opt = param_dtype, grad_dtype, opt
+        self.threads, self.wire_dtype = threads, wire_dtype
+        pdt = torch.bfloat16 if param_dtype == zs.ZS_BF16 else torch.float16
+        self.master = torch.empty(n, dtype=torch.float32)
+        self.m = torch.zeros(n, dtype=torch.float32)
+        self.v = torch.zeros(n, dtype=torch.float32)
+        self.grad = torch.empty(n, dtype=torch.float32, device=device)   # reduced, on the GPU
+        self.grad_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
+        self.params_host = torch.empty(n, dtype=pdt, pin_memory=True)
+        self.gather = torch.zeros(gather_len, dtype=pdt, device=device)
+        self.scaler = zs.zs_loss_scaler(scale=loss_scale, clean_steps=0,
+                                        growth_interval=growth_interval,
+                                        dynamic=1 if dynamic else 0, step_t=0, skipped=0)
+        self.last_flag = 0
+
+    @property
+    def params(self):
+        return self.gather[self.offset:self.offset + self.n]
+
+    @property
+    def t(self):
+        return int(self.scaler.step_t)
+
+    @property
+    def loss_scale(self):
+        return float(self.scaler.scale)
+
+    def reduce_micro(self, worker_grads, first: bool, stream=None):
+        """Reduce one micro-batch's gradients into the device partition."""
+        zs.zs_reduce_scatter_avg(worker_grads, self.grad_dtype, self.world, self.rank, self.n,
+                                 self.grad, accumulate=not first, overflow_flag=None,
+                                 loss_scale=self.loss_scale, stream=stream,
+                                 wire_dtype=self.wire_dtype)
+
+    def step(self, worker_grads=None, first=True, stream=None):
+        """Reduce the last micro-batch (unless worker_grads is None, when it
+        was reduced already), move the gradient to the host, update there,
+        and move the parameters back. Returns True when committed."""
+        s = stream if stream is not None else torch.cuda.current_stream()
+        if worker_grads is not None:
+            self.reduce_micro(worker_grads, first, stream)
+        self.grad_host.copy_(self.grad, non_blocking=True)
+        s.synchronize()
+        o = self.opt
+        hp = zs.hparams(o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.loss_scale,
+                        self.t + 1)
+        flag = zs.zs_cpu_step(self.master, self.m, self.v, self.grad_host, hp, self.params_host,
+                              self.param_dtype, self.threads)
+        if flag == 0:
+            self.params.copy_(self.params_host, non_blocking=True)
+        zs.zs_scaler_update(self.scaler, flag)
+        self.last_flag = flag
+        return flag == 0

@@ -75,6 +75,8 @@ def _load():
         "zs_step_commit": ([C.POINTER(zs_step_args), C.POINTER(zs_loss_scaler), vp, vp, vp, vp,
                             C.POINTER(C.c_int)], i32),
         "zs_all_gather_step": ([C.POINTER(vp), u32, u64, u32, u32, vp], i32),
+        "zs_cpu_step": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, i32, i32,
+                         C.POINTER(u32)], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -274,3 +276,29 @@ def zs_all_gather_step(replicas: Sequence, phi: int, step: int, sigma: int = 0, 
     arr = (C.c_void_p * len(ptrs))(*ptrs)
     _check("zs_all_gather_step", _lib.zs_all_gather_step(arr, len(ptrs), phi, sigma, step,
                                                          _stream(stream)))
+
+
+def zs_cpu_step(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param_dtype=None,
+                threads=0):
+    """ZeRO-Offload update on host tensors/arrays (torch CPU tensors or numpy
+    arrays, contiguous). Returns the overflow flag (1: skipped)."""
+    def hptr(x, elem, what):
+        if hasattr(x, "data_ptr"):
+            if x.is_cuda or not x.is_contiguous() or x.element_size() != elem:
+                raise ValueError(f"{what}: contiguous host tensor of {elem}-byte elements expected")
+            return x.data_ptr(), x.numel()
+        if not x.flags.c_contiguous or x.itemsize != elem:
+            raise ValueError(f"{what}: contiguous array of {elem}-byte elements expected")
+        return x.ctypes.data, x.size
+    (pm, n), (p1, n1), (p2, n2), (pg, n3) = (hptr(master, 4, "master"), hptr(m, 4, "m"),
+                                              hptr(v, 4, "v"), hptr(grad_part, 4, "grad_part"))
+    pp, n4 = hptr(params16, 2, "params16")
+    if not (n == n1 == n2 == n3 <= n4):
+        raise ValueError("zs_cpu_step: size mismatch")
+    if param_dtype is None:
+        param_dtype = _dtype_code(params16, None) if hasattr(params16, "dtype") and \
+            str(params16.dtype).startswith("torch") else ZS_BF16
+    flag = C.c_uint32(0)
+    _check("zs_cpu_step", _lib.zs_cpu_step(pm, p1, p2, pg, n, C.byref(hp), pp, param_dtype,
+                                           threads, C.byref(flag)))
+    return int(flag.value)

@@ -202,3 +202,44 @@ def test_checkpoint_resume_is_bit_identical(env, tmp_path):
     assert (b.t, b.loss_scale, int(b.scaler.skipped)) == (ref.t, ref.loss_scale,
                                                           int(ref.scaler.skipped))
     assert int(ref.scaler.skipped) == 2
+
+
+@pytest.mark.parametrize("name,phi", [("gpt2s-w8", 8 * 250_003), ("1p3b-w4-acc4-fp16", 4 * 200_001)])
+def test_offload_equals_fused(env, name, phi):
+    """The ZeRO-Offload variant (reduce on the GPU, update on the host) and
+    the fused GPU step produce the same bits, skipped steps included."""
+    zs, synth, shard = env
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS[name], phi=phi, name=name + "-offload",
+                             steps=6, inject_steps=(3,) if name.startswith("1p3b") else ())
+    n, W, A = wl.n, wl.world, wl.accum
+    opt = shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay)
+    kw = dict(dynamic=wl.dynamic_scale, growth_interval=wl.scale_interval)
+    gpu = shard.ShardState(n, W, 0, 0, n, wl.param_dtype, wl.grad_dtype, opt, wl.loss_scale,
+                           accumulate=A > 1, **kw)
+    off = shard.OffloadShard(n, W, 0, 0, n, wl.param_dtype, wl.grad_dtype, opt, wl.loss_scale,
+                             threads=8, **kw)
+    synth.dev_state(wl, 0, gpu.master, gpu.m, gpu.v)
+    off.master.copy_(gpu.master.cpu())
+    off.m.copy_(gpu.m.cpu())
+    off.v.copy_(gpu.v.cpu())
+    grads = torch.empty((W, -(-n // 128) * 128), dtype=torch.int16, device="cuda")
+    g = [grads[k, :n] for k in range(W)]
+    for step in range(1, wl.steps + 1):
+        announce(f"offload vs fused {name} step {step}")
+        assert gpu.loss_scale == off.loss_scale
+        for j in range(A):
+            for k in range(W):
+                synth.dev_grad(wl, k, step, j, 0, g[k], scale=gpu.loss_scale)
+            if j < A - 1:
+                gpu.reduce_micro(g, first=(j == 0))
+                off.reduce_micro(g, first=(j == 0))
+            else:
+                ok1 = gpu.step(g, acc_in=gpu.acc if A > 1 else None)
+                ok2 = off.step(g, first=(A == 1))
+                assert ok1 == ok2
+    torch.cuda.synchronize()
+    for x, y in ((gpu.master, off.master), (gpu.m, off.m), (gpu.v, off.v)):
+        assert_bits_equal(down32(x), y.numpy(), f"{name} offload state")
+    assert np.array_equal(down16(gpu.params.view(torch.int16)), down16(off.params.view(torch.int16)))
+    assert (gpu.t, gpu.loss_scale) == (off.t, off.loss_scale)

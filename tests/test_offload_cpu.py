@@ -1,0 +1,114 @@
+"""The ZeRO-Offload host update (zs_cpu_step) against the oracle (CPU only).
+
+zs_cpu_step is product code that runs on the host: AdamW and the 16-bit
+cast on CPU memory, AVX-512 where available. It must equal the oracle's
+arithmetic bit for bit (fp32 state) and the oracle's round-to-nearest-even
+casts (16-bit parameters, NaN by class).
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def zs(hip_built):
+    from sharded_mixed_precision_zs_amd import zeroshard
+    return zeroshard
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _inputs(rng, n, scale):
+    master = (rng.standard_normal(n) * 0.02).astype(F32)
+    m = (rng.standard_normal(n) * 1e-4).astype(F32)
+    v = rng.uniform(0, 1e-6, n).astype(F32)
+    a = (rng.standard_normal(n) * 1e-3 * scale).astype(F32)
+    return master, m, v, a
+
+
+def _nan_class_equal(x, y):
+    return np.array_equal(np.isnan(x), np.isnan(y)) and \
+        np.array_equal(x[~np.isnan(x)].view(np.uint32), y[~np.isnan(y)].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("n,threads", [(1, 1), (15, 1), (16, 1), (100_003, 1), (100_003, 3),
+                                       (1_000_000, 0)])
+def test_cpu_step_matches_oracle(zs, dtype, n, threads):
+    rng = np.random.default_rng(n + threads)
+    for scale, t in ((1.0, 1), (1024.0, 7), (3.0, 300)):
+        master, m, v, a = _inputs(rng, n, scale)
+        got = [x.copy() for x in (master, m, v)]
+        params = np.full(n, 7, np.uint16)
+        hp = zs.hparams(**HP, loss_scale=scale, step_t=t)
+        flag = zs.zs_cpu_step(*got, a, hp, params, zs.ZS_BF16 if dtype == "bf16" else zs.ZS_FP16,
+                              threads)
+        assert flag == 0
+        oracle.adamw(master, m, v, a, scale, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"],
+                     HP["weight_decay"], t)
+        for x, y in zip(got, (master, m, v)):
+            assert _nan_class_equal(x, y)
+        assert np.array_equal(params, oracle.float_to_half(master, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_cpu_step_special_values_and_casts(zs, dtype):
+    """Masters chosen to land on rounding ties, subnormals and overflow of the
+    16-bit format; the update itself is made the identity (lr = wd = 0)."""
+    rng = np.random.default_rng(5)
+    pats = np.concatenate([
+        (np.arange(1 << 16, dtype=np.uint32) << 16) | 0x8000,      # bf16 ties
+        (np.arange(1 << 16, dtype=np.uint32) << 16) | 0x7FFF,
+        rng.integers(0, 1 << 32, 1 << 18, dtype=np.uint64).astype(np.uint32),
+    ]).view(F32)
+    n = pats.size
+    master = pats.copy()
+    m = np.zeros(n, F32)
+    v = np.zeros(n, F32)
+    a = np.zeros(n, F32)
+    params = np.empty(n, np.uint16)
+    hp = zs.hparams(0.0, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
+    zs.zs_cpu_step(master, m, v, a, hp, params, zs.ZS_BF16 if dtype == "bf16" else zs.ZS_FP16, 4)
+    want = oracle.float_to_half(pats, dtype)
+    nanmask = 0x7F80 if dtype == "bf16" else 0x7C00
+    frac = 0x007F if dtype == "bf16" else 0x03FF
+
+    def isnan(b):
+        b = b.astype(np.int32)
+        return ((b & nanmask) == nanmask) & ((b & frac) != 0)
+    assert np.array_equal(isnan(params), isnan(want))
+    assert np.array_equal(params[~isnan(want)], want[~isnan(want)])
+
+
+def test_cpu_step_skips_on_overflow(zs):
+    rng = np.random.default_rng(6)
+    n = 50_000
+    master, m, v, a = _inputs(rng, n, 1.0)
+    for pos, val in ((0, np.inf), (n - 1, -np.inf), (31_337, np.nan)):
+        x = a.copy()
+        x[pos] = val
+        st = [y.copy() for y in (master, m, v)]
+        params = np.full(n, 7, np.uint16)
+        assert zs.zs_cpu_step(*st, x, zs.hparams(**HP, loss_scale=1.0, step_t=1), params,
+                              zs.ZS_BF16, 2) == 1
+        for y, z in zip(st, (master, m, v)):
+            assert np.array_equal(y.view(np.uint32), z.view(np.uint32))
+        assert np.all(params == 7)
+
+
+def test_cpu_step_rejects_bad_arguments(zs):
+    x = np.zeros(10, F32)
+    p = np.zeros(10, np.uint16)
+    with pytest.raises(zs.ZsError):
+        zs.zs_cpu_step(x, x.copy(), x.copy(), x.copy(), zs.hparams(**HP, loss_scale=0.0, step_t=1),
+                       p, zs.ZS_BF16)
+    with pytest.raises(zs.ZsError):
+        zs.zs_cpu_step(x, x.copy(), x.copy(), x.copy(), zs.hparams(**HP, loss_scale=1.0, step_t=0),
+                       p, zs.ZS_BF16)
+    with pytest.raises(zs.ZsError):
+        zs.zs_cpu_step(x, x.copy(), x.copy(), x.copy(), zs.hparams(**HP, loss_scale=1.0, step_t=1),
+                       p, 9)
