@@ -2,10 +2,12 @@
 
 One step = one pass of the whole shard step over one batch of synthetic
 gradients already resident in HBM: ring-order W-way fp32 sum, average,
-unscale, overflow check, AdamW, cast into the gather buffer (one
-zs_step_fused launch), plus the 4-byte flag readback and the commit/skip
-bookkeeping on the host. Inputs come from the seeded generator, on the
-device.
+unscale, overflow check, AdamW, cast into the gather buffer (the fused
+kernel), then the commit or skip with its loss-scaler update on the device
+(zs_step_device: the commit kernel), steps queued back to back. The same
+step with the decision taken on the host (zs_step_commit: 4-byte flag
+readback, scaler on the host, one wait per step) is reported beside it
+under `host_commit`. Inputs come from the seeded generator, on the device.
 
 Prints ONE JSON line (rank 0). `value` is parameters updated per second of
 the chosen workload; the HBM side of the metric is in `hbm_gbps`,
@@ -32,10 +34,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak (vendor figure)
 DEFAULT_WORKLOAD = "gpt2s-w8"   # GPT-2-small-shaped flat model, W = 8
-DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1"
+DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1,1p3b-w4-acc4-fp16"
 KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zs_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.md")
-EVENT_EVERY = 2
+EVENT_EVERY = 4
 METRIC = "params updated/sec per ZeRO-2 shard step + achieved HBM GB/s (% of peak)"
 
 
@@ -124,7 +126,7 @@ def replicas_for(wl, bytes_per_step):
     return max(1, min(8, -(-(1 << 30) // max(bytes_per_step, 1))))
 
 
-def run_workload(name, steps, warmup, torch, wire=0):
+def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
     from sharded_mixed_precision_zs_amd import shard, synth
 
     wl = synth.WORKLOADS[name]
@@ -142,7 +144,7 @@ def run_workload(name, steps, warmup, torch, wire=0):
         st = shard.ShardState(n, W, wl.rank, wl.offset, wl.offset + n, wl.param_dtype,
                               wl.grad_dtype, opt, wl.loss_scale, dynamic=wl.dynamic_scale,
                               growth_interval=wl.scale_interval, accumulate=A > 1,
-                              wire_dtype=wire)
+                              wire_dtype=wire, device_commit=device_commit)
         synth.dev_state(wl, wl.offset, st.master, st.m, st.v)
         # one row per worker, rows padded to 256 B like separate allocations
         grads = torch.empty((A, W, pad_elems(n)), dtype=torch.int16, device="cuda")
@@ -160,31 +162,38 @@ def run_workload(name, steps, warmup, torch, wire=0):
         st, g = reps[i % R]
         for j in range(A - 1):
             st.reduce_micro(g[j], first=(j == 0))
-        if events is None:
-            return st.step()
-        return st.step(ev_start=events[0], ev_stop=events[1])
+        ev = events if events is not None else (None, None)
+        if device_commit:
+            st.step_device(ev_start=ev[0], ev_stop=ev[1])
+            return 0
+        return st.step(ev_start=ev[0], ev_stop=ev[1])
+
+    def committed_so_far():
+        return sum(int(st.sync_scaler().step_t) for st, _ in reps) if device_commit else 0
 
     for i in range(warmup):
         one_step(i)
     torch.cuda.synchronize()
     # HIP events bracket the fused kernel on every EVENT_EVERY-th timed step
-    # (recording them costs a few microseconds per step)
+    # (each record puts a ~5 us gap between kernels, so not on every step)
     timed = list(range(0, steps, EVENT_EVERY))
     evs = {i: (hip.create(), hip.create()) for i in timed}
-    committed = 0
+    committed = -committed_so_far()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         committed += one_step(warmup + i, evs.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    committed += committed_so_far()
     kern_ms = [hip.elapsed_ms(*evs[i]) for i in timed]
     for s, e in evs.values():
         hip.destroy(s)
         hip.destroy(e)
     kern_avg = sum(kern_ms) / len(kern_ms)
     ms_per_step = elapsed * 1e3 / steps
-    res = dict(workload=name, n=n, world=W, accum=A, replicas=R,
+    res = dict(workload=name, commit="device" if device_commit else "host", n=n, world=W,
+               accum=A, replicas=R,
                ms_per_step=ms_per_step, params_per_s=n / (ms_per_step * 1e-3),
                step_bytes=step_bytes, hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9,
                fused_kernel_ms=kern_avg, fused_bytes=fused_bytes,
@@ -271,8 +280,8 @@ def cpu_baseline(name, target_s=25.0):
                               acc_in=acc, threads=threads, **kw)
         return time.perf_counter() - t0
 
-    probe = min(wl.n, 1 << 18)
-    dt = timed(probe, 1)
+    probe = min(wl.n, 1 << 21)
+    dt = timed(probe, 2) / 2
     # host memory bound on the sample: ~6 GB of generated inputs and state
     cap = (6 << 30) // (2 * wl.world * wl.accum + 30)
     want = int(probe * target_s / max(dt, 1e-6))
@@ -317,6 +326,9 @@ def main():
     wire = {"fp32": 0, "bf16": 1, "fp16": 2}[args.wire]
     main_res = run_workload(args.workload, args.steps, args.warmup, torch, wire)
     log(json.dumps(main_res))
+    host_res = run_workload(args.workload, args.steps, args.warmup, torch, wire,
+                            device_commit=False)
+    log(json.dumps(host_res))
     others = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         r = run_workload(name, max(3, args.steps // 2), 2, torch, wire)
@@ -364,6 +376,9 @@ def main():
                      "algorithmic_bytes_per_launch": main_res["fused_bytes"]},
         "cpu_baseline": cpu,
         "other_workloads": others,
+        "host_commit": {"ms_per_step": host_res["ms_per_step"],
+                        "params_per_s": host_res["params_per_s"],
+                        "fused_kernel_ms": host_res["fused_kernel_ms"]},
         "offload": offload,
     }
     print(json.dumps(out))

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ZS_ABI_VERSION 2
+#define ZS_ABI_VERSION 3
 #define ZS_MAX_WORLD 64
 
 typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
@@ -265,6 +265,74 @@ int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow);
  * on any error the scaler is left unchanged. */
 int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
                    void *stream, void *ev_start, void *ev_stop, int *committed);
+
+/* Device-resident commit-or-skip ([Intro] 一.3 items (1) and (3): dynamic
+ * loss scaling skips the update of a step whose unscaled gradient is not
+ * finite and adjusts the scale). The same rule as zs_scaler_update, kept in
+ * device memory and applied by a kernel, so consecutive steps need no
+ * device-to-host round trip and can be queued (or captured in a HIP graph)
+ * back to back. The layout is public: the caller allocates
+ * sizeof(zs_device_scaler) bytes of device memory (8-byte aligned), fills it
+ * from zs_device_scaler_make's host image with one copy, and may copy it back
+ * at any time the stream is idle to read the scaler.
+ *   scale .. skipped : as in zs_loss_scaler; scale is the next step's.
+ *   beta1_t, beta2_t : beta1^(step_t+1), beta2^(step_t+1) in binary64, the
+ *                      powers the next step's bias corrections use; the
+ *                      commit multiplies them by beta once per committed
+ *                      step, the same repeated products zs_adamw_step forms.
+ *   flag             : OR of the running step's overflow checks (kernels
+ *                      OR into it; the commit clears it).
+ *   last_flag        : 1 if the most recent step was skipped, else 0.
+ *   arrived          : work counter of the commit kernel, 0 between steps.
+ *   bad_scale        : steps that found the scale not finite or not > 0
+ *                      (such a step is skipped like an overflow).
+ *   last_alpha, last_bc2 : lr/(1-beta1^t) and sqrt(1-beta2^t), rounded to
+ *                      fp32, as the most recent step used them. */
+typedef struct {
+  float scale;
+  uint32_t clean_steps;
+  uint32_t growth_interval;
+  uint32_t dynamic;
+  uint64_t step_t;
+  uint64_t skipped;
+  double beta1_t, beta2_t;
+  uint32_t flag;
+  uint32_t last_flag;
+  uint32_t arrived;
+  uint32_t bad_scale;
+  float last_alpha, last_bc2;
+  uint32_t reserved[2];
+} zs_device_scaler;
+
+/* Host image of a device scaler that continues from the host scaler `s`
+ * (beta powers formed by step_t + 1 repeated binary64 multiplications).
+ * Errors: ZS_ERR_INVALID_ARG for NULL pointers or a scale that is not
+ * finite and > 0. */
+int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
+                          zs_device_scaler *out);
+
+/* One optimizer step with the commit-or-skip decision taken on the device.
+ * Enqueues on `stream`, never waits:
+ *   1. the zs_step_fused pass with hp.loss_scale = dev->scale and the bias
+ *      corrections from dev->beta1_t / dev->beta2_t (a->hp.loss_scale and
+ *      a->hp.step_t are ignored; lr, betas, eps and weight decay come from
+ *      a->hp); it ORs into dev->flag (a->overflow_flag is ignored);
+ *   2. a commit kernel: when dev->flag is set it copies the input set into
+ *      the output set and writes the cast of master_in into the gather
+ *      slice, so the output set always holds the state after the step
+ *      (updated, or unchanged when skipped); then it applies the
+ *      zs_scaler_update rule to *dev, records last_flag and clears flag.
+ * The caller swaps the input and output sets after every call, without
+ * looking at the flag. Micro-batches before the last one go through
+ * zs_reduce_scatter_avg with no flag: a non-finite partial stays non-finite
+ * through the fp32 accumulation, so the fused pass's check of
+ * (acc_in + average) / scale sees it.
+ * ev_start / ev_stop: NULL, or hipEvent_t handles recorded immediately
+ * before and after the fused kernel. Calls that share a dev must be ordered
+ * (one stream). Errors: as zs_step_fused (ZS_ERR_INVALID_ARG also for a
+ * NULL dev); nothing is enqueued on an error. */
+int zs_step_device(const zs_step_args *a, zs_device_scaler *dev, void *stream, void *ev_start,
+                   void *ev_stop);
 
 #ifdef __cplusplus
 }

@@ -332,11 +332,14 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
 
 /* zs_step_fused with optional start/stop events recorded on the stream
  * immediately before and after the kernel launch. */
+/* zs_step_fused; with `dev`, the scale, bias corrections and flag of the
+ * device-resident flow (a->hp.loss_scale, a->hp.step_t and
+ * a->overflow_flag unused). */
 static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_start,
-                           hipEvent_t ev_stop) {
+                           hipEvent_t ev_stop, zs_device_scaler *dev) {
   if (!a) return fail(ZS_ERR_INVALID_ARG, "null args%s");
   if (!a->worker_grads || !a->master_in || !a->m_in || !a->v_in || !a->master_out ||
-      !a->m_out || !a->v_out || !a->gather_buf || !a->overflow_flag)
+      !a->m_out || !a->v_out || !a->gather_buf || (!a->overflow_flag && !dev))
     return fail(ZS_ERR_INVALID_ARG, "null pointer in zs_step_args%s");
   if (a->world == 0 || a->world > ZS_MAX_WORLD || a->rank >= a->world)
     return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64 and rank < world%s");
@@ -345,9 +348,17 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   if (!valid_wire(a->wire_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad wire dtype%s");
   FusedArgs p;
   p.wire = a->wire_dtype;
-  if (!make_scales(a->world, a->hp.loss_scale, &p.k))
+  zs_adamw_hparams hp = a->hp;
+  if (dev) {
+    /* placeholders: the kernel replaces the scale and the bias corrections */
+    hp.loss_scale = 1.0f;
+    hp.step_t = 1;
+  }
+  if (!make_scales(a->world, hp.loss_scale, &p.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
-  if (!make_adam(&a->hp, &p.h)) return fail(ZS_ERR_INVALID_ARG, "step_t must be >= 1%s");
+  if (!make_adam(&hp, &p.h)) return fail(ZS_ERR_INVALID_ARG, "step_t must be >= 1%s");
+  p.dev = dev;
+  p.lr = (double)a->hp.lr;
   const uint64_t n = a->n;
   if (n == 0) return ZS_OK;
   int rc = fill_ring(a->worker_grads, a->world, a->rank, &p.g);
@@ -382,7 +393,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   p.m_out = a->m_out;
   p.v_out = a->v_out;
   p.param_out = param_out;
-  p.flag = a->overflow_flag;
+  p.flag = dev ? &dev->flag : a->overflow_flag;
 
   const void *p16[ZS_MAX_WORLD + 1];
   for (uint32_t w = 0; w < a->world; ++w) p16[w] = p.g.p[w];
@@ -445,7 +456,79 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
 }
 
 int zs_step_fused(const zs_step_args *a, void *stream) {
-  return step_fused_impl(a, stream, nullptr, nullptr);
+  return step_fused_impl(a, stream, nullptr, nullptr, nullptr);
+}
+
+int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
+                          zs_device_scaler *out) {
+  if (!s || !out) return fail(ZS_ERR_INVALID_ARG, "null scaler or output%s");
+  if (!(s->scale > 0.0f) || !isfinite(s->scale))
+    return fail(ZS_ERR_INVALID_ARG, "scale must be finite and > 0%s");
+  zs_device_scaler d;
+  memset(&d, 0, sizeof d);
+  d.scale = s->scale;
+  d.clean_steps = s->clean_steps;
+  d.growth_interval = s->growth_interval;
+  d.dynamic = s->dynamic;
+  d.step_t = s->step_t;
+  d.skipped = s->skipped;
+  /* beta^(t+1) by t+1 repeated multiplications, as make_adam forms it */
+  double b1 = beta1, b2 = beta2, b1t = 1.0, b2t = 1.0;
+  for (uint64_t i = 0; i <= s->step_t; ++i) {
+    b1t *= b1;
+    b2t *= b2;
+  }
+  d.beta1_t = b1t;
+  d.beta2_t = b2t;
+  *out = d;
+  g_err[0] = 0;
+  return ZS_OK;
+}
+
+int zs_step_device(const zs_step_args *a, zs_device_scaler *dev, void *stream, void *ev_start,
+                   void *ev_stop) {
+  if (!dev) return fail(ZS_ERR_INVALID_ARG, "null device scaler%s");
+  int rc = step_fused_impl(a, stream, static_cast<hipEvent_t>(ev_start),
+                           static_cast<hipEvent_t>(ev_stop), dev);
+  if (rc != ZS_OK) return rc;
+  CommitArgs c;
+  c.dev = dev;
+  c.master_in = a->master_in;
+  c.m_in = a->m_in;
+  c.v_in = a->v_in;
+  c.master_out = a->master_out;
+  c.m_out = a->m_out;
+  c.v_out = a->v_out;
+  c.param_out = static_cast<uint16_t *>(a->gather_buf) + a->gather_offset;
+  c.n = a->n;
+  c.beta1 = (double)a->hp.beta1;
+  c.beta2 = (double)a->hp.beta2;
+  const void *p16[] = {c.param_out};
+  const void *f32[] = {c.master_in, c.m_in, c.v_in, c.master_out, c.m_out, c.v_out};
+  const int vec = pick_vec(p16, 1, f32, 6);
+  /* a few large blocks: they only copy on a skipped step (grid-stride) */
+  const uint64_t per_block = (uint64_t)kCommitBlock * (uint64_t)vec;
+  const uint64_t want = (a->n + per_block - 1) / per_block;
+  const unsigned blocks =
+      (unsigned)(want < 1 ? 1 : (want > (uint64_t)kCommitBlocks ? kCommitBlocks : want));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define ZS_COMMIT_K(V, P) \
+  hipLaunchKernelGGL((commit_kernel<V, P>), dim3(blocks), dim3(kCommitBlock), 0, s, c)
+#define ZS_COMMIT_VEC(P)                      \
+  switch (vec) {                              \
+    case 8: ZS_COMMIT_K(8, P); break;         \
+    case 4: ZS_COMMIT_K(4, P); break;         \
+    case 2: ZS_COMMIT_K(2, P); break;         \
+    default: ZS_COMMIT_K(1, P); break;        \
+  }
+  if (a->param_dtype == ZS_BF16) {
+    ZS_COMMIT_VEC(ZS_BF16)
+  } else {
+    ZS_COMMIT_VEC(ZS_FP16)
+  }
+#undef ZS_COMMIT_VEC
+#undef ZS_COMMIT_K
+  return launch_result();
 }
 
 int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
@@ -460,7 +543,7 @@ int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host
   local.hp.loss_scale = scaler->scale;
   local.hp.step_t = (uint32_t)(scaler->step_t + 1);
   int rc = step_fused_impl(&local, stream, static_cast<hipEvent_t>(ev_start),
-                           static_cast<hipEvent_t>(ev_stop));
+                           static_cast<hipEvent_t>(ev_stop), nullptr);
   if (rc != ZS_OK) return rc;
   if (a->n == 0) {
     *committed = 1;

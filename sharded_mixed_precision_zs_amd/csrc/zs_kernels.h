@@ -61,6 +61,21 @@ __device__ __forceinline__ float unscale(float a, const Scales &k) {
   return k.s_pow2 ? a * k.inv_s : a / k.sf;
 }
 
+/* The loss-scale half of Scales for a scale read from device memory (the
+ * device-resident commit flow): the same power-of-two test as the host's
+ * (a normal 2^k, |k| <= 126, whose reciprocal 2^-k is exact). Values are
+ * moved to scalar registers: they are the same for every lane. Returns false
+ * when the scale is not finite and > 0 (the step is then skipped). */
+__device__ __forceinline__ bool dev_scales(float sc, Scales &k) {
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(sc));
+  const uint32_t e = (b >> 23) & 0xffu;
+  k.sf = __uint_as_float(b);
+  k.s_pow2 = (b & 0x807fffffu) == 0 && e >= 1 && e <= 253;
+  k.inv_s = k.s_pow2 ? __uint_as_float((254u - e) << 23) : 0.0f;
+  const float s = __uint_as_float(b);
+  return s > 0.0f && __builtin_isfinite(s);
+}
+
 __device__ __forceinline__ float adamw_elem(float theta, float &m, float &v,
                                             float g, const AdamK &k) {
   float decayed = theta * k.delta;             /* decoupled weight decay  */
@@ -339,24 +354,24 @@ struct ReduceArgs {
 };
 
 template <int VEC, int DT>
-__device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, uint64_t i0) {
+__device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, const Scales &k, uint64_t i0) {
   float s[VEC], acc[VEC];
   if (a.accumulate) ldf<VEC>(a.out + i0, acc);
   ring_sum<VEC, DT>(a.g, a.world, a.wire, i0, s);
   bool bad = false;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    float v = average(s[e], a.k);
+    float v = average(s[e], k);
     if (a.accumulate) v = acc[e] + v;
     s[e] = v;
-    bad |= !__builtin_isfinite(unscale(v, a.k));
+    bad |= !__builtin_isfinite(unscale(v, k));
   }
   stf<VEC>(a.out + i0, s);
   return bad;
 }
 
 template <int VEC, int U, int DT, int WIRE>
-__device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, uint64_t base) {
+__device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, const Scales &k, uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
@@ -369,10 +384,10 @@ __device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, uint64_t base) 
     if (a.accumulate) ldf<VEC>(a.out + i0[u], acc);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      float v = average(s[u][e], a.k);
+      float v = average(s[u][e], k);
       if (a.accumulate) v = acc[e] + v;
       s[u][e] = v;
-      bad |= !__builtin_isfinite(unscale(v, a.k));
+      bad |= !__builtin_isfinite(unscale(v, k));
     }
     stf<VEC>(a.out + i0[u], s[u]);
   }
@@ -385,10 +400,10 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
   const uint64_t full = a.n / tile;  /* blocks past `full` cover the tail */
   bool bad = false;
   if (blockIdx.x < full) {
-    bad = reduce_tile<VEC, U, DT, WIRE>(a, (uint64_t)blockIdx.x * tile);
+    bad = reduce_tile<VEC, U, DT, WIRE>(a, a.k, (uint64_t)blockIdx.x * tile);
   } else {
     uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * kBlock + threadIdx.x;
-    if (i < a.n) bad = reduce_vec<1, DT>(a, i);
+    if (i < a.n) bad = reduce_vec<1, DT>(a, a.k, i);
   }
   if (a.flag) flag_or(a.flag, bad);
 }
@@ -486,10 +501,13 @@ struct FusedArgs {
   uint32_t *flag;
   Scales k;
   AdamK h;
+  zs_device_scaler *dev;  /* non-null: scale and bias corrections come from it */
+  double lr;              /* for the bias correction formed on the device */
 };
 
 template <int VEC, int GDT, int PDT>
-__device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
+__device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, const AdamK &h,
+                                          uint64_t i0) {
   float th[VEC], m[VEC], v[VEC], acc[VEC], s[VEC];
   ldf<VEC>(p.master_in + i0, th);
   ldf<VEC>(p.m_in + i0, m);
@@ -499,11 +517,11 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
   bool bad = false;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    float a = average(s[e], p.k);
+    float a = average(s[e], sk);
     if (p.acc_in) a = acc[e] + a;
-    float g = unscale(a, p.k);
+    float g = unscale(a, sk);
     bad |= !__builtin_isfinite(g);
-    th[e] = adamw_elem(th[e], m[e], v[e], g, p.h);
+    th[e] = adamw_elem(th[e], m[e], v[e], g, h);
   }
   stf<VEC>(p.master_out + i0, th);
   stf<VEC>(p.m_out + i0, m);
@@ -517,7 +535,8 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, uint64_t i0) {
  * gradient streams; with a single worker (W = 1) there is no sum, one
  * gradient load, and the state loads go first. */
 template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
-__device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
+__device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk, const AdamK &h,
+                                           uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
@@ -543,11 +562,11 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      float a = average(s[u][e], p.k);
+      float a = average(s[u][e], sk);
       if constexpr (ACC) a = acc[u][e] + a;
-      float g = unscale(a, p.k);
+      float g = unscale(a, sk);
       bad |= !__builtin_isfinite(g);
-      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, p.h);
+      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, h);
     }
     stf<VEC>(p.master_out + i0[u], th[u]);
     stf<VEC>(p.m_out + i0[u], m[u]);
@@ -557,6 +576,28 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, uint64_t base) {
   return bad;
 }
 
+/* Step constants of the device-resident flow: the loss scale and the
+ * bias corrections alpha = lr / (1 - beta1^t), bc2 = sqrt(1 - beta2^t)
+ * formed in binary64 from the running powers and rounded once to fp32,
+ * exactly as the host forms them for an explicit step_t. Block 0 records
+ * the pair it used (and counts a bad scale); returns false for a scale that
+ * is not finite and > 0. */
+__device__ __forceinline__ bool dev_step_consts(const FusedArgs &p, Scales &sk, AdamK &h) {
+  zs_device_scaler *d = p.dev;
+  const bool ok = dev_scales(d->scale, sk);
+  const double b1t = d->beta1_t, b2t = d->beta2_t;
+  const float alpha = (float)(p.lr / (1.0 - b1t));
+  const float bc2 = (float)__builtin_sqrt(1.0 - b2t);
+  h.alpha = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(alpha)));
+  h.b2 = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(bc2)));
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    d->last_alpha = h.alpha;
+    d->last_bc2 = h.b2;
+    if (!ok) d->bad_scale = d->bad_scale + 1u;
+  }
+  return ok;
+}
+
 /* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
  * added before the unscale; a separate instance so the common case carries
  * no registers for it. */
@@ -564,16 +605,98 @@ template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
 __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   const uint64_t tile = (uint64_t)kBlock * U * VEC;
   const uint64_t full = p.n / tile;  /* blocks past `full` cover the tail */
-  bool bad = false;
+  Scales sk = p.k;
+  AdamK h = p.h;
+  bool bad = p.dev ? !dev_step_consts(p, sk, h) : false;
   if (blockIdx.x < full) {
-    bad = fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE>(p, (uint64_t)blockIdx.x * tile);
+    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE>(p, sk, h, (uint64_t)blockIdx.x * tile);
   } else {
     /* ragged end: one element per thread, spread over enough blocks that
      * no thread walks a chain of them */
     uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * kBlock + threadIdx.x;
-    if (i < p.n) bad = fused_vec<1, GDT, PDT>(p, i);
+    if (i < p.n) bad |= fused_vec<1, GDT, PDT>(p, sk, h, i);
   }
   flag_or(p.flag, bad);
+}
+
+/* ------------------------------------------------------------------------
+ * Commit or skip on the device ([Intro] 一.3 items (1) and (3): a step whose
+ * unscaled gradient is not finite is skipped and the loss scale adjusted).
+ * Runs after the fused pass on the same stream. Every block reads the
+ * step's flag; when it is set, the blocks copy the input set into the
+ * output set and recast master_in into the gather slice (grid-stride), so
+ * the output set holds the state after the step either way. The last block
+ * to arrive applies the scaler rule (the host's zs_scaler_update, field for
+ * field), advances the beta powers on a commit, records the flag and clears
+ * it and the arrival counter for the next step. Same-address atomics
+ * serialize in L2 (about 20 ns each), so the grid is a few large blocks:
+ * kCommitBlocks arrivals per step.
+ * ---------------------------------------------------------------------- */
+
+constexpr int kCommitBlock = 1024;  /* threads per commit block     */
+constexpr int kCommitBlocks = 64;   /* at most this many blocks     */
+
+struct CommitArgs {
+  zs_device_scaler *dev;
+  const float *master_in, *m_in, *v_in;
+  float *master_out, *m_out, *v_out;
+  uint16_t *param_out;  /* already at this rank's offset */
+  uint64_t n;
+  double beta1, beta2;
+};
+
+template <int VEC, int PDT>
+__device__ __forceinline__ void restore_vec(const CommitArgs &c, uint64_t i0) {
+  float x[VEC];
+  ldf<VEC>(c.master_in + i0, x);
+  stf<VEC>(c.master_out + i0, x);
+  st16<VEC, PDT>(c.param_out + i0, x);
+  ldf<VEC>(c.m_in + i0, x);
+  stf<VEC>(c.m_out + i0, x);
+  ldf<VEC>(c.v_in + i0, x);
+  stf<VEC>(c.v_out + i0, x);
+}
+
+template <int VEC, int PDT>
+__global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
+  zs_device_scaler *d = c.dev;
+  const uint32_t f = __hip_atomic_load(&d->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (f) {
+    const uint64_t stride = (uint64_t)gridDim.x * kCommitBlock * VEC;
+    for (uint64_t i0 = ((uint64_t)blockIdx.x * kCommitBlock + threadIdx.x) * VEC; i0 < c.n;
+         i0 += stride) {
+      if (i0 + VEC <= c.n) {
+        restore_vec<VEC, PDT>(c, i0);
+      } else {
+        for (uint64_t i = i0; i < c.n; ++i) restore_vec<1, PDT>(c, i);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  __threadfence();
+  const uint32_t before = atomicAdd(&d->arrived, 1u);
+  if (before != gridDim.x - 1) return;
+  __threadfence();
+  if (f) {
+    if (d->dynamic) d->scale = d->scale * 0.5f;
+    d->clean_steps = 0;
+    d->skipped = d->skipped + 1;
+  } else {
+    d->step_t = d->step_t + 1;
+    d->beta1_t = d->beta1_t * c.beta1;
+    d->beta2_t = d->beta2_t * c.beta2;
+    const uint32_t clean = d->clean_steps + 1;
+    if (d->dynamic && d->growth_interval && clean >= d->growth_interval) {
+      d->scale = d->scale * 2.0f;
+      d->clean_steps = 0;
+    } else {
+      d->clean_steps = clean;
+    }
+  }
+  d->last_flag = f ? 1u : 0u;
+  __hip_atomic_store(&d->flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&d->arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 /* ------------------------------------------------------------------------

@@ -41,7 +41,8 @@ class ShardState:
 
     def __init__(self, n, world, rank, offset, gather_len, param_dtype, grad_dtype,
                  opt: AdamW, loss_scale, dynamic=False, growth_interval=0,
-                 device="cuda", accumulate=False, wire_dtype=zs.ZS_WIRE_FP32):
+                 device="cuda", accumulate=False, wire_dtype=zs.ZS_WIRE_FP32,
+                 device_commit=False):
         self.n, self.world, self.rank, self.offset = n, world, rank, offset
         self.wire_dtype = wire_dtype  # precision of the ring's partial sums
         self.param_dtype, self.grad_dtype = param_dtype, grad_dtype
@@ -62,6 +63,12 @@ class ShardState:
         self._prepared = {}
         self._flag_base = self.flags.data_ptr()
         self._bound = None
+        # device-resident commit-or-skip: the scaler lives in HBM and steps
+        # are queued without waiting (step_device); self.scaler is refreshed
+        # by sync_scaler()
+        self.device_commit = device_commit
+        self.dev = self._upload_scaler() if device_commit else None
+        self.device = device
 
     # -- state access -------------------------------------------------------
     @property
@@ -93,6 +100,8 @@ class ShardState:
     def state_dict(self):
         """Host copy of everything the next step depends on: the current fp32
         set, this rank's 16-bit parameters and the scaler."""
+        if self.device_commit:
+            self.sync_scaler()
         sc = self.scaler
         return {"master": self.master.cpu(), "m": self.m.cpu(), "v": self.v.cpu(),
                 "params": self.params.cpu(),
@@ -109,6 +118,22 @@ class ShardState:
             dst.copy_(sd[key])
         for k, v in sd["scaler"].items():
             setattr(self.scaler, k, v)
+        if self.device_commit:
+            self.dev.copy_(self._upload_scaler())
+
+    # -- device-resident scaler ---------------------------------------------
+    def _upload_scaler(self):
+        img = zs.zs_device_scaler_make(self.scaler, self.opt.beta1, self.opt.beta2)
+        return zs.device_scaler_upload(img, self.sets[0][0].device)
+
+    def sync_scaler(self):
+        """Wait for the queued steps and copy the device scaler into
+        self.scaler; returns the device image."""
+        d = zs.device_scaler_read(self.dev)
+        for k in ("scale", "clean_steps", "growth_interval", "dynamic", "step_t", "skipped"):
+            setattr(self.scaler, k, getattr(d, k))
+        self.last_flag = int(d.last_flag)
+        return d
 
     def hparams(self):
         o = self.opt
@@ -133,11 +158,12 @@ class ShardState:
     # -- micro-batches before the last one ------------------------------------
     def reduce_micro(self, worker_grads: Sequence[torch.Tensor], first: bool, stream=None):
         """acc = mean of this micro-batch's worker gradients (first) or
-        acc += that mean (later micro-batches)."""
+        acc += that mean (later micro-batches). No overflow check here: a
+        non-finite partial stays non-finite through the accumulation, and the
+        step's fused pass checks (acc + last average) / scale."""
         zs.zs_reduce_scatter_avg(worker_grads, self.grad_dtype, self.world, self.rank, self.n,
                                  self.acc, accumulate=not first, overflow_flag=None,
-                                 loss_scale=self.loss_scale, stream=stream,
-                                 wire_dtype=self.wire_dtype)
+                                 loss_scale=1.0, stream=stream, wire_dtype=self.wire_dtype)
 
     # -- one optimizer step -------------------------------------------------
     def _args(self, worker_grads, acc_in):
@@ -204,6 +230,19 @@ class ShardState:
         if ok:
             self.cur = 1 - self.cur
         return ok
+
+    def step_device(self, worker_grads=None, acc_in=None, stream=None, ev_start=None,
+                    ev_stop=None):
+        """One optimizer step through zs_step_device: queued, never waits. The
+        commit or skip happens on the device, which leaves the state after
+        the step in the output set either way, so the sets swap every call;
+        sync_scaler() reads the outcome."""
+        if not self.device_commit:
+            raise RuntimeError("ShardState was built without device_commit=True")
+        args = (self._bound[self.cur] if worker_grads is None
+                else self._args(worker_grads, acc_in))
+        zs.zs_step_device(args, self.dev, stream, ev_start, ev_stop)
+        self.cur = 1 - self.cur
 
 
 class OffloadShard:

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 
 from . import build as _build
 
-ZS_ABI_VERSION = 2
+ZS_ABI_VERSION = 3
 ZS_MAX_WORLD = 64
 ZS_BF16, ZS_FP16 = 0, 1
 ZS_WIRE_FP32, ZS_WIRE_BF16, ZS_WIRE_FP16 = 0, 1, 2
@@ -54,6 +54,16 @@ class zs_loss_scaler(C.Structure):
                 ("step_t", C.c_uint64), ("skipped", C.c_uint64)]
 
 
+class zs_device_scaler(C.Structure):
+    _fields_ = [("scale", C.c_float), ("clean_steps", C.c_uint32),
+                ("growth_interval", C.c_uint32), ("dynamic", C.c_uint32),
+                ("step_t", C.c_uint64), ("skipped", C.c_uint64),
+                ("beta1_t", C.c_double), ("beta2_t", C.c_double),
+                ("flag", C.c_uint32), ("last_flag", C.c_uint32), ("arrived", C.c_uint32),
+                ("bad_scale", C.c_uint32), ("last_alpha", C.c_float), ("last_bc2", C.c_float),
+                ("reserved", C.c_uint32 * 2)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libzeroshard is not built ({LIB_PATH}); "
@@ -77,6 +87,9 @@ def _load():
         "zs_all_gather_step": ([C.POINTER(vp), u32, u64, u32, u32, vp], i32),
         "zs_cpu_step": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, i32, i32,
                          C.POINTER(u32)], i32),
+        "zs_device_scaler_make": ([C.POINTER(zs_loss_scaler), f32, f32,
+                                   C.POINTER(zs_device_scaler)], i32),
+        "zs_step_device": ([C.POINTER(zs_step_args), vp, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -268,6 +281,43 @@ def zs_step_commit(args, scaler: zs_loss_scaler, host_flag, stream=None, ev_star
                                                  _stream(stream), ev_start, ev_stop,
                                                  C.byref(committed)))
     return bool(committed.value)
+
+
+DEVICE_SCALER_BYTES = C.sizeof(zs_device_scaler)
+
+
+def zs_device_scaler_make(scaler: zs_loss_scaler, beta1: float, beta2: float) -> zs_device_scaler:
+    """Host image of a device-resident scaler continuing from `scaler`."""
+    out = zs_device_scaler()
+    _check("zs_device_scaler_make", _lib.zs_device_scaler_make(C.byref(scaler), beta1, beta2,
+                                                               C.byref(out)))
+    return out
+
+
+def device_scaler_upload(image: zs_device_scaler, device="cuda"):
+    """A device buffer (uint8 CUDA tensor) holding `image`."""
+    torch = _torch()
+    raw = bytes(memoryview(image).cast("B"))
+    host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
+    return host.to(device)
+
+
+def device_scaler_read(dev_buf) -> zs_device_scaler:
+    """Host copy of a device scaler buffer (synchronizes with the device)."""
+    raw = dev_buf[:DEVICE_SCALER_BYTES].cpu().numpy().tobytes()
+    return zs_device_scaler.from_buffer_copy(raw)
+
+
+def _dev_scaler_ptr(dev):
+    return _ptr(dev, DEVICE_SCALER_BYTES, 1, "device scaler")
+
+
+def zs_step_device(args, dev, stream=None, ev_start=None, ev_stop=None):
+    """Fused step + on-device commit or skip (never waits). dev: the device
+    scaler buffer (device_scaler_upload) or its address."""
+    raw = args.args if isinstance(args, StepArgs) else args
+    _check("zs_step_device", _lib.zs_step_device(C.byref(raw), _dev_scaler_ptr(dev),
+                                                 _stream(stream), ev_start, ev_stop))
 
 
 def zs_all_gather_step(replicas: Sequence, phi: int, step: int, sigma: int = 0, stream=None):

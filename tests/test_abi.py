@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(zs):
     lib = C.CDLL(zs.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 2
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 3
 
 
 def test_status_strings(zs):
@@ -219,3 +219,47 @@ def test_all_gather_step_rejects_bad_arguments(zs):
     close = (C.c_void_p * 3)(FAKE, FAKE + 1000, FAKE + 0x200000)  # 2*phi bytes overlap
     assert lib.zs_all_gather_step(close, 3, 1000, 0, 1, None) == zs.ZS_ERR_ALIAS
     assert lib.zs_all_gather_step(reps, 3, 0, 0, 1, None) == zs.ZS_OK  # phi == 0
+
+
+def test_device_scaler_layout_and_image(zs):
+    """The host image of the device scaler: fields copied from the host
+    scaler, beta powers formed by t+1 repeated binary64 products, and the
+    bias corrections they give equal the oracle's for step t+1."""
+    assert C.sizeof(zs.zs_device_scaler) == 80
+    assert zs.zs_device_scaler.beta1_t.offset == 32 and zs.zs_device_scaler.flag.offset == 48
+    import numpy as np
+    for b1, b2, lr, t in ((0.9, 0.999, 1e-3, 0), (0.9, 0.95, 3e-4, 7), (0.8, 0.9999, 1e-2, 1234)):
+        host = zs.zs_loss_scaler(scale=2.0 ** 15, clean_steps=3, growth_interval=4, dynamic=1,
+                                 step_t=t, skipped=2)
+        img = zs.zs_device_scaler_make(host, b1, b2)
+        assert (img.scale, img.clean_steps, img.growth_interval, img.dynamic, img.step_t,
+                img.skipped) == (2.0 ** 15, 3, 4, 1, t, 2)
+        assert (img.flag, img.last_flag, img.arrived, img.bad_scale) == (0, 0, 0, 0)
+        p1 = p2 = 1.0
+        for _ in range(t + 1):
+            p1 *= float(np.float32(b1))
+            p2 *= float(np.float32(b2))
+        assert (img.beta1_t, img.beta2_t) == (p1, p2)
+        k = oracle.adamw_consts(lr, b1, b2, 1e-8, 0.01, t + 1)
+        lr64 = float(np.float32(lr))
+        assert np.float32(lr64 / (1.0 - img.beta1_t)) == np.float32(k["alpha"])
+        assert np.float32(np.sqrt(1.0 - img.beta2_t)) == np.float32(k["b2"])
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        with pytest.raises(zs.ZsError):
+            zs.zs_device_scaler_make(zs.zs_loss_scaler(scale=bad, clean_steps=0,
+                                                       growth_interval=0, dynamic=0, step_t=0,
+                                                       skipped=0), 0.9, 0.999)
+
+
+def test_device_step_rejects_bad_arguments(zs):
+    """Argument errors return before anything is enqueued (no GPU needed)."""
+    lib = _raw(zs)
+    a, keep = _fused_args(zs)
+    E = zs.ZS_ERR_INVALID_ARG
+    dev = C.c_void_p(FAKE + 0x7000000)
+    assert lib.zs_step_device(C.byref(a), None, None, None, None) == E
+    assert lib.zs_step_device(None, dev, None, None, None) == E
+    bad, keep2 = _fused_args(zs, grad_dtype=5)
+    assert lib.zs_step_device(C.byref(bad), dev, None, None, None) == E
+    alias, keep3 = _fused_args(zs, master_out=FAKE + 0x1000000)
+    assert lib.zs_step_device(C.byref(alias), dev, None, None, None) == zs.ZS_ERR_ALIAS

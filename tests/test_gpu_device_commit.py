@@ -1,0 +1,217 @@
+"""The device-resident commit or skip (zs_step_device) on the GPU.
+
+The decision of dynamic loss scaling (skip a step whose unscaled gradient is
+not finite, adjust the scale) runs in a kernel against a scaler kept in
+device memory, so steps queue back to back with no host round trip. These
+tests check that it changes nothing else: queued device steps equal the
+host-synchronous flow bit for bit (skipped steps included), the bias
+corrections formed on the device from the running beta powers equal the
+oracle's at every step t, the scaler follows the oracle's rule, and a step
+captured in a HIP graph replays to the eager result.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import F32, announce, assert_bits_equal, down16, down32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def env(hip_built):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sharded_mixed_precision_zs_amd import shard, synth, zeroshard
+    return zeroshard, synth, shard
+
+
+def _make(env, wl, device_commit, **kw):
+    zs, synth, shard = env
+    n = wl.n
+    opt = shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay)
+    st = shard.ShardState(n, wl.world, 0, 0, n, wl.param_dtype, wl.grad_dtype, opt,
+                          kw.pop("loss_scale", wl.loss_scale), accumulate=wl.accum > 1,
+                          device_commit=device_commit, **kw)
+    synth.dev_state(wl, 0, st.master, st.m, st.v)
+    grads = torch.empty((wl.world, -(-n // 128) * 128), dtype=torch.int16, device="cuda")
+    return st, [grads[k, :n] for k in range(wl.world)]
+
+
+def _same_state(a, b, what):
+    for x, y, name in ((a.master, b.master, "master"), (a.m, b.m, "m"), (a.v, b.v, "v")):
+        assert_bits_equal(down32(x), down32(y), f"{what} {name}")
+    assert np.array_equal(down16(a.params.view(torch.int16)), down16(b.params.view(torch.int16))), \
+        f"{what} params"
+
+
+def test_queued_device_steps_equal_host_commit(env):
+    """Six steps queued without any synchronization (gradients regenerated
+    on the same stream between them), one of them hit by injected inf/NaN,
+    against the host-synchronous zs_step_commit flow."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=8 * 250_003, steps=6,
+                             inject_steps=(3,), inject_rate=1e-3, name="queued")
+    host, gh = _make(env, wl, False)
+    dev, gd = _make(env, wl, True)
+    announce("queued device steps vs host commit")
+    committed = []
+    for step in range(1, wl.steps + 1):
+        for k in range(wl.world):
+            synth.dev_grad(wl, k, step, 0, 0, gh[k], scale=wl.loss_scale)
+            synth.dev_grad(wl, k, step, 0, 0, gd[k], scale=wl.loss_scale)
+        committed.append(host.step(gh))
+        dev.step_device(gd)
+    assert committed == [True, True, False, True, True, True]
+    d = dev.sync_scaler()
+    assert (d.step_t, d.skipped, d.last_flag, d.flag, d.arrived) == (5, 1, 0, 0, 0)
+    assert d.scale == wl.loss_scale
+    _same_state(host, dev, "queued")
+
+
+def test_skip_restores_state_and_params(env):
+    """A skipped device step leaves the output set equal to the input set and
+    the gather slice equal to the cast of the kept master weights."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["mlp9-w3"], phi=3 * 40_009, steps=2,
+                             inject_steps=(2,), inject_rate=1e-3, name="skip")
+    st, g = _make(env, wl, True, dynamic=True, growth_interval=4)
+    for step in (1, 2):
+        for k in range(wl.world):
+            synth.dev_grad(wl, k, step, 0, 0, g[k], scale=st.loss_scale)
+        if step == 2:
+            before = [down32(x).copy() for x in (st.master, st.m, st.v)]
+        st.step_device(g)
+        d = st.sync_scaler()
+    assert d.last_flag == 1 and d.skipped == 1 and d.step_t == 1
+    assert d.scale == wl.loss_scale * 0.5
+    for got, want, name in zip((st.master, st.m, st.v), before, ("master", "m", "v")):
+        assert_bits_equal(down32(got), want, f"kept {name}")
+    want = oracle.float_to_half(before[0], wl.param_dtype)
+    assert np.array_equal(down16(st.params.view(torch.int16)), want)
+
+
+@pytest.mark.parametrize("lr,b1,b2", [(1e-3, 0.9, 0.999), (3e-4, 0.9, 0.95), (2e-2, 0.8, 0.9999)])
+def test_bias_corrections_match_oracle_every_step(env, lr, b1, b2):
+    """1500 committed steps: the fp32 bias corrections the device forms from
+    its running beta powers equal the oracle's (formed from t repeated
+    products on the host) at every t, and the final state equals the
+    oracle's 1500-step run bit for bit."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["mlp9-w3"], phi=2 * 4099, world=2, lr=lr,
+                             beta1=b1, beta2=b2, loss_scale=1.0, name="consts")
+    st, g = _make(env, wl, True)
+    for k in range(wl.world):
+        synth.dev_grad(wl, k, 1, 0, 0, g[k], scale=1.0)
+    st.bind(g)
+    parts = [synth.host_grad(wl, k, 1, 0, 0, wl.n, scale=1.0) for k in range(wl.world)]
+    master, m, v = synth.host_state(wl, 0, wl.n)
+    announce(f"bias corrections lr={lr} b1={b1} b2={b2}")
+    steps = 1500
+    for t in range(1, steps + 1):
+        st.step_device()
+        d = st.sync_scaler()
+        k = oracle.adamw_consts(lr, b1, b2, wl.eps, wl.weight_decay, t)
+        assert (np.float32(d.last_alpha), np.float32(d.last_bc2)) == \
+            (np.float32(k["alpha"]), np.float32(k["b2"])), f"t={t}"
+        f, master, m, v, p = oracle.shard_step(parts, 0, wl.grad_dtype, wl.param_dtype, master,
+                                               m, v, lr=lr, beta1=b1, beta2=b2, eps=wl.eps,
+                                               weight_decay=wl.weight_decay, loss_scale=1.0,
+                                               step_t=t)
+        assert f == 0 and d.last_flag == 0
+    assert d.step_t == steps
+    for got, want, name in ((st.master, master, "master"), (st.m, m, "m"), (st.v, v, "v")):
+        assert_bits_equal(down32(got), want, f"after {steps} steps: {name}")
+    assert np.array_equal(down16(st.params.view(torch.int16)), p)
+
+
+def test_scale_growth_to_infinity_then_skip(env):
+    """Growth every 2 clean steps from 2^126: 2^127 after step 2, inf after
+    step 4 (no cap, as the host rule); a step that finds the scale not
+    finite is skipped, counted in bad_scale, and changes no state."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["mlp9-w3"], phi=10_007, world=1, name="growth")
+    st, g = _make(env, wl, True, loss_scale=2.0 ** 126, dynamic=True, growth_interval=2)
+    for k in range(wl.world):
+        synth.dev_grad(wl, k, 1, 0, 0, g[k], scale=1.0)
+    st.bind(g)
+    parts = [synth.host_grad(wl, 0, 1, 0, 0, wl.n, scale=1.0)]
+    master, m, v = synth.host_state(wl, 0, wl.n)
+    hs = oracle.Scaler(2.0 ** 126, 2)
+    scales = []
+    for step in range(1, 5):
+        scales.append(st.loss_scale)
+        assert st.loss_scale == hs.scale
+        st.step_device()
+        d = st.sync_scaler()
+        f, master, m, v, p = oracle.shard_step(parts, 0, wl.grad_dtype, wl.param_dtype, master,
+                                               m, v, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
+                                               eps=wl.eps, weight_decay=wl.weight_decay,
+                                               loss_scale=hs.scale, step_t=hs.t + 1)
+        hs.update(f)
+        assert f == 0 and d.last_flag == 0
+        for got, want, name in ((st.master, master, "master"), (st.m, m, "m"), (st.v, v, "v")):
+            assert_bits_equal(down32(got), want, f"step {step}: {name}")
+    assert scales == [2.0 ** 126, 2.0 ** 126, 2.0 ** 127, 2.0 ** 127]
+    assert d.scale == float("inf") and d.bad_scale == 0
+    st.step_device()
+    d = st.sync_scaler()
+    assert (d.last_flag, d.bad_scale, d.skipped, d.step_t) == (1, 1, 1, 4)
+    for got, want, name in ((st.master, master, "master"), (st.m, m, "m"), (st.v, v, "v")):
+        assert_bits_equal(down32(got), want, f"bad-scale step: {name}")
+    assert np.array_equal(down16(st.params.view(torch.int16)), p)
+
+
+def test_empty_shard_commits(env):
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["mlp9-w3"], phi=3, world=4, name="empty")
+    assert wl.n == 1
+    st, g = _make(env, wl, True)
+    a = st._args(g, None).args
+    a.n = 0
+    zs.zs_step_device(a, st.dev)
+    d = st.sync_scaler()
+    assert (d.step_t, d.skipped, d.last_flag, d.flag, d.arrived) == (1, 0, 0, 0, 0)
+
+
+def test_graph_capture_replays_match_eager(env):
+    """Two device steps (one per direction of the ping-pong sets) captured in
+    a graph; three replays, with eager work and synchronizations between
+    them, each equal to two eager steps."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=8 * 100_003, name="graph")
+    eager, ge = _make(env, wl, True)
+    graph, gg = _make(env, wl, True)
+    for k in range(wl.world):
+        synth.dev_grad(wl, k, 1, 0, 0, ge[k], scale=wl.loss_scale)
+        synth.dev_grad(wl, k, 1, 0, 0, gg[k], scale=wl.loss_scale)
+    eager.bind(ge)
+    graph.bind(gg)
+    torch.cuda.synchronize()
+    announce("graph capture of two device steps")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            graph.step_device()
+            graph.step_device()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # capture enqueued nothing: the graph shard is still at its initial state
+    assert graph.sync_scaler().step_t == 0
+    for r in range(3):
+        eager.step_device()
+        eager.step_device()
+        junk = torch.arange(1 << 20, device="cuda", dtype=torch.float32).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(junk) > 0
+        _same_state(eager, graph, f"replay {r}")
+        de, dg = eager.sync_scaler(), graph.sync_scaler()
+        assert (dg.step_t, dg.skipped, dg.flag, dg.arrived) == (de.step_t, 0, 0, 0) == \
+            (2 * (r + 1), 0, 0, 0)

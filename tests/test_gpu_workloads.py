@@ -43,17 +43,22 @@ def _windows(n, count, seed):
     return [(s, WINDOW) for s in sorted(starts)]
 
 
-def run_workload(env, name, windows=None, gather_full=False):
+def run_workload(env, name, windows=None, gather_full=False, device_commit=False, wl=None):
+    """device_commit: steps through zs_step_device (commit or skip decided on
+    the device); the host reads the device scaler back after each step only
+    to check it and to scale the next step's synthetic gradients."""
     zs, synth, shard = env
-    wl = synth.WORKLOADS[name]
+    wl = wl if wl is not None else synth.WORKLOADS[name]
     n, off, W, A = wl.n, wl.offset, wl.world, wl.accum
     wins = windows if windows is not None else [(0, n)]
-    announce(f"workload {name}: n={n} W={W} A={A} steps={wl.steps} windows={len(wins)}")
+    announce(f"workload {name}: n={n} W={W} A={A} steps={wl.steps} windows={len(wins)} "
+             f"device_commit={device_commit}")
     st = shard.ShardState(n, W, wl.rank, off, (W * wl.chunk) if gather_full else off + n,
                           wl.param_dtype, wl.grad_dtype,
                           shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay),
                           wl.loss_scale, dynamic=wl.dynamic_scale,
-                          growth_interval=wl.scale_interval, accumulate=A > 1)
+                          growth_interval=wl.scale_interval, accumulate=A > 1,
+                          device_commit=device_commit)
     synth.dev_state(wl, off, st.master, st.m, st.v)
     # one row per worker, padded to 256 B like separate allocations
     row = -(-n // 128) * 128
@@ -80,7 +85,11 @@ def run_workload(env, name, windows=None, gather_full=False):
                         accs[i] = np.empty(L, F32)
                     oracle.reduce_avg(parts_w[i], wl.rank, gdt, accs[i], j > 0, scale)
             else:
-                committed = st.step(gviews, acc_in=st.acc if A > 1 else None)
+                if device_commit:
+                    st.step_device(gviews, acc_in=st.acc if A > 1 else None)
+                    committed = st.sync_scaler().last_flag == 0
+                else:
+                    committed = st.step(gviews, acc_in=st.acc if A > 1 else None)
                 rflag = 0
                 outs = []
                 for i, (s, L) in enumerate(wins):
@@ -108,6 +117,13 @@ def run_workload(env, name, windows=None, gather_full=False):
                         nonbit += assert_ulp16(down16(st.params[s:s + L].view(torch.int16)),
                                                outs[i][3], wl.param_dtype, 1,
                                                f"{name} step {step} params window {s}")
+                    elif device_commit:
+                        # skipped on the device: the gather slice holds the
+                        # cast of the kept master weights
+                        nonbit += assert_ulp16(down16(st.params[s:s + L].view(torch.int16)),
+                                               oracle.float_to_half(hs[i][0], wl.param_dtype),
+                                               wl.param_dtype, 0,
+                                               f"{name} step {step} kept params window {s}")
                 assert nonbit == 0, f"{name} step {step}: {nonbit} elements not bit-identical"
     assert (st.t, st.loss_scale, int(st.scaler.skipped)) == (hscaler.t, hscaler.scale,
                                                               hscaler.skipped)
@@ -154,6 +170,22 @@ def test_1p3b_w4_acc4_fp16_windows(env):
     st = run_workload(env, wl.name, windows=_windows(wl.n, 6, 4))
     # two injected steps skipped: 2^16 -> 2^15 -> 2^14, eight steps committed
     assert st.loss_scale == 2.0 ** 14 and st.t == 8
+
+
+def test_gpt2s_w8_full_device_commit(env):
+    run_workload(env, "gpt2s-w8", device_commit=True)
+
+
+def test_1p3b_schedule_device_commit(env):
+    """The dynamic-scaler schedule (fp16, W=4, four micro-batches, injected
+    inf/NaN at steps 3 and 7) with commit or skip on the device, the whole
+    partition compared with the oracle after every step."""
+    zs, synth, shard = env
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["1p3b-w4-acc4-fp16"], phi=4 * 200_003,
+                             name="1p3b-device-commit")
+    st = run_workload(env, wl.name, device_commit=True, wl=wl)
+    assert st.loss_scale == 2.0 ** 14 and st.t == 8 and int(st.scaler.skipped) == 2
 
 
 def test_checkpoint_resume_is_bit_identical(env, tmp_path):
