@@ -1,0 +1,81 @@
+/*
+ * Exercises zs_cpu_step (the ZeRO-Offload host update, product code) for a
+ * build under AddressSanitizer + UndefinedBehaviorSanitizer or
+ * ThreadSanitizer (test infrastructure; run by tests/test_sanitizers.py):
+ * ragged sizes, one and several worker threads (results must not depend on
+ * the thread count), both parameter dtypes, and the skip on a non-finite
+ * gradient at either end. Exits non-zero on an inconsistency.
+ */
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "zeroshard.h"
+
+static unsigned long long rs = 0x9E3779B97F4A7C15ull;
+static float rf(float scale) {
+  rs ^= rs << 13;
+  rs ^= rs >> 7;
+  rs ^= rs << 17;
+  return ((float)((rs >> 40) & 0xffffff) / 16777216.0f - 0.5f) * scale;
+}
+
+#define CHECK(c)                                                   \
+  do {                                                             \
+    if (!(c)) {                                                    \
+      fprintf(stderr, "check failed line %d: %s\n", __LINE__, #c); \
+      return 1;                                                    \
+    }                                                              \
+  } while (0)
+
+int main() {
+  const uint64_t sizes[] = {0, 1, 15, 16, 17, 4099, 100003};
+  zs_adamw_hparams hp = {1e-3f, 0.9f, 0.999f, 1e-8f, 0.01f, 1024.0f, 5};
+  for (uint64_t n : sizes)
+    for (int dtype = 0; dtype < 2; ++dtype) {
+      /* one spare element so that n == 0 still passes valid pointers */
+      std::vector<float> master(n + 1), m(n + 1), v(n + 1), g(n + 1);
+      for (uint64_t i = 0; i < n; ++i) {
+        master[i] = rf(0.04f);
+        m[i] = rf(2e-4f);
+        v[i] = fabsf(rf(2e-6f));
+        g[i] = rf(4.0f);
+      }
+      std::vector<float> st[2][3];
+      std::vector<uint16_t> p[2];
+      const int threads[2] = {1, 3};
+      for (int t = 0; t < 2; ++t) {
+        st[t][0] = master;
+        st[t][1] = m;
+        st[t][2] = v;
+        p[t].assign(n + 1, 0);
+        uint32_t ovf = 7;
+        CHECK(zs_cpu_step(st[t][0].data(), st[t][1].data(), st[t][2].data(), g.data(), n, &hp,
+                          p[t].data(), dtype, threads[t], &ovf) == ZS_OK);
+        CHECK(ovf == 0);
+      }
+      for (int j = 0; j < 3; ++j)
+        CHECK(n == 0 || memcmp(st[0][j].data(), st[1][j].data(), n * 4) == 0);
+      CHECK(n == 0 || memcmp(p[0].data(), p[1].data(), n * 2) == 0);
+      if (n == 0) continue;
+      for (uint64_t pos : {(uint64_t)0, n - 1}) {
+        std::vector<float> bad = g;
+        bad[pos] = pos ? NAN : -INFINITY;
+        std::vector<float> a = master, b = m, c = v;
+        std::vector<uint16_t> q(n, 0x1234);
+        uint32_t ovf = 0;
+        CHECK(zs_cpu_step(a.data(), b.data(), c.data(), bad.data(), n, &hp, q.data(), dtype, 4,
+                          &ovf) == ZS_OK);
+        CHECK(ovf == 1);
+        CHECK(memcmp(a.data(), master.data(), n * 4) == 0 && q[n - 1] == 0x1234);
+      }
+    }
+  uint32_t ovf;
+  float x = 0;
+  uint16_t h = 0;
+  CHECK(zs_cpu_step(nullptr, &x, &x, &x, 1, &hp, &h, 0, 1, &ovf) == ZS_ERR_INVALID_ARG);
+  printf("offload driver ok\n");
+  return 0;
+}
