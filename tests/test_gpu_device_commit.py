@@ -215,3 +215,38 @@ def test_graph_capture_replays_match_eager(env):
         de, dg = eager.sync_scaler(), graph.sync_scaler()
         assert (dg.step_t, dg.skipped, dg.flag, dg.arrived) == (de.step_t, 0, 0, 0) == \
             (2 * (r + 1), 0, 0, 0)
+
+
+@pytest.mark.parametrize("off,n", [(0, 40_000), (3, 40_003)])
+def test_skip_restore_on_misaligned_slices(env, off, n):
+    """Skip through zs_step_device with the gather slice at an odd offset and
+    a ragged length (the commit kernel's narrow vector path): the output set
+    equals the input set and the slice holds the fp16 cast of master_in;
+    elements outside the slice are untouched."""
+    zs, synth, shard = env
+    rng = np.random.default_rng(off + n)
+    world = 3
+    g = (rng.standard_normal((world, n)) * 64.0).astype(np.float16)
+    g[1, n // 2] = np.inf
+    dg = [torch.from_numpy(g[k].copy()).cuda() for k in range(world)]
+    state = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    state[2] = np.abs(state[2])
+    din = [torch.from_numpy(x.copy()).cuda() for x in state]
+    dout = [torch.full((n,), 5.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    gather = torch.full((n + off + 5,), 0x1234, dtype=torch.int16, device="cuda")
+    host = zs.zs_loss_scaler(scale=1024.0, clean_steps=0, growth_interval=0, dynamic=1,
+                             step_t=0, skipped=0)
+    dev = zs.device_scaler_upload(zs.zs_device_scaler_make(host, 0.9, 0.999))
+    args = zs.StepArgs(dg, 0, n, *din, *dout, gather, off, None,
+                       zs.hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01,
+                                  loss_scale=1.0, step_t=1),
+                       grad_dtype=zs.ZS_FP16, param_dtype=zs.ZS_FP16)
+    announce(f"skip restore off={off} n={n}")
+    zs.zs_step_device(args, dev)
+    d = zs.device_scaler_read(dev)
+    assert (d.last_flag, d.skipped, d.step_t, d.scale) == (1, 1, 0, 512.0)
+    for got, want, name in zip(dout, state, ("master", "m", "v")):
+        assert_bits_equal(down32(got), want, f"restored {name}")
+    gb = down16(gather)
+    assert np.all(gb[:off] == 0x1234) and np.all(gb[off + n:] == 0x1234)
+    assert np.array_equal(gb[off:off + n], oracle.float_to_half(state[0], "fp16"))

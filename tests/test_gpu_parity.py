@@ -516,3 +516,32 @@ def test_sharded_step_over_all_ranks_then_all_gather(zs):
     assert not flags.any()
     for k in range(W):
         assert np.array_equal(down16(reps[k].view(torch.int16)), want), k
+
+
+def test_step_fused_vector_widths_agree(zs):
+    """The same step at element offsets 0, 4, 2 and 1 of the gradient and
+    gather buffers takes the 8-, 4-, 2- and 1-element vector paths (different
+    grids and tile shapes); every result is bit-identical."""
+    rng = np.random.default_rng(11)
+    world, rank, n = 5, 2, 50_021
+    g16 = [rand16(rng, n, 1e-3 * 1024.0, "bf16") for _ in range(world)]
+    state = [(rng.standard_normal(n) * 0.02).astype(F32), (rng.standard_normal(n) * 1e-4).astype(F32),
+             rng.uniform(0, 1e-6, n).astype(F32)]
+    hp = zs.hparams(**HP, loss_scale=1024.0, step_t=4)
+    results = []
+    for off in (0, 4, 2, 1):
+        announce(f"vector widths: offset {off}")
+        pad = np.zeros(off, np.uint16)
+        dg = [up16(np.concatenate([pad, g]), "bf16")[off:] for g in g16]
+        din = [up32(x) for x in state]
+        dout = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+        gather = torch.zeros(n + off, dtype=torch.int16, device="cuda")
+        flag = _flag()
+        zs.zs_step_fused(zs.StepArgs(dg, rank, n, *din, *dout, gather, off, flag, hp,
+                                     grad_dtype=0, param_dtype=0))
+        assert int(flag.item()) == 0
+        results.append(([down32(d) for d in dout], down16(gather)[off:]))
+    for outs, params in results[1:]:
+        for a, b in zip(outs, results[0][0]):
+            assert_bits_equal(a, b, "vector width")
+        assert np.array_equal(params, results[0][1])
