@@ -14,7 +14,7 @@
 
 #include "zeroshard.h"
 
-#include "zs_kernels.h"
+#include "zs_aux_kernels.h"
 
 
 namespace {

@@ -1,8 +1,9 @@
 /*
  * zs_kernels.h -- device code of libzeroshard (gfx950): per-element
- * arithmetic, vector loads/stores, the ring-order sum and the kernels. The
- * host side and the C ABI are in zeroshard.hip, which includes this file
- * once. Sources, cited by page title and section:
+ * arithmetic, vector loads/stores, the ring-order sum and the reduction,
+ * update and fused-step kernels. The commit and all-gather kernels are in
+ * zs_aux_kernels.h. The host side and the C ABI are in zeroshard.hip, which
+ * includes both once. Sources, cited by page title and section:
  *   [Notes] lecture notes on DP / DDP / DeepSpeed ZeRO (gitcode.csdn.net)
  *   [Intro] "并行训练框架DeepSpeed介绍"
  *   [L7]    "第 7 讲：Parallelism（上）" (CS336 lecture 7)
@@ -617,125 +618,6 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
     if (i < p.n) bad |= fused_vec<1, GDT, PDT>(p, sk, h, i);
   }
   flag_or(p.flag, bad);
-}
-
-/* ------------------------------------------------------------------------
- * Commit or skip on the device ([Intro] 一.3 items (1) and (3): a step whose
- * unscaled gradient is not finite is skipped and the loss scale adjusted).
- * Runs after the fused pass on the same stream. Every block reads the
- * step's flag; when it is set, the blocks copy the input set into the
- * output set and recast master_in into the gather slice (grid-stride), so
- * the output set holds the state after the step either way. The last block
- * to arrive applies the scaler rule (the host's zs_scaler_update, field for
- * field), advances the beta powers on a commit, records the flag and clears
- * it and the arrival counter for the next step. Same-address atomics
- * serialize in L2 (about 20 ns each), so the grid is a few large blocks:
- * kCommitBlocks arrivals per step.
- * ---------------------------------------------------------------------- */
-
-constexpr int kCommitBlock = 1024;  /* threads per commit block     */
-constexpr int kCommitBlocks = 64;   /* at most this many blocks     */
-
-struct CommitArgs {
-  zs_device_scaler *dev;
-  const float *master_in, *m_in, *v_in;
-  float *master_out, *m_out, *v_out;
-  uint16_t *param_out;  /* already at this rank's offset */
-  uint64_t n;
-  double beta1, beta2;
-};
-
-template <int VEC, int PDT>
-__device__ __forceinline__ void restore_vec(const CommitArgs &c, uint64_t i0) {
-  float x[VEC];
-  ldf<VEC>(c.master_in + i0, x);
-  stf<VEC>(c.master_out + i0, x);
-  st16<VEC, PDT>(c.param_out + i0, x);
-  ldf<VEC>(c.m_in + i0, x);
-  stf<VEC>(c.m_out + i0, x);
-  ldf<VEC>(c.v_in + i0, x);
-  stf<VEC>(c.v_out + i0, x);
-}
-
-template <int VEC, int PDT>
-__global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
-  zs_device_scaler *d = c.dev;
-  const uint32_t f = __hip_atomic_load(&d->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (f) {
-    const uint64_t stride = (uint64_t)gridDim.x * kCommitBlock * VEC;
-    for (uint64_t i0 = ((uint64_t)blockIdx.x * kCommitBlock + threadIdx.x) * VEC; i0 < c.n;
-         i0 += stride) {
-      if (i0 + VEC <= c.n) {
-        restore_vec<VEC, PDT>(c, i0);
-      } else {
-        for (uint64_t i = i0; i < c.n; ++i) restore_vec<1, PDT>(c, i);
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  __threadfence();
-  const uint32_t before = atomicAdd(&d->arrived, 1u);
-  if (before != gridDim.x - 1) return;
-  __threadfence();
-  if (f) {
-    if (d->dynamic) d->scale = d->scale * 0.5f;
-    d->clean_steps = 0;
-    d->skipped = d->skipped + 1;
-  } else {
-    d->step_t = d->step_t + 1;
-    d->beta1_t = d->beta1_t * c.beta1;
-    d->beta2_t = d->beta2_t * c.beta2;
-    const uint32_t clean = d->clean_steps + 1;
-    if (d->dynamic && d->growth_interval && clean >= d->growth_interval) {
-      d->scale = d->scale * 2.0f;
-      d->clean_steps = 0;
-    } else {
-      d->clean_steps = clean;
-    }
-  }
-  d->last_flag = f ? 1u : 0u;
-  __hip_atomic_store(&d->flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&d->arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-/* ------------------------------------------------------------------------
- * One step of the ring all-gather over W replicas of the flat 16-bit
- * parameter buffer ([Notes] 二: after the scatter-reduce each GPU passes the
- * chunk total it holds to its successor; after W-1 such steps every GPU has
- * every chunk; [L7] "Ring AllReduce 算法", phase two). Rank k sends chunk
- * c_k = (k + sigma - step + 1) mod W to rank k+1. blockIdx.y is the sender;
- * each thread copies 8 elements (16 bytes) or, on the ragged end or with
- * misaligned chunks, one at a time.
- * ---------------------------------------------------------------------- */
-
-struct GatherArgs {
-  uint16_t *r[ZS_MAX_WORLD];   /* replica k's flat buffer */
-  uint32_t world, sigma, step;
-  uint64_t phi, chunk;
-};
-
-template <int VEC>
-__global__ __launch_bounds__(kBlock) void gather_step_kernel(GatherArgs a) {
-  const uint32_t k = blockIdx.y;
-  const uint32_t c = (uint32_t)(((uint64_t)k + a.sigma + (uint64_t)a.world * a.step - a.step + 1) %
-                                a.world);
-  const uint64_t begin = (uint64_t)c * a.chunk;
-  if (begin >= a.phi) return;
-  const uint64_t len = a.phi - begin < a.chunk ? a.phi - begin : a.chunk;
-  const uint16_t *src = a.r[k] + begin;
-  uint16_t *dst = a.r[(k + 1) % a.world] + begin;
-  const uint64_t i0 = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * VEC;
-  if (i0 >= len) return;
-  if (VEC > 1 && i0 + VEC <= len) {
-    Raw16<VEC> v = ld16<VEC, true>(src + i0);
-    if constexpr (VEC == 8) {
-      u32x4 w = {v.w[0], v.w[1], v.w[2], v.w[3]};
-      *reinterpret_cast<u32x4 *>(dst + i0) = w;
-    }
-  } else {
-    for (uint64_t i = i0; i < len && i < i0 + VEC; ++i) dst[i] = src[i];
-  }
 }
 
 }  // namespace zs
