@@ -49,16 +49,18 @@ def _same_state(a, b, what):
         f"{what} params"
 
 
-def test_queued_device_steps_equal_host_commit(env):
+@pytest.mark.parametrize("wire", [0, 1])
+def test_queued_device_steps_equal_host_commit(env, wire):
     """Six steps queued without any synchronization (gradients regenerated
     on the same stream between them), one of them hit by injected inf/NaN,
-    against the host-synchronous zs_step_commit flow."""
+    against the host-synchronous zs_step_commit flow; fp32 and bf16 ring
+    partials."""
     zs, synth, shard = env
     wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=8 * 250_003, steps=6,
                              inject_steps=(3,), inject_rate=1e-3, name="queued")
-    host, gh = _make(env, wl, False)
-    dev, gd = _make(env, wl, True)
-    announce("queued device steps vs host commit")
+    host, gh = _make(env, wl, False, wire_dtype=wire)
+    dev, gd = _make(env, wl, True, wire_dtype=wire)
+    announce(f"queued device steps vs host commit, wire {wire}")
     committed = []
     for step in range(1, wl.steps + 1):
         for k in range(wl.world):
