@@ -24,11 +24,12 @@
  *
  * Conventions for every entry point
  *   - Device pointers are HIP device (HBM) addresses the caller allocated;
- *     the library never allocates or frees device memory, never keeps a
- *     pointer after the call returns and never synchronizes. Work is
- *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *     completes asynchronously; kernel faults surface at the caller's next
- *     synchronization.
+ *     the library never allocates or frees device memory and never keeps a
+ *     pointer after the call returns. Work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) and completes asynchronously;
+ *     kernel faults surface at the caller's next synchronization. Two calls
+ *     wait by contract: zs_step_commit (for its flag) and zs_cpu_step (host
+ *     work); no other call synchronizes.
  *   - Host pointers (arrays of device pointers, hyper-parameter structs,
  *     outputs of zs_partition) are read or written during the call only.
  *   - 16-bit values are IEEE binary16 (ZS_FP16) or bfloat16 (ZS_BF16).
@@ -330,7 +331,7 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
  * ev_start / ev_stop: NULL, or hipEvent_t handles recorded immediately
  * before and after the fused kernel. Calls that share a dev must be ordered
  * (one stream). Errors: as zs_step_fused (ZS_ERR_INVALID_ARG also for a
- * NULL dev); nothing is enqueued on an error. */
+ * NULL or not 8-byte-aligned dev); nothing is enqueued on an error. */
 int zs_step_device(const zs_step_args *a, zs_device_scaler *dev, void *stream, void *ev_start,
                    void *ev_stop);
 

@@ -487,7 +487,8 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
 
 int zs_step_device(const zs_step_args *a, zs_device_scaler *dev, void *stream, void *ev_start,
                    void *ev_stop) {
-  if (!dev) return fail(ZS_ERR_INVALID_ARG, "null device scaler%s");
+  if (!dev || (uintptr_t)dev % alignof(zs_device_scaler) != 0)
+    return fail(ZS_ERR_INVALID_ARG, "device scaler must be non-null and 8-byte aligned%s");
   int rc = step_fused_impl(a, stream, static_cast<hipEvent_t>(ev_start),
                            static_cast<hipEvent_t>(ev_stop), dev);
   if (rc != ZS_OK) return rc;

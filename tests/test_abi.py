@@ -258,6 +258,7 @@ def test_device_step_rejects_bad_arguments(zs):
     E = zs.ZS_ERR_INVALID_ARG
     dev = C.c_void_p(FAKE + 0x7000000)
     assert lib.zs_step_device(C.byref(a), None, None, None, None) == E
+    assert lib.zs_step_device(C.byref(a), C.c_void_p(FAKE + 0x7000004), None, None, None) == E
     assert lib.zs_step_device(None, dev, None, None, None) == E
     bad, keep2 = _fused_args(zs, grad_dtype=5)
     assert lib.zs_step_device(C.byref(bad), dev, None, None, None) == E
