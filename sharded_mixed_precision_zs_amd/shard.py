@@ -2,14 +2,18 @@
 
 `ShardState` owns this rank's optimizer shard in HBM -- two sets of fp32
 (master, m, v) and two 16-bit gather buffers (ping-pong), the overflow flag
-and the loss scaler -- and runs one optimizer step as
+and the loss scaler -- and runs one optimizer step in one of two ways.
+step() decides on the host:
 
     zs_step_fused(in-set -> out-set)    one pass over HBM
     flag -> host (4 bytes)              the only synchronization
     flag == 0: swap sets, t += 1        commit
     flag == 1: keep the in-set          skip (scale halves when dynamic)
 
-which is the owner's update sequence of the DeepSpeed ZeRO notes (section
+step_device() (device_commit=True) decides on the GPU with no host round
+trip: the fused pass reads the scale from a device-resident scaler, a
+commit kernel restores the out-set on a skip and updates the scaler, and
+the sets swap every step. Both follow the owner's update sequence of the DeepSpeed ZeRO notes (section
 三): gradients averaged and unscaled in fp32, moments and master updated, the
 16-bit copy refreshed for the all-gather. Micro-batches before the last are
 reduced into an fp32 accumulator with zs_reduce_scatter_avg (lecture 7,
