@@ -339,7 +339,7 @@ def main():
                            roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS))
     offload = None
     if not args.no_offload:
-        offload = run_offload(args.workload, max(3, args.steps // 4), 1, torch)
+        offload = run_offload(args.workload, max(10, args.steps // 2), 2, torch)
         log(json.dumps(offload))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
 

@@ -228,6 +228,16 @@ int zs_cpu_step(float *master, float *m, float *v, const float *grad_part, uint6
                 const zs_adamw_hparams *hp, void *params16, int param_dtype, int threads,
                 uint32_t *overflow);
 
+/* Pass 2 of zs_cpu_step alone, for a caller that has already established
+ * that no grad_part[i] / loss_scale is non-finite, e.g. with
+ * zs_check_overflow on the device before the copy (which lets the update
+ * start on the first pieces of the gradient while the rest is still in
+ * flight). Same arithmetic, same arguments; with a non-finite gradient the
+ * state is updated with it (nothing is checked). Blocks until done.
+ * Errors: as zs_cpu_step. */
+int zs_cpu_update(float *master, float *m, float *v, const float *grad_part, uint64_t n,
+                  const zs_adamw_hparams *hp, void *params16, int param_dtype, int threads);
+
 /* Host-side commit/skip bookkeeping of dynamic loss scaling ([Intro] 一.3
  * items (1) and (3) name it without a rule). With dynamic != 0: on overflow
  * the scale halves, clean_steps resets and step_t stays; otherwise

@@ -20,6 +20,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -129,20 +133,140 @@ void update_scalar(float *master, float *m, float *v, const float *a, uint64_t l
   }
 }
 
-/* Runs fn(lo, hi) over `threads` contiguous ranges, each on a fresh thread
- * with MXCSR set to round-to-nearest, subnormals kept. */
+/* A persistent pool of worker threads, created on first use and grown on
+ * demand, so a step does not pay for thread creation. Every worker runs
+ * with MXCSR set to round-to-nearest, subnormals kept (the caller's thread,
+ * which takes task 0, switches for the duration of run()). One run() at a
+ * time: calls from several host threads are serialized. Every worker checks
+ * out of every run, with or without a task, and run() returns only after
+ * all have: no worker can still be claiming tasks of a finished run when
+ * the next one starts. The workers live until the process ends. */
+class Pool {
+ public:
+  static Pool &instance() {
+    static Pool *p = new Pool();  /* never destroyed: workers may be parked */
+    return *p;
+  }
+
+  /* fn(task) for task in [0, tasks); returns when all are done. */
+  void run(int tasks, const std::function<void(int)> &fn) {
+    std::lock_guard<std::mutex> serial(run_mu_);
+    grow(tasks - 1);
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      fn_ = &fn;
+      tasks_ = tasks;
+      next_.store(1);
+      pending_ = (int)workers_.size();
+      ++generation_;
+    }
+    cv_work_.notify_all();
+    const unsigned saved = _mm_getcsr();
+    _mm_setcsr(kMxcsrNearest);
+    fn(0);
+    _mm_setcsr(saved);
+    std::unique_lock<std::mutex> lk(mu_);
+    cv_done_.wait(lk, [&] { return pending_ == 0; });
+    fn_ = nullptr;
+  }
+
+ private:
+  /* Called by run() before it opens the next generation; generation_ only
+   * changes inside run(), so a new worker starts out waiting for exactly
+   * that next generation. */
+  void grow(int want) {
+    while ((int)workers_.size() < want) {
+      const uint64_t current = generation_;
+      workers_.emplace_back([this, current] { loop(current); });
+    }
+  }
+
+  void loop(uint64_t seen) {
+    _mm_setcsr(kMxcsrNearest);
+    for (;;) {
+      const std::function<void(int)> *fn;
+      int tasks;
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_work_.wait(lk, [&] { return generation_ != seen; });
+        seen = generation_;
+        fn = fn_;
+        tasks = tasks_;
+      }
+      for (int t = next_.fetch_add(1); t < tasks; t = next_.fetch_add(1)) (*fn)(t);
+      std::lock_guard<std::mutex> lk(mu_);
+      if (--pending_ == 0) cv_done_.notify_one();
+    }
+  }
+
+  std::mutex run_mu_, mu_;
+  std::condition_variable cv_work_, cv_done_;
+  std::vector<std::thread> workers_;
+  const std::function<void(int)> *fn_ = nullptr;
+  int tasks_ = 0;
+  int pending_ = 0;
+  std::atomic<int> next_{0};
+  uint64_t generation_ = 0;
+};
+
+/* Runs fn(t, lo, hi) over `threads` contiguous ranges on the pool. */
 template <typename F>
 void parallel_ranges(uint64_t n, int threads, F fn) {
-  std::vector<std::thread> pool;
-  pool.reserve((size_t)threads);
-  for (int t = 0; t < threads; ++t) {
-    uint64_t lo = n * (uint64_t)t / (uint64_t)threads, hi = n * (uint64_t)(t + 1) / (uint64_t)threads;
-    pool.emplace_back([=] {
-      _mm_setcsr(kMxcsrNearest);
-      fn(t, lo, hi);
-    });
+  Pool::instance().run(threads, [&](int t) {
+    uint64_t lo = n * (uint64_t)t / (uint64_t)threads;
+    uint64_t hi = n * (uint64_t)(t + 1) / (uint64_t)threads;
+    fn(t, lo, hi);
+  });
+}
+
+}  // namespace
+
+namespace {
+
+/* Argument checks shared by both entry points, and the per-step scalars:
+ * binary64, beta^t by t repeated products, rounded once to fp32 (the
+ * device kernels' make-up of the same constants). */
+int prepare(const float *master, const float *m, const float *v, const float *grad_part,
+            const zs_adamw_hparams *hp, const void *params16, int param_dtype, Consts *k) {
+  if (!master || !m || !v || !grad_part || !hp || !params16) return ZS_ERR_INVALID_ARG;
+  if (param_dtype != ZS_BF16 && param_dtype != ZS_FP16) return ZS_ERR_INVALID_ARG;
+  if (!(hp->loss_scale > 0.0f) || !isfinite(hp->loss_scale) || hp->step_t == 0)
+    return ZS_ERR_INVALID_ARG;
+  double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
+  double b1t = 1.0, b2t = 1.0;
+  for (uint32_t t = 0; t < hp->step_t; ++t) {
+    b1t *= b1;
+    b2t *= b2;
   }
-  for (auto &th : pool) th.join();
+  k->alpha = (float)(lr / (1.0 - b1t));
+  k->bc2 = (float)sqrt(1.0 - b2t);
+  k->delta = (float)(1.0 - lr * wd);
+  k->c1 = (float)(1.0 - b1);
+  k->c2 = (float)(1.0 - b2);
+  k->beta1 = hp->beta1;
+  k->beta2 = hp->beta2;
+  k->eps = hp->eps;
+  k->scale = hp->loss_scale;
+  return ZS_OK;
+}
+
+int thread_count(int threads, uint64_t n) {
+  if (threads <= 0) threads = (int)std::min(64u, std::max(1u, std::thread::hardware_concurrency()));
+  return (int)std::min<uint64_t>((uint64_t)threads, std::max<uint64_t>(1, n / 4096));
+}
+
+bool have_avx512() {
+  return __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+}
+
+/* Pass 2: AdamW in place and the 16-bit parameters. */
+void update_all(float *master, float *m, float *v, const float *grad_part, uint64_t n,
+                const Consts &k, uint16_t *out, int param_dtype, int threads) {
+  const bool avx512 = have_avx512();
+  parallel_ranges(n, threads, [&](int, uint64_t lo, uint64_t hi) {
+    if (avx512) update_avx512(master, m, v, grad_part, lo, hi, k, out, param_dtype);
+    else update_scalar(master, m, v, grad_part, lo, hi, k, out, param_dtype);
+  });
 }
 
 }  // namespace
@@ -150,34 +274,14 @@ void parallel_ranges(uint64_t n, int threads, F fn) {
 extern "C" int zs_cpu_step(float *master, float *m, float *v, const float *grad_part, uint64_t n,
                            const zs_adamw_hparams *hp, void *params16, int param_dtype,
                            int threads, uint32_t *overflow) {
-  if (!master || !m || !v || !grad_part || !hp || !params16 || !overflow) return ZS_ERR_INVALID_ARG;
-  if (param_dtype != ZS_BF16 && param_dtype != ZS_FP16) return ZS_ERR_INVALID_ARG;
-  if (!(hp->loss_scale > 0.0f) || !isfinite(hp->loss_scale) || hp->step_t == 0)
-    return ZS_ERR_INVALID_ARG;
+  if (!overflow) return ZS_ERR_INVALID_ARG;
+  Consts k;
+  int rc = prepare(master, m, v, grad_part, hp, params16, param_dtype, &k);
+  if (rc != ZS_OK) return rc;
   *overflow = 0;
   if (n == 0) return ZS_OK;
-  Consts k;
-  double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
-  double b1t = 1.0, b2t = 1.0;
-  for (uint32_t t = 0; t < hp->step_t; ++t) {
-    b1t *= b1;
-    b2t *= b2;
-  }
-  k.alpha = (float)(lr / (1.0 - b1t));
-  k.bc2 = (float)sqrt(1.0 - b2t);
-  k.delta = (float)(1.0 - lr * wd);
-  k.c1 = (float)(1.0 - b1);
-  k.c2 = (float)(1.0 - b2);
-  k.beta1 = hp->beta1;
-  k.beta2 = hp->beta2;
-  k.eps = hp->eps;
-  k.scale = hp->loss_scale;
-
-  if (threads <= 0) threads = (int)std::min(64u, std::max(1u, std::thread::hardware_concurrency()));
-  threads = (int)std::min<uint64_t>((uint64_t)threads, std::max<uint64_t>(1, n / 4096));
-  const bool avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
-  uint16_t *out = static_cast<uint16_t *>(params16);
-
+  threads = thread_count(threads, n);
+  const bool avx512 = have_avx512();
   /* Pass 1: the overflow check over the whole partition (skip before
    * touching any state). */
   std::vector<char> bad((size_t)threads, 0);
@@ -190,10 +294,19 @@ extern "C" int zs_cpu_step(float *master, float *m, float *v, const float *grad_
       *overflow = 1;
       return ZS_OK;
     }
-  /* Pass 2: AdamW in place and the 16-bit parameters. */
-  parallel_ranges(n, threads, [&](int, uint64_t lo, uint64_t hi) {
-    if (avx512) update_avx512(master, m, v, grad_part, lo, hi, k, out, param_dtype);
-    else update_scalar(master, m, v, grad_part, lo, hi, k, out, param_dtype);
-  });
+  update_all(master, m, v, grad_part, n, k, static_cast<uint16_t *>(params16), param_dtype,
+             threads);
+  return ZS_OK;
+}
+
+extern "C" int zs_cpu_update(float *master, float *m, float *v, const float *grad_part,
+                             uint64_t n, const zs_adamw_hparams *hp, void *params16,
+                             int param_dtype, int threads) {
+  Consts k;
+  int rc = prepare(master, m, v, grad_part, hp, params16, param_dtype, &k);
+  if (rc != ZS_OK) return rc;
+  if (n == 0) return ZS_OK;
+  update_all(master, m, v, grad_part, n, k, static_cast<uint16_t *>(params16), param_dtype,
+             thread_count(threads, n));
   return ZS_OK;
 }

@@ -87,6 +87,7 @@ def _load():
         "zs_all_gather_step": ([C.POINTER(vp), u32, u64, u32, u32, vp], i32),
         "zs_cpu_step": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, i32, i32,
                          C.POINTER(u32)], i32),
+        "zs_cpu_update": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, i32, i32], i32),
         "zs_device_scaler_make": ([C.POINTER(zs_loss_scaler), f32, f32,
                                    C.POINTER(zs_device_scaler)], i32),
         "zs_step_device": ([C.POINTER(zs_step_args), vp, vp, vp, vp], i32),
@@ -328,10 +329,9 @@ def zs_all_gather_step(replicas: Sequence, phi: int, step: int, sigma: int = 0, 
                                                          _stream(stream)))
 
 
-def zs_cpu_step(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param_dtype=None,
-                threads=0):
-    """ZeRO-Offload update on host tensors/arrays (torch CPU tensors or numpy
-    arrays, contiguous). Returns the overflow flag (1: skipped)."""
+def _host_args(fn, master, m, v, grad_part, params16, param_dtype):
+    """Pointers and size of host tensors/arrays (torch CPU tensors or numpy
+    arrays, contiguous) for the host update entry points."""
     def hptr(x, elem, what):
         if hasattr(x, "data_ptr"):
             if x.is_cuda or not x.is_contiguous() or x.element_size() != elem:
@@ -344,11 +344,27 @@ def zs_cpu_step(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param_d
                                               hptr(v, 4, "v"), hptr(grad_part, 4, "grad_part"))
     pp, n4 = hptr(params16, 2, "params16")
     if not (n == n1 == n2 == n3 <= n4):
-        raise ValueError("zs_cpu_step: size mismatch")
+        raise ValueError(f"{fn}: size mismatch")
     if param_dtype is None:
         param_dtype = _dtype_code(params16, None) if hasattr(params16, "dtype") and \
             str(params16.dtype).startswith("torch") else ZS_BF16
+    return pm, p1, p2, pg, n, pp, param_dtype
+
+
+def zs_cpu_step(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param_dtype=None,
+                threads=0):
+    """ZeRO-Offload update on host memory. Returns the overflow flag (1: skipped)."""
+    pm, p1, p2, pg, n, pp, dt = _host_args("zs_cpu_step", master, m, v, grad_part, params16,
+                                           param_dtype)
     flag = C.c_uint32(0)
-    _check("zs_cpu_step", _lib.zs_cpu_step(pm, p1, p2, pg, n, C.byref(hp), pp, param_dtype,
-                                           threads, C.byref(flag)))
+    _check("zs_cpu_step", _lib.zs_cpu_step(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads,
+                                           C.byref(flag)))
     return int(flag.value)
+
+
+def zs_cpu_update(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param_dtype=None,
+                  threads=0):
+    """zs_cpu_step without its check (the caller has checked the gradient)."""
+    pm, p1, p2, pg, n, pp, dt = _host_args("zs_cpu_update", master, m, v, grad_part, params16,
+                                           param_dtype)
+    _check("zs_cpu_update", _lib.zs_cpu_update(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads))

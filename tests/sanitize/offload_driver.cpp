@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <thread>
 #include <vector>
 
 #include "zeroshard.h"
@@ -72,6 +73,47 @@ int main() {
         CHECK(memcmp(a.data(), master.data(), n * 4) == 0 && q[n - 1] == 0x1234);
       }
     }
+  /* Many short runs back to back with changing thread counts (the worker
+   * pool's run boundaries), then two host threads calling at once (runs are
+   * serialized); each result must equal a one-thread reference. */
+  {
+    const uint64_t n = 70001;  /* up to 17 threads (n / 4096) */
+    std::vector<float> g(n), m0(n), v0(n), t0(n);
+    for (uint64_t i = 0; i < n; ++i) {
+      t0[i] = rf(0.04f);
+      m0[i] = rf(2e-4f);
+      v0[i] = fabsf(rf(2e-6f));
+      g[i] = rf(4.0f);
+    }
+    std::vector<float> rt = t0, rm = m0, rv = v0;
+    std::vector<uint16_t> rp(n);
+    uint32_t ovf;
+    CHECK(zs_cpu_step(rt.data(), rm.data(), rv.data(), g.data(), n, &hp, rp.data(), 0, 1, &ovf) ==
+          ZS_OK);
+    for (int rep = 0; rep < 200; ++rep) {
+      std::vector<float> a = t0, b = m0, c = v0;
+      std::vector<uint16_t> q(n);
+      CHECK(zs_cpu_step(a.data(), b.data(), c.data(), g.data(), n, &hp, q.data(), 0,
+                        1 + rep % 7, &ovf) == ZS_OK);
+      CHECK(memcmp(a.data(), rt.data(), n * 4) == 0 && memcmp(q.data(), rp.data(), n * 2) == 0);
+    }
+    int bad = 0;
+    auto caller = [&](int seed) {
+      for (int rep = 0; rep < 50; ++rep) {
+        std::vector<float> a = t0, b = m0, c = v0;
+        std::vector<uint16_t> q(n);
+        uint32_t o;
+        if (zs_cpu_step(a.data(), b.data(), c.data(), g.data(), n, &hp, q.data(), 0,
+                        2 + (seed + rep) % 5, &o) != ZS_OK ||
+            memcmp(a.data(), rt.data(), n * 4) != 0)
+          __atomic_fetch_add(&bad, 1, __ATOMIC_RELAXED);
+      }
+    };
+    std::thread x(caller, 1), y(caller, 2);
+    x.join();
+    y.join();
+    CHECK(bad == 0);
+  }
   uint32_t ovf;
   float x = 0;
   uint16_t h = 0;

@@ -112,3 +112,27 @@ def test_cpu_step_rejects_bad_arguments(zs):
     with pytest.raises(zs.ZsError):
         zs.zs_cpu_step(x, x.copy(), x.copy(), x.copy(), zs.hparams(**HP, loss_scale=1.0, step_t=1),
                        p, 9)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("n,threads", [(1, 1), (4099, 2), (200_003, 0)])
+def test_cpu_update_equals_cpu_step(zs, dtype, n, threads):
+    """zs_cpu_update is zs_cpu_step's update pass alone: the same bits on
+    finite gradients, in pieces or whole."""
+    rng = np.random.default_rng(n)
+    master, m, v, a = _inputs(rng, n, 1024.0)
+    hp = zs.hparams(**HP, loss_scale=1024.0, step_t=9)
+    code = zs.ZS_BF16 if dtype == "bf16" else zs.ZS_FP16
+    ref = [x.copy() for x in (master, m, v)]
+    pref = np.empty(n, np.uint16)
+    assert zs.zs_cpu_step(*ref, a, hp, pref, code, threads) == 0
+    got = [x.copy() for x in (master, m, v)]
+    pgot = np.empty(n, np.uint16)
+    cuts = sorted({0, n // 3, n // 2, n})
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        zs.zs_cpu_update(*(x[lo:hi] for x in got), a[lo:hi], hp, pgot[lo:hi], code, threads)
+    for x, y in zip(got, ref):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(pgot, pref)
+    with pytest.raises(zs.ZsError):
+        zs.zs_cpu_update(*got, a, zs.hparams(**HP, loss_scale=0.0, step_t=1), pgot, code)
