@@ -485,12 +485,14 @@ def test_all_gather_matches_the_oracle(zs, world, phi, sigma):
             assert_bits_equal(got, oracle_after(step), f"after step {step}")
 
 
-def test_sharded_step_over_all_ranks_then_all_gather(zs):
+@pytest.mark.parametrize("W,phi", [(4, 4 * 50_003 + 3), (4, 9), (5, 13), (7, 6995)])
+def test_sharded_step_over_all_ranks_then_all_gather(zs, W, phi):
     """A whole ZeRO-2 step for W ranks on one GPU: every rank's fused step
     on its own partition (gradients reduced in that rank's ring order), then
-    the ring all-gather; every replica must hold the oracle's parameters."""
-    rng = np.random.default_rng(77)
-    W, phi = 4, 4 * 50_003 + 3
+    the ring all-gather; every replica must hold the oracle's parameters.
+    phi = 9, W = 4 leaves the last rank an empty partition (P = 3); 13 over
+    5 leaves it one element; 6995 over 7 a ragged one."""
+    rng = np.random.default_rng(77 + phi)
     P = -(-phi // W)
     announce(f"sharded step W={W} phi={phi}")
     grads = [rand16(rng, phi, 1e-3 * 1024, "bf16") for _ in range(W)]
@@ -501,11 +503,18 @@ def test_sharded_step_over_all_ranks_then_all_gather(zs):
     want = np.empty(phi, np.uint16)
     for r in range(W):
         p, off, cnt = oracle.partition(phi, W, r)
-        din = [up32(master[off:off + cnt]), up32(np.zeros(cnt, F32)), up32(np.zeros(cnt, F32))]
-        dout = [torch.empty(cnt, dtype=torch.float32, device="cuda") for _ in range(3)]
-        args = zs.StepArgs([g[off:off + cnt] for g in dgrads], r, cnt, *din, *dout, reps[r], off,
-                           flags[r:r + 1], zs.hparams(**HP, loss_scale=1024.0, step_t=1))
+        # an empty partition still passes valid (one-element) buffers
+        room = max(cnt, 1)
+        mst = np.zeros(room, F32)
+        mst[:cnt] = master[off:off + cnt]
+        din = [up32(mst), up32(np.zeros(room, F32)), up32(np.zeros(room, F32))]
+        dout = [torch.empty(room, dtype=torch.float32, device="cuda") for _ in range(3)]
+        args = zs.StepArgs([g[min(off, phi - 1):] for g in dgrads], r, cnt, *din, *dout, reps[r],
+                           min(off, phi), flags[r:r + 1],
+                           zs.hparams(**HP, loss_scale=1024.0, step_t=1))
         zs.zs_step_fused(args)
+        if cnt == 0:
+            continue
         f, mo, mmo, vo, po = oracle.shard_step([g[off:off + cnt] for g in grads], r, "bf16",
                                                "bf16", master[off:off + cnt],
                                                np.zeros(cnt, F32), np.zeros(cnt, F32),
