@@ -211,6 +211,13 @@ class ShardState:
             self.cur = 1 - self.cur
         return self.last_flag == 0
 
+    def _step_args(self, worker_grads, acc_in):
+        if worker_grads is not None:
+            return self._args(worker_grads, acc_in)
+        if self._bound is None:
+            raise RuntimeError("no gradients given and none bound: call bind() first")
+        return self._bound[self.cur]
+
     def bind(self, worker_grads: Sequence[torch.Tensor], acc_in: Optional[torch.Tensor] = None):
         """Prepare both directions' arguments once for gradients that stay at
         the same addresses every step; step() with no gradients uses them."""
@@ -226,8 +233,7 @@ class ShardState:
         """One optimizer step through zs_step_commit (launch, flag readback,
         scaler update in one native call); returns True when committed.
         ev_start / ev_stop: optional raw hipEvent_t handles around the kernel."""
-        args = (self._bound[self.cur] if worker_grads is None
-                else self._args(worker_grads, acc_in))
+        args = self._step_args(worker_grads, acc_in)
         args.args.overflow_flag = self._next_flag_addr()
         ok = zs.zs_step_commit(args, self.scaler, self.flag_host, stream, ev_start, ev_stop)
         self.last_flag = 0 if ok else 1
@@ -243,8 +249,7 @@ class ShardState:
         sync_scaler() reads the outcome."""
         if not self.device_commit:
             raise RuntimeError("ShardState was built without device_commit=True")
-        args = (self._bound[self.cur] if worker_grads is None
-                else self._args(worker_grads, acc_in))
+        args = self._step_args(worker_grads, acc_in)
         zs.zs_step_device(args, self.dev, stream, ev_start, ev_stop)
         self.cur = 1 - self.cur
 
