@@ -554,3 +554,35 @@ def test_step_fused_vector_widths_agree(zs):
         for a, b in zip(outs, results[0][0]):
             assert_bits_equal(a, b, "vector width")
         assert np.array_equal(params, results[0][1])
+
+
+@pytest.mark.parametrize("eps", [1e-8, 0.0])
+def test_step_fused_special_state_values(zs, eps):
+    """master, m and v drawn from special values (signed zeros, subnormals,
+    values near the fp32 maximum, infinities, NaN) with ordinary gradients:
+    the kernel's IEEE behaviour (subnormals kept, correctly rounded divide
+    and square root, inf and NaN propagation, 0/0 when eps = 0) equals the
+    oracle's element for element; NaN compared by class."""
+    rng = np.random.default_rng(int(eps == 0.0) + 31)
+    world, rank, n = 3, 1, 4099
+    specials = np.array([0.0, -0.0, 1e-45, -1e-45, 1.17549421e-38, 5.877e-39, 1e-30, 3.4e38,
+                         -3.4e38, 1.7e38, np.inf, -np.inf, np.nan, 1.0, -1.0, 1e-3], F32)
+    master = specials[rng.integers(0, specials.size, n)]
+    m = specials[rng.integers(0, specials.size, n)]
+    v = np.abs(specials[rng.integers(0, specials.size, n)])
+    g16 = [rand16(rng, n, 1e-3 * 1024.0, "bf16") for _ in range(world)]
+    hp = dict(HP, eps=eps)
+    announce(f"special state values eps={eps}")
+    din = [up32(x) for x in (master, m, v)]
+    dout = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    gather = torch.zeros(n, dtype=torch.int16, device="cuda")
+    flag = _flag()
+    zs.zs_step_fused(zs.StepArgs([up16(g, "bf16") for g in g16], rank, n, *din, *dout, gather, 0,
+                                 flag, zs.hparams(**hp, loss_scale=1024.0, step_t=2),
+                                 grad_dtype=0, param_dtype=0))
+    f, mo, mmo, vo, po = oracle.shard_step(g16, rank, "bf16", "bf16", master, m, v,
+                                           loss_scale=1024.0, step_t=2, **hp)
+    assert int(flag.item()) == f == 0      # the flag looks at gradients only
+    for got, want, what in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
+        assert_bits_equal(down32(got), want, what)
+    assert assert_ulp16(down16(gather), po, "bf16", 0, "params") == 0
