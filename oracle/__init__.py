@@ -28,9 +28,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    lib = C.CDLL(_build.LIB)
+    # ZSO_ORACLE_LIB: load another build of the oracle (the mutation test
+    # points it at copies with planted mistakes)
+    path = os.environ.get("ZSO_ORACLE_LIB")
+    if path is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        path = _build.LIB
+    lib = C.CDLL(path)
     u16p = C.POINTER(C.c_uint16)
     f32p = C.POINTER(C.c_float)
     u64p = C.POINTER(C.c_uint64)

@@ -262,6 +262,16 @@ def test_flag_is_taken_after_the_unscale():
     assert oracle.check_overflow(out, 1.0) == 0
 
 
+def test_shard_step_flag_is_taken_after_the_unscale():
+    # The whole step flags the unscaled gradient too: a finite average of
+    # 2^126 is fine at S = 1 and overflows at S = 1/4.
+    big = to_bf16_bits(np.full(8, 2.0 ** 126, F32))
+    z = np.zeros(8, F32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step_t=1)
+    assert oracle.shard_step([big, big], 0, "bf16", "bf16", z, z, z, loss_scale=1.0, **hp)[0] == 0
+    assert oracle.shard_step([big, big], 0, "bf16", "bf16", z, z, z, loss_scale=0.25, **hp)[0] == 1
+
+
 # ---- a7: AdamW ------------------------------------------------------------------
 
 def _ulp(x):
@@ -282,6 +292,23 @@ def test_adamw_first_step_is_lr_sign_g():
     oracle.adamw(master, m, v, g, 1.0, lr, 0.9, 0.999, 0.0, 0.0, 1)
     err = np.abs(master.astype(np.float64) + lr * np.sign(g))
     assert np.all(err <= 8 * _ulp(lr))
+
+
+def test_adamw_first_step_decay_is_decoupled():
+    # First step (m = v = 0, t = 1, eps = 0) with a large decay: the decay
+    # multiplies the old weight only, theta'' = theta (1 - lr wd) - lr sign(g),
+    # not (theta - lr sign(g)) (1 - lr wd), which differs by lr^2 wd.
+    rng = np.random.default_rng(3)
+    n = 5000
+    theta = rng.uniform(-1, 1, n).astype(F32)
+    g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 2, n)).astype(F32)
+    g[g == 0] = F32(1.0)
+    lr, wd = 0.1, 0.5
+    master, m, v = theta.copy(), np.zeros(n, F32), np.zeros(n, F32)
+    oracle.adamw(master, m, v, g, 1.0, lr, 0.9, 0.999, 0.0, wd, 1)
+    lr32, wd32 = float(F32(lr)), float(F32(wd))
+    want = theta.astype(np.float64) * (1.0 - lr32 * wd32) - lr32 * np.sign(g)
+    assert np.all(np.abs(master - want) <= 16 * _ulp(np.maximum(np.abs(want), lr)))
 
 
 def test_adamw_zero_gradient_is_pure_decay():
@@ -470,6 +497,21 @@ def test_wire_bf16_witnesses():
     np.testing.assert_array_equal(wire, np.array([1.0, 1.0078125, 1.015625, 1.0], F32))
     np.testing.assert_array_equal(fp32, np.array([1.00390625, 1.005859375, 1.01171875,
                                                   0.998046875], F32))
+
+
+def test_wire_rounds_the_first_term_too():
+    # fp16 gradients on a bf16 wire, W = 2, rank 0: the successor's value
+    # goes on the wire (rounded to bf16) before the owner's term is added.
+    # 1 + 2^-10 rounds to 1 on the wire; 1 + 2^-8 is then a tie -> even = 1.
+    # 1 + 3*2^-10 rounds to 1; 1 + 2^-9 is below the tie -> 1.
+    # Without the first rounding both would give 1 + 5*2^-10 -> 1 + 2^-7.
+    owner = np.array([2.0 ** -8, 2.0 ** -9], np.float16).view(np.uint16)
+    succ = np.array([1.0 + 2.0 ** -10, 1.0 + 3 * 2.0 ** -10], np.float16).view(np.uint16)
+    got = oracle.ring_chunk_sum([owner, succ], 0, "fp16", wire="bf16")
+    np.testing.assert_array_equal(got, np.array([1.0, 1.0], F32))
+    a = np.empty(2, F32)
+    oracle.reduce_avg([owner, succ], 0, "fp16", a, False, 1.0, wire="bf16")
+    np.testing.assert_array_equal(a, np.array([0.5, 0.5], F32))
 
 
 @pytest.mark.parametrize("wire,dtype,u", [("bf16", "bf16", 2.0 ** -8), ("fp16", "fp16", 2.0 ** -11)])
