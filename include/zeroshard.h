@@ -36,7 +36,8 @@
  *   - Any element offset is accepted; 16-byte-aligned operands take the
  *     widest (8-element) vector path, others a narrower one of the same
  *     kernel.
- *   - n == 0 is a no-op that returns ZS_OK.
+ *   - n == 0 is a no-op that returns ZS_OK; element counts and offsets
+ *     above 2^48 return ZS_ERR_UNSUPPORTED before anything is enqueued.
  *   - Status codes: ZS_OK on success; ZS_ERR_INVALID_ARG (null pointer,
  *     world == 0 or > ZS_MAX_WORLD, rank >= world, bad dtype or wire dtype, non-finite or
  *     zero loss scale, step_t == 0) before anything is enqueued;

@@ -227,8 +227,10 @@ namespace {
  * binary64, beta^t by t repeated products, rounded once to fp32 (the
  * device kernels' make-up of the same constants). */
 int prepare(const float *master, const float *m, const float *v, const float *grad_part,
-            const zs_adamw_hparams *hp, const void *params16, int param_dtype, Consts *k) {
+            uint64_t n, const zs_adamw_hparams *hp, const void *params16, int param_dtype,
+            Consts *k) {
   if (!master || !m || !v || !grad_part || !hp || !params16) return ZS_ERR_INVALID_ARG;
+  if (n > (1ull << 48)) return ZS_ERR_UNSUPPORTED;
   if (param_dtype != ZS_BF16 && param_dtype != ZS_FP16) return ZS_ERR_INVALID_ARG;
   if (!(hp->loss_scale > 0.0f) || !isfinite(hp->loss_scale) || hp->step_t == 0)
     return ZS_ERR_INVALID_ARG;
@@ -276,7 +278,7 @@ extern "C" int zs_cpu_step(float *master, float *m, float *v, const float *grad_
                            int threads, uint32_t *overflow) {
   if (!overflow) return ZS_ERR_INVALID_ARG;
   Consts k;
-  int rc = prepare(master, m, v, grad_part, hp, params16, param_dtype, &k);
+  int rc = prepare(master, m, v, grad_part, n, hp, params16, param_dtype, &k);
   if (rc != ZS_OK) return rc;
   *overflow = 0;
   if (n == 0) return ZS_OK;
@@ -303,7 +305,7 @@ extern "C" int zs_cpu_update(float *master, float *m, float *v, const float *gra
                              uint64_t n, const zs_adamw_hparams *hp, void *params16,
                              int param_dtype, int threads) {
   Consts k;
-  int rc = prepare(master, m, v, grad_part, hp, params16, param_dtype, &k);
+  int rc = prepare(master, m, v, grad_part, n, hp, params16, param_dtype, &k);
   if (rc != ZS_OK) return rc;
   if (n == 0) return ZS_OK;
   update_all(master, m, v, grad_part, n, k, static_cast<uint16_t *>(params16), param_dtype,

@@ -41,6 +41,12 @@ int launch_result() {
 
 bool valid_dtype(int dt) { return dt == ZS_BF16 || dt == ZS_FP16; }
 
+/* Element counts and offsets above 2^48 are refused before any size
+ * arithmetic (byte extents below are 4 * n and must not wrap). */
+constexpr uint64_t kMaxElems = 1ull << 48;
+
+bool too_big(uint64_t n) { return n > kMaxElems; }
+
 bool valid_wire(int w) { return w == ZS_WIRE_FP32 || w == ZS_WIRE_BF16 || w == ZS_WIRE_FP16; }
 
 /* zs_step_commit polls the stream for errors this often while it waits. */
@@ -191,6 +197,7 @@ int zs_reduce_scatter_avg(const void *const *worker_grads, int grad_dtype,
     return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64 and rank < world%s");
   if (!valid_dtype(grad_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad grad dtype%s");
   if (!valid_wire(wire_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad wire dtype%s");
+  if (too_big(n)) return fail(ZS_ERR_UNSUPPORTED, "n exceeds 2^48 elements%s");
   ReduceArgs a;
   a.wire = wire_dtype;
   if (!make_scales(world, loss_scale, &a.k))
@@ -241,6 +248,7 @@ int zs_check_overflow(const float *grad_part, uint64_t n, float loss_scale,
                       uint32_t *overflow_flag, void *stream) {
   if (!grad_part || !overflow_flag)
     return fail(ZS_ERR_INVALID_ARG, "null grad_part or overflow_flag%s");
+  if (too_big(n)) return fail(ZS_ERR_UNSUPPORTED, "n exceeds 2^48 elements%s");
   CheckArgs c;
   if (!make_scales(1, loss_scale, &c.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
@@ -267,6 +275,7 @@ int zs_adamw_step(float *master, float *m, float *v, const float *grad_part,
                   const uint32_t *overflow_flag, void *stream) {
   if (!master || !m || !v || !grad_part || !hp)
     return fail(ZS_ERR_INVALID_ARG, "null master, m, v, grad_part or hparams%s");
+  if (too_big(n)) return fail(ZS_ERR_UNSUPPORTED, "n exceeds 2^48 elements%s");
   AdamArgs p;
   if (!make_scales(1, hp->loss_scale, &p.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
@@ -298,6 +307,8 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
   if (!master || !gather_buf)
     return fail(ZS_ERR_INVALID_ARG, "null master or gather_buf%s");
   if (!valid_dtype(param_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad param dtype%s");
+  if (too_big(n) || too_big(offset))
+    return fail(ZS_ERR_UNSUPPORTED, "n or offset exceeds 2^48 elements%s");
   if (n == 0) return ZS_OK;
   CastArgs c;
   c.master = master;
@@ -346,6 +357,8 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   if (!valid_dtype(a->grad_dtype) || !valid_dtype(a->param_dtype))
     return fail(ZS_ERR_INVALID_ARG, "bad grad or param dtype%s");
   if (!valid_wire(a->wire_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad wire dtype%s");
+  if (too_big(a->n) || too_big(a->gather_offset))
+    return fail(ZS_ERR_UNSUPPORTED, "n or gather_offset exceeds 2^48 elements%s");
   FusedArgs p;
   p.wire = a->wire_dtype;
   zs_adamw_hparams hp = a->hp;
@@ -587,6 +600,7 @@ int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint
     return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64%s");
   if (sigma >= world || step == 0 || step >= world)
     return fail(ZS_ERR_INVALID_ARG, "need sigma < world and 1 <= step < world%s");
+  if (too_big(phi)) return fail(ZS_ERR_UNSUPPORTED, "phi exceeds 2^48 elements%s");
   GatherArgs g;
   for (uint32_t k = 0; k < world; ++k) {
     if (!replicas[k]) return fail(ZS_ERR_INVALID_ARG, "replicas has a null pointer%s");

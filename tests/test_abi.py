@@ -264,3 +264,30 @@ def test_device_step_rejects_bad_arguments(zs):
     assert lib.zs_step_device(C.byref(bad), dev, None, None, None) == E
     alias, keep3 = _fused_args(zs, master_out=FAKE + 0x1000000)
     assert lib.zs_step_device(C.byref(alias), dev, None, None, None) == zs.ZS_ERR_ALIAS
+
+
+def test_huge_sizes_are_refused_before_any_arithmetic(zs):
+    """Counts and offsets above 2^48 return ZS_ERR_UNSUPPORTED (byte extents
+    are 4 n and must not wrap around in the overlap checks)."""
+    lib = _raw(zs)
+    U = zs.ZS_ERR_UNSUPPORTED
+    huge = 1 << 62
+    arr = (C.c_void_p * 2)(FAKE, FAKE + 4096)
+    out = C.c_void_p(FAKE + 65536)
+    assert lib.zs_reduce_scatter_avg(arr, 0, 0, 2, 0, huge, out, 0, None, 1.0, None) == U
+    assert lib.zs_check_overflow(out, huge, 1.0, out, None) == U
+    hp = zs.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    assert lib.zs_adamw_step(out, out, out, out, huge, C.byref(hp), None, None) == U
+    assert lib.zs_cast_gather(out, out, 0, 0, huge, None, None) == U
+    assert lib.zs_cast_gather(out, out, 0, huge, 10, None, None) == U
+    a, keep = _fused_args(zs, n=huge)
+    assert lib.zs_step_fused(C.byref(a), None) == U
+    b, keep2 = _fused_args(zs, gather_offset=huge)
+    assert lib.zs_step_fused(C.byref(b), None) == U
+    reps = (C.c_void_p * 2)(FAKE, FAKE + 0x100000)
+    assert lib.zs_all_gather_step(reps, 2, huge, 0, 1, None) == U
+    x = (C.c_float * 1)()
+    h = (C.c_uint16 * 1)()
+    ovf = C.c_uint32(0)
+    assert lib.zs_cpu_step(x, x, x, x, huge, C.byref(hp), h, 0, 1, C.byref(ovf)) == U
+    assert lib.zs_cpu_update(x, x, x, x, huge, C.byref(hp), h, 0, 1) == U
