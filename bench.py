@@ -329,6 +329,13 @@ def main():
     host_res = run_workload(args.workload, args.steps, args.warmup, torch, wire,
                             device_commit=False)
     log(json.dumps(host_res))
+    # the host-side legs run before the large workloads, which churn
+    # hundreds of GB of device memory
+    offload = None
+    if not args.no_offload:
+        offload = run_offload(args.workload, max(10, args.steps // 2), 2, torch)
+        log(json.dumps(offload))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
     others = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         r = run_workload(name, max(3, args.steps // 2), 2, torch, wire)
@@ -337,11 +344,6 @@ def main():
                            ms_per_step=r["ms_per_step"], hbm_gbps=r["hbm_gbps"],
                            fused_kernel_ms=r["fused_kernel_ms"], fused_gbps=r["fused_gbps"],
                            roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS))
-    offload = None
-    if not args.no_offload:
-        offload = run_offload(args.workload, max(10, args.steps // 2), 2, torch)
-        log(json.dumps(offload))
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
 
     from sharded_mixed_precision_zs_amd import synth as s
     wl = s.WORKLOADS[args.workload]
