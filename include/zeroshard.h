@@ -342,7 +342,8 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
  * ev_start / ev_stop: NULL, or hipEvent_t handles recorded immediately
  * before and after the fused kernel. Calls that share a dev must be ordered
  * (one stream). Errors: as zs_step_fused (ZS_ERR_INVALID_ARG also for a
- * NULL or not 8-byte-aligned dev); argument errors return before anything
+ * NULL or not 8-byte-aligned dev, ZS_ERR_ALIAS also for a dev inside an
+ * output buffer); argument errors return before anything
  * is enqueued. ZS_ERR_HIP from the second launch leaves the fused pass
  * enqueued without its commit: *dev then still holds that step's flag, and
  * the caller must not swap the sets (rerunning the step is safe, since the

@@ -2,7 +2,8 @@
  * zeroshard.hip -- libzeroshard: the per-rank ZeRO-2 optimizer-shard step for
  * AMD Instinct MI355X (gfx950, CDNA4). Host side: argument validation,
  * per-step scalars, vector-width choice, launches and the C ABI declared and
- * documented in include/zeroshard.h. The device code is in zs_kernels.h.
+ * documented in include/zeroshard.h. The device code is in zs_kernels.h (hot
+ * path) and zs_aux_kernels.h (commit, all-gather).
  */
 #include <hip/hip_runtime.h>
 
@@ -341,11 +342,10 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
   return launch_result();
 }
 
-/* zs_step_fused with optional start/stop events recorded on the stream
- * immediately before and after the kernel launch. */
-/* zs_step_fused; with `dev`, the scale, bias corrections and flag of the
- * device-resident flow (a->hp.loss_scale, a->hp.step_t and
- * a->overflow_flag unused). */
+/* zs_step_fused, with optional start/stop events recorded on the stream
+ * immediately before and after the kernel launch; with `dev`, the scale,
+ * bias corrections and flag of the device-resident flow (a->hp.loss_scale,
+ * a->hp.step_t and a->overflow_flag unused). */
 static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_start,
                            hipEvent_t ev_stop, zs_device_scaler *dev) {
   if (!a) return fail(ZS_ERR_INVALID_ARG, "null args%s");
@@ -394,6 +394,8 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
         return fail(ZS_ERR_ALIAS, "zs_step_fused: two outputs overlap%s");
+    if (dev && overlaps(outs[i], out_bytes[i], dev, sizeof(zs_device_scaler)))
+      return fail(ZS_ERR_ALIAS, "zs_step_device: an output overlaps the device scaler%s");
   }
 
   p.world = a->world;

@@ -264,6 +264,9 @@ def test_device_step_rejects_bad_arguments(zs):
     assert lib.zs_step_device(C.byref(bad), dev, None, None, None) == E
     alias, keep3 = _fused_args(zs, master_out=FAKE + 0x1000000)
     assert lib.zs_step_device(C.byref(alias), dev, None, None, None) == zs.ZS_ERR_ALIAS
+    good, keep4 = _fused_args(zs)
+    inside = C.c_void_p(good.m_out + 64)          # the scaler inside an output
+    assert lib.zs_step_device(C.byref(good), inside, None, None, None) == zs.ZS_ERR_ALIAS
 
 
 def test_huge_sizes_are_refused_before_any_arithmetic(zs):
