@@ -188,9 +188,11 @@ def test_1p3b_schedule_device_commit(env):
     assert st.loss_scale == 2.0 ** 14 and st.t == 8 and int(st.scaler.skipped) == 2
 
 
-def test_checkpoint_resume_is_bit_identical(env, tmp_path):
+@pytest.mark.parametrize("device_commit", [False, True])
+def test_checkpoint_resume_is_bit_identical(env, tmp_path, device_commit):
     """k steps, save, reload into a fresh shard, continue: identical bits to
-    an uninterrupted run (dynamic scaler and skipped steps included)."""
+    an uninterrupted run (dynamic scaler and skipped steps included), with
+    the commit decided on the host or on the device."""
     zs, synth, shard = env
     import dataclasses
     wl = dataclasses.replace(synth.WORKLOADS["1p3b-w4-acc4-fp16"], phi=4 * 300_007,
@@ -200,7 +202,8 @@ def test_checkpoint_resume_is_bit_identical(env, tmp_path):
 
     def fresh():
         st = shard.ShardState(n, W, 0, 0, n, wl.param_dtype, wl.grad_dtype, opt, wl.loss_scale,
-                              dynamic=True, growth_interval=2, accumulate=True)
+                              dynamic=True, growth_interval=2, accumulate=True,
+                              device_commit=device_commit)
         synth.dev_state(wl, 0, st.master, st.m, st.v)
         return st
 
@@ -214,10 +217,13 @@ def test_checkpoint_resume_is_bit_identical(env, tmp_path):
                     synth.dev_grad(wl, k, step, j, 0, g[k], scale=st.loss_scale)
                 if j < A - 1:
                     st.reduce_micro(g, first=(j == 0))
+                elif device_commit:
+                    st.step_device(g, acc_in=st.acc)
+                    st.sync_scaler()   # the next step's gradients use the scale
                 else:
                     st.step(g, acc_in=st.acc)
 
-    announce("checkpoint/resume")
+    announce(f"checkpoint/resume, device_commit={device_commit}")
     ref = fresh()
     run(ref, range(1, 8))
     a = fresh()
