@@ -485,7 +485,7 @@ def test_all_gather_matches_the_oracle(zs, world, phi, sigma):
             assert_bits_equal(got, oracle_after(step), f"after step {step}")
 
 
-@pytest.mark.parametrize("W,phi", [(4, 4 * 50_003 + 3), (4, 9), (5, 13), (7, 6995)])
+@pytest.mark.parametrize("W,phi", [(4, 4 * 50_003 + 3), (4, 9), (5, 13), (7, 6995), (64, 64 * 1009 - 17)])
 def test_sharded_step_over_all_ranks_then_all_gather(zs, W, phi):
     """A whole ZeRO-2 step for W ranks on one GPU: every rank's fused step
     on its own partition (gradients reduced in that rank's ring order), then
