@@ -191,6 +191,7 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
         hip.destroy(s)
         hip.destroy(e)
     kern_avg = sum(kern_ms) / len(kern_ms)
+    kern_med = sorted(kern_ms)[len(kern_ms) // 2]
     ms_per_step = elapsed * 1e3 / steps
     res = dict(workload=name, commit="device" if device_commit else "host", n=n, world=W,
                accum=A, replicas=R,
@@ -198,7 +199,8 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
                step_bytes=step_bytes, hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9,
                fused_kernel_ms=kern_avg, fused_bytes=fused_bytes,
                fused_gbps=fused_bytes / (kern_avg * 1e-3) / 1e9, committed=committed,
-               kernel_ms_min=min(kern_ms), kernel_ms_max=max(kern_ms))
+               kernel_ms_min=min(kern_ms), kernel_ms_max=max(kern_ms),
+               kernel_ms_median=kern_med, kernel_samples=len(kern_ms))
     del reps
     torch.cuda.empty_cache()
     return res
@@ -297,7 +299,7 @@ def cpu_baseline(name, target_s=25.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--also", default=DEFAULT_ALSO,
@@ -375,6 +377,8 @@ def main():
                      "frac": main_res["fused_gbps"] / PEAK_HBM_GBPS,
                      "traffic": traffic,
                      "kernel": "zs::fused_kernel", "kernel_ms": main_res["fused_kernel_ms"],
+                     "kernel_ms_median": main_res["kernel_ms_median"],
+                     "kernel_samples": main_res["kernel_samples"],
                      "algorithmic_bytes_per_launch": main_res["fused_bytes"]},
         "cpu_baseline": cpu,
         "other_workloads": others,
