@@ -28,6 +28,7 @@
 #include <vector>
 
 #include "zeroshard.h"
+#include "zs_host_powers.h"
 
 namespace {
 
@@ -235,11 +236,8 @@ int prepare(const float *master, const float *m, const float *v, const float *gr
   if (!(hp->loss_scale > 0.0f) || !isfinite(hp->loss_scale) || hp->step_t == 0)
     return ZS_ERR_INVALID_ARG;
   double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
-  double b1t = 1.0, b2t = 1.0;
-  for (uint32_t t = 0; t < hp->step_t; ++t) {
-    b1t *= b1;
-    b2t *= b2;
-  }
+  double b1t, b2t;
+  zs_host::beta_powers(hp->beta1, hp->beta2, hp->step_t, &b1t, &b2t);
   k->alpha = (float)(lr / (1.0 - b1t));
   k->bc2 = (float)sqrt(1.0 - b2t);
   k->delta = (float)(1.0 - lr * wd);

@@ -16,6 +16,7 @@
 #include "zeroshard.h"
 
 #include "zs_aux_kernels.h"
+#include "zs_host_powers.h"
 
 
 namespace {
@@ -77,15 +78,12 @@ bool make_scales(uint32_t world, float loss_scale, Scales *k) {
 }
 
 /* Per-step scalars in double, rounded once to fp32. beta^t is formed by t
- * repeated multiplications. */
+ * repeated multiplications (continued from the previous call when t grows). */
 bool make_adam(const zs_adamw_hparams *hp, AdamK *k) {
   if (hp->step_t == 0) return false;
   double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
-  double b1t = 1.0, b2t = 1.0;
-  for (uint32_t t = 0; t < hp->step_t; ++t) {
-    b1t *= b1;
-    b2t *= b2;
-  }
+  double b1t, b2t;
+  zs_host::beta_powers(hp->beta1, hp->beta2, hp->step_t, &b1t, &b2t);
   k->alpha = (float)(lr / (1.0 - b1t));
   k->b2 = (float)sqrt(1.0 - b2t);
   k->delta = (float)(1.0 - lr * wd);
@@ -488,11 +486,8 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
   d.step_t = s->step_t;
   d.skipped = s->skipped;
   /* beta^(t+1) by t+1 repeated multiplications, as make_adam forms it */
-  double b1 = beta1, b2 = beta2, b1t = 1.0, b2t = 1.0;
-  for (uint64_t i = 0; i <= s->step_t; ++i) {
-    b1t *= b1;
-    b2t *= b2;
-  }
+  double b1t, b2t;
+  zs_host::beta_powers(beta1, beta2, s->step_t + 1, &b1t, &b2t);
   d.beta1_t = b1t;
   d.beta2_t = b2t;
   *out = d;

@@ -136,3 +136,22 @@ def test_cpu_update_equals_cpu_step(zs, dtype, n, threads):
     assert np.array_equal(pgot, pref)
     with pytest.raises(zs.ZsError):
         zs.zs_cpu_update(*got, a, zs.hparams(**HP, loss_scale=0.0, step_t=1), pgot, code)
+
+
+def test_bias_correction_powers_continue_exactly(zs):
+    """The host forms beta^t by t repeated products and continues the
+    product from the previous call when t grows: t = 1 .. 3000 in order,
+    then a jump back to t = 7 and forward to 5000, each equal bit for bit
+    to the oracle's from-scratch products."""
+    rng = np.random.default_rng(9)
+    n = 64
+    master, m, v, a = _inputs(rng, n, 1.0)
+    for t in list(range(1, 3001)) + [7, 5000]:
+        got = [x.copy() for x in (master, m, v)]
+        p = np.empty(n, np.uint16)
+        zs.zs_cpu_update(*got, a, zs.hparams(**HP, loss_scale=1.0, step_t=t), p, zs.ZS_BF16, 1)
+        want = [x.copy() for x in (master, m, v)]
+        oracle.adamw(*want, a, 1.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"],
+                     HP["weight_decay"], t)
+        for x, y in zip(got, want):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), t
