@@ -252,3 +252,38 @@ def test_skip_restore_on_misaligned_slices(env, off, n):
     gb = down16(gather)
     assert np.all(gb[:off] == 0x1234) and np.all(gb[off + n:] == 0x1234)
     assert np.array_equal(gb[off:off + n], oracle.float_to_half(state[0], "fp16"))
+
+
+def test_long_run_matches_the_oracle(env):
+    """2000 device-commit steps with fresh gradients every step, a dynamic
+    scale growing every 50 clean steps and injected inf/NaN at steps 100,
+    777 and 1500: the whole state equals the oracle's run bit for bit at
+    several points and at the end, and the scaler follows the oracle's."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=4 * 65_537, world=4, steps=2000,
+                             inject_steps=(100, 777, 1500), inject_rate=1e-3, loss_scale=1024.0,
+                             name="long")
+    n = wl.n
+    st, g = _make(env, wl, True, dynamic=True, growth_interval=50)
+    master, m, v = synth.host_state(wl, 0, n)
+    hs = oracle.Scaler(1024.0, 50)
+    hp = dict(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay)
+    announce("long run: 2000 device-commit steps")
+    for step in range(1, wl.steps + 1):
+        scale = hs.scale
+        for k in range(wl.world):
+            synth.dev_grad(wl, k, step, 0, 0, g[k], scale=scale)
+        st.step_device(g)
+        parts = [synth.host_grad(wl, k, step, 0, 0, n, scale=scale) for k in range(wl.world)]
+        f, mo, mmo, vo, po = oracle.shard_step(parts, 0, wl.grad_dtype, wl.param_dtype, master, m,
+                                               v, loss_scale=scale, step_t=hs.t + 1, threads=8,
+                                               **hp)
+        hs.update(f)
+        if f == 0:
+            master, m, v = mo, mmo, vo
+        d = st.sync_scaler()
+        assert (d.last_flag, d.scale, d.step_t, d.skipped) == (f, hs.scale, hs.t, hs.s.skipped), step
+        if step in (1, 101, 778, 1000, 1501, wl.steps):
+            for got, want, name in ((st.master, master, "master"), (st.m, m, "m"), (st.v, v, "v")):
+                assert_bits_equal(down32(got), want, f"step {step}: {name}")
+    assert hs.s.skipped == 3 and hs.t == 1997
