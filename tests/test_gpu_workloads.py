@@ -152,22 +152,25 @@ def test_gpt2s_w8_full(env):
     run_workload(env, "gpt2s-w8")
 
 
-def test_7p5b_shard_w64_windows(env):
+@pytest.mark.parametrize("device_commit", [False, True])
+def test_7p5b_shard_w64_windows(env, device_commit):
     zs, synth, shard = env
     wl = synth.WORKLOADS["7p5b-shard-w64"]
-    run_workload(env, wl.name, windows=_windows(wl.n, 8, 2))
+    run_workload(env, wl.name, windows=_windows(wl.n, 8, 2), device_commit=device_commit)
 
 
-def test_7b_full_w1_windows(env):
+@pytest.mark.parametrize("device_commit", [False, True])
+def test_7b_full_w1_windows(env, device_commit):
     zs, synth, shard = env
     wl = synth.WORKLOADS["7b-full-w1"]
-    run_workload(env, wl.name, windows=_windows(wl.n, 8, 3))
+    run_workload(env, wl.name, windows=_windows(wl.n, 8, 3), device_commit=device_commit)
 
 
-def test_1p3b_w4_acc4_fp16_windows(env):
+@pytest.mark.parametrize("device_commit", [False, True])
+def test_1p3b_w4_acc4_fp16_windows(env, device_commit):
     zs, synth, shard = env
     wl = synth.WORKLOADS["1p3b-w4-acc4-fp16"]
-    st = run_workload(env, wl.name, windows=_windows(wl.n, 6, 4))
+    st = run_workload(env, wl.name, windows=_windows(wl.n, 6, 4), device_commit=device_commit)
     # two injected steps skipped: 2^16 -> 2^15 -> 2^14, eight steps committed
     assert st.loss_scale == 2.0 ** 14 and st.t == 8
 
