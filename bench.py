@@ -296,6 +296,32 @@ def cpu_baseline(name, target_s=25.0):
                        f"{dt:.1f} s")
 
 
+def world_sweep(worlds, n, steps, warmup, torch):
+    """The fused step at one shard size for several worker counts W: the
+    read/write mix goes from 14:14 bytes per parameter (W = 1) to
+    (2W + 12):14. Each W gets its own n (n + 4096 W), so a kernel trace of
+    the sweep can be split by grid size. Returns one record per W."""
+    import dataclasses
+
+    from sharded_mixed_precision_zs_amd import synth
+
+    out = []
+    base = synth.WORKLOADS[DEFAULT_WORKLOAD]
+    for w in worlds:
+        nw = n + 4096 * w
+        name = f"sweep-w{w}"
+        synth.WORKLOADS[name] = dataclasses.replace(base, name=name, world=w, phi=w * nw,
+                                                    description=f"world sweep, W={w}")
+        r = run_workload(name, steps, warmup, torch)
+        log(json.dumps(r))
+        out.append(dict(world=w, n=nw, fused_kernel_ms=r["fused_kernel_ms"],
+                        fused_gbps=r["fused_gbps"], roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS,
+                        bytes_per_param_read=2 * w + 12, bytes_per_param_written=14,
+                        ms_per_step=r["ms_per_step"]))
+        del synth.WORKLOADS[name]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +336,11 @@ def main():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host update) leg")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--sweep-world", default="",
+                    help="comma-separated W values: time the fused step at one shard size for "
+                         "each and print that table as the JSON line instead")
+    ap.add_argument("--sweep-n", type=int, default=1 << 25,
+                    help="shard size of the --sweep-world runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: the shard step takes one "
@@ -322,6 +353,12 @@ def main():
     from sharded_mixed_precision_zs_amd import synth  # noqa: F401  (fails loudly if unbuilt)
     from sharded_mixed_precision_zs_amd import zeroshard  # noqa: F401
 
+    if args.sweep_world:
+        worlds = [int(x) for x in args.sweep_world.split(",") if x]
+        sweep = world_sweep(worlds, args.sweep_n, args.steps, args.warmup, torch)
+        print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
+                          "peak": PEAK_HBM_GBPS, "sweep": sweep}))
+        return
     ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
     if ceiling:
         log(f"plain copy ceiling {ceiling:.0f} GB/s")
