@@ -11,6 +11,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "zeroshard.h"
@@ -93,6 +94,73 @@ bool make_adam(const zs_adamw_hparams *hp, AdamK *k) {
   k->beta2 = hp->beta2;
   k->eps = hp->eps;
   return true;
+}
+
+/* ------------------------------------------------------------------------
+ * Residency of the fused kernel. With writes mixed into the read stream,
+ * HBM delivered more on MI355X when fewer blocks per CU were in flight
+ * (fewer DRAM rows in contention): capping the fused kernel at 3 blocks
+ * (12 waves) per CU, against the register-limited 5 to 6, measured +2.7 to
+ * +4.6 % for W = 1, 4 and 8 (interleaved A/B runs on one GPU, shards of
+ * 33 M to 1 G parameters), while for W = 16 to 64 no cap was reliably better
+ * than none (-1.3 to +1.1 %), so larger W runs uncapped. The cap is dynamic
+ * LDS that the kernel never touches: LDS per CU / 3, less 1 KB.
+ * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..8 = that many blocks) overrides
+ * the choice, for measurements.
+ * ---------------------------------------------------------------------- */
+
+struct DeviceLds {
+  int lds_per_cu = 0;  /* bytes */
+};
+
+DeviceLds device_lds() {
+  static thread_local int cached_dev = -1;
+  static thread_local DeviceLds cached;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DeviceLds{};
+  if (dev != cached_dev) {
+    DeviceLds d;
+    if (hipDeviceGetAttribute(&d.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) != hipSuccess)
+      return DeviceLds{};
+    cached = d;
+    cached_dev = dev;
+  }
+  return cached;
+}
+
+int env_blocks_per_cu() {
+  static const int v = [] {
+    const char *s = getenv("ZS_FUSED_BLOCKS_PER_CU");
+    if (!s || !*s) return -1;
+    int x = atoi(s);
+    return x < 0 || x > 8 ? -1 : x;
+  }();
+  return v;
+}
+
+/* Dynamic LDS bytes that cap the fused kernel's residency (0: no cap). */
+size_t fused_lds_bytes(uint32_t world) {
+  int cap = env_blocks_per_cu();
+  if (cap < 0) cap = world <= 8 ? 3 : 0;
+  if (cap == 0) return 0;
+  const DeviceLds d = device_lds();
+  if (d.lds_per_cu <= 0) return 0;
+  const int bytes = (d.lds_per_cu / cap - 1024) / 256 * 256;
+  return bytes > 0 ? (size_t)bytes : 0;
+}
+
+/* Launch of one fused-kernel instance with `lds` bytes of (unused) dynamic
+ * LDS; above the default 64 KB limit the instance's limit is raised once. */
+template <int V, int U, bool L, bool A, int G, int P, int W>
+void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedArgs &p) {
+  if (lds > 65536) {
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)device_lds().lds_per_cu);
+    (void)raised;  /* a refusal surfaces as the launch's error */
+  }
+  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W>), grid, block, lds, s, p);
 }
 
 /* Widest vector width every operand's alignment allows: 16-bit operands
@@ -419,8 +487,9 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
   const int mode = (a->world > 1 ? 1 : 0) | (a->acc_in ? 2 : 0);
+  const size_t lds = fused_lds_bytes(a->world);
 #define ZS_FUSED_KW(V, L, A, G, P, W) \
-  hipLaunchKernelGGL((fused_kernel<V, kTileVecs, L, A, G, P, W>), grid, block, 0, s, p)
+  launch_fused<V, kTileVecs, L, A, G, P, W>(grid, block, lds, s, p)
 #define ZS_FUSED_K(V, L, A, G, P)                                             \
   do {                                                                        \
     if (p.wire == ZS_WIRE_BF16) ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_BF16);     \
