@@ -97,16 +97,21 @@ bool make_adam(const zs_adamw_hparams *hp, AdamK *k) {
 }
 
 /* ------------------------------------------------------------------------
- * Residency of the fused kernel. With writes mixed into the read stream,
- * HBM delivered more on MI355X when fewer blocks per CU were in flight
- * (fewer DRAM rows in contention): capping the fused kernel at 3 blocks
- * (12 waves) per CU, against the register-limited 5 to 6, measured +2.7 to
- * +4.6 % for W = 1, 4 and 8 (interleaved A/B runs on one GPU, shards of
- * 33 M to 1 G parameters), while for W = 16 to 64 no cap was reliably better
- * than none (-1.3 to +1.1 %), so larger W runs uncapped. The cap is dynamic
- * LDS that the kernel never touches: LDS per CU / 3, less 1 KB.
- * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..8 = that many blocks) overrides
- * the choice, for measurements.
+ * Residency and tile of the fused kernel. With writes mixed into the read
+ * stream, HBM delivered more on MI355X when fewer blocks per CU were in
+ * flight (fewer DRAM rows in contention). Interleaved A/B runs on one GPU,
+ * shards of 15 M to 1 G parameters:
+ *   - W = 2 to 8: 3 blocks (12 waves) per CU, against the register-limited
+ *     5 to 6, measured +2.7 to +4.6 %;
+ *   - W = 1: one vector per thread (2048-element tiles) and 2 blocks per CU
+ *     beat that by a further 2.7 to 6 % in every variant tried (bf16 and
+ *     fp16, with and without an accumulated gradient); with W = 2 to 16
+ *     the same shape lost up to 18 %;
+ *   - W = 16 to 64: no cap was reliably better than none (-1.3 to +2 %),
+ *     so larger W runs uncapped.
+ * The cap is dynamic LDS that the kernel never touches: LDS per CU / cap,
+ * less 1 KB. ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..8 = that many blocks)
+ * overrides the cap, for measurements.
  * ---------------------------------------------------------------------- */
 
 struct DeviceLds {
@@ -139,10 +144,13 @@ int env_blocks_per_cu() {
   return v;
 }
 
+/* Vectors per thread of the fused kernel: kTileVecs, but one when W = 1. */
+constexpr int fused_tile_vecs(bool multi) { return multi ? kTileVecs : 1; }
+
 /* Dynamic LDS bytes that cap the fused kernel's residency (0: no cap). */
 size_t fused_lds_bytes(uint32_t world) {
   int cap = env_blocks_per_cu();
-  if (cap < 0) cap = world <= 8 ? 3 : 0;
+  if (cap < 0) cap = world == 1 ? 2 : world <= 8 ? 3 : 0;
   if (cap == 0) return 0;
   const DeviceLds d = device_lds();
   if (d.lds_per_cu <= 0) return 0;
@@ -482,14 +490,14 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   const void *f32[] = {a->master_in, a->m_in, a->v_in, a->master_out, a->m_out,
                        a->v_out, a->acc_in ? a->acc_in : a->master_in};
   int vec = pick_vec(p16, (int)a->world + 1, f32, 7);
-  const int per_thread = vec * kTileVecs;
+  const int per_thread = vec * fused_tile_vecs(a->world > 1);
   if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
   const int mode = (a->world > 1 ? 1 : 0) | (a->acc_in ? 2 : 0);
   const size_t lds = fused_lds_bytes(a->world);
 #define ZS_FUSED_KW(V, L, A, G, P, W) \
-  launch_fused<V, kTileVecs, L, A, G, P, W>(grid, block, lds, s, p)
+  launch_fused<V, fused_tile_vecs(L), L, A, G, P, W>(grid, block, lds, s, p)
 #define ZS_FUSED_K(V, L, A, G, P)                                             \
   do {                                                                        \
     if (p.wire == ZS_WIRE_BF16) ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_BF16);     \
