@@ -82,7 +82,10 @@ typedef enum {
 /* AdamW hyper-parameters of one step. lr, betas, eps and weight_decay are
  * the usual AdamW settings; loss_scale is the factor the gradients carry
  * (the update divides it out); step_t is the 1-based index of the step being
- * attempted, i.e. committed steps + 1 (skipped steps do not advance it). */
+ * attempted, i.e. committed steps + 1 (skipped steps do not advance it).
+ * Every entry point that takes them returns ZS_ERR_INVALID_ARG, before any
+ * launch, unless 0 <= beta1, beta2 < 1 and lr, eps and weight_decay are
+ * finite and >= 0 (outside these ranges the update is inf or NaN). */
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
   float loss_scale;
@@ -224,7 +227,8 @@ int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint
  *   threads: worker threads (<= 0: the machine's hardware threads, at most
  *            64); every range runs with round-to-nearest, subnormals kept.
  * Blocks until done. Errors: ZS_ERR_INVALID_ARG for null pointers, a bad
- * param dtype, a non-finite or non-positive loss scale, step_t == 0. */
+ * param dtype, a non-finite or non-positive loss scale, step_t == 0 or
+ * hyper-parameters outside their ranges (zs_adamw_hparams). */
 int zs_cpu_step(float *master, float *m, float *v, const float *grad_part, uint64_t n,
                 const zs_adamw_hparams *hp, void *params16, int param_dtype, int threads,
                 uint32_t *overflow);
@@ -318,8 +322,8 @@ typedef struct {
 
 /* Host image of a device scaler that continues from the host scaler `s`
  * (beta powers formed by step_t + 1 repeated binary64 multiplications).
- * Errors: ZS_ERR_INVALID_ARG for NULL pointers or a scale that is not
- * finite and > 0. */
+ * Errors: ZS_ERR_INVALID_ARG for NULL pointers, a scale that is not
+ * finite and > 0, or a beta outside [0, 1). */
 int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
                           zs_device_scaler *out);
 

@@ -28,6 +28,7 @@
 #include <vector>
 
 #include "zeroshard.h"
+#include "zs_hparams.h"
 #include "zs_host_powers.h"
 
 namespace {
@@ -235,6 +236,7 @@ int prepare(const float *master, const float *m, const float *v, const float *gr
   if (param_dtype != ZS_BF16 && param_dtype != ZS_FP16) return ZS_ERR_INVALID_ARG;
   if (!(hp->loss_scale > 0.0f) || !isfinite(hp->loss_scale) || hp->step_t == 0)
     return ZS_ERR_INVALID_ARG;
+  if (zs_host::hparams_problem(hp)) return ZS_ERR_INVALID_ARG;
   double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
   double b1t, b2t;
   zs_host::beta_powers(hp->beta1, hp->beta2, hp->step_t, &b1t, &b2t);

@@ -17,6 +17,7 @@
 #include "zeroshard.h"
 
 #include "zs_aux_kernels.h"
+#include "zs_hparams.h"
 #include "zs_host_powers.h"
 
 
@@ -354,6 +355,7 @@ int zs_adamw_step(float *master, float *m, float *v, const float *grad_part,
   AdamArgs p;
   if (!make_scales(1, hp->loss_scale, &p.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
+  if (const char *bad = zs_host::hparams_problem(hp)) return fail(ZS_ERR_INVALID_ARG, "%s", bad);
   if (!make_adam(hp, &p.h)) return fail(ZS_ERR_INVALID_ARG, "step_t must be >= 1%s");
   if (n == 0) return ZS_OK;
   p.master = master;
@@ -443,6 +445,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   }
   if (!make_scales(a->world, hp.loss_scale, &p.k))
     return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
+  if (const char *bad = zs_host::hparams_problem(&hp)) return fail(ZS_ERR_INVALID_ARG, "%s", bad);
   if (!make_adam(&hp, &p.h)) return fail(ZS_ERR_INVALID_ARG, "step_t must be >= 1%s");
   p.dev = dev;
   p.lr = (double)a->hp.lr;
@@ -554,6 +557,8 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
   if (!s || !out) return fail(ZS_ERR_INVALID_ARG, "null scaler or output%s");
   if (!(s->scale > 0.0f) || !isfinite(s->scale))
     return fail(ZS_ERR_INVALID_ARG, "scale must be finite and > 0%s");
+  if (!zs_host::beta_ok(beta1) || !zs_host::beta_ok(beta2))
+    return fail(ZS_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)%s");
   zs_device_scaler d;
   memset(&d, 0, sizeof d);
   d.scale = s->scale;

@@ -294,3 +294,69 @@ def test_huge_sizes_are_refused_before_any_arithmetic(zs):
     ovf = C.c_uint32(0)
     assert lib.zs_cpu_step(x, x, x, x, huge, C.byref(hp), h, 0, 1, C.byref(ovf)) == U
     assert lib.zs_cpu_update(x, x, x, x, huge, C.byref(hp), h, 0, 1) == U
+
+
+BAD_HPARAMS = [
+    dict(beta1=1.0), dict(beta1=-0.1), dict(beta2=1.0), dict(beta2=float("nan")),
+    dict(lr=float("nan")), dict(lr=-1e-3), dict(lr=float("inf")),
+    dict(eps=-1e-8), dict(eps=float("nan")),
+    dict(weight_decay=-0.01), dict(weight_decay=float("inf")),
+]
+
+
+def _hp(zs, **over):
+    kw = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, loss_scale=1.0,
+              step_t=1)
+    kw.update(over)
+    return zs.hparams(**kw)
+
+
+@pytest.mark.parametrize("bad", BAD_HPARAMS, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_hyperparameters_out_of_range_are_refused(zs, bad):
+    """A beta outside [0, 1) or a negative or non-finite lr, eps or weight
+    decay would make every parameter inf or NaN with no overflow reported:
+    each entry point that takes them refuses before any launch."""
+    lib = _raw(zs)
+    E = zs.ZS_ERR_INVALID_ARG
+    hp = _hp(zs, **bad)
+    p = C.c_void_p(FAKE)
+    assert lib.zs_adamw_step(p, p, p, p, 10, C.byref(hp), None, None) == E
+    a, keep = _fused_args(zs)
+    a.hp = hp
+    assert lib.zs_step_fused(C.byref(a), None) == E
+    assert lib.zs_step_device(C.byref(a), C.c_void_p(FAKE + 0x7000000), None, None, None) == E
+    sc = zs.zs_loss_scaler(scale=1024.0, clean_steps=0, growth_interval=4, dynamic=1,
+                           step_t=0, skipped=0)
+    hf, ok = C.c_uint32(0), C.c_int(7)
+    assert lib.zs_step_commit(C.byref(a), C.byref(sc), C.byref(hf), None, None, None,
+                              C.byref(ok)) == E
+    assert (sc.scale, sc.step_t, sc.skipped) == (1024.0, 0, 0)
+    x = (C.c_float * 4)(0.5, 0.0, 0.0, 0.25)
+    h = (C.c_uint16 * 4)()
+    ovf = C.c_uint32(9)
+    assert lib.zs_cpu_step(x, x, x, x, 4, C.byref(hp), h, 0, 1, C.byref(ovf)) == E
+    assert lib.zs_cpu_update(x, x, x, x, 4, C.byref(hp), h, 0, 1) == E
+    assert list(x) == [0.5, 0.0, 0.0, 0.25] and ovf.value == 9    # nothing written
+    if "beta1" in bad or "beta2" in bad:
+        host = zs.zs_loss_scaler(scale=1.0, clean_steps=0, growth_interval=0, dynamic=0,
+                                 step_t=0, skipped=0)
+        with pytest.raises(zs.ZsError):
+            zs.zs_device_scaler_make(host, hp.beta1, hp.beta2)
+
+
+def test_hyperparameter_range_edges_are_accepted(zs):
+    """beta = 0 and lr = eps = weight_decay = 0 are valid settings."""
+    lib = _raw(zs)
+    hp = _hp(zs, lr=0.0, beta1=0.0, beta2=0.0, eps=0.0, weight_decay=0.0)
+    p = C.c_void_p(FAKE)
+    assert lib.zs_adamw_step(p, p, p, p, 0, C.byref(hp), None, None) == zs.ZS_OK
+    a, keep = _fused_args(zs, n=0)
+    a.hp = hp
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_OK
+    x = (C.c_float * 4)(0.5, 0.0, 0.0, 0.25)
+    h = (C.c_uint16 * 4)()
+    ovf = C.c_uint32(9)
+    assert lib.zs_cpu_step(x, x, x, x, 4, C.byref(hp), h, 0, 1, C.byref(ovf)) == zs.ZS_OK
+    assert ovf.value == 0
+    zs.zs_device_scaler_make(zs.zs_loss_scaler(scale=1.0, clean_steps=0, growth_interval=0,
+                                               dynamic=0, step_t=0, skipped=0), 0.0, 0.0)
