@@ -71,6 +71,7 @@ class ShardState:
         # are queued without waiting (step_device); self.scaler is refreshed
         # by sync_scaler()
         self.device_commit = device_commit
+        self._dev_betas = None
         self.dev = self._upload_scaler() if device_commit else None
         self.device = device
 
@@ -123,12 +124,16 @@ class ShardState:
         for k, v in sd["scaler"].items():
             setattr(self.scaler, k, v)
         if self.device_commit:
-            self.dev.copy_(self._upload_scaler())
+            zs.device_scaler_write(self.dev, self._scaler_image())
 
     # -- device-resident scaler ---------------------------------------------
+    def _scaler_image(self):
+        """Device-scaler image continuing self.scaler with the current betas."""
+        self._dev_betas = (self.opt.beta1, self.opt.beta2)
+        return zs.zs_device_scaler_make(self.scaler, self.opt.beta1, self.opt.beta2)
+
     def _upload_scaler(self):
-        img = zs.zs_device_scaler_make(self.scaler, self.opt.beta1, self.opt.beta2)
-        return zs.device_scaler_upload(img, self.sets[0][0].device)
+        return zs.device_scaler_upload(self._scaler_image(), self.sets[0][0].device)
 
     def sync_scaler(self):
         """Wait for the queued steps and copy the device scaler into
@@ -143,6 +148,12 @@ class ShardState:
         o = self.opt
         return zs.hparams(o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.loss_scale,
                           self.t + 1)
+
+    def _refresh_hparams(self, args):
+        """Write the step's settings into prepared arguments: self.opt may
+        change between steps (a learning-rate schedule), the scale and t
+        change with every commit or skip."""
+        args.args.hp = self.hparams()
 
     # -- flag ring ----------------------------------------------------------
     def _next_flag_addr(self):
@@ -193,10 +204,8 @@ class ShardState:
         slot it ORs into (finish() reads it back)."""
         flag = self._next_flag()
         args = self._args(worker_grads, acc_in)
-        a = args.args
-        a.overflow_flag = flag.data_ptr()
-        a.hp.loss_scale = self.loss_scale
-        a.hp.step_t = self.t + 1
+        self._refresh_hparams(args)
+        args.args.overflow_flag = flag.data_ptr()
         zs.zs_step_fused(args, stream)
         return flag
 
@@ -213,10 +222,13 @@ class ShardState:
 
     def _step_args(self, worker_grads, acc_in):
         if worker_grads is not None:
-            return self._args(worker_grads, acc_in)
-        if self._bound is None:
+            args = self._args(worker_grads, acc_in)
+        elif self._bound is None:
             raise RuntimeError("no gradients given and none bound: call bind() first")
-        return self._bound[self.cur]
+        else:
+            args = self._bound[self.cur]
+        self._refresh_hparams(args)
+        return args
 
     def bind(self, worker_grads: Sequence[torch.Tensor], acc_in: Optional[torch.Tensor] = None):
         """Prepare both directions' arguments once for gradients that stay at
@@ -246,9 +258,15 @@ class ShardState:
         """One optimizer step through zs_step_device: queued, never waits. The
         commit or skip happens on the device, which leaves the state after
         the step in the output set either way, so the sets swap every call;
-        sync_scaler() reads the outcome."""
+        sync_scaler() reads the outcome. lr, eps and weight decay are read
+        from self.opt at every call; the beta powers live on the device, so
+        a change of betas waits for the queued steps once and re-forms
+        beta^(t+1) from the new values (what the host flow computes)."""
         if not self.device_commit:
             raise RuntimeError("ShardState was built without device_commit=True")
+        if (self.opt.beta1, self.opt.beta2) != self._dev_betas:
+            self.sync_scaler()
+            zs.device_scaler_write(self.dev, self._scaler_image())
         args = self._step_args(worker_grads, acc_in)
         zs.zs_step_device(args, self.dev, stream, ev_start, ev_stop)
         self.cur = 1 - self.cur

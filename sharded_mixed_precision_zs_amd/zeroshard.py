@@ -304,9 +304,23 @@ def device_scaler_upload(image: zs_device_scaler, device="cuda"):
 
 
 def device_scaler_read(dev_buf) -> zs_device_scaler:
-    """Host copy of a device scaler buffer (synchronizes with the device)."""
+    """Host copy of a device scaler buffer. Waits for all work on the
+    buffer's device first: steps may be queued on any stream."""
+    torch = _torch()
+    torch.cuda.synchronize(dev_buf.device)
     raw = dev_buf[:DEVICE_SCALER_BYTES].cpu().numpy().tobytes()
     return zs_device_scaler.from_buffer_copy(raw)
+
+
+def device_scaler_write(dev_buf, image: zs_device_scaler):
+    """Overwrite a device scaler buffer with `image`. Waits for all work on
+    the device before and after the copy, so no queued step on any stream
+    sees a partly written scaler."""
+    torch = _torch()
+    raw = bytes(memoryview(image).cast("B"))
+    torch.cuda.synchronize(dev_buf.device)
+    dev_buf[:DEVICE_SCALER_BYTES].copy_(torch.frombuffer(bytearray(raw), dtype=torch.uint8))
+    torch.cuda.synchronize(dev_buf.device)
 
 
 def _dev_scaler_ptr(dev):

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import F32, announce, assert_bits_equal, down16, down32
+from gpu_util import F32, announce, assert_bits_equal, assert_rel, assert_ulp16, down16, down32
 
 pytestmark = pytest.mark.gpu
 
@@ -287,3 +287,63 @@ def test_long_run_matches_the_oracle(env):
             for got, want, name in ((st.master, master, "master"), (st.m, m, "m"), (st.v, v, "v")):
                 assert_bits_equal(down32(got), want, f"step {step}: {name}")
     assert hs.s.skipped == 3 and hs.t == 1997
+
+
+def test_hyperparameters_follow_opt_every_step(env):
+    """A learning-rate schedule (with eps and weight decay changing too) and
+    a change of betas at step 3 reach every step path of ShardState: step()
+    (host commit), step_device() (device commit, where the beta change
+    re-forms beta^t on the device) and launch()/finish(). Every step of every
+    path matches the oracle run on that path's previous state with the
+    step's settings, and the three paths agree bit for bit."""
+    zs, synth, shard = env
+    rng = np.random.default_rng(23)
+    world, n, scale = 3, 5003, 1024.0
+    sched = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (5e-4, 0.9, 0.999, 1e-8, 0.02),
+             (2e-4, 0.85, 0.99, 1e-7, 0.02), (1e-4, 0.85, 0.99, 0.0, 0.0)]
+    g16 = [[((rng.standard_normal(n) * 1e-3 * scale).astype(F32).view(np.uint32) >> 16)
+            .astype(np.uint16) for _ in range(world)] for _ in sched]
+    init = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    init[2] = np.abs(init[2])
+
+    def make(device_commit):
+        st = shard.ShardState(n, world, 0, 0, n, zs.ZS_BF16, zs.ZS_BF16, shard.AdamW(*sched[0]),
+                              scale, device_commit=device_commit)
+        for dst, x in zip((st.master, st.m, st.v), init):
+            dst.copy_(torch.from_numpy(x))
+        return st
+
+    paths = {"step": make(False), "step_device": make(True), "launch": make(False)}
+    grads = torch.empty((world, n), dtype=torch.bfloat16, device="cuda")
+    for i, (lr, b1, b2, eps, wd) in enumerate(sched):
+        announce(f"hyper-parameter schedule, step {i + 1}")
+        for k in range(world):
+            grads[k].copy_(torch.from_numpy(g16[i][k].view(np.int16)).view(torch.bfloat16))
+        gl = [grads[k] for k in range(world)]
+        outs = {}
+        for name, st in paths.items():
+            prev = [down32(x).copy() for x in (st.master, st.m, st.v)]
+            st.opt.lr, st.opt.beta1, st.opt.beta2 = lr, b1, b2
+            st.opt.eps, st.opt.weight_decay = eps, wd
+            if name == "step":
+                assert st.step(gl)
+            elif name == "step_device":
+                st.step_device(gl)
+                assert st.sync_scaler().last_flag == 0
+            else:
+                assert st.finish(st.launch(gl))
+            f, mo, mmo, vo, po = oracle.shard_step(g16[i], 0, "bf16", "bf16", *prev, lr=lr,
+                                                   beta1=b1, beta2=b2, eps=eps, weight_decay=wd,
+                                                   loss_scale=scale, step_t=i + 1)
+            assert f == 0
+            got = [down32(x) for x in (st.master, st.m, st.v)]
+            for g_, w_, what in zip(got, (mo, mmo, vo), ("master", "m", "v")):
+                assert_rel(g_, w_, 1e-6, f"{name} step {i + 1} {what}")
+            p = down16(st.params.view(torch.int16))
+            assert_ulp16(p, po, "bf16", 1, f"{name} step {i + 1} params")
+            outs[name] = got + [p]
+        for name in ("step_device", "launch"):
+            for a, b in zip(outs["step"], outs[name]):
+                assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), \
+                    f"{name} differs from step at step {i + 1}"
+    assert all(st.t == len(sched) for st in paths.values())
