@@ -146,9 +146,17 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
-def _check(fn, status):
+def _check(fn, status, detail=None):
     if status != ZS_OK:
-        raise ZsError(fn, status, zs_last_error())
+        raise ZsError(fn, status, detail if detail is not None else zs_last_error())
+
+
+# The host update (offload_cpu.cpp) reports status codes only.
+_CPU_DETAIL = {
+    ZS_ERR_INVALID_ARG: "a null pointer, a bad param dtype, a loss scale that is not finite "
+                        "and > 0, step_t == 0, or a hyper-parameter out of range",
+    ZS_ERR_UNSUPPORTED: "n exceeds 2^48 elements",
+}
 
 
 def hparams(lr, beta1, beta2, eps, weight_decay, loss_scale, step_t):
@@ -371,8 +379,8 @@ def zs_cpu_step(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param_d
     pm, p1, p2, pg, n, pp, dt = _host_args("zs_cpu_step", master, m, v, grad_part, params16,
                                            param_dtype)
     flag = C.c_uint32(0)
-    _check("zs_cpu_step", _lib.zs_cpu_step(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads,
-                                           C.byref(flag)))
+    rc = _lib.zs_cpu_step(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads, C.byref(flag))
+    _check("zs_cpu_step", rc, _CPU_DETAIL.get(rc, ""))
     return int(flag.value)
 
 
@@ -381,4 +389,5 @@ def zs_cpu_update(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param
     """zs_cpu_step without its check (the caller has checked the gradient)."""
     pm, p1, p2, pg, n, pp, dt = _host_args("zs_cpu_update", master, m, v, grad_part, params16,
                                            param_dtype)
-    _check("zs_cpu_update", _lib.zs_cpu_update(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads))
+    rc = _lib.zs_cpu_update(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads)
+    _check("zs_cpu_update", rc, _CPU_DETAIL.get(rc, ""))

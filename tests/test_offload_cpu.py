@@ -112,6 +112,11 @@ def test_cpu_step_rejects_bad_arguments(zs):
     with pytest.raises(zs.ZsError):
         zs.zs_cpu_step(x, x.copy(), x.copy(), x.copy(), zs.hparams(**HP, loss_scale=1.0, step_t=1),
                        p, 9)
+    # the message names what the host update checks, not an earlier call's error
+    bad = dict(HP, beta1=1.0)
+    with pytest.raises(zs.ZsError, match="hyper-parameter out of range"):
+        zs.zs_cpu_update(x, x.copy(), x.copy(), x.copy(), zs.hparams(**bad, loss_scale=1.0, step_t=1),
+                         p, zs.ZS_BF16)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
