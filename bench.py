@@ -252,6 +252,18 @@ def run_offload(name, steps, warmup, torch):
                 pcie_bytes_per_step=6 * n, hbm_state_bytes_saved=12 * n)
 
 
+def cpu_model():
+    """The host CPU's model string (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(name, target_s=25.0):
     """The CPU oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
@@ -264,7 +276,7 @@ def cpu_baseline(name, target_s=25.0):
     kw = dict(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
               weight_decay=wl.weight_decay, loss_scale=wl.loss_scale, step_t=1)
 
-    def timed(ns, reps):
+    def timed(ns, reps, threads=threads):
         # distinct inputs for up to the workload's step count, then cycled
         distinct = []
         for r in range(min(reps, wl.steps)):
@@ -290,10 +302,17 @@ def cpu_baseline(name, target_s=25.0):
     ns = int(min(wl.n, cap, max(probe, want)))
     reps = max(1, min(1000, int(want // ns)))
     dt = timed(ns, reps)
+    # one thread, on a smaller sample (about a third of the time budget)
+    dt1 = timed(probe, 1, threads=1)
+    reps1 = max(1, min(100, int(target_s / 3 / max(dt1, 1e-6))))
+    dt1 = timed(probe, reps1, threads=1)
     return dict(value=ns * reps / dt, unit="params/s", cores=threads, kind="oracle",
                 sample=f"{ns} params of the {name} rank-{wl.rank} partition (W={wl.world}, "
                        f"{wl.accum} micro-batch(es)) x {reps} step(s), {threads} threads, "
-                       f"{dt:.1f} s")
+                       f"{dt:.1f} s",
+                value_1_thread=probe * reps1 / dt1,
+                sample_1_thread=f"{probe} params x {reps1} step(s), 1 thread, {dt1:.1f} s",
+                cpu_model=cpu_model(), host_cpus=os.cpu_count())
 
 
 def world_sweep(worlds, n, steps, warmup, torch):
@@ -325,7 +344,7 @@ def world_sweep(worlds, n, steps, warmup, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=80)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--also", default=DEFAULT_ALSO,
@@ -409,6 +428,7 @@ def main():
         "hbm_gbps": main_res["hbm_gbps"],
         "hbm_pct_of_peak": 100.0 * main_res["hbm_gbps"] / PEAK_HBM_GBPS,
         "copy_ceiling_gbps": ceiling,
+        "hbm_pct_of_copy_ceiling": 100.0 * main_res["hbm_gbps"] / ceiling if ceiling else None,
         "roofline": {"bound": "hbm", "achieved": main_res["fused_gbps"],
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": main_res["fused_gbps"] / PEAK_HBM_GBPS,
