@@ -7,6 +7,7 @@
  */
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <chrono>
 #include <math.h>
 #include <stdint.h>
@@ -160,14 +161,22 @@ size_t fused_lds_bytes(uint32_t world) {
 }
 
 /* Launch of one fused-kernel instance with `lds` bytes of (unused) dynamic
- * LDS; above the default 64 KB limit the instance's limit is raised once. */
+ * LDS; above the default 64 KB limit the instance's limit is raised once
+ * per device (a bit per device id; ids past 63 raise it at every launch). */
 template <int V, int U, bool L, bool A, int G, int P, int W>
 void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedArgs &p) {
   if (lds > 65536) {
-    static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)device_lds().lds_per_cu);
-    (void)raised;  /* a refusal surfaces as the launch's error */
+    static std::atomic<uint64_t> raised{0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;
+    if (!bit || !(raised.load(std::memory_order_relaxed) & bit)) {
+      /* a refusal surfaces as the launch's error */
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)device_lds().lds_per_cu) == hipSuccess)
+        raised.fetch_or(bit, std::memory_order_relaxed);
+    }
   }
   hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W>), grid, block, lds, s, p);
 }
