@@ -341,6 +341,18 @@ def world_sweep(worlds, n, steps, warmup, torch):
     return out
 
 
+def side_leg(name, fn, torch):
+    """Run a leg reported beside the headline; a failure (for instance too
+    little free device memory for a 7B state) is recorded in the JSON line
+    as {"error": ...} instead of taking the headline down with it."""
+    try:
+        return fn()
+    except (RuntimeError, MemoryError, OSError, ValueError) as e:
+        log(f"{name} failed: {type(e).__name__}: {e}")
+        torch.cuda.empty_cache()
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,13 +403,19 @@ def main():
     # hundreds of GB of device memory
     offload = None
     if not args.no_offload:
-        offload = run_offload(args.workload, max(10, args.steps // 2), 2, torch)
+        offload = side_leg("offload", lambda: run_offload(args.workload, max(10, args.steps // 2),
+                                                          2, torch), torch)
         log(json.dumps(offload))
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
+    cpu = None if args.no_cpu_baseline else side_leg("cpu_baseline",
+                                                     lambda: cpu_baseline(args.workload), torch)
     others = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
-        r = run_workload(name, max(3, args.steps // 2), 2, torch, wire)
+        r = side_leg(name, lambda: run_workload(name, max(3, args.steps // 2), 2, torch, wire),
+                     torch)
         log(json.dumps(r))
+        if "error" in r:
+            others.append(dict(workload=name, error=r["error"]))
+            continue
         others.append(dict(workload=name, params_per_s=r["params_per_s"],
                            ms_per_step=r["ms_per_step"], hbm_gbps=r["hbm_gbps"],
                            fused_kernel_ms=r["fused_kernel_ms"], fused_gbps=r["fused_gbps"],
