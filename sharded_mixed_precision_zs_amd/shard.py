@@ -156,17 +156,24 @@ class ShardState:
         args.args.hp = self.hparams()
 
     # -- flag ring ----------------------------------------------------------
-    def _next_flag_addr(self):
-        """Device address of a fresh zeroed uint32 flag slot."""
+    def _next_flag_addr(self, stream=None):
+        """Device address of a fresh zeroed uint32 flag slot. The ring is
+        re-zeroed on the stream of the step that will use it (the earlier
+        slots' steps ran on that stream or were waited for)."""
         if self.slot == self.FLAG_RING:
-            self.flags.zero_()   # stream-ordered before the next launch
+            if stream is None:
+                stream = torch.cuda.current_stream()
+            elif isinstance(stream, int):
+                stream = torch.cuda.ExternalStream(stream)
+            with torch.cuda.stream(stream):
+                self.flags.zero_()
             self.slot = 0
         addr = self._flag_base + 4 * self.slot
         self.slot += 1
         return addr
 
-    def _next_flag(self):
-        addr = self._next_flag_addr()
+    def _next_flag(self, stream=None):
+        addr = self._next_flag_addr(stream)
         i = (addr - self._flag_base) // 4
         return self.flags[i:i + 1]
 
@@ -202,7 +209,7 @@ class ShardState:
                stream=None):
         """Enqueue the fused step without waiting; returns the device flag
         slot it ORs into (finish() reads it back)."""
-        flag = self._next_flag()
+        flag = self._next_flag(stream)
         args = self._args(worker_grads, acc_in)
         self._refresh_hparams(args)
         args.args.overflow_flag = flag.data_ptr()
@@ -210,9 +217,17 @@ class ShardState:
         return flag
 
     def finish(self, flag, stream=None):
-        """Read the flag back (the step's only synchronization), then commit or skip."""
-        s = stream if stream is not None else torch.cuda.current_stream()
-        self.flag_host.copy_(flag, non_blocking=True)
+        """Read the flag back (the step's only synchronization), then commit or
+        skip. `stream` must be the one launch() used: the copy is ordered
+        after the step on it."""
+        if stream is None:
+            s = torch.cuda.current_stream()
+        elif isinstance(stream, int):
+            s = torch.cuda.ExternalStream(stream)
+        else:
+            s = stream
+        with torch.cuda.stream(s):
+            self.flag_host.copy_(flag, non_blocking=True)
         s.synchronize()
         self.last_flag = int(self.flag_host[0])
         zs.zs_scaler_update(self.scaler, self.last_flag)
@@ -246,7 +261,7 @@ class ShardState:
         scaler update in one native call); returns True when committed.
         ev_start / ev_stop: optional raw hipEvent_t handles around the kernel."""
         args = self._step_args(worker_grads, acc_in)
-        args.args.overflow_flag = self._next_flag_addr()
+        args.args.overflow_flag = self._next_flag_addr(stream)
         ok = zs.zs_step_commit(args, self.scaler, self.flag_host, stream, ev_start, ev_stop)
         self.last_flag = 0 if ok else 1
         if ok:

@@ -586,3 +586,51 @@ def test_step_fused_special_state_values(zs, eps):
     for got, want, what in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
         assert_bits_equal(down32(got), want, what)
     assert assert_ulp16(down16(gather), po, "bf16", 0, "params") == 0
+
+
+def test_flag_ring_wraps_on_the_steps_stream(zs):
+    """ShardState's host-commit flow takes a fresh zeroed flag slot per step
+    from a ring of 256 and re-zeroes the ring on the stream of the step that
+    wraps it. Step 5 overflows (slot 4 set); step 261 reuses slot 4 with
+    finite gradients and must commit; step 100 overflows through
+    launch()/finish(), whose flag readback must be ordered after the step on
+    its stream. Steps run on a side stream through step() and
+    launch()/finish() alternately; the final state equals the same schedule
+    on the default stream, bit for bit."""
+    from sharded_mixed_precision_zs_amd import shard
+    world, n, steps = 2, 1024, 300
+    rng = np.random.default_rng(31)
+    g16 = [rand16(rng, n, 1e-3 * 1024, "bf16") for _ in range(world)]
+    state = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    state[2] = np.abs(state[2])
+
+    def run(stream):
+        st = shard.ShardState(n, world, 0, 0, n, zs.ZS_BF16, zs.ZS_BF16, shard.AdamW(**HP),
+                              1024.0)
+        for dst, x in zip((st.master, st.m, st.v), state):
+            dst.copy_(torch.from_numpy(x))
+        good = [up16(g, "bf16") for g in g16]
+        bad = [g.clone() for g in good]
+        bad[1][77] = float("inf")
+        torch.cuda.synchronize()
+        outcome = []
+        for step in range(1, steps + 1):
+            grads = bad if step in (5, 100) else good
+            if step % 2:
+                outcome.append(st.step(grads, stream=stream))
+            else:
+                outcome.append(st.finish(st.launch(grads, stream=stream), stream=stream))
+        torch.cuda.synchronize()
+        return st, outcome
+
+    announce("flag ring wrap on a side stream")
+    side, got = run(torch.cuda.Stream())
+    assert got[4] is False and got[99] is False and got[260] is True
+    assert got.count(False) == 2 and side.t == steps - 2 and side.scaler.skipped == 2
+    announce("flag ring wrap on the default stream")
+    ref, want = run(None)
+    assert got == want
+    for a, b, what in ((side.master, ref.master, "master"), (side.m, ref.m, "m"),
+                       (side.v, ref.v, "v")):
+        assert_bits_equal(down32(a), down32(b), f"flag ring {what}")
+    assert np.array_equal(down16(side.params), down16(ref.params))
