@@ -104,7 +104,9 @@ class ShardState:
     # -- checkpoint / resume ---------------------------------------------------
     def state_dict(self):
         """Host copy of everything the next step depends on: the current fp32
-        set, this rank's 16-bit parameters and the scaler."""
+        set, this rank's 16-bit parameters and the scaler (waits for every
+        queued step, on any stream)."""
+        torch.cuda.synchronize(self.sets[0][0].device)
         if self.device_commit:
             self.sync_scaler()
         sc = self.scaler
@@ -115,7 +117,9 @@ class ShardState:
                            "step_t": int(sc.step_t), "skipped": int(sc.skipped)}}
 
     def load_state_dict(self, sd):
-        """Restore a state_dict() into the current set (shapes must match)."""
+        """Restore a state_dict() into the current set (shapes must match;
+        waits for every queued step first, on any stream)."""
+        torch.cuda.synchronize(self.sets[0][0].device)
         for dst, key in ((self.master, "master"), (self.m, "m"), (self.v, "v"),
                          (self.params, "params")):
             if dst.shape != sd[key].shape or dst.dtype != sd[key].dtype:
