@@ -37,7 +37,8 @@ DEFAULT_WORKLOAD = "gpt2s-w8"   # GPT-2-small-shaped flat model, W = 8
 DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1,1p3b-w4-acc4-fp16"
 KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zs_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.md")
-EVENT_EVERY = 4
+EVENT_EVERY_MAX = 16   # at most one launch in 16 is bracketed by HIP events
+EVENT_SAMPLES = 20     # ... and at least this many are, where the steps allow
 METRIC = "params updated/sec per ZeRO-2 shard step + achieved HBM GB/s (% of peak)"
 
 
@@ -174,9 +175,11 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
     for i in range(warmup):
         one_step(i)
     torch.cuda.synchronize()
-    # HIP events bracket the fused kernel on every EVENT_EVERY-th timed step
-    # (each record puts a ~5 us gap between kernels, so not on every step)
-    timed = list(range(0, steps, EVENT_EVERY))
+    # HIP events bracket the fused kernel on every k-th timed step: each
+    # record puts a gap of a few us between kernels, which the step time
+    # would carry, so k is as large as EVENT_SAMPLES samples allow (up to 16)
+    every = max(1, min(EVENT_EVERY_MAX, steps // EVENT_SAMPLES))
+    timed = list(range(0, steps, every))
     evs = {i: (hip.create(), hip.create()) for i in timed}
     committed = -committed_so_far()
     torch.cuda.synchronize()
@@ -200,7 +203,7 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
                fused_kernel_ms=kern_avg, fused_bytes=fused_bytes,
                fused_gbps=fused_bytes / (kern_avg * 1e-3) / 1e9, committed=committed,
                kernel_ms_min=min(kern_ms), kernel_ms_max=max(kern_ms),
-               kernel_ms_median=kern_med, kernel_samples=len(kern_ms))
+               kernel_ms_median=kern_med, kernel_samples=len(kern_ms), event_every=every)
     del reps
     torch.cuda.empty_cache()
     return res
@@ -356,7 +359,7 @@ def side_leg(name, fn, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=80)
+    ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--also", default=DEFAULT_ALSO,
@@ -454,6 +457,7 @@ def main():
                      "kernel": "zs::fused_kernel", "kernel_ms": main_res["fused_kernel_ms"],
                      "kernel_ms_median": main_res["kernel_ms_median"],
                      "kernel_samples": main_res["kernel_samples"],
+                     "event_every": main_res["event_every"],
                      "algorithmic_bytes_per_launch": main_res["fused_bytes"]},
         "cpu_baseline": cpu,
         "other_workloads": others,
