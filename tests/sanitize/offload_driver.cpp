@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <chrono>
 #include <thread>
 #include <vector>
 
@@ -113,6 +114,17 @@ int main() {
     x.join();
     y.join();
     CHECK(bad == 0);
+    /* runs spaced past the pool's spin window, so the workers (and the
+     * caller waiting for them) go to sleep and are woken through the
+     * condition variables */
+    for (int rep = 0; rep < 12; ++rep) {
+      std::this_thread::sleep_for(std::chrono::milliseconds(2));
+      std::vector<float> a = t0, b = m0, c = v0;
+      std::vector<uint16_t> q(n);
+      CHECK(zs_cpu_step(a.data(), b.data(), c.data(), g.data(), n, &hp, q.data(), 0,
+                        2 + rep % 6, &ovf) == ZS_OK);
+      CHECK(memcmp(a.data(), rt.data(), n * 4) == 0 && memcmp(q.data(), rp.data(), n * 2) == 0);
+    }
   }
   uint32_t ovf;
   float x = 0;
