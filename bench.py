@@ -252,7 +252,7 @@ def run_offload(name, steps, warmup, torch):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     return dict(workload=name, params_per_s=n / (ms * 1e-3), ms_per_step=ms, host_threads=threads,
-                pcie_bytes_per_step=6 * n, hbm_state_bytes_saved=12 * n)
+                pieces=off.pieces, pcie_bytes_per_step=6 * n, hbm_state_bytes_saved=12 * n)
 
 
 def cpu_model():

@@ -27,9 +27,10 @@
  *     the library never allocates or frees device memory and never keeps a
  *     pointer after the call returns. Work is enqueued on `stream` (a
  *     hipStream_t; NULL = the null stream) and completes asynchronously;
- *     kernel faults surface at the caller's next synchronization. Two calls
- *     wait by contract: zs_step_commit (for its flag) and zs_cpu_step (host
- *     work); no other call synchronizes.
+ *     kernel faults surface at the caller's next synchronization. These
+ *     calls wait by contract: zs_step_commit (for its flag), zs_offload_step
+ *     (for its flag and the gradient pieces), and zs_cpu_step and
+ *     zs_cpu_update (host work); no other call synchronizes.
  *   - Host pointers (arrays of device pointers, hyper-parameter structs,
  *     outputs of zs_partition) are read or written during the call only.
  *   - 16-bit values are IEEE binary16 (ZS_FP16) or bfloat16 (ZS_BF16).
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ZS_ABI_VERSION 3
+#define ZS_ABI_VERSION 4
 #define ZS_MAX_WORLD 64
 
 typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
@@ -242,6 +243,42 @@ int zs_cpu_step(float *master, float *m, float *v, const float *grad_part, uint6
  * Errors: as zs_cpu_step. */
 int zs_cpu_update(float *master, float *m, float *v, const float *grad_part, uint64_t n,
                   const zs_adamw_hparams *hp, void *params16, int param_dtype, int threads);
+
+/* One whole ZeRO-Offload optimizer step after the reduction ([Intro] 一.3
+ * item (16)), pipelined over PCIe: the GPU checks the partition
+ * (zs_check_overflow's test) and its 4-byte flag reaches the host first; on
+ * a clean step the gradient comes to the host in `pieces` consecutive
+ * pieces, the host pool updates each piece as it lands (the arithmetic of
+ * zs_cpu_update), and each finished piece's 16-bit parameters are copied
+ * back while later pieces are still being updated. All copies run on
+ * `stream`, after the work already queued there.
+ *   grad_dev:    device fp32[n], the averaged, still loss-scaled gradient
+ *                partition (zs_reduce_scatter_avg's output).
+ *   grad_host:   host fp32[n] staging for it; params_host: host 16-bit[n]
+ *                staging for the parameters. Both should be pinned
+ *                (hipHostMalloc) for the copies to overlap the update.
+ *   master, m, v: host fp32[n], updated in place on a clean step.
+ *   params_dev:  device 16-bit[n], this rank's slice of the gather buffer.
+ *   flag_dev:    device uint32 scratch (the call zeroes it); flag_host: a
+ *                host uint32 (pinned) that receives the flag.
+ *   threads:     as zs_cpu_step; pieces: 1 .. 1024 (boundaries at
+ *                multiples of 64 elements).
+ *   stream:      HIP stream (NULL = the default stream).
+ *   *committed:  1 if the step was applied, 0 if it was skipped (then
+ *                nothing on the host or in params_dev is written).
+ * Blocks until the host update is done; the last parameter copies may still
+ * be in flight on `stream`, so work queued there afterwards sees the new
+ * parameters, and params_host must not be rewritten before `stream` passes
+ * this point. Errors: ZS_ERR_INVALID_ARG (null pointer, bad dtype, pieces
+ * out of range, host buffers that overlap, or arguments zs_cpu_update
+ * refuses), ZS_ERR_UNSUPPORTED for n > 2^48, both before any HIP call;
+ * ZS_ERR_HIP if a copy, the check or a wait fails (the call then waits for
+ * the stream; the host state may be partly updated). n == 0 commits without
+ * touching the GPU. */
+int zs_offload_step(const float *grad_dev, float *grad_host, float *master, float *m, float *v,
+                    void *params_host, void *params_dev, uint64_t n, const zs_adamw_hparams *hp,
+                    int param_dtype, uint32_t *flag_dev, uint32_t *flag_host, int threads,
+                    int pieces, void *stream, int *committed);
 
 /* Host-side commit/skip bookkeeping of dynamic loss scaling ([Intro] 一.3
  * items (1) and (3) name it without a rule). With dynamic != 0: on overflow

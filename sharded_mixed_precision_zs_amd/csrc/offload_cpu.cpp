@@ -24,6 +24,7 @@
 #include <chrono>
 #include <condition_variable>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -31,6 +32,7 @@
 #include "zeroshard.h"
 #include "zs_hparams.h"
 #include "zs_host_powers.h"
+#include "zs_offload_pieces.h"
 
 namespace {
 
@@ -358,4 +360,72 @@ extern "C" int zs_cpu_update(float *master, float *m, float *v, const float *gra
   update_all(master, m, v, grad_part, n, k, static_cast<uint16_t *>(params16), param_dtype,
              thread_count(threads, n));
   return ZS_OK;
+}
+
+namespace {
+
+/* Waits (pause, then yielding the core) until flag leaves `from`. */
+int wait_while(const std::atomic<int> &flag, int from) {
+  for (unsigned i = 0;; ++i) {
+    const int s = flag.load();
+    if (s != from) return s;
+    if (i < 2048) _mm_pause();
+    else std::this_thread::yield();
+  }
+}
+
+}  // namespace
+
+int zs_host::update_in_pieces(float *master, float *m, float *v, const float *grad, uint64_t n,
+                              const zs_adamw_hparams *hp, void *params16, int param_dtype,
+                              int threads, const uint64_t *cuts, int pieces,
+                              const PieceHooks &hooks) {
+  Consts k;
+  int rc = prepare(master, m, v, grad, n, hp, params16, param_dtype, &k);
+  if (rc != ZS_OK) return rc;
+  if (!cuts || pieces <= 0 || !hooks.arrived || !hooks.updated) return ZS_ERR_INVALID_ARG;
+  if (cuts[0] != 0 || cuts[pieces] != n) return ZS_ERR_INVALID_ARG;
+  for (int p = 0; p < pieces; ++p)
+    if (cuts[p] > cuts[p + 1]) return ZS_ERR_INVALID_ARG;
+  if (n == 0) return ZS_OK;
+  threads = thread_count(threads, n);
+  const bool avx512 = have_avx512();
+  uint16_t *out = static_cast<uint16_t *>(params16);
+  /* per piece: 0 not yet claimed, 1 a thread waits in arrived(), 2 arrived,
+   * -1 arrived() failed; and the threads still working on it */
+  std::unique_ptr<std::atomic<int>[]> state(new std::atomic<int>[pieces]);
+  std::unique_ptr<std::atomic<int>[]> left(new std::atomic<int>[pieces]);
+  for (int p = 0; p < pieces; ++p) {
+    state[p].store(0);
+    left[p].store(threads);
+  }
+  std::atomic<bool> failed{false};
+  Pool::instance().run(threads, [&](int t) {
+    for (int p = 0; p < pieces; ++p) {
+      int s = state[p].load();
+      if (s == 0) {
+        int expected = 0;
+        if (state[p].compare_exchange_strong(expected, 1)) {
+          s = hooks.arrived(hooks.ctx, p) == 0 ? 2 : -1;
+          state[p].store(s);
+        } else {
+          s = expected;
+        }
+      }
+      if (s == 1) s = wait_while(state[p], 1);
+      if (s < 0) {
+        failed.store(true);
+        return;
+      }
+      const uint64_t len = cuts[p + 1] - cuts[p];
+      const uint64_t lo = cuts[p] + len * (uint64_t)t / (uint64_t)threads;
+      const uint64_t hi = cuts[p] + len * (uint64_t)(t + 1) / (uint64_t)threads;
+      if (hi > lo) {
+        if (avx512) update_avx512(master, m, v, grad, lo, hi, k, out, param_dtype);
+        else update_scalar(master, m, v, grad, lo, hi, k, out, param_dtype);
+      }
+      if (left[p].fetch_sub(1) == 1) hooks.updated(hooks.ctx, p);
+    }
+  });
+  return failed.load() ? ZS_ERR_HIP : ZS_OK;
 }

@@ -15,11 +15,14 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "zeroshard.h"
 
 #include "zs_aux_kernels.h"
 #include "zs_hparams.h"
 #include "zs_host_powers.h"
+#include "zs_offload_pieces.h"
 
 
 namespace {
@@ -232,6 +235,74 @@ bool overlaps(const void *a, uint64_t abytes, const void *b, uint64_t bbytes) {
   if (!a || !b || !abytes || !bbytes) return false;
   uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+/* ------------------------------------------------------------------------
+ * Pipelined ZeRO-Offload step: the events of one call and the hooks the
+ * host update calls from its pool threads (each makes the caller's device
+ * current on that thread before its HIP call).
+ * ---------------------------------------------------------------------- */
+
+constexpr int kMaxOffloadPieces = 1024;
+
+/* The events of one call. Each is complete (or its stream synchronized)
+ * before the call returns, so none is released while pending. */
+struct OffloadEvents {
+  hipEvent_t flag = nullptr;
+  std::vector<hipEvent_t> piece;
+
+  int create(int pieces) {
+    piece.assign((size_t)pieces, nullptr);
+    if (hipEventCreateWithFlags(&flag, hipEventDisableTiming) != hipSuccess)
+      return fail(ZS_ERR_HIP, "zs_offload_step: hipEventCreate failed%s");
+    for (hipEvent_t &ev : piece)
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+        return fail(ZS_ERR_HIP, "zs_offload_step: hipEventCreate failed%s");
+    return ZS_OK;
+  }
+
+  ~OffloadEvents() {
+    if (flag) (void)hipEventDestroy(flag);
+    for (hipEvent_t ev : piece)
+      if (ev) (void)hipEventDestroy(ev);
+  }
+};
+
+struct OffloadHooks {
+  int device = 0;
+  const hipEvent_t *ev_piece = nullptr;
+  const uint64_t *cuts = nullptr;
+  uint16_t *params_dev = nullptr;
+  const uint16_t *params_host = nullptr;
+  hipStream_t stream = nullptr;
+  std::atomic<int> error{0};  /* first HIP error of a hook */
+
+  void note(hipError_t e) {
+    int none = 0;
+    if (e != hipSuccess) error.compare_exchange_strong(none, (int)e);
+  }
+};
+
+/* piece k's gradient is in host memory once its event has completed */
+int offload_arrived(void *c, int k) {
+  OffloadHooks *h = static_cast<OffloadHooks *>(c);
+  hipError_t e = hipSetDevice(h->device);
+  if (e == hipSuccess) e = hipEventSynchronize(h->ev_piece[k]);
+  h->note(e);
+  return e == hipSuccess ? 0 : 1;
+}
+
+/* piece k's parameters are final: send them back (same stream, so after
+ * every gradient piece) */
+void offload_updated(void *c, int k) {
+  OffloadHooks *h = static_cast<OffloadHooks *>(c);
+  const uint64_t lo = h->cuts[k], hi = h->cuts[k + 1];
+  if (hi == lo) return;
+  hipError_t e = hipSetDevice(h->device);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->params_dev + lo, h->params_host + lo, 2 * (hi - lo),
+                       hipMemcpyHostToDevice, h->stream);
+  h->note(e);
 }
 
 }  // namespace
@@ -717,6 +788,90 @@ int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint
   if (wide) hipLaunchKernelGGL(gather_step_kernel<8>, grid, block, 0, s, g);
   else hipLaunchKernelGGL(gather_step_kernel<1>, grid, block, 0, s, g);
   return launch_result();
+}
+
+int zs_offload_step(const float *grad_dev, float *grad_host, float *master, float *m, float *v,
+                    void *params_host, void *params_dev, uint64_t n, const zs_adamw_hparams *hp,
+                    int param_dtype, uint32_t *flag_dev, uint32_t *flag_host, int threads,
+                    int pieces, void *stream, int *committed) {
+  if (!grad_dev || !grad_host || !master || !m || !v || !params_host || !params_dev || !hp ||
+      !flag_dev || !flag_host || !committed)
+    return fail(ZS_ERR_INVALID_ARG, "zs_offload_step: null pointer%s");
+  if (!valid_dtype(param_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad param dtype%s");
+  if (too_big(n)) return fail(ZS_ERR_UNSUPPORTED, "n exceeds 2^48 elements%s");
+  if (pieces < 1 || pieces > kMaxOffloadPieces)
+    return fail(ZS_ERR_INVALID_ARG, "pieces must lie in [1, 1024]%s");
+  if (!(hp->loss_scale > 0.0f) || !isfinite(hp->loss_scale))
+    return fail(ZS_ERR_INVALID_ARG, "loss_scale must be finite and > 0%s");
+  if (hp->step_t == 0) return fail(ZS_ERR_INVALID_ARG, "step_t must be >= 1%s");
+  if (const char *bad = zs_host::hparams_problem(hp)) return fail(ZS_ERR_INVALID_ARG, "%s", bad);
+  {
+    const void *host[] = {grad_host, master, m, v, params_host};
+    const uint64_t bytes[] = {4 * n, 4 * n, 4 * n, 4 * n, 2 * n};
+    for (int i = 0; i < 5; ++i)
+      for (int j = i + 1; j < 5; ++j)
+        if (overlaps(host[i], bytes[i], host[j], bytes[j]))
+          return fail(ZS_ERR_INVALID_ARG, "zs_offload_step: host buffers overlap%s");
+  }
+  *committed = 0;
+  if (n == 0) {
+    *committed = 1;
+    g_err[0] = 0;
+    return ZS_OK;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  OffloadEvents ev;
+  int rc = ev.create(pieces);
+  if (rc != ZS_OK) return rc;
+  /* the check, then the flag to the host */
+  hipError_t e = hipMemsetAsync(flag_dev, 0, sizeof(uint32_t), s);
+  if (e != hipSuccess) return fail(ZS_ERR_HIP, "zs_offload_step: %s", hipGetErrorString(e));
+  rc = zs_check_overflow(grad_dev, n, hp->loss_scale, flag_dev, stream);
+  if (rc != ZS_OK) return rc;
+  e = hipMemcpyAsync(flag_host, flag_dev, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipEventRecord(ev.flag, s);
+  if (e == hipSuccess) e = hipEventSynchronize(ev.flag);
+  if (e != hipSuccess) return fail(ZS_ERR_HIP, "zs_offload_step: %s", hipGetErrorString(e));
+  if (*static_cast<volatile uint32_t *>(flag_host) != 0) {
+    g_err[0] = 0;
+    return ZS_OK;  /* skipped: nothing copied or written */
+  }
+  /* the gradient in pieces, each announced by its event; the parameter
+   * copies that the host update enqueues follow on the same stream */
+  std::vector<uint64_t> cuts((size_t)pieces + 1);
+  for (int k = 0; k < pieces; ++k) cuts[(size_t)k] = n * (uint64_t)k / (uint64_t)pieces / 64 * 64;
+  cuts[(size_t)pieces] = n;
+  for (int k = 0; k < pieces && e == hipSuccess; ++k) {
+    const uint64_t lo = cuts[(size_t)k], hi = cuts[(size_t)k + 1];
+    if (hi > lo)
+      e = hipMemcpyAsync(grad_host + lo, grad_dev + lo, 4 * (hi - lo), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(ev.piece[(size_t)k], s);
+  }
+  if (e != hipSuccess) {
+    /* wait for what was enqueued before the events are released */
+    (void)hipStreamSynchronize(s);
+    return fail(ZS_ERR_HIP, "zs_offload_step: %s", hipGetErrorString(e));
+  }
+  OffloadHooks ctx;
+  ctx.ev_piece = ev.piece.data();
+  ctx.cuts = cuts.data();
+  ctx.params_dev = static_cast<uint16_t *>(params_dev);
+  ctx.params_host = static_cast<const uint16_t *>(params_host);
+  ctx.stream = s;
+  if (hipGetDevice(&ctx.device) != hipSuccess) ctx.device = 0;
+  zs_host::PieceHooks hooks{&ctx, &offload_arrived, &offload_updated};
+  rc = zs_host::update_in_pieces(master, m, v, grad_host, n, hp, params_host, param_dtype,
+                                 threads, cuts.data(), pieces, hooks);
+  const int herr = ctx.error.load();
+  if (herr != 0 || rc != ZS_OK) {
+    (void)hipStreamSynchronize(s);
+    if (herr != 0)
+      return fail(ZS_ERR_HIP, "zs_offload_step: %s", hipGetErrorString((hipError_t)herr));
+    return fail(rc, "zs_offload_step: the host update refused its arguments%s");
+  }
+  *committed = 1;
+  g_err[0] = 0;
+  return ZS_OK;
 }
 
 int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow) {

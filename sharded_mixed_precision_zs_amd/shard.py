@@ -294,27 +294,25 @@ class ShardState:
 class OffloadShard:
     """ZeRO-Offload variant of one rank's shard (the DeepSpeed introduction,
     item (16)): fp32 master, m and v live in host memory and the update runs
-    on the host (zs_cpu_step); the GPU keeps the W-way ring-order reduction
+    on the host; the GPU keeps the W-way ring-order reduction
     (zs_reduce_scatter_avg) and the 16-bit parameters. Per step, 4 bytes per
     parameter cross PCIe to the host (the averaged fp32 gradient) and 2 back
     (the parameters), against the fused GPU step's 12 B/param of optimizer
     state kept in HBM. The arithmetic is the fused step's, element for
     element, so both variants produce the same bits.
 
-    A step is pipelined: the overflow check runs on the GPU
-    (zs_check_overflow, the same test zs_cpu_step applies) and its 4-byte
-    flag reaches the host first, so a skipped step does no host work; the
-    gradient then comes back in `chunks` pieces on the compute stream while
-    the host updates the pieces already there, and each piece's parameters
-    go back on a second stream, so both PCIe directions overlap the
-    update."""
+    A step is one native call (zs_offload_step): the overflow check runs on
+    the GPU and its flag reaches the host first, so a skipped step does no
+    host work; the gradient then comes back in `pieces` pieces while the host
+    pool updates the pieces already there, and each finished piece's
+    parameters go back at once."""
 
     def __init__(self, n, world, rank, offset, gather_len, param_dtype, grad_dtype,
                  opt: AdamW, loss_scale, dynamic=False, growth_interval=0, device="cuda",
-                 threads=0, wire_dtype=zs.ZS_WIRE_FP32, chunks=8):
+                 threads=0, wire_dtype=zs.ZS_WIRE_FP32, pieces=16):
         self.n, self.world, self.rank, self.offset = n, world, rank, offset
         self.param_dtype, self.grad_dtype, self.opt = param_dtype, grad_dtype, opt
-        self.threads, self.wire_dtype = threads, wire_dtype
+        self.threads, self.wire_dtype, self.pieces = threads, wire_dtype, pieces
         pdt = torch.bfloat16 if param_dtype == zs.ZS_BF16 else torch.float16
         self.master = torch.empty(n, dtype=torch.float32)
         self.m = torch.zeros(n, dtype=torch.float32)
@@ -329,13 +327,6 @@ class OffloadShard:
         self.last_flag = 0
         self.flag_dev = torch.zeros(1, dtype=torch.int32, device=device)
         self.flag_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
-        # piece boundaries on multiples of 64 elements (whole vectors)
-        k = max(1, min(chunks, -(-n // 65536)))
-        cuts = [min(n, (n * i // k) // 64 * 64) for i in range(k)] + [n]
-        self.bounds = [(lo, hi) for lo, hi in zip(cuts[:-1], cuts[1:]) if hi > lo]
-        self.flag_ready = torch.cuda.Event()
-        self.piece_ready = [torch.cuda.Event() for _ in self.bounds]
-        self.h2d = torch.cuda.Stream(device=device)
 
     @property
     def params(self):
@@ -358,36 +349,17 @@ class OffloadShard:
 
     def step(self, worker_grads=None, first=True, stream=None):
         """Reduce the last micro-batch (unless worker_grads is None, when it
-        was reduced already), check it on the GPU, and unless it overflowed
-        update on the host piece by piece while the gradient streams in and
-        the parameters stream out. Returns True when committed."""
-        s = stream if stream is not None else torch.cuda.current_stream()
+        was reduced already), then the pipelined check, transfer and host
+        update of zs_offload_step. Returns True when committed."""
         if worker_grads is not None:
-            self.reduce_micro(worker_grads, first, s)
-        with torch.cuda.stream(s):
-            self.flag_dev.zero_()
-            zs.zs_check_overflow(self.grad, self.n, self.loss_scale, self.flag_dev, stream=s)
-            self.flag_host.copy_(self.flag_dev, non_blocking=True)
-            self.flag_ready.record(s)
-            for (lo, hi), ev in zip(self.bounds, self.piece_ready):
-                self.grad_host[lo:hi].copy_(self.grad[lo:hi], non_blocking=True)
-                ev.record(s)
-        self.flag_ready.synchronize()
-        flag = int(self.flag_host[0])
-        if flag == 0:
-            o = self.opt
-            hp = zs.hparams(o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.loss_scale,
-                            self.t + 1)
-            self.h2d.wait_stream(s)
-            for (lo, hi), ev in zip(self.bounds, self.piece_ready):
-                ev.synchronize()
-                # the GPU checked the whole partition: the update alone
-                zs.zs_cpu_update(self.master[lo:hi], self.m[lo:hi], self.v[lo:hi],
-                                 self.grad_host[lo:hi], hp, self.params_host[lo:hi],
-                                 self.param_dtype, self.threads)
-                with torch.cuda.stream(self.h2d):
-                    self.params[lo:hi].copy_(self.params_host[lo:hi], non_blocking=True)
-            s.wait_stream(self.h2d)
+            self.reduce_micro(worker_grads, first, stream)
+        o = self.opt
+        hp = zs.hparams(o.lr, o.beta1, o.beta2, o.eps, o.weight_decay, self.loss_scale,
+                        self.t + 1)
+        ok = zs.zs_offload_step(self.grad, self.grad_host, self.master, self.m, self.v,
+                                self.params_host, self.params, hp, self.flag_dev, self.flag_host,
+                                self.param_dtype, self.threads, self.pieces, stream)
+        flag = 0 if ok else 1
         zs.zs_scaler_update(self.scaler, flag)
         self.last_flag = flag
-        return flag == 0
+        return ok

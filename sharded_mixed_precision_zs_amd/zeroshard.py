@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 
 from . import build as _build
 
-ZS_ABI_VERSION = 3
+ZS_ABI_VERSION = 4
 ZS_MAX_WORLD = 64
 ZS_BF16, ZS_FP16 = 0, 1
 ZS_WIRE_FP32, ZS_WIRE_BF16, ZS_WIRE_FP16 = 0, 1, 2
@@ -91,6 +91,8 @@ def _load():
         "zs_device_scaler_make": ([C.POINTER(zs_loss_scaler), f32, f32,
                                    C.POINTER(zs_device_scaler)], i32),
         "zs_step_device": ([C.POINTER(zs_step_args), vp, vp, vp, vp], i32),
+        "zs_offload_step": ([vp, vp, vp, vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), i32,
+                             vp, vp, i32, i32, vp, C.POINTER(C.c_int)], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -391,3 +393,38 @@ def zs_cpu_update(master, m, v, grad_part, hp: zs_adamw_hparams, params16, param
                                            param_dtype)
     rc = _lib.zs_cpu_update(pm, p1, p2, pg, n, C.byref(hp), pp, dt, threads)
     _check("zs_cpu_update", rc, _CPU_DETAIL.get(rc, ""))
+
+
+def _host_ptr(x, n, elem, what):
+    """Address of a contiguous host (CPU) tensor or array of >= n elements of
+    `elem` bytes."""
+    if hasattr(x, "data_ptr"):
+        if x.is_cuda or not x.is_contiguous() or x.element_size() != elem or x.numel() < n:
+            raise ValueError(f"{what}: contiguous host tensor of >= {n} {elem}-byte elements "
+                             "expected")
+        return x.data_ptr()
+    if not x.flags.c_contiguous or x.itemsize != elem or x.size < n:
+        raise ValueError(f"{what}: contiguous array of >= {n} {elem}-byte elements expected")
+    return x.ctypes.data
+
+
+def zs_offload_step(grad_dev, grad_host, master, m, v, params_host, params_dev,
+                    hp: zs_adamw_hparams, flag_dev, flag_host, param_dtype=None, threads=0,
+                    pieces=16, stream=None):
+    """Pipelined ZeRO-Offload step (blocks until the host update is done).
+    grad_dev, params_dev, flag_dev: CUDA tensors; grad_host, master, m, v,
+    params_host, flag_host: host tensors (the staging ones pinned). n is
+    master's length. Returns True when committed, False when skipped."""
+    n = master.numel() if hasattr(master, "numel") else master.size
+    if param_dtype is None:
+        param_dtype = _dtype_code(params_dev, None)
+    committed = C.c_int(0)
+    rc = _lib.zs_offload_step(
+        _ptr(grad_dev, n, 4, "grad_dev"), _host_ptr(grad_host, n, 4, "grad_host"),
+        _host_ptr(master, n, 4, "master"), _host_ptr(m, n, 4, "m"), _host_ptr(v, n, 4, "v"),
+        _host_ptr(params_host, n, 2, "params_host"), _ptr(params_dev, n, 2, "params_dev"), n,
+        C.byref(hp), param_dtype, _ptr(flag_dev, 1, 4, "flag_dev"),
+        _host_ptr(flag_host, 1, 4, "flag_host"), threads, pieces, _stream(stream),
+        C.byref(committed))
+    _check("zs_offload_step", rc)
+    return bool(committed.value)

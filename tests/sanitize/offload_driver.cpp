@@ -4,7 +4,10 @@
  * ThreadSanitizer (test infrastructure; run by tests/test_sanitizers.py):
  * ragged sizes, one and several worker threads (results must not depend on
  * the thread count), both parameter dtypes, and the skip on a non-finite
- * gradient at either end. Exits non-zero on an inconsistency.
+ * gradient at either end; and the piecewise update behind zs_offload_step
+ * (zs_host::update_in_pieces) with host-side hooks: pieces that arrive
+ * late, each piece announced once and only when final, a failing arrival.
+ * Exits non-zero on an inconsistency.
  */
 #include <math.h>
 #include <stdio.h>
@@ -15,6 +18,7 @@
 #include <vector>
 
 #include "zeroshard.h"
+#include "zs_offload_pieces.h"
 
 static unsigned long long rs = 0x9E3779B97F4A7C15ull;
 static float rf(float scale) {
@@ -125,6 +129,98 @@ int main() {
                         2 + rep % 6, &ovf) == ZS_OK);
       CHECK(memcmp(a.data(), rt.data(), n * 4) == 0 && memcmp(q.data(), rp.data(), n * 2) == 0);
     }
+  }
+  /* update_in_pieces against zs_cpu_update: several piece and thread
+   * counts, empty pieces, late arrivals; every piece announced once, after
+   * its elements are final; a failing arrival stops at that piece. */
+  {
+    const uint64_t n = 90011;
+    std::vector<float> g(n), m0(n), v0(n), t0(n);
+    for (uint64_t i = 0; i < n; ++i) {
+      t0[i] = rf(0.04f);
+      m0[i] = rf(2e-4f);
+      v0[i] = fabsf(rf(2e-6f));
+      g[i] = rf(4.0f);
+    }
+    std::vector<float> rt = t0, rm = m0, rv = v0;
+    std::vector<uint16_t> rp(n);
+    CHECK(zs_cpu_update(rt.data(), rm.data(), rv.data(), g.data(), n, &hp, rp.data(), 0, 1) ==
+          ZS_OK);
+    struct Ctx {
+      const uint64_t *cuts;
+      const float *ref;
+      const float *master;
+      std::vector<int> arrived_calls, updated_calls;
+      int fail_at;
+      int bad;
+    };
+    auto arrived = [](void *c, int k) -> int {
+      Ctx *x = static_cast<Ctx *>(c);
+      __atomic_fetch_add(&x->arrived_calls[(size_t)k], 1, __ATOMIC_RELAXED);
+      if (k % 3 == 1) std::this_thread::sleep_for(std::chrono::microseconds(300));
+      return k == x->fail_at ? 1 : 0;
+    };
+    auto updated = [](void *c, int k) {
+      Ctx *x = static_cast<Ctx *>(c);
+      __atomic_fetch_add(&x->updated_calls[(size_t)k], 1, __ATOMIC_RELAXED);
+      const uint64_t lo = x->cuts[k], hi = x->cuts[k + 1];
+      if (hi > lo && memcmp(x->master + lo, x->ref + lo, (hi - lo) * 4) != 0)
+        __atomic_fetch_add(&x->bad, 1, __ATOMIC_RELAXED);
+    };
+    const int piece_counts[] = {1, 2, 7, 33};
+    const int thread_counts[] = {1, 3, 8};
+    for (int pieces : piece_counts)
+      for (int threads : thread_counts)
+        for (int fail_at : {-1, 2}) {
+          if (fail_at >= pieces) continue;
+          std::vector<uint64_t> cuts((size_t)pieces + 1);
+          for (int k = 0; k < pieces; ++k)
+            cuts[(size_t)k] = (k == 1 ? 0 : n * (uint64_t)k / (uint64_t)pieces / 64 * 64);
+          cuts[(size_t)pieces] = n;  /* piece 0 is empty when pieces > 1 */
+          std::vector<float> a = t0, b = m0, c = v0;
+          std::vector<uint16_t> q(n, 0);
+          Ctx ctx{cuts.data(), rt.data(), a.data(), std::vector<int>((size_t)pieces, 0),
+                  std::vector<int>((size_t)pieces, 0), fail_at, 0};
+          zs_host::PieceHooks hooks{&ctx, +arrived, +updated};
+          const int rc = zs_host::update_in_pieces(a.data(), b.data(), c.data(), g.data(), n, &hp,
+                                                   q.data(), 0, threads, cuts.data(), pieces,
+                                                   hooks);
+          CHECK(ctx.bad == 0);
+          if (fail_at < 0) {
+            CHECK(rc == ZS_OK);
+            for (int k = 0; k < pieces; ++k)
+              CHECK(ctx.arrived_calls[(size_t)k] == 1 && ctx.updated_calls[(size_t)k] == 1);
+            CHECK(memcmp(a.data(), rt.data(), n * 4) == 0 &&
+                  memcmp(b.data(), rm.data(), n * 4) == 0 &&
+                  memcmp(c.data(), rv.data(), n * 4) == 0 &&
+                  memcmp(q.data(), rp.data(), n * 2) == 0);
+          } else {
+            CHECK(rc == ZS_ERR_HIP);
+            for (int k = 0; k < pieces; ++k) {
+              CHECK(ctx.updated_calls[(size_t)k] == (k < fail_at ? 1 : 0));
+              CHECK(ctx.arrived_calls[(size_t)k] == (k <= fail_at ? 1 : 0));
+            }
+            const uint64_t done = cuts[(size_t)fail_at];
+            CHECK(memcmp(a.data(), rt.data(), done * 4) == 0);
+            CHECK(memcmp(a.data() + done, t0.data() + done, (n - done) * 4) == 0);
+          }
+        }
+    /* bad cuts and hooks are refused */
+    std::vector<float> a = t0, b = m0, c = v0;
+    std::vector<uint16_t> q(n, 0);
+    Ctx ctx{nullptr, rt.data(), a.data(), std::vector<int>(4, 0), std::vector<int>(4, 0), -1, 0};
+    zs_host::PieceHooks hooks{&ctx, +arrived, +updated};
+    const uint64_t bad1[] = {0, 500, 100, n};
+    const uint64_t bad2[] = {1, 500, 1000, n};
+    const uint64_t bad3[] = {0, 500, 1000, n - 1};
+    for (const uint64_t *bc : {bad1, bad2, bad3})
+      CHECK(zs_host::update_in_pieces(a.data(), b.data(), c.data(), g.data(), n, &hp, q.data(), 0,
+                                      2, bc, 3, hooks) == ZS_ERR_INVALID_ARG);
+    zs_host::PieceHooks none{&ctx, nullptr, +updated};
+    const uint64_t good[] = {0, n};
+    CHECK(zs_host::update_in_pieces(a.data(), b.data(), c.data(), g.data(), n, &hp, q.data(), 0, 2,
+                                    good, 1, none) == ZS_ERR_INVALID_ARG);
+    CHECK(memcmp(a.data(), t0.data(), n * 4) == 0);
   }
   uint32_t ovf;
   float x = 0;

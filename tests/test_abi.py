@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(zs):
     lib = C.CDLL(zs.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 3
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 4
 
 
 def test_status_strings(zs):
@@ -360,3 +360,38 @@ def test_hyperparameter_range_edges_are_accepted(zs):
     assert ovf.value == 0
     zs.zs_device_scaler_make(zs.zs_loss_scaler(scale=1.0, clean_steps=0, growth_interval=0,
                                                dynamic=0, step_t=0, skipped=0), 0.0, 0.0)
+
+
+def test_offload_step_rejects_bad_arguments(zs):
+    """zs_offload_step refuses bad arguments before any HIP call, and an
+    empty partition commits without touching the GPU."""
+    lib = _raw(zs)
+    E = zs.ZS_ERR_INVALID_ARG
+    hp = _hp(zs)
+    n = 1000
+    host = FAKE + 0x40000000
+    gd, pd, fd = FAKE, FAKE + 0x100000, FAKE + 0x200000
+    gh, ms, m, v, ph, fh = (host + i * 0x100000 for i in range(6))
+    ok = C.c_int(7)
+
+    def call(*, n=n, hp=hp, dtype=0, pieces=16, threads=1, **over):
+        a = dict(gd=gd, gh=gh, ms=ms, m=m, v=v, ph=ph, pd=pd, fd=fd, fh=fh)
+        a.update(over)
+        return lib.zs_offload_step(a["gd"], a["gh"], a["ms"], a["m"], a["v"], a["ph"], a["pd"], n,
+                                   C.byref(hp) if hp is not None else None, dtype, a["fd"],
+                                   a["fh"], threads, pieces, None, C.byref(ok))
+
+    for field in ("gd", "gh", "ms", "m", "v", "ph", "pd", "fd", "fh"):
+        assert call(**{field: None}) == E, field
+    assert call(hp=None) == E
+    assert call(dtype=4) == E
+    assert call(pieces=0) == E and call(pieces=1025) == E
+    assert call(hp=_hp(zs, step_t=0)) == E
+    assert call(hp=_hp(zs, loss_scale=float("inf"))) == E
+    assert call(hp=_hp(zs, beta1=1.0)) == E
+    assert call(m=ms + 8) == E                       # host buffers overlap
+    assert call(ph=v + 4 * n - 2) == E
+    assert call(n=1 << 50) == zs.ZS_ERR_UNSUPPORTED
+    assert lib.zs_offload_step(gd, gh, ms, m, v, ph, pd, n, C.byref(hp), 0, fd, fh, 1, 16, None,
+                               None) == E            # no committed
+    assert call(n=0) == zs.ZS_OK and ok.value == 1

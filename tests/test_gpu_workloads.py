@@ -284,3 +284,57 @@ def test_offload_equals_fused(env, name, phi):
         assert_bits_equal(down32(x), y.numpy(), f"{name} offload state")
     assert np.array_equal(down16(gpu.params.view(torch.int16)), down16(off.params.view(torch.int16)))
     assert (gpu.t, gpu.loss_scale) == (off.t, off.loss_scale)
+
+
+@pytest.mark.parametrize("n,pieces,threads", [(1, 1, 1), (4099, 3, 2), (200_003, 16, 0),
+                                              (65_536, 1024, 4), (100_000, 7, 16)])
+def test_offload_step_equals_cpu_step(env, n, pieces, threads):
+    """zs_offload_step (GPU check, gradient in pieces, host update as the
+    pieces land, parameters copied back per piece) leaves the host state and
+    the device parameters exactly as zs_cpu_step on the same gradient, for
+    ragged sizes, more pieces than elements per thread, and any thread
+    count; a gradient with one non-finite value is skipped with nothing
+    written; the call runs on a side stream."""
+    zs, synth, shard = env
+    rng = np.random.default_rng(n + pieces)
+    grad = (rng.standard_normal(n) * 3e-3 * 1024).astype(F32)
+    state = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    state[2] = np.abs(state[2])
+    hp = zs.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1024.0, 3)
+    # reference: the host update alone
+    ref = [x.copy() for x in state]
+    ref_p = np.zeros(n, np.uint16)
+    assert zs.zs_cpu_step(*ref, grad, hp, ref_p, zs.ZS_BF16, 1) == 0
+    host = [torch.from_numpy(x.copy()) for x in state]
+    grad_dev = torch.from_numpy(grad).cuda()
+    params_dev = torch.full((n + 16,), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    grad_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
+    params_host = torch.empty(n, dtype=torch.bfloat16, pin_memory=True)
+    flag_dev = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    flag_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()   # the fills above ran on the default stream
+    announce(f"offload step n={n} pieces={pieces} threads={threads}")
+    ok = zs.zs_offload_step(grad_dev, grad_host, *host, params_host, params_dev[8:8 + n], hp,
+                            flag_dev, flag_host, zs.ZS_BF16, threads, pieces, stream=side)
+    side.synchronize()
+    assert ok and int(flag_host[0]) == 0
+    for got, want, what in zip(host, ref, ("master", "m", "v")):
+        assert_bits_equal(got.numpy(), want, f"offload step {what}")
+    p = down16(params_dev.view(torch.int16))
+    assert np.array_equal(p[8:8 + n], ref_p) and np.all(p[:8] == 7) and np.all(p[8 + n:] == 7)
+    # a non-finite gradient value: skipped, nothing written
+    bad = grad.copy()
+    bad[n // 2] = np.inf
+    grad_dev.copy_(torch.from_numpy(bad))
+    before = [x.numpy().copy() for x in host]
+    params_dev[8:8 + n].view(torch.int16).fill_(3)
+    torch.cuda.synchronize()
+    announce(f"offload step skip n={n}")
+    ok = zs.zs_offload_step(grad_dev, grad_host, *host, params_host, params_dev[8:8 + n], hp,
+                            flag_dev, flag_host, zs.ZS_BF16, threads, pieces, stream=side)
+    side.synchronize()
+    assert not ok and int(flag_host[0]) == 1
+    for got, want in zip(host, before):
+        assert_bits_equal(got.numpy(), want, "skipped offload step")
+    assert np.all(down16(params_dev.view(torch.int16))[8:8 + n] == 3)

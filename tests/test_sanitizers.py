@@ -6,7 +6,8 @@ ThreadSanitizer:
   - oracle_driver.c: every oracle function, including the threaded shard
     step (results must not depend on the thread count);
   - offload_driver.cpp: zs_cpu_step, the ZeRO-Offload host update of the
-    product library, with one and several worker threads;
+    product library, with one and several worker threads, and the piecewise
+    update behind zs_offload_step with host-side hooks;
   - abi_driver.c: the host-only logic of libzeroshard (partition, scaler,
     device-scaler image, argument rejection), linked against a build of the
     library whose host code is sanitized (the device code is not: GPU
@@ -52,7 +53,7 @@ def test_offload_update_under_sanitizer(tmp_path, san):
     exe = str(tmp_path / f"offload_{san}")
     flags = ASAN_UBSAN if san == "asan_ubsan" else TSAN
     _run(["g++", "-std=c++17", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-mf16c",
-          "-pthread", *flags, "-I", INCLUDE, os.path.join(SAN, "offload_driver.cpp"),
+          "-pthread", *flags, "-I", INCLUDE, "-I", CSRC, os.path.join(SAN, "offload_driver.cpp"),
           os.path.join(CSRC, "offload_cpu.cpp"), "-o", exe])
     assert "offload driver ok" in _run([exe])
 
