@@ -225,8 +225,9 @@ int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint
  *   Pass 2: master, m, v updated in place with exactly the arithmetic of
  *           zs_adamw_step, and params16[i] = RNE16(master'[i]).
  *   master, m, v, grad_part: host fp32[n]; params16: host 16-bit[n].
- *   threads: worker threads (<= 0: the machine's hardware threads, at most
- *            64); every range runs with round-to-nearest, subnormals kept.
+ *   threads: worker threads (<= 0: the CPUs in the process's affinity mask,
+ *            at most 64); every range runs with round-to-nearest,
+ *            subnormals kept.
  * Blocks until done. Errors: ZS_ERR_INVALID_ARG for null pointers, a bad
  * param dtype, a non-finite or non-positive loss scale, step_t == 0 or
  * hyper-parameters outside their ranges (zs_adamw_hparams). */

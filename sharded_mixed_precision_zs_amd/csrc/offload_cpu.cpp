@@ -16,6 +16,7 @@
 #include <immintrin.h>
 
 #include <math.h>
+#include <sched.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -301,8 +302,19 @@ int prepare(const float *master, const float *m, const float *v, const float *gr
   return ZS_OK;
 }
 
+/* CPUs this process may run on (its affinity mask; a container or job
+ * share is usually far below the machine's count), at most 64. */
+int default_threads() {
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  int cpus = 0;
+  if (sched_getaffinity(0, sizeof set, &set) == 0) cpus = CPU_COUNT(&set);
+  if (cpus <= 0) cpus = (int)std::thread::hardware_concurrency();
+  return std::min(64, std::max(1, cpus));
+}
+
 int thread_count(int threads, uint64_t n) {
-  if (threads <= 0) threads = (int)std::min(64u, std::max(1u, std::thread::hardware_concurrency()));
+  if (threads <= 0) threads = default_threads();
   return (int)std::min<uint64_t>((uint64_t)threads, std::max<uint64_t>(1, n / 4096));
 }
 
