@@ -16,7 +16,10 @@ bytes of one fused launch ((2W + 12) read + 14 written per parameter, plus
 4 read per parameter for an accumulated micro-batch input) divided by that
 launch's average duration measured with HIP events on the launch stream.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload
-on this host's cores.
+on this host's cores. Beside the headline, on the same workload: the step
+with its decision on the host (`host_commit`), with bf16 partial sums on
+the ring (`wire_bf16`), the ZeRO-Offload variant (`offload`), and one full
+ring all-gather of the 16-bit parameters over W replicas (`all_gather`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload NAME] [--also NAME,...] [--no-cpu-baseline]
@@ -37,6 +40,7 @@ DEFAULT_WORKLOAD = "gpt2s-w8"   # GPT-2-small-shaped flat model, W = 8
 DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1,1p3b-w4-acc4-fp16"
 KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zs_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.md")
+ALL_GATHER_LARGE = "1p3b-w4-acc4-fp16"  # 4 replicas of 1.3e9 params: beyond any cache
 EVENT_EVERY_MAX = 16   # at most one launch in 16 is bracketed by HIP events
 EVENT_SAMPLES = 20     # ... and at least this many are, where the steps allow
 METRIC = "params updated/sec per ZeRO-2 shard step + achieved HBM GB/s (% of peak)"
@@ -255,6 +259,52 @@ def run_offload(name, steps, warmup, torch):
                 pieces=off.pieces, pcie_bytes_per_step=6 * n, hbm_state_bytes_saved=12 * n)
 
 
+def run_all_gather(name, reps, torch):
+    """One full ring all-gather (W - 1 zs_all_gather_step calls) over W
+    replicas of the workload's flat 16-bit parameter buffer on one GPU.
+    Each step copies one chunk per replica: 2 bytes read and 2 written per
+    element moved."""
+    from sharded_mixed_precision_zs_amd import synth
+    from sharded_mixed_precision_zs_amd import zeroshard as zs
+
+    wl = synth.WORKLOADS[name]
+    W, phi = wl.world, wl.phi
+    chunk = -(-phi // W)
+    row = pad_elems(phi)
+    buf = torch.zeros((W, row), dtype=torch.int16, device="cuda")
+    replicas = [buf[k, :phi] for k in range(W)]
+
+    def gather():
+        for step in range(1, W):
+            zs.zs_all_gather_step(replicas, phi, step, sigma=0)
+
+    gather()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        gather()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    moved = 4 * (W - 1) * sum(min(chunk, max(0, phi - c * chunk)) for c in range(W))
+    del buf, replicas
+    torch.cuda.empty_cache()
+    gbps = moved / (ms * 1e-3) / 1e9
+    # each step reads the chunks the step before wrote: 2*phi bytes over all
+    # replicas, which the 256 MB last-level cache can hold for small models
+    cached = 2 * phi <= (256 << 20)
+    out = dict(workload=name, world=W, phi=phi, steps=W - 1, ms_per_gather=ms,
+               bytes_per_gather=moved, gbps=gbps)
+    if cached:
+        out["note"] = (f"each step reads the chunks the step before wrote ({2 * phi / 1e6:.0f} MB "
+                       "over all replicas, within the 256 MB last-level cache), so this is not "
+                       "an HBM rate")
+    else:
+        out["roofline_frac"] = gbps / PEAK_HBM_GBPS
+    return out
+
+
 def cpu_model():
     """The host CPU's model string (Linux), or None."""
     try:
@@ -315,7 +365,8 @@ def cpu_baseline(name, target_s=25.0):
                        f"{dt:.1f} s",
                 value_1_thread=probe * reps1 / dt1,
                 sample_1_thread=f"{probe} params x {reps1} step(s), 1 thread, {dt1:.1f} s",
-                cpu_model=cpu_model(), host_cpus=os.cpu_count())
+                cpu_model=cpu_model(), host_cpus_machine=os.cpu_count(),
+                host_cpus_available=len(os.sched_getaffinity(0)))
 
 
 def world_sweep(worlds, n, steps, warmup, torch):
@@ -402,6 +453,22 @@ def main():
     host_res = run_workload(args.workload, args.steps, args.warmup, torch, wire,
                             device_commit=False)
     log(json.dumps(host_res))
+    # the beyond-core legs on the same workload: the fused step with bf16
+    # partial sums on the wire, and the ring all-gather of the parameters
+    wire_bf16 = None
+    if args.wire == "fp32":
+        r = side_leg("wire_bf16", lambda: run_workload(args.workload, max(3, args.steps // 2), 2,
+                                                        torch, 1), torch)
+        log(json.dumps(r))
+        wire_bf16 = r if "error" in r else dict(
+            workload=args.workload, ms_per_step=r["ms_per_step"],
+            params_per_s=r["params_per_s"], fused_kernel_ms=r["fused_kernel_ms"],
+            fused_gbps=r["fused_gbps"], roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS)
+    all_gather = []
+    for name in dict.fromkeys([args.workload, ALL_GATHER_LARGE]):
+        r = side_leg(f"all_gather {name}", lambda: run_all_gather(name, 10, torch), torch)
+        log(json.dumps(r))
+        all_gather.append(r if "error" not in r else dict(workload=name, error=r["error"]))
     # the host-side legs run before the large workloads, which churn
     # hundreds of GB of device memory
     offload = None
@@ -465,6 +532,8 @@ def main():
                         "params_per_s": host_res["params_per_s"],
                         "fused_kernel_ms": host_res["fused_kernel_ms"]},
         "offload": offload,
+        "wire_bf16": wire_bf16,
+        "all_gather": all_gather,
     }
     print(json.dumps(out))
 
