@@ -1,0 +1,135 @@
+"""Randomized GPU parity: seeded random configurations of the fused step and
+of the reduction, each against the oracle through the C ABI.
+
+Every case draws the worker count (1 to 64), a ragged size, the rank, the
+gradient and parameter dtypes, the precision of the ring's partial sums,
+an accumulated micro-batch input or none, the loss scale (powers of two
+and others), the step index, the AdamW settings (within their valid
+ranges), the gather offset and misaligned gradient starts (so every vector
+width of the kernels runs), and sometimes one non-finite gradient value.
+Bars as in the fixed parity tests: the flag bit-exact; fp32 state within
+1e-6 relative, 16-bit parameters within 1 ulp; the reduced gradient
+bit-exact; inputs never written.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (F32, announce, assert_bits_equal, assert_rel, assert_ulp16, down16,
+                      down32, up16, up32)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+DT = {"bf16": 0, "fp16": 1}
+WIRES = [None, "bf16", "fp16"]
+WIRE_CODE = {None: 0, "bf16": 1, "fp16": 2}
+
+
+@pytest.fixture(scope="module")
+def zs(hip_built):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sharded_mixed_precision_zs_amd import zeroshard
+    return zeroshard
+
+
+def _rand16(rng, n, sigma, dtype):
+    x = (rng.standard_normal(n) * sigma).astype(F32)
+    if dtype == "bf16":
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    return x.astype(np.float16).view(np.uint16)
+
+
+def _draw(rng):
+    world = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 13, 16, 31, 64]))
+    n = int(rng.integers(1, 200_000 if rng.random() < 0.2 else 20_000))
+    scale = float(rng.choice([1.0, 2.0 ** int(rng.integers(0, 17)), 3.0, 1000.0]))
+    gdt = str(rng.choice(["bf16", "fp16"]))
+    if gdt == "fp16":
+        scale = min(scale, 1024.0)   # keeps N(0, 1e-3) * scale sums inside fp16
+    return dict(
+        world=world, n=n, rank=int(rng.integers(0, world)), gdt=gdt,
+        pdt=str(rng.choice(["bf16", "fp16"])), wire=WIRES[int(rng.integers(0, 3))],
+        acc=bool(rng.random() < 0.3), scale=scale, t=int(rng.integers(1, 5000)),
+        lr=float(10 ** rng.uniform(-5, -2)), beta1=float(rng.uniform(0.8, 0.99)),
+        beta2=float(rng.uniform(0.9, 0.9999)), eps=float(rng.choice([0.0, 1e-8, 1e-6])),
+        weight_decay=float(rng.uniform(0.0, 0.1)), off=int(rng.integers(0, 10)),
+        shifts=[int(x) for x in rng.integers(0, 4, world)],
+        inject=bool(rng.random() < 0.1))
+
+
+def _upload_grads(g16, shifts, dtype):
+    """Each worker's buffer starts `shift` elements into its allocation, so
+    some start off the 16-byte boundary."""
+    out = []
+    for g, s in zip(g16, shifts):
+        pad = np.zeros(s, np.uint16)
+        out.append(up16(np.concatenate([pad, g]), dtype)[s:])
+    return out
+
+
+@pytest.mark.parametrize("case", range(200))
+def test_fused_step_random_configuration(zs, case):
+    rng = np.random.default_rng(5000 + case)
+    c = _draw(rng)
+    W, n, gdt, pdt = c["world"], c["n"], c["gdt"], c["pdt"]
+    announce(f"fuzz fused #{case}: " + ", ".join(f"{k}={v}" for k, v in c.items()
+                                                 if k != "shifts"))
+    g16 = [_rand16(rng, n, 1e-3 * c["scale"], gdt) for _ in range(W)]
+    if c["inject"]:
+        bad = 0x7F80 if gdt == "bf16" else 0x7C00
+        g16[int(rng.integers(0, W))][int(rng.integers(0, n))] = bad | (1 if rng.random() < 0.5 else 0)
+    master = (rng.standard_normal(n) * 0.02).astype(F32)
+    m = (rng.standard_normal(n) * 1e-4).astype(F32)
+    v = rng.uniform(0, 1e-6, n).astype(F32)
+    acc = (rng.standard_normal(n) * c["scale"] * 1e-3).astype(F32) if c["acc"] else None
+    hp = dict(lr=c["lr"], beta1=c["beta1"], beta2=c["beta2"], eps=c["eps"],
+              weight_decay=c["weight_decay"])
+    dg = _upload_grads(g16, c["shifts"], gdt)
+    din = [up32(x) for x in (master, m, v)]
+    dout = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    gather = torch.full((n + c["off"] + 3,), 7, dtype=torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    args = zs.StepArgs(dg, c["rank"], n, *din, *dout, gather, c["off"], flag,
+                       zs.hparams(**hp, loss_scale=c["scale"], step_t=c["t"]),
+                       acc_in=up32(acc) if acc is not None else None, grad_dtype=DT[gdt],
+                       param_dtype=DT[pdt], wire_dtype=WIRE_CODE[c["wire"]])
+    zs.zs_step_fused(args)
+    f, mo, mmo, vo, po = oracle.shard_step(g16, c["rank"], gdt, pdt, master, m, v,
+                                           step_t=c["t"], acc_in=acc, loss_scale=c["scale"],
+                                           threads=4, wire=c["wire"], **hp)
+    assert int(flag.item()) == f
+    assert f == (1 if c["inject"] else 0)
+    for d, x in zip(din, (master, m, v)):
+        assert_bits_equal(down32(d), x, "inputs untouched")
+    if f == 0:
+        for got, want, what in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
+            assert_rel(down32(got), want, 1e-6, f"#{case} {what}")
+        gb = down16(gather)
+        off = c["off"]
+        assert np.all(gb[:off] == 7) and np.all(gb[off + n:] == 7)
+        assert_ulp16(gb[off:off + n], po, pdt, 1, f"#{case} params")
+
+
+@pytest.mark.parametrize("case", range(100))
+def test_reduce_random_configuration(zs, case):
+    rng = np.random.default_rng(9000 + case)
+    c = _draw(rng)
+    W, n, gdt = c["world"], c["n"], c["gdt"]
+    announce(f"fuzz reduce #{case}: W={W} n={n} {gdt} wire={c['wire']} acc={c['acc']} "
+             f"scale={c['scale']} inject={c['inject']}")
+    g16 = [_rand16(rng, n, 1e-3 * c["scale"], gdt) for _ in range(W)]
+    if c["inject"]:
+        g16[int(rng.integers(0, W))][int(rng.integers(0, n))] = 0x7F80 if gdt == "bf16" else 0x7C00
+    start = (rng.standard_normal(n) * c["scale"] * 1e-3).astype(F32)
+    out = up32(start) if c["acc"] else torch.zeros(n, dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    zs.zs_reduce_scatter_avg(_upload_grads(g16, c["shifts"], gdt), DT[gdt], W, c["rank"], n,
+                             out, accumulate=c["acc"], overflow_flag=flag,
+                             loss_scale=c["scale"], wire_dtype=WIRE_CODE[c["wire"]])
+    ref = start.copy() if c["acc"] else np.zeros(n, F32)
+    f = oracle.reduce_avg(g16, c["rank"], gdt, ref, c["acc"], c["scale"], wire=c["wire"])
+    assert int(flag.item()) == f
+    assert_bits_equal(down32(out), ref, f"#{case} reduced gradient")
