@@ -347,3 +347,53 @@ def test_hyperparameters_follow_opt_every_step(env):
                 assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), \
                     f"{name} differs from step at step {i + 1}"
     assert all(st.t == len(sched) for st in paths.values())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_schedule_device_equals_host(env, seed):
+    """60 steps with a learning rate that changes every step, dynamic loss
+    scaling with a growth interval of 3 and non-finite gradients injected on
+    about 15 % of the steps (so the scale halves and doubles many times):
+    the queued device-commit flow ends in the same state, parameters and
+    scaler as the host-commit flow, bit for bit."""
+    zs, synth, shard = env
+    rng = np.random.default_rng(700 + seed)
+    world, n, steps = 4, 30_011, 60
+    gdt = ("bf16", "fp16", "bf16")[seed]
+    code = zs.ZS_BF16 if gdt == "bf16" else zs.ZS_FP16
+    init = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    init[2] = np.abs(init[2])
+
+    def make(device_commit):
+        st = shard.ShardState(n, world, 0, 0, n, code, code, shard.AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01),
+                              2.0 ** 10, dynamic=True, growth_interval=3, device_commit=device_commit)
+        for dst, x in zip((st.master, st.m, st.v), init):
+            dst.copy_(torch.from_numpy(x))
+        return st
+
+    host, dev = make(False), make(True)
+    gh = torch.empty((world, n), dtype=torch.int16, device="cuda")
+    gd = torch.empty((world, n), dtype=torch.int16, device="cuda")
+    lhs, lds = [gh[k] for k in range(world)], [gd[k] for k in range(world)]
+    tdt = torch.bfloat16 if gdt == "bf16" else torch.float16
+    announce(f"random schedule, seed {seed} ({gdt})")
+    committed = 0
+    for step in range(steps):
+        lr = float(10 ** rng.uniform(-4, -2.5))
+        host.opt.lr = dev.opt.lr = lr
+        # both flows draw the same gradient, scaled by the host scaler's scale
+        # (the device scaler follows the same rule, checked at the end)
+        g = (torch.from_numpy(rng.standard_normal((world, n)).astype(F32) * 1e-3) *
+             host.loss_scale).to(tdt).view(torch.int16)
+        if rng.random() < 0.15:
+            g[int(rng.integers(0, world)), int(rng.integers(0, n))] = 0x7F80 if gdt == "bf16" else 0x7C00
+        gh.copy_(g)
+        gd.copy_(g)
+        committed += host.step([x.view(tdt) for x in lhs])
+        dev.step_device([x.view(tdt) for x in lds])
+    d = dev.sync_scaler()
+    assert (d.step_t, d.skipped) == (host.scaler.step_t, host.scaler.skipped) == (committed,
+                                                                                 steps - committed)
+    assert d.scale == host.loss_scale and d.clean_steps == host.scaler.clean_steps
+    assert steps - committed >= 3 and committed >= 30   # both paths exercised
+    _same_state(host, dev, f"random schedule {seed}")
