@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ZS_ABI_VERSION 4
+#define ZS_ABI_VERSION 5
 #define ZS_MAX_WORLD 64
 
 typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
@@ -334,10 +334,16 @@ int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host
  *                      powers the next step's bias corrections use; the
  *                      commit multiplies them by beta once per committed
  *                      step, the same repeated products zs_adamw_step forms.
- *   flag             : OR of the running step's overflow checks (kernels
- *                      OR into it; the commit clears it).
+ *   epoch            : steps run on this image (committed + skipped); the
+ *                      commit advances it.
+ *   flag_epoch       : epoch + 1 of the latest step whose check failed
+ *                      (0: none). A fused pass that finds a non-finite
+ *                      value stores its epoch + 1 here, so nothing has to
+ *                      be cleared between steps.
+ *   checked_epoch    : the epoch the latest fused pass ran with; its step
+ *                      is skipped exactly when flag_epoch == checked_epoch
+ *                      + 1.
  *   last_flag        : 1 if the most recent step was skipped, else 0.
- *   arrived          : work counter of the commit kernel, 0 between steps.
  *   bad_scale        : steps that found the scale not finite or not > 0
  *                      (such a step is skipped like an overflow).
  *   last_alpha, last_bc2 : lr/(1-beta1^t) and sqrt(1-beta2^t), rounded to
@@ -350,12 +356,12 @@ typedef struct {
   uint64_t step_t;
   uint64_t skipped;
   double beta1_t, beta2_t;
-  uint32_t flag;
+  uint64_t epoch;
+  uint64_t flag_epoch;
+  uint64_t checked_epoch;
   uint32_t last_flag;
-  uint32_t arrived;
   uint32_t bad_scale;
   float last_alpha, last_bc2;
-  uint32_t reserved[2];
 } zs_device_scaler;
 
 /* Host image of a device scaler that continues from the host scaler `s`
@@ -370,12 +376,16 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
  *   1. the zs_step_fused pass with hp.loss_scale = dev->scale and the bias
  *      corrections from dev->beta1_t / dev->beta2_t (a->hp.loss_scale and
  *      a->hp.step_t are ignored; lr, betas, eps and weight decay come from
- *      a->hp); it ORs into dev->flag (a->overflow_flag is ignored);
- *   2. a commit kernel: when dev->flag is set it copies the input set into
- *      the output set and writes the cast of master_in into the gather
- *      slice, so the output set always holds the state after the step
- *      (updated, or unchanged when skipped); then it applies the
- *      zs_scaler_update rule to *dev, records last_flag and clears flag.
+ *      a->hp); it records the epoch it ran with in dev->checked_epoch and,
+ *      on a non-finite value, stores that epoch + 1 in dev->flag_epoch
+ *      (a->overflow_flag is ignored);
+ *   2. a commit kernel: when dev->flag_epoch == dev->checked_epoch + 1 it
+ *      copies the input set into the output set and writes the cast of
+ *      master_in into the gather slice, so the output set always holds the
+ *      state after the step (updated, or unchanged when skipped); then it
+ *      applies the zs_scaler_update rule to *dev, records last_flag and
+ *      advances dev->epoch. With n == 0 there is no fused pass and the
+ *      step commits.
  * The caller swaps the input and output sets after every call, without
  * looking at the flag. Micro-batches before the last one go through
  * zs_reduce_scatter_avg with no flag: a non-finite partial stays non-finite
@@ -387,9 +397,9 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
  * NULL or not 8-byte-aligned dev, ZS_ERR_ALIAS also for a dev inside an
  * output buffer); argument errors return before anything
  * is enqueued. ZS_ERR_HIP from the second launch leaves the fused pass
- * enqueued without its commit: *dev then still holds that step's flag, and
- * the caller must not swap the sets (rerunning the step is safe, since the
- * fused pass does not write its input set). */
+ * enqueued without its commit: dev->epoch has not advanced, and the caller
+ * must not swap the sets (rerunning the step is safe: the fused pass does
+ * not write its input set and runs again at the same epoch). */
 int zs_step_device(const zs_step_args *a, zs_device_scaler *dev, void *stream, void *ev_start,
                    void *ev_stop);
 

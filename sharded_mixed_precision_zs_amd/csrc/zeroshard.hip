@@ -565,7 +565,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   p.m_out = a->m_out;
   p.v_out = a->v_out;
   p.param_out = param_out;
-  p.flag = dev ? &dev->flag : a->overflow_flag;
+  p.flag = dev ? nullptr : a->overflow_flag;  /* the device flow marks dev->flag_epoch */
 
   const void *p16[ZS_MAX_WORLD + 1];
   for (uint32_t w = 0; w < a->world; ++w) p16[w] = p.g.p[w];

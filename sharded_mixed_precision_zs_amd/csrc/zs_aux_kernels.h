@@ -16,15 +16,17 @@ namespace zs {
 /* ------------------------------------------------------------------------
  * Commit or skip on the device ([Intro] 一.3 items (1) and (3): a step whose
  * unscaled gradient is not finite is skipped and the loss scale adjusted).
- * Runs after the fused pass on the same stream. Every block reads the
- * step's flag; when it is set, the blocks copy the input set into the
- * output set and recast master_in into the gather slice (grid-stride), so
- * the output set holds the state after the step either way. The last block
- * to arrive applies the scaler rule (the host's zs_scaler_update, field for
- * field), advances the beta powers on a commit, records the flag and clears
- * it and the arrival counter for the next step. Same-address atomics
- * serialize in L2 (about 20 ns each), so the grid is a few large blocks:
- * kCommitBlocks arrivals per step.
+ * Runs after the fused pass on the same stream. The fused pass recorded the
+ * epoch it ran with (checked_epoch) and, if it found a non-finite value,
+ * stored that epoch + 1 in flag_epoch; both were written by the previous
+ * kernel, so every block reads them with plain loads and they stay fixed
+ * while this kernel runs. A skipped step's blocks copy the input set into
+ * the output set and recast master_in into the gather slice (grid-stride),
+ * so the output set holds the state after the step either way. Thread 0 of
+ * block 0 alone applies the scaler rule (the host's zs_scaler_update, field
+ * for field), advances the beta powers on a commit and advances the epoch;
+ * no other block reads what it writes, so the grid needs no arrival count,
+ * atomic or fence, and nothing has to be cleared for the next step.
  * ---------------------------------------------------------------------- */
 
 constexpr int kCommitBlock = 1024;  /* threads per commit block     */
@@ -54,8 +56,13 @@ __device__ __forceinline__ void restore_vec(const CommitArgs &c, uint64_t i0) {
 template <int VEC, int PDT>
 __global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
   zs_device_scaler *d = c.dev;
-  const uint32_t f = __hip_atomic_load(&d->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (f) {
+  /* an empty partition had no fused pass (nothing to check, nothing
+   * recorded): it commits at the current epoch; its grid is one block, so
+   * reading the epoch that block 0 advances is safe */
+  const bool empty = c.n == 0;
+  const uint64_t e = empty ? d->epoch : d->checked_epoch;
+  const bool skip = !empty && d->flag_epoch == e + 1;
+  if (skip) {
     const uint64_t stride = (uint64_t)gridDim.x * kCommitBlock * VEC;
     for (uint64_t i0 = ((uint64_t)blockIdx.x * kCommitBlock + threadIdx.x) * VEC; i0 < c.n;
          i0 += stride) {
@@ -66,27 +73,17 @@ __global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
       }
     }
   }
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  /* The scaler fields change only in the last block, after every arrival,
-   * so each block may read them early; reading before the fence keeps the
-   * loads off the last block's path after its atomic. */
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
   const float scale = d->scale;
   const uint32_t clean0 = d->clean_steps, interval = d->growth_interval, dynamic = d->dynamic;
-  const uint64_t step_t = d->step_t, skipped = d->skipped;
-  const double b1t = d->beta1_t, b2t = d->beta2_t;
-  __threadfence();
-  const uint32_t before = atomicAdd(&d->arrived, 1u);
-  if (before != gridDim.x - 1) return;
-  __threadfence();
-  if (f) {
+  if (skip) {
     if (dynamic) d->scale = scale * 0.5f;
     d->clean_steps = 0;
-    d->skipped = skipped + 1;
+    d->skipped = d->skipped + 1;
   } else {
-    d->step_t = step_t + 1;
-    d->beta1_t = b1t * c.beta1;
-    d->beta2_t = b2t * c.beta2;
+    d->step_t = d->step_t + 1;
+    d->beta1_t = d->beta1_t * c.beta1;
+    d->beta2_t = d->beta2_t * c.beta2;
     const uint32_t clean = clean0 + 1;
     if (dynamic && interval && clean >= interval) {
       d->scale = scale * 2.0f;
@@ -95,9 +92,8 @@ __global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
       d->clean_steps = clean;
     }
   }
-  d->last_flag = f ? 1u : 0u;
-  __hip_atomic_store(&d->flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&d->arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  d->last_flag = skip ? 1u : 0u;
+  d->epoch = e + 1;
 }
 
 /* ------------------------------------------------------------------------

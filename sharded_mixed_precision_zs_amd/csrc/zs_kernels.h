@@ -502,7 +502,7 @@ struct FusedArgs {
   uint32_t *flag;
   Scales k;
   AdamK h;
-  zs_device_scaler *dev;  /* non-null: scale and bias corrections come from it */
+  zs_device_scaler *dev;  /* non-null: scale, bias corrections and epoch come from it */
   double lr;              /* for the bias correction formed on the device */
 };
 
@@ -580,10 +580,12 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
 /* Step constants of the device-resident flow: the loss scale and the
  * bias corrections alpha = lr / (1 - beta1^t), bc2 = sqrt(1 - beta2^t)
  * formed in binary64 from the running powers and rounded once to fp32,
- * exactly as the host forms them for an explicit step_t. Block 0 records
- * the pair it used (and counts a bad scale); returns false for a scale that
- * is not finite and > 0. */
-__device__ __forceinline__ bool dev_step_consts(const FusedArgs &p, Scales &sk, AdamK &h) {
+ * exactly as the host forms them for an explicit step_t, and the step's
+ * epoch. Block 0 records the pair it used, counts a bad scale and records
+ * the epoch (checked_epoch, which the commit compares with flag_epoch);
+ * returns false for a scale that is not finite and > 0. */
+__device__ __forceinline__ bool dev_step_consts(const FusedArgs &p, Scales &sk, AdamK &h,
+                                                uint64_t &epoch) {
   zs_device_scaler *d = p.dev;
   const bool ok = dev_scales(d->scale, sk);
   const double b1t = d->beta1_t, b2t = d->beta2_t;
@@ -591,12 +593,23 @@ __device__ __forceinline__ bool dev_step_consts(const FusedArgs &p, Scales &sk, 
   const float bc2 = (float)__builtin_sqrt(1.0 - b2t);
   h.alpha = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(alpha)));
   h.b2 = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(bc2)));
+  epoch = d->epoch;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     d->last_alpha = h.alpha;
     d->last_bc2 = h.b2;
+    d->checked_epoch = epoch;
     if (!ok) d->bad_scale = d->bad_scale + 1u;
   }
   return ok;
+}
+
+/* The device-resident flow's overflow mark: a wave that saw a non-finite
+ * value stores the step's epoch + 1 (one lane; every such store of a step
+ * writes the same value, so no read-modify-write is needed). */
+__device__ __forceinline__ void flag_epoch_mark(uint64_t *flag_epoch, uint64_t value, bool bad) {
+  unsigned long long m = __ballot(bad);
+  if (m && bad && (threadIdx.x & 63u) == (unsigned)(__ffsll(m) - 1))
+    __hip_atomic_store(flag_epoch, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 /* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
@@ -608,7 +621,8 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   const uint64_t full = p.n / tile;  /* blocks past `full` cover the tail */
   Scales sk = p.k;
   AdamK h = p.h;
-  bool bad = p.dev ? !dev_step_consts(p, sk, h) : false;
+  uint64_t epoch = 0;
+  bool bad = p.dev ? !dev_step_consts(p, sk, h, epoch) : false;
   if (blockIdx.x < full) {
     bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE>(p, sk, h, (uint64_t)blockIdx.x * tile);
   } else {
@@ -617,7 +631,8 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
     uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * kBlock + threadIdx.x;
     if (i < p.n) bad |= fused_vec<1, GDT, PDT>(p, sk, h, i);
   }
-  flag_or(p.flag, bad);
+  if (p.dev) flag_epoch_mark(&p.dev->flag_epoch, epoch + 1, bad);
+  else flag_or(p.flag, bad);
 }
 
 }  // namespace zs

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 
 from . import build as _build
 
-ZS_ABI_VERSION = 4
+ZS_ABI_VERSION = 5
 ZS_MAX_WORLD = 64
 ZS_BF16, ZS_FP16 = 0, 1
 ZS_WIRE_FP32, ZS_WIRE_BF16, ZS_WIRE_FP16 = 0, 1, 2
@@ -59,9 +59,9 @@ class zs_device_scaler(C.Structure):
                 ("growth_interval", C.c_uint32), ("dynamic", C.c_uint32),
                 ("step_t", C.c_uint64), ("skipped", C.c_uint64),
                 ("beta1_t", C.c_double), ("beta2_t", C.c_double),
-                ("flag", C.c_uint32), ("last_flag", C.c_uint32), ("arrived", C.c_uint32),
-                ("bad_scale", C.c_uint32), ("last_alpha", C.c_float), ("last_bc2", C.c_float),
-                ("reserved", C.c_uint32 * 2)]
+                ("epoch", C.c_uint64), ("flag_epoch", C.c_uint64), ("checked_epoch", C.c_uint64),
+                ("last_flag", C.c_uint32), ("bad_scale", C.c_uint32),
+                ("last_alpha", C.c_float), ("last_bc2", C.c_float)]
 
 
 def _load():

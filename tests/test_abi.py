@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(zs):
     lib = C.CDLL(zs.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 4
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 5
 
 
 def test_status_strings(zs):
@@ -225,8 +225,9 @@ def test_device_scaler_layout_and_image(zs):
     """The host image of the device scaler: fields copied from the host
     scaler, beta powers formed by t+1 repeated binary64 products, and the
     bias corrections they give equal the oracle's for step t+1."""
-    assert C.sizeof(zs.zs_device_scaler) == 80
-    assert zs.zs_device_scaler.beta1_t.offset == 32 and zs.zs_device_scaler.flag.offset == 48
+    assert C.sizeof(zs.zs_device_scaler) == 88
+    assert zs.zs_device_scaler.beta1_t.offset == 32 and zs.zs_device_scaler.epoch.offset == 48
+    assert zs.zs_device_scaler.checked_epoch.offset == 64 and zs.zs_device_scaler.last_alpha.offset == 80
     import numpy as np
     for b1, b2, lr, t in ((0.9, 0.999, 1e-3, 0), (0.9, 0.95, 3e-4, 7), (0.8, 0.9999, 1e-2, 1234)):
         host = zs.zs_loss_scaler(scale=2.0 ** 15, clean_steps=3, growth_interval=4, dynamic=1,
@@ -234,7 +235,8 @@ def test_device_scaler_layout_and_image(zs):
         img = zs.zs_device_scaler_make(host, b1, b2)
         assert (img.scale, img.clean_steps, img.growth_interval, img.dynamic, img.step_t,
                 img.skipped) == (2.0 ** 15, 3, 4, 1, t, 2)
-        assert (img.flag, img.last_flag, img.arrived, img.bad_scale) == (0, 0, 0, 0)
+        assert (img.epoch, img.flag_epoch, img.checked_epoch, img.last_flag, img.bad_scale) == \
+            (0, 0, 0, 0, 0)
         p1 = p2 = 1.0
         for _ in range(t + 1):
             p1 *= float(np.float32(b1))

@@ -70,7 +70,9 @@ def test_queued_device_steps_equal_host_commit(env, wire):
         dev.step_device(gd)
     assert committed == [True, True, False, True, True, True]
     d = dev.sync_scaler()
-    assert (d.step_t, d.skipped, d.last_flag, d.flag, d.arrived) == (5, 1, 0, 0, 0)
+    # six steps run (epoch 6); the third (epoch 2) overflowed; the last ran at epoch 5
+    assert (d.step_t, d.skipped, d.last_flag) == (5, 1, 0)
+    assert (d.epoch, d.flag_epoch, d.checked_epoch) == (6, 3, 5)
     assert d.scale == wl.loss_scale
     _same_state(host, dev, "queued")
 
@@ -169,6 +171,8 @@ def test_scale_growth_to_infinity_then_skip(env):
 
 
 def test_empty_shard_commits(env):
+    """An empty partition commits, also right after a skipped step (it has no
+    fused pass, so the previous step's overflow mark must not count)."""
     zs, synth, shard = env
     wl = dataclasses.replace(synth.WORKLOADS["mlp9-w3"], phi=3, world=4, name="empty")
     assert wl.n == 1
@@ -177,7 +181,18 @@ def test_empty_shard_commits(env):
     a.n = 0
     zs.zs_step_device(a, st.dev)
     d = st.sync_scaler()
-    assert (d.step_t, d.skipped, d.last_flag, d.flag, d.arrived) == (1, 0, 0, 0, 0)
+    assert (d.step_t, d.skipped, d.last_flag, d.epoch) == (1, 0, 0, 1)
+    # a skipped step on the one-element shard, then an empty one
+    for k in range(wl.world):
+        g[k].fill_(0x7F80)                      # +inf (bf16) from every worker
+    a.n = 1
+    zs.zs_step_device(a, st.dev)
+    d = st.sync_scaler()
+    assert (d.step_t, d.skipped, d.last_flag, d.epoch, d.flag_epoch) == (1, 1, 1, 2, 2)
+    a.n = 0
+    zs.zs_step_device(a, st.dev)
+    d = st.sync_scaler()
+    assert (d.step_t, d.skipped, d.last_flag, d.epoch) == (2, 1, 0, 3)
 
 
 def test_graph_capture_replays_match_eager(env):
@@ -215,8 +230,8 @@ def test_graph_capture_replays_match_eager(env):
         assert float(junk) > 0
         _same_state(eager, graph, f"replay {r}")
         de, dg = eager.sync_scaler(), graph.sync_scaler()
-        assert (dg.step_t, dg.skipped, dg.flag, dg.arrived) == (de.step_t, 0, 0, 0) == \
-            (2 * (r + 1), 0, 0, 0)
+        assert (dg.step_t, dg.skipped, dg.epoch) == (de.step_t, 0, de.epoch) == \
+            (2 * (r + 1), 0, 2 * (r + 1))
 
 
 @pytest.mark.parametrize("off,n", [(0, 40_000), (3, 40_003)])
