@@ -290,6 +290,33 @@ class ShardState:
         zs.zs_step_device(args, self.dev, stream, ev_start, ev_stop)
         self.cur = 1 - self.cur
 
+    def capture(self, worker_grads=None, acc_in=None):
+        """Capture two device-commit steps, one per direction of the ping-pong
+        sets, into a HIP graph and return a function that replays them (two
+        steps per call; the sets end where they started). For shards small
+        enough that launching from Python costs more than the kernels.
+        The graph holds this moment's hyper-parameters and gradient
+        addresses: refill the same gradient buffers between replays, and
+        capture again after changing the settings."""
+        if not self.device_commit:
+            raise RuntimeError("ShardState was built without device_commit=True")
+        if worker_grads is not None:
+            self.bind(worker_grads, acc_in)
+        if self._bound is None:
+            raise RuntimeError("no gradients given and none bound: call bind() first")
+        if (self.opt.beta1, self.opt.beta2) != self._dev_betas:   # waits: not inside a capture
+            self.sync_scaler()
+            zs.device_scaler_write(self.dev, self._scaler_image())
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                self.step_device()
+                self.step_device()
+        torch.cuda.current_stream().wait_stream(side)
+        return graph.replay
+
 
 class OffloadShard:
     """ZeRO-Offload variant of one rank's shard (the DeepSpeed introduction,

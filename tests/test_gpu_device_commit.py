@@ -412,3 +412,29 @@ def test_random_schedule_device_equals_host(env, seed):
     assert d.scale == host.loss_scale and d.clean_steps == host.scaler.clean_steps
     assert steps - committed >= 3 and committed >= 30   # both paths exercised
     _same_state(host, dev, f"random schedule {seed}")
+
+
+def test_shard_capture_replays_match_eager(env):
+    """ShardState.capture(): each replay runs two device steps (one per
+    direction of the ping-pong sets) on whatever the gradient buffers hold;
+    three replays, with the gradients refilled in place before each, equal
+    six eager steps on the same fills, bit for bit."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["mlp9-w3"], phi=3 * 50_001, name="capture")
+    graph, gg = _make(env, wl, True)
+    ref, rg = _make(env, wl, True)
+    announce("ShardState.capture")
+    replay = graph.capture(gg)
+    torch.cuda.synchronize()
+    assert graph.sync_scaler().step_t == 0      # capturing ran nothing
+    for r in range(3):
+        for k in range(wl.world):
+            synth.dev_grad(wl, k, r + 1, 0, 0, gg[k], scale=wl.loss_scale)
+            synth.dev_grad(wl, k, r + 1, 0, 0, rg[k], scale=wl.loss_scale)
+        replay()
+        ref.step_device(rg)
+        ref.step_device(rg)
+    torch.cuda.synchronize()
+    _same_state(ref, graph, "capture replays")
+    d = graph.sync_scaler()
+    assert (d.step_t, d.epoch) == (6, 6) and graph.cur == ref.cur
