@@ -1,5 +1,6 @@
-"""Randomized GPU parity: seeded random configurations of the fused step and
-of the reduction, each against the oracle through the C ABI.
+"""Randomized GPU parity: seeded random configurations of the fused step, of
+the reduction and of the unfused check / update / cast chain, each against
+the oracle through the C ABI.
 
 Every case draws the worker count (1 to 64), a ragged size, the rank, the
 gradient and parameter dtypes, the precision of the ring's partial sums,
@@ -135,3 +136,54 @@ def test_reduce_random_configuration(zs, case):
     f = oracle.reduce_avg(g16, c["rank"], gdt, ref, c["acc"], c["scale"], wire=c["wire"])
     assert int(flag.item()) == f
     assert_bits_equal(down32(out), ref, f"#{case} reduced gradient")
+
+
+@pytest.mark.parametrize("case", range(100))
+def test_unfused_chain_random_configuration(zs, case):
+    """zs_check_overflow, zs_adamw_step and zs_cast_gather on a random
+    averaged gradient partition (sometimes with a non-finite value) at a
+    random misaligned start, with random AdamW settings and loss scale:
+    the flag, the updated state and the 16-bit parameters equal the
+    oracle's; a set flag makes both later calls leave everything as it was."""
+    rng = np.random.default_rng(13000 + case)
+    c = _draw(rng)
+    n, pdt = c["n"], c["pdt"]
+    skew = int(rng.integers(0, 4))            # misaligns every fp32 operand
+    announce(f"fuzz unfused #{case}: n={n} {pdt} scale={c['scale']} t={c['t']} skew={skew} "
+             f"inject={c['inject']}")
+    a = (rng.standard_normal(n) * 1e-3 * c["scale"]).astype(F32)
+    if c["inject"]:
+        a[int(rng.integers(0, n))] = np.inf if rng.random() < 0.5 else np.nan
+    state = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    state[2] = np.abs(state[2])
+
+    def dev32(x):
+        buf = torch.empty(n + skew, dtype=torch.float32, device="cuda")
+        buf[skew:].copy_(torch.from_numpy(x))
+        return buf[skew:]
+
+    da = dev32(a)
+    dst = [dev32(x) for x in state]
+    gather = torch.full((n + c["off"] + 3,), 7, dtype=torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hp = dict(lr=c["lr"], beta1=c["beta1"], beta2=c["beta2"], eps=c["eps"],
+              weight_decay=c["weight_decay"])
+    zs.zs_check_overflow(da, n, c["scale"], flag)
+    zs.zs_adamw_step(*dst, da, n, zs.hparams(**hp, loss_scale=c["scale"], step_t=c["t"]), flag)
+    zs.zs_cast_gather(dst[0], gather, DT[pdt], c["off"], n, flag)
+    f = oracle.check_overflow(a, c["scale"])
+    assert int(flag.item()) == f == (1 if c["inject"] else 0)
+    gb = down16(gather)
+    off = c["off"]
+    assert np.all(gb[:off] == 7) and np.all(gb[off + n:] == 7)
+    if f:
+        for d, x, what in zip(dst, state, ("master", "m", "v")):
+            assert_bits_equal(down32(d), x, f"#{case} skipped {what}")
+        assert np.all(gb == 7)
+        return
+    ref = [x.copy() for x in state]
+    oracle.adamw(*ref, a, c["scale"], t=c["t"], **hp)
+    for d, want, what in zip(dst, ref, ("master", "m", "v")):
+        assert assert_rel(down32(d), want, 1e-6, f"#{case} {what}") == 0
+    want_p = oracle.float_to_half(ref[0], pdt)
+    assert assert_ulp16(gb[off:off + n], want_p, pdt, 1, f"#{case} params") == 0
