@@ -187,3 +187,73 @@ def test_unfused_chain_random_configuration(zs, case):
         assert assert_rel(down32(d), want, 1e-6, f"#{case} {what}") == 0
     want_p = oracle.float_to_half(ref[0], pdt)
     assert assert_ulp16(gb[off:off + n], want_p, pdt, 1, f"#{case} params") == 0
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_all_gather_random_configuration(zs, case):
+    """zs_all_gather_step over a random worker count and flat length (also
+    shorter than W, so some chunks are empty), a random sigma and, for some
+    cases, replicas starting off the 16-byte boundary (the one-element
+    path): every replica equals the oracle's ring simulation after every
+    step."""
+    rng = np.random.default_rng(17000 + case)
+    world = int(rng.choice([2, 3, 4, 5, 7, 8, 13, 16, 31, 64]))
+    phi = int(rng.integers(1, 3 * world if rng.random() < 0.2 else 60_000))
+    sigma = int(rng.integers(0, world))
+    shift = int(rng.integers(0, 4)) if rng.random() < 0.4 else 0
+    announce(f"fuzz all-gather #{case}: W={world} phi={phi} sigma={sigma} shift={shift}")
+    P = -(-phi // world)
+    data = rng.integers(0, 1 << 16, size=(world, phi), dtype=np.uint64).astype(np.uint16)
+    reps = []
+    for k in range(world):
+        buf = torch.zeros(phi + shift, dtype=torch.int16, device="cuda")
+        buf[shift:].copy_(torch.from_numpy(data[k].view(np.int16)))
+        reps.append(buf[shift:].view(torch.bfloat16))
+    ref = np.zeros((world, world * P), F32)
+    ref[:, :phi] = np.stack([oracle.half_to_float(d, "bf16") for d in data])
+    for step in range(1, world):
+        zs.zs_all_gather_step(reps, phi, step, sigma=sigma)
+        want = oracle.ring_all_gather(ref.copy(), sigma, step)[:, :phi]
+        got = np.stack([oracle.half_to_float(down16(r.view(torch.int16)), "bf16") for r in reps])
+        assert_bits_equal(got, want, f"#{case} after step {step}")
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_offload_step_random_configuration(zs, case):
+    """zs_offload_step (GPU check, gradient in pieces, host update per piece,
+    parameters back per piece) against zs_cpu_step on the same random
+    gradient: random size, piece count, thread count, AdamW settings, loss
+    scale and parameter dtype, sometimes a non-finite value (then nothing is
+    written)."""
+    rng = np.random.default_rng(21000 + case)
+    c = _draw(rng)
+    n, pdt = c["n"], c["pdt"]
+    pieces = int(rng.choice([1, 2, 7, 16, 64, 1024]))
+    threads = int(rng.integers(1, 17))
+    announce(f"fuzz offload #{case}: n={n} {pdt} pieces={pieces} threads={threads} "
+             f"scale={c['scale']} inject={c['inject']}")
+    a = (rng.standard_normal(n) * 1e-3 * c["scale"]).astype(F32)
+    if c["inject"]:
+        a[int(rng.integers(0, n))] = np.inf
+    state = [(rng.standard_normal(n) * s).astype(F32) for s in (0.02, 1e-4, 1e-6)]
+    state[2] = np.abs(state[2])
+    hp = zs.hparams(c["lr"], c["beta1"], c["beta2"], c["eps"], c["weight_decay"], c["scale"],
+                    c["t"])
+    ref = [x.copy() for x in state]
+    ref_p = np.full(n, 7, np.uint16)
+    ref_flag = zs.zs_cpu_step(*ref, a, hp, ref_p, DT[pdt], 1)
+    host = [torch.from_numpy(x.copy()) for x in state]
+    tdt = torch.bfloat16 if pdt == "bf16" else torch.float16
+    params_dev = torch.full((n,), 7, dtype=torch.int16, device="cuda")
+    grad_dev = torch.from_numpy(a).cuda()
+    torch.cuda.synchronize()
+    ok = zs.zs_offload_step(grad_dev, torch.empty(n, dtype=torch.float32, pin_memory=True), *host,
+                            torch.empty(n, dtype=tdt, pin_memory=True), params_dev.view(tdt), hp,
+                            torch.zeros(1, dtype=torch.int32, device="cuda"),
+                            torch.zeros(1, dtype=torch.int32, pin_memory=True), DT[pdt], threads,
+                            pieces)
+    torch.cuda.synchronize()
+    assert ok == (ref_flag == 0) == (not c["inject"])
+    for got, want, what in zip(host, ref, ("master", "m", "v")):
+        assert_bits_equal(got.numpy(), want, f"#{case} {what}")
+    assert np.array_equal(down16(params_dev), ref_p)
