@@ -20,6 +20,10 @@ on this host's cores. Beside the headline, on the same workload: the step
 with its decision on the host (`host_commit`), with bf16 partial sums on
 the ring (`wire_bf16`), the ZeRO-Offload variant (`offload`), and one full
 ring all-gather of the 16-bit parameters over W replicas (`all_gather`).
+`copy_ceiling_gbps` is the read + write rate of libzscopy's plain 4 GiB
+copy timed in the same run (the fastest copy shape found on MI355X), and
+`hbm_pct_of_copy_ceiling` the step's HBM rate against it; the runtime's
+device-to-device memcpy is reported beside it (`memcpy_d2d_gbps`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload NAME] [--also NAME,...] [--no-cpu-baseline]
@@ -99,24 +103,54 @@ def recorded_traffic(workload):
     return float(m.group(1)) if m else None
 
 
-def copy_ceiling_gbps(torch, gib=4, reps=10):
-    """Plain device copy (read + write) bandwidth: the practical ceiling."""
-    n = gib * (1 << 30) // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+def _time_copy(torch, copy, nbytes, reps):
+    """Average ms of copy(src, dst) over `reps` calls between two 4-byte-
+    aligned device buffers of nbytes, timed with events on the current
+    stream after three untimed calls."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
-        b.copy_(a)
+        copy(a, b)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(reps):
-        b.copy_(a)
+        copy(a, b)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / reps
     del a, b
     torch.cuda.empty_cache()
-    return 2 * n * 4 / (ms * 1e-3) / 1e9
+    return ms
+
+
+def copy_rates_gbps(torch, gib=4, reps=10):
+    """Read + write rate of two plain device copies of `gib` GiB: the copy
+    kernel of libzscopy (16 bytes per lane, the shape that streamed fastest
+    on MI355X: the practical ceiling) and the runtime's device-to-device
+    memcpy (the copy the counter calibration uses)."""
+    import ctypes
+    from sharded_mixed_precision_zs_amd import build as pkg_build
+    if not os.path.exists(pkg_build.COPY):
+        raise RuntimeError(f"{pkg_build.COPY} is not built: run the package build first")
+    lib = ctypes.CDLL(pkg_build.COPY)  # after torch: it shares torch's HIP runtime
+    lib.zs_copy_ceiling.restype = ctypes.c_int
+    lib.zs_copy_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                    ctypes.c_void_p]
+    lib.zs_copy_last_error.restype = ctypes.c_char_p
+    nbytes = gib << 30
+
+    def kernel_copy(a, b):
+        rc = lib.zs_copy_ceiling(a.data_ptr(), b.data_ptr(), nbytes,
+                                 torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"zs_copy_ceiling returned {rc}: "
+                               f"{lib.zs_copy_last_error().decode()}")
+
+    rates = {}
+    for name, copy in (("ceiling", kernel_copy), ("memcpy", lambda a, b: b.copy_(a))):
+        rates[name] = 2 * nbytes / (_time_copy(torch, copy, nbytes, reps) * 1e-3) / 1e9
+    return rates
 
 
 def pad_elems(n, align_bytes=256):
@@ -444,9 +478,10 @@ def main():
         print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "sweep": sweep}))
         return
-    ceiling = None if args.no_copy_ceiling else copy_ceiling_gbps(torch)
-    if ceiling:
-        log(f"plain copy ceiling {ceiling:.0f} GB/s")
+    copies = {} if args.no_copy_ceiling else copy_rates_gbps(torch)
+    ceiling = copies.get("ceiling")
+    if copies:
+        log(f"plain copy ceiling {ceiling:.0f} GB/s; runtime memcpy {copies['memcpy']:.0f} GB/s")
     wire = {"fp32": 0, "bf16": 1, "fp16": 2}[args.wire]
     main_res = run_workload(args.workload, args.steps, args.warmup, torch, wire)
     log(json.dumps(main_res))
@@ -516,6 +551,7 @@ def main():
         "hbm_gbps": main_res["hbm_gbps"],
         "hbm_pct_of_peak": 100.0 * main_res["hbm_gbps"] / PEAK_HBM_GBPS,
         "copy_ceiling_gbps": ceiling,
+        "memcpy_d2d_gbps": copies.get("memcpy"),
         "hbm_pct_of_copy_ceiling": 100.0 * main_res["hbm_gbps"] / ceiling if ceiling else None,
         "roofline": {"bound": "hbm", "achieved": main_res["fused_gbps"],
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -4,6 +4,8 @@
                          + its host-side offload update (gcc) <- csrc/offload_cpu.cpp
   synth/libzssynth_dev.so   device twin of the input generator (HIP, gfx950)
   synth/libzssynth_host.so  host twin of the input generator (gcc)
+  libzscopy.so           the plain copy the benchmark times as the HBM
+                         ceiling (HIP, gfx950; measurement only) <- csrc/copy_ceiling.hip
 
 Every call compiles from source. The libraries stay in the source tree so a
 snapshot of the tree carries them to the GPU host.
@@ -19,6 +21,7 @@ LIB = os.path.join(PKG, "libzeroshard.so")
 SYNTH = os.path.join(PKG, "synth")
 SYNTH_DEV = os.path.join(SYNTH, "libzssynth_dev.so")
 SYNTH_HOST = os.path.join(SYNTH, "libzssynth_host.so")
+COPY = os.path.join(PKG, "libzscopy.so")
 
 ARCH = os.environ.get("ZS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -72,8 +75,14 @@ def build_synth_host(verbose=False):
     return SYNTH_HOST
 
 
+def build_copy(verbose=False):
+    _hip_lib(os.path.join(PKG, "csrc", "copy_ceiling.hip"), COPY, verbose)
+    return COPY
+
+
 def build_all(verbose=False):
-    return [build_zeroshard(verbose), build_synth_dev(verbose), build_synth_host(verbose)]
+    return [build_zeroshard(verbose), build_synth_dev(verbose), build_synth_host(verbose),
+            build_copy(verbose)]
 
 
 if __name__ == "__main__":
