@@ -478,7 +478,10 @@ def main():
         print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "sweep": sweep}))
         return
-    copies = {} if args.no_copy_ceiling else copy_rates_gbps(torch)
+    copies = {} if args.no_copy_ceiling else side_leg("copy_ceiling",
+                                                       lambda: copy_rates_gbps(torch), torch)
+    if "error" in copies:
+        copies = {}
     ceiling = copies.get("ceiling")
     if copies:
         log(f"plain copy ceiling {ceiling:.0f} GB/s; runtime memcpy {copies['memcpy']:.0f} GB/s")
