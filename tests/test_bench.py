@@ -1,0 +1,64 @@
+"""bench.py's host-side contract, on the CPU: the one-GPU refusal, the HBM
+traffic figure that follows the kernel source, the shard replicas that keep
+a step's inputs out of the last-level cache, and the CPU-baseline record."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402  (imports no GPU library at module level)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"]
+
+
+def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
+    """The committed counter summary is used only while the kernel source
+    hashes to the value it was taken on; any other source gets None."""
+    with open(bench.TRAFFIC_FILE) as f:
+        text = f.read()
+    assert f"kernel_source_sha256_16: {bench.kernel_source_hash()}" in text, \
+        "profiles/fused_step_traffic.md was taken on another kernel source"
+    got = bench.recorded_traffic("gpt2s-w8")
+    assert got is not None and got > 0
+    assert bench.recorded_traffic("no-such-workload") is None
+    other = tmp_path / "zs_kernels.h"
+    other.write_text("// a different kernel source\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(other))
+    assert bench.recorded_traffic("gpt2s-w8") is None
+
+
+@pytest.mark.parametrize("step_bytes,want", [(1, 8), (1 << 20, 8), (200 << 20, 6),
+                                             (653308992, 2), (1 << 30, 1), (18 << 30, 1)])
+def test_replicas_cover_a_gigabyte(step_bytes, want):
+    """Copies cycled per step: enough that the working set reaches 1 GB
+    (past the 256 MB last-level cache), at most 8, at least 1."""
+    got = bench.replicas_for(None, step_bytes)
+    assert got == want
+    assert got == 8 or got * step_bytes >= 1 << 30
+
+
+def test_pad_elems_rounds_rows_to_256_bytes():
+    assert [bench.pad_elems(n) for n in (0, 1, 128, 129, 15554976)] == \
+        [0, 128, 128, 256, 15555072]
+
+
+def test_cpu_baseline_record_on_the_smallest_workload():
+    """The oracle timed on a bounded sample: the record's fields, and a
+    sample no larger than the workload."""
+    r = bench.cpu_baseline("mlp9-w3", target_s=0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "params/s"
+    assert r["value"] > 0 and r["value_1_thread"] > 0
+    assert 1 <= r["cores"] <= 16
+    assert r["sample"].startswith("349526 params of the mlp9-w3 rank-0 partition")
+    assert r["host_cpus_available"] >= 1
