@@ -37,7 +37,8 @@ extern "C" {
  * allocated. Returns 0 when the launch was enqueued; 1 (nothing enqueued)
  * for a null pointer, a base that is not 16-byte aligned, a size that is
  * not a multiple of 16 or too large for one grid, or buffers that overlap;
- * 4 when the launch fails (zs_copy_last_error() has HIP's message). bytes == 0 returns 0 and does nothing. */
+ * 4 when the launch fails (zs_copy_last_error() has HIP's message).
+ * bytes == 0 returns 0 and does nothing. */
 int zs_copy_ceiling(const void *src, void *dst, uint64_t bytes, void *stream) {
   if (!src || !dst || (uintptr_t)src % 16 || (uintptr_t)dst % 16 || bytes % 16) return 1;
   const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
