@@ -532,9 +532,10 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, 
 }
 
 /* One tile of U vectors per thread. MULTI (W > 1) loads the state after
- * the gradient sum, which keeps registers (and so waves in flight) for the
- * gradient streams; with a single worker (W = 1) there is no sum, one
- * gradient load, and the state loads go first. */
+ * the gradient sum: on MI355X that order streamed 5-10 % faster than
+ * loading the state first, registers to spare or not. With a single worker
+ * (W = 1) there is no sum, one gradient load, and the state loads go
+ * first. */
 template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
 __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk, const AdamK &h,
                                            uint64_t base) {
