@@ -1,6 +1,7 @@
-"""Randomized GPU parity: seeded random configurations of the fused step, of
-the reduction and of the unfused check / update / cast chain, each against
-the oracle through the C ABI.
+"""Randomized GPU parity: seeded random configurations of the fused step
+(with the decision on the host and on the device), of the reduction, of the
+unfused check / update / cast chain, of the ring all-gather and of the
+pipelined offload step, each against the oracle through the C ABI.
 
 Every case draws the worker count (1 to 64), a ragged size, the rank, the
 gradient and parameter dtypes, the precision of the ring's partial sums,
@@ -257,3 +258,73 @@ def test_offload_step_random_configuration(zs, case):
     for got, want, what in zip(host, ref, ("master", "m", "v")):
         assert_bits_equal(got.numpy(), want, f"#{case} {what}")
     assert np.array_equal(down16(params_dev), ref_p)
+
+
+@pytest.mark.parametrize("case", range(100))
+def test_device_step_random_configuration(zs, case):
+    """zs_step_device (fused pass + commit kernel, the scale and bias
+    corrections read from a device scaler) over the same random
+    configurations, with non-finite values injected more often: a commit
+    writes the oracle's step and advances the scaler by the commit rule; a
+    skip restores the output set to the input set and the parameters to the
+    cast of the input master, and applies the skip rule."""
+    rng = np.random.default_rng(31000 + case)
+    c = _draw(rng)
+    c["inject"] = bool(rng.random() < 0.35)
+    W, n, gdt, pdt = c["world"], c["n"], c["gdt"], c["pdt"]
+    interval = int(rng.choice([0, 1, 2, 5, 2000]))
+    clean0 = int(rng.integers(0, max(interval, 1)))
+    dynamic = bool(rng.random() < 0.7)
+    announce(f"fuzz device #{case}: " + ", ".join(f"{k}={v}" for k, v in c.items()
+                                                  if k != "shifts")
+             + f", interval={interval}, clean={clean0}, dynamic={dynamic}")
+    g16 = [_rand16(rng, n, 1e-3 * c["scale"], gdt) for _ in range(W)]
+    if c["inject"]:
+        bad = 0x7F80 if gdt == "bf16" else 0x7C00
+        g16[int(rng.integers(0, W))][int(rng.integers(0, n))] = bad | (1 if rng.random() < 0.5 else 0)
+    master = (rng.standard_normal(n) * 0.02).astype(F32)
+    m = (rng.standard_normal(n) * 1e-4).astype(F32)
+    v = rng.uniform(0, 1e-6, n).astype(F32)
+    acc = (rng.standard_normal(n) * c["scale"] * 1e-3).astype(F32) if c["acc"] else None
+    hp = dict(lr=c["lr"], beta1=c["beta1"], beta2=c["beta2"], eps=c["eps"],
+              weight_decay=c["weight_decay"])
+    dg = _upload_grads(g16, c["shifts"], gdt)
+    din = [up32(x) for x in (master, m, v)]
+    dout = [torch.full((n,), 5.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    gather = torch.full((n + c["off"] + 3,), 7, dtype=torch.int16, device="cuda")
+    unused = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ls = zs.zs_loss_scaler(scale=c["scale"], clean_steps=clean0, growth_interval=interval,
+                           dynamic=1 if dynamic else 0, step_t=c["t"] - 1, skipped=3)
+    dev = zs.device_scaler_upload(zs.zs_device_scaler_make(ls, c["beta1"], c["beta2"]))
+    # loss_scale and step_t here are placeholders: the device scaler supplies both
+    args = zs.StepArgs(dg, c["rank"], n, *din, *dout, gather, c["off"], unused,
+                       zs.hparams(**hp, loss_scale=1.0, step_t=1),
+                       acc_in=up32(acc) if acc is not None else None, grad_dtype=DT[gdt],
+                       param_dtype=DT[pdt], wire_dtype=WIRE_CODE[c["wire"]])
+    zs.zs_step_device(args, dev)
+    d = zs.device_scaler_read(dev)
+    f, mo, mmo, vo, po = oracle.shard_step(g16, c["rank"], gdt, pdt, master, m, v,
+                                           step_t=c["t"], acc_in=acc, loss_scale=c["scale"],
+                                           threads=4, wire=c["wire"], **hp)
+    assert f == (1 if c["inject"] else 0)
+    assert (d.last_flag, d.epoch) == (f, 1)
+    for x, want in zip(din, (master, m, v)):
+        assert_bits_equal(down32(x), want, "inputs untouched")
+    gb = down16(gather)
+    off = c["off"]
+    assert np.all(gb[:off] == 7) and np.all(gb[off + n:] == 7)
+    if f == 0:
+        for got, want, what in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
+            assert_bits_equal(down32(got), want, f"#{case} {what}")
+        assert np.array_equal(gb[off:off + n], po)
+        clean = clean0 + 1
+        grow = dynamic and interval and clean >= interval
+        assert d.step_t == c["t"] and d.skipped == 3
+        assert d.clean_steps == (0 if grow else clean)
+        assert d.scale == np.float32(c["scale"] * 2.0 if grow else c["scale"])
+    else:
+        for got, want, what in zip(dout, (master, m, v), ("master", "m", "v")):
+            assert_bits_equal(down32(got), want, f"#{case} restored {what}")
+        assert np.array_equal(gb[off:off + n], oracle.float_to_half(master, pdt))
+        assert d.step_t == c["t"] - 1 and d.skipped == 4 and d.clean_steps == 0
+        assert d.scale == np.float32(c["scale"] * 0.5 if dynamic else c["scale"])
