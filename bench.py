@@ -443,18 +443,22 @@ def side_leg(name, fn, torch):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=320)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--gpus", type=int, default=1,
+                    help="GPUs to use; only 1 is supported (one rank's shard on one MI355X)")
+    ap.add_argument("--steps", type=int, default=320, help="timed steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps before the timed ones")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="headline workload (a key of synth.WORKLOADS)")
     ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="comma-separated extra workloads reported under 'other_workloads'")
     ap.add_argument("--wire", choices=["fp32", "bf16", "fp16"], default="fp32",
                     help="precision of the ring's partial sums (default fp32)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (cpu_baseline)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host update) leg")
-    ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip timing the plain copies (copy_ceiling_gbps, memcpy_d2d_gbps)")
     ap.add_argument("--sweep-world", default="",
                     help="comma-separated W values: time the fused step at one shard size for "
                          "each and print that table as the JSON line instead")
