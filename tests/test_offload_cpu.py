@@ -160,3 +160,44 @@ def test_bias_correction_powers_continue_exactly(zs):
                      HP["weight_decay"], t)
         for x, y in zip(got, want):
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), t
+
+
+def test_concurrent_callers_share_the_pool_safely(zs):
+    """Host threads calling zs_cpu_step at the same time (ctypes releases the
+    GIL, so the calls overlap) on disjoint buffers: the library serialises
+    them on its one worker pool, and every result equals the oracle's."""
+    import threading
+
+    n, callers, rounds = 200_003, 6, 4
+    rng = np.random.default_rng(77)
+    jobs = []
+    for k in range(callers):
+        master, m, v, a = _inputs(rng, n, 1024.0)
+        jobs.append(dict(inp=(master, m, v, a), got=[master.copy(), m.copy(), v.copy()],
+                         params=np.zeros(n, np.uint16), t=1 + k))
+    errors = []
+
+    def work(job):
+        try:
+            for r in range(rounds):
+                hp = zs.hparams(**HP, loss_scale=1024.0, step_t=job["t"] + r)
+                if zs.zs_cpu_step(*job["got"], job["inp"][3], hp, job["params"], zs.ZS_BF16,
+                                  1 + job["t"] % 4) != 0:
+                    errors.append("flag")
+        except Exception as e:  # noqa: BLE001 (reported below)
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for job in jobs:
+        master, m, v, a = (x.copy() for x in job["inp"])
+        for r in range(rounds):
+            oracle.adamw(master, m, v, a, 1024.0, HP["lr"], HP["beta1"], HP["beta2"], HP["eps"],
+                         HP["weight_decay"], job["t"] + r)
+        for x, y in zip(job["got"], (master, m, v)):
+            assert _nan_class_equal(x, y)
+        assert np.array_equal(job["params"], oracle.float_to_half(master, "bf16"))
