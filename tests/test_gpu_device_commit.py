@@ -438,3 +438,44 @@ def test_shard_capture_replays_match_eager(env):
     _same_state(ref, graph, "capture replays")
     d = graph.sync_scaler()
     assert (d.step_t, d.epoch) == (6, 6) and graph.cur == ref.cur
+
+
+def test_two_shards_on_two_streams_equal_each_alone(env):
+    """Two shards with their own device scalers stepping on two streams at
+    the same time (gradients generated and steps queued on each shard's
+    stream, launches interleaved, no synchronization in between; one shard
+    takes a skip): each ends bit-identical to the same shard stepped alone on
+    the default stream. Disjoint buffers on different streams share nothing
+    in the library."""
+    zs, synth, shard = env
+    base = synth.WORKLOADS["gpt2s-w8"]
+    wls = [dataclasses.replace(base, phi=8 * 300_007, steps=5, inject_steps=(2,),
+                               inject_rate=1e-3, name="stream-a", seed=21),
+           dataclasses.replace(base, phi=8 * 200_003, steps=5, name="stream-b", seed=22)]
+    announce("two shards on two streams against each alone")
+
+    def run(wl, st, grads, stream=None):
+        for step in range(1, wl.steps + 1):
+            for k in range(wl.world):
+                synth.dev_grad(wl, k, step, 0, 0, grads[k], scale=wl.loss_scale, stream=stream)
+            st.step_device(grads, stream=stream)
+
+    alone = []
+    for wl in wls:
+        st, g = _make(env, wl, True)
+        run(wl, st, g)
+        alone.append(st)
+    pairs = [_make(env, wl, True) for wl in wls]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for step in range(1, 6):
+        for wl, (st, g), s in zip(wls, pairs, streams):
+            for k in range(wl.world):
+                synth.dev_grad(wl, k, step, 0, 0, g[k], scale=wl.loss_scale, stream=s)
+            st.step_device(g, stream=s)
+    torch.cuda.synchronize()
+    for (st, _), ref, wl in zip(pairs, alone, wls):
+        d, r = st.sync_scaler(), ref.sync_scaler()
+        assert (d.step_t, d.skipped, d.epoch) == (r.step_t, r.skipped, r.epoch)
+        assert d.skipped == (1 if wl.inject_steps else 0)
+        _same_state(ref, st, wl.name)
