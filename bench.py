@@ -4,29 +4,36 @@ One step = one pass of the whole shard step over one batch of synthetic
 gradients already resident in HBM: ring-order W-way fp32 sum, average,
 unscale, overflow check, AdamW, cast into the gather buffer (the fused
 kernel), then the commit or skip with its loss-scaler update on the device
-(zs_step_device: the commit kernel), steps queued back to back. The same
-step with the decision taken on the host (zs_step_commit: 4-byte flag
-readback, scaler on the host, one wait per step) is reported beside it
-under `host_commit`. Inputs come from the seeded generator, on the device.
+(zs_step_device: the commit kernel), steps queued back to back. Inputs come
+from the seeded generator, on the device.
 
-Prints ONE JSON line (rank 0). `value` is parameters updated per second of
-the chosen workload; the HBM side of the metric is in `hbm_gbps`,
-`hbm_pct_of_peak` and `roofline`. `roofline.achieved` is the algorithmic
-bytes of one fused launch ((2W + 12) read + 14 written per parameter, plus
-4 read per parameter for an accumulated micro-batch input) divided by that
-launch's average duration measured with HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
-on this host's cores. Beside the headline, on the same workload: the step
-with its decision on the host (`host_commit`), with bf16 partial sums on
-the ring (`wire_bf16`), the ZeRO-Offload variant (`offload`), and one full
-ring all-gather of the 16-bit parameters over W replicas (`all_gather`).
-`copy_ceiling_gbps` is the read + write rate of libzscopy's plain 4 GiB
-copy timed in the same run (the fastest copy shape found on MI355X), and
-`hbm_pct_of_copy_ceiling` the step's HBM rate against it; the runtime's
-device-to-device memcpy is reported beside it (`memcpy_d2d_gbps`).
+The headline workload is the 7B model's full state on one rank (W = 1,
+7e9 parameters, 196 GB moved per step); the 7.5B model's rank-0 shard at
+W = 64 and the other workloads are reported in the same line, each with its
+own roofline object (`roofline_by_workload`).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload NAME] [--also NAME,...] [--no-cpu-baseline]
+Prints ONE JSON line. `value` is parameters updated per second of the
+headline workload: n / (wall time of K steps queued back to back, with no
+timing events among them) -- `ms_per_step`. `roofline.achieved` is the
+algorithmic bytes of one fused launch ((2W + 12) read + 14 written per
+parameter, plus 4 read per parameter for an accumulated micro-batch input)
+divided by that launch's average duration, measured with HIP events that the
+library records on the launch stream right around the kernel, in a second
+pass of K steps. `roofline.traffic` is the HBM bytes per launch from the
+committed rocprofv3 request-counter passes (profiles/fused_step_traffic.md),
+when they were taken on the current kernel source. `ceilings` are the rates
+of libzscopy's measurement kernels in the same run: a plain copy, read-only
+and write-only streams, and the step's own mix of streams with no arithmetic
+(the stream probe). `cpu_baseline` times the CPU oracle on a bounded sample of
+the headline workload on this host's cores.
+
+Beside the headline: the step with its decision on the host (`host_commit`),
+with bf16 partial sums on the ring (`wire_bf16`, on the W = 64 shard), the
+ZeRO-Offload variant (`offload`), and a full ring all-gather of the 16-bit
+parameters over W replicas (`all_gather`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--also NAME,...] [--no-cpu-baseline] [--no-ceilings] ...
 """
 import argparse
 import hashlib
@@ -39,14 +46,15 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak (vendor figure)
-DEFAULT_WORKLOAD = "gpt2s-w8"   # GPT-2-small-shaped flat model, W = 8
-DEFAULT_ALSO = "7p5b-shard-w64,7b-full-w1,1p3b-w4-acc4-fp16"
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E peak (vendor figure)
+DEFAULT_WORKLOAD = "7b-full-w1"  # the 7B model's full state on one rank, W = 1
+DEFAULT_ALSO = "7p5b-shard-w64,1p3b-w4-acc4-fp16,gpt2s-w8,mlp9-w3"
+WIRE_WORKLOAD = "7p5b-shard-w64"       # the bf16-wire leg: the most partial sums
+HOST_LEG_WORKLOAD = "gpt2s-w8"         # the ZeRO-Offload leg (host memory bound)
+ALL_GATHER_WORKLOADS = ("1p3b-w4-acc4-fp16", "gpt2s-w8")
 KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zs_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_traffic.md")
-ALL_GATHER_LARGE = "1p3b-w4-acc4-fp16"  # 4 replicas of 1.3e9 params: beyond any cache
-EVENT_EVERY_MAX = 16   # at most one launch in 16 is bracketed by HIP events
-EVENT_SAMPLES = 20     # ... and at least this many are, where the steps allow
+CPU_WINDOW = 1 << 26     # oracle window for workloads too large for host memory
 METRIC = "params updated/sec per ZeRO-2 shard step + achieved HBM GB/s (% of peak)"
 
 
@@ -55,44 +63,15 @@ def log(msg):
     sys.stderr.flush()
 
 
-class HipEvents:
-    """Raw hipEvent_t handles (libamdhip64 through ctypes). The library's
-    zs_step_commit records them on the launch stream immediately before and
-    after the fused kernel."""
-
-    def __init__(self):
-        import ctypes
-        self.C = ctypes
-        self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
-
-    def create(self):
-        ev = self.C.c_void_p()
-        if self.lib.hipEventCreate(self.C.byref(ev)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        return ev.value
-
-    def elapsed_ms(self, start, stop):
-        ms = self.C.c_float()
-        if self.lib.hipEventElapsedTime(self.C.byref(ms), start, stop) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def destroy(self, ev):
-        self.lib.hipEventDestroy(ev)
-
-
 def kernel_source_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def recorded_traffic(workload):
-    """HBM bytes per fused launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+    """HBM bytes per fused launch of `workload` from the committed rocprofv3
+    request-counter summary, if it was taken on the current kernel source;
+    else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
@@ -103,55 +82,152 @@ def recorded_traffic(workload):
     return float(m.group(1)) if m else None
 
 
-def _time_copy(torch, copy, nbytes, reps):
-    """Average ms of copy(src, dst) over `reps` calls between two 4-byte-
-    aligned device buffers of nbytes, timed with events on the current
-    stream after three untimed calls."""
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        copy(a, b)
+def fused_bytes_per_param(world, accum):
+    """Algorithmic (read, write) bytes per parameter of one fused launch."""
+    return 2 * world + 12 + (4 if accum > 1 else 0), 14
+
+
+def fused_instance(wl, wire=0):
+    """Template instance of zs::fused_kernel that a 16-byte-aligned shard of
+    this workload launches (the name rocprofv3 shows)."""
+    multi = wl.world > 1
+    return (f"zs::fused_kernel<8, {2 if multi else 1}, {str(multi).lower()}, "
+            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}>")
+
+
+def timing_events(torch, count):
+    """`count` pairs of timing events, each recorded once so that its raw
+    hipEvent_t exists (the library re-records it around the kernel)."""
+    pairs = []
+    for _ in range(count):
+        pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for ev in pair:
+            ev.record()
+        pairs.append(pair)
+    torch.cuda.synchronize()
+    return pairs
+
+
+# ---- ceilings: libzscopy's measurement kernels -------------------------------
+
+def _copylib():
+    import ctypes as C
+    from sharded_mixed_precision_zs_amd import build as pkg_build
+    if not os.path.exists(pkg_build.COPY):
+        raise RuntimeError(f"{pkg_build.COPY} is not built: run the package build first")
+    lib = C.CDLL(pkg_build.COPY)
+    lib.zs_copy_ceiling.restype = C.c_int
+    lib.zs_copy_ceiling.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]
+    lib.zs_copy_last_error.restype = C.c_char_p
+    lib.zs_stream_probe.restype = C.c_int
+    lib.zs_stream_probe.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_uint32, C.c_void_p,
+                                    C.c_uint32, C.c_void_p, C.c_uint64, C.c_uint32, C.c_uint32,
+                                    C.c_void_p, C.c_uint32, C.c_void_p]
+    return lib
+
+
+def _time_calls(torch, fn, reps, warm=2):
+    """Average ms of fn() over `reps` calls on the current stream, timed with
+    events after `warm` untimed calls."""
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(reps):
-        copy(a, b)
+        fn()
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    del a, b
-    torch.cuda.empty_cache()
-    return ms
+    return s.elapsed_time(e) / reps
 
 
 def copy_rates_gbps(torch, gib=4, reps=10):
-    """Read + write rate of two plain device copies of `gib` GiB: the copy
-    kernel of libzscopy (16 bytes per lane, the shape that streamed fastest
-    on MI355X: the practical ceiling) and the runtime's device-to-device
-    memcpy (the copy the counter calibration uses)."""
-    import ctypes
-    from sharded_mixed_precision_zs_amd import build as pkg_build
-    if not os.path.exists(pkg_build.COPY):
-        raise RuntimeError(f"{pkg_build.COPY} is not built: run the package build first")
-    lib = ctypes.CDLL(pkg_build.COPY)  # after torch: it shares torch's HIP runtime
-    lib.zs_copy_ceiling.restype = ctypes.c_int
-    lib.zs_copy_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
-                                    ctypes.c_void_p]
-    lib.zs_copy_last_error.restype = ctypes.c_char_p
+    """Read + write rate of two plain device copies of `gib` GiB: libzscopy's
+    copy kernel (16 bytes per lane, the copy shape that streamed fastest on
+    MI355X) and the runtime's device-to-device memcpy."""
+    lib = _copylib()
     nbytes = gib << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
 
-    def kernel_copy(a, b):
+    def kernel_copy():
         rc = lib.zs_copy_ceiling(a.data_ptr(), b.data_ptr(), nbytes,
                                  torch.cuda.current_stream().cuda_stream)
         if rc != 0:
             raise RuntimeError(f"zs_copy_ceiling returned {rc}: "
                                f"{lib.zs_copy_last_error().decode()}")
 
-    rates = {}
-    for name, copy in (("ceiling", kernel_copy), ("memcpy", lambda a, b: b.copy_(a))):
-        rates[name] = 2 * nbytes / (_time_copy(torch, copy, nbytes, reps) * 1e-3) / 1e9
+    rates = {name: 2 * nbytes / (_time_calls(torch, fn, reps) * 1e-3) / 1e9
+             for name, fn in (("ceiling", kernel_copy), ("memcpy", lambda: b.copy_(a)))}
+    del a, b
+    torch.cuda.empty_cache()
     return rates
 
+
+# (name, 16-bit input streams, fp32 inputs, fp32 outputs, 16-bit output,
+#  vectors per thread, blocks per CU (0: no cap), shard size)
+N_W1 = 1 << 30                 # 1 G parameters: 28 GB for the W = 1 mix
+N_W64 = 117_186_560            # the 7.5B shard rounded down to the 4096-element tile
+PROBES = (
+    ("step_mix_w1", 1, 3, 3, True, 1, 2, N_W1),
+    ("read_only_w1_streams", 1, 3, 0, False, 1, 2, N_W1),
+    ("write_only_w1_streams", 0, 0, 3, True, 1, 2, N_W1),
+    ("step_mix_w64", 64, 3, 3, True, 2, 5, N_W64),
+    ("step_mix_w64_uncapped", 64, 3, 3, True, 2, 0, N_W64),
+    ("read_only_w64_streams", 64, 3, 0, False, 2, 5, N_W64),
+    ("read_only_w64_grads", 64, 0, 0, False, 2, 0, N_W64),
+    ("w64_grads_plus_param_store", 64, 0, 0, True, 2, 0, N_W64),
+    ("w64_reduce_shape", 64, 0, 1, False, 2, 0, N_W64),
+)
+
+
+def stream_ceilings(torch, reps=8, names=None):
+    """Rates of the stream probe in the shapes above: for each, HBM bytes
+    per launch (2 per 16-bit stream element, 4 per fp32 stream element) over
+    the average launch time. step_mix_w1 and step_mix_w64 are the fused
+    step's own streams (W = 1 with 2 blocks per CU; W = 64 with 5, the
+    residency the register count gives the fused kernel), with integer folds
+    in place of the arithmetic."""
+    import ctypes as C
+    lib = _copylib()
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, w, nin, nout, p16, vecs, cap, n in PROBES:
+        if names is not None and name not in names:
+            continue
+        row = -(-n // 128) * 128
+        g = torch.empty((max(w, 1), row), dtype=torch.int16, device="cuda").random_()
+        ins = [torch.empty(n, dtype=torch.int32, device="cuda").random_() for _ in range(nin)]
+        outs = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(nout)]
+        o16 = torch.empty(n, dtype=torch.int16, device="cuda") if p16 else None
+        gp = (C.c_void_p * 64)(*[g[k].data_ptr() for k in range(w)])
+        ip = (C.c_void_p * 3)(*[t.data_ptr() for t in ins])
+        op = (C.c_void_p * 3)(*[t.data_ptr() for t in outs])
+
+        def launch():
+            rc = lib.zs_stream_probe(gp, w, ip, nin, op, nout,
+                                     o16.data_ptr() if p16 else None, n, vecs, cap,
+                                     sink.data_ptr(), 0x6D2B79F5,
+                                     torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"zs_stream_probe({name}) returned {rc}: "
+                                   f"{lib.zs_copy_last_error().decode()}")
+
+        ms = _time_calls(torch, launch, reps)
+        rd, wr = 2 * w + 4 * nin, 4 * nout + (2 if p16 else 0)
+        gbps = (rd + wr) * n / (ms * 1e-3) / 1e9
+        out[name] = dict(gbps=gbps, frac_of_peak=gbps / PEAK_HBM_GBPS, ms=ms, n=n,
+                         read_bytes_per_param=rd, write_bytes_per_param=wr,
+                         blocks_per_cu=cap or None,
+                         kernel=f"stream_probe<{vecs}, {str(w > 1).lower()}, {nin}, {nout}, "
+                                f"{str(p16).lower()}>")
+        log(f"ceiling {name}: {gbps:.0f} GB/s ({ms:.3f} ms)")
+        del g, ins, outs, o16
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---- the shard step ------------------------------------------------------------
 
 def pad_elems(n, align_bytes=256):
     """Row length (16-bit elements) rounded up to a multiple of align_bytes."""
@@ -162,21 +238,24 @@ def pad_elems(n, align_bytes=256):
 def replicas_for(wl, bytes_per_step):
     """Independent shard copies cycled through so a step never finds its
     inputs in the 256 MB last-level cache (whole working set >= 1 GB)."""
-    return max(1, min(8, -(-(1 << 30) // max(bytes_per_step, 1))))
+    return max(1, min(128, -(-(1 << 30) // max(bytes_per_step, 1))))
 
 
-def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
+def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_pass=True):
+    """Time `steps` steps of one workload queued back to back (no events),
+    then (event_pass) the fused kernel alone over another `steps` steps,
+    each bracketed by HIP events."""
     from sharded_mixed_precision_zs_amd import shard, synth
 
     wl = synth.WORKLOADS[name]
     n, W, A = wl.n, wl.world, wl.accum
     rd, wr = wl.bytes_per_param()
-    # bytes of the fused launch alone (the last micro-batch) and of the step
-    fused_rd = 2 * W + 12 + (4 if A > 1 else 0)
-    fused_bytes = (fused_rd + 14) * n
+    frd, fwr = fused_bytes_per_param(W, A)
+    fused_bytes = (frd + fwr) * n
     step_bytes = (rd + wr) * n
     R = replicas_for(wl, step_bytes)
-    log(f"{name}: n={n} W={W} A={A} replicas={R} step bytes={step_bytes / 1e9:.3f} GB")
+    log(f"{name}: n={n} W={W} A={A} replicas={R} step bytes={step_bytes / 1e9:.3f} GB "
+        f"commit={'device' if device_commit else 'host'} wire={wire}")
     opt = shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay)
     reps = []
     for r in range(R):
@@ -190,18 +269,18 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
         views = [[grads[j, k, :n] for k in range(W)] for j in range(A)]
         for j in range(A):
             for k in range(W):
-                synth.dev_grad(wl, k, 1 + r, j, wl.offset, views[j][k], scale=wl.loss_scale)
+                synth.dev_grad(wl, k, 1 + r % max(1, wl.steps), j, wl.offset, views[j][k],
+                               scale=wl.loss_scale)
         reps.append((st, views))
     for st, g in reps:
         st.bind(g[A - 1], acc_in=st.acc if A > 1 else None)
     torch.cuda.synchronize()
-    hip = HipEvents()
 
     def one_step(i, events=None):
         st, g = reps[i % R]
         for j in range(A - 1):
             st.reduce_micro(g[j], first=(j == 0))
-        ev = events if events is not None else (None, None)
+        ev = (events[0].cuda_event, events[1].cuda_event) if events else (None, None)
         if device_commit:
             st.step_device(ev_start=ev[0], ev_stop=ev[1])
             return 0
@@ -212,45 +291,53 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True):
 
     for i in range(warmup):
         one_step(i)
-    torch.cuda.synchronize()
-    # HIP events bracket the fused kernel on every k-th timed step: each
-    # record puts a gap of a few us between kernels, which the step time
-    # would carry, so k is as large as EVENT_SAMPLES samples allow (up to 16)
-    every = max(1, min(EVENT_EVERY_MAX, steps // EVENT_SAMPLES))
-    timed = list(range(0, steps, every))
-    evs = {i: (hip.create(), hip.create()) for i in timed}
     committed = -committed_so_far()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        committed += one_step(warmup + i, evs.get(i))
+        committed += one_step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     committed += committed_so_far()
-    kern_ms = [hip.elapsed_ms(*evs[i]) for i in timed]
-    for s, e in evs.values():
-        hip.destroy(s)
-        hip.destroy(e)
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    kern_med = sorted(kern_ms)[len(kern_ms) // 2]
     ms_per_step = elapsed * 1e3 / steps
     res = dict(workload=name, commit="device" if device_commit else "host", n=n, world=W,
-               accum=A, replicas=R,
-               ms_per_step=ms_per_step, params_per_s=n / (ms_per_step * 1e-3),
-               step_bytes=step_bytes, hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9,
-               fused_kernel_ms=kern_avg, fused_bytes=fused_bytes,
-               fused_gbps=fused_bytes / (kern_avg * 1e-3) / 1e9, committed=committed,
-               kernel_ms_min=min(kern_ms), kernel_ms_max=max(kern_ms),
-               kernel_ms_median=kern_med, kernel_samples=len(kern_ms), event_every=every)
+               accum=A, replicas=R, wire=wire, ms_per_step=ms_per_step,
+               params_per_s=n / (ms_per_step * 1e-3), step_bytes=step_bytes,
+               hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9, committed=committed,
+               fused_bytes=fused_bytes)
+    if event_pass:
+        evs = timing_events(torch, steps)
+        for i in range(steps):
+            one_step(warmup + steps + i, evs[i])
+        torch.cuda.synchronize()
+        kern = sorted(s.elapsed_time(e) for s, e in evs)
+        avg = sum(kern) / len(kern)
+        res.update(fused_kernel_ms=avg, kernel_ms_median=kern[len(kern) // 2],
+                   kernel_ms_min=kern[0], kernel_ms_max=kern[-1], kernel_samples=len(kern),
+                   fused_gbps=fused_bytes / (avg * 1e-3) / 1e9)
     del reps
     torch.cuda.empty_cache()
     return res
 
 
+def roofline_of(res, wl, wire=0):
+    """The roofline object of one workload's fused kernel."""
+    traffic = recorded_traffic(res["workload"]) if wire == 0 else None
+    rd, wr = fused_bytes_per_param(wl.world, wl.accum)
+    return {"bound": "hbm", "achieved": res["fused_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": res["fused_gbps"] / PEAK_HBM_GBPS, "traffic": traffic,
+            "traffic_over_algorithmic": traffic / res["fused_bytes"] if traffic else None,
+            "kernel": fused_instance(wl, wire), "kernel_ms": res["fused_kernel_ms"],
+            "kernel_ms_median": res["kernel_ms_median"],
+            "kernel_samples": res["kernel_samples"], "event_every": 1,
+            "algorithmic_bytes_per_launch": res["fused_bytes"],
+            "bytes_per_param": {"read": rd, "write": wr}, "shard_params": wl.n}
+
+
 def run_offload(name, steps, warmup, torch):
-    """The ZeRO-Offload variant on the same workload: the ring reduction on
-    the GPU, the fp32 gradient to the host, AdamW + cast on the host cores,
-    the 16-bit parameters back (reported beside the fused GPU step)."""
+    """The ZeRO-Offload variant on a workload: the ring reduction on the GPU,
+    the fp32 gradient to the host, AdamW + cast on the host cores, the 16-bit
+    parameters back."""
     from sharded_mixed_precision_zs_amd import shard, synth
 
     wl = synth.WORKLOADS[name]
@@ -312,15 +399,7 @@ def run_all_gather(name, reps, torch):
         for step in range(1, W):
             zs.zs_all_gather_step(replicas, phi, step, sigma=0)
 
-    gather()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        gather()
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
+    ms = _time_calls(torch, gather, reps, warm=1)
     moved = 4 * (W - 1) * sum(min(chunk, max(0, phi - c * chunk)) for c in range(W))
     del buf, replicas
     torch.cuda.empty_cache()
@@ -339,6 +418,8 @@ def run_all_gather(name, reps, torch):
     return out
 
 
+# ---- the CPU oracle as a baseline ------------------------------------------------
+
 def cpu_model():
     """The host CPU's model string (Linux), or None."""
     try:
@@ -351,8 +432,19 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(name, target_s=25.0):
-    """The CPU oracle (as it stands) on a bounded sample of the workload."""
+def cpu_windows(wl, cap):
+    """Flat starts (within the shard) and size of the oracle's sample: the
+    whole shard when it fits `cap` parameters, else three windows of
+    CPU_WINDOW parameters at the head, the middle and the tail."""
+    if wl.n <= cap:
+        return [0], wl.n
+    L = min(CPU_WINDOW, cap // 3)
+    return [0, (wl.n // 2) // 4096 * 4096, wl.n - L], L
+
+
+def cpu_baseline(name, target_s=15.0):
+    """The CPU oracle (as it stands) on a bounded sample of the workload:
+    params/s, the step's rate if the whole shard ran at the sample's rate."""
     import numpy as np
 
     import oracle
@@ -362,45 +454,60 @@ def cpu_baseline(name, target_s=25.0):
     threads = min(16, len(os.sched_getaffinity(0)))
     kw = dict(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
               weight_decay=wl.weight_decay, loss_scale=wl.loss_scale, step_t=1)
+    # host memory bound on the sample: ~6 GB of generated inputs and state
+    cap = (6 << 30) // (2 * wl.world * wl.accum + 30)
+    starts, L = cpu_windows(wl, cap)
+    extrapolated = len(starts) > 1 or L < wl.n
 
-    def timed(ns, reps, threads=threads):
-        # distinct inputs for up to the workload's step count, then cycled
-        distinct = []
-        for r in range(min(reps, wl.steps)):
-            micro = [[synth.host_grad(wl, k, 1 + r, j, wl.offset, ns) for k in range(wl.world)]
-                     for j in range(wl.accum)]
-            distinct.append(micro)
-        master, m, v = synth.host_state(wl, wl.offset, ns)
-        acc = np.empty(ns, np.float32) if wl.accum > 1 else None
+    def inputs(first, ns, r):
+        micro = [[synth.host_grad(wl, k, 1 + r, j, wl.offset + first, ns)
+                  for k in range(wl.world)] for j in range(wl.accum)]
+        return micro, synth.host_state(wl, wl.offset + first, ns)
+
+    def timed(sets, reps, threads):
+        acc = np.empty(sets[0][1][0].size, np.float32) if wl.accum > 1 else None
         t0 = time.perf_counter()
         for r in range(reps):
-            micro = distinct[r % len(distinct)]
+            micro, (master, m, v) = sets[r % len(sets)]
             for j, parts in enumerate(micro[:-1]):
                 oracle.reduce_avg(parts, wl.rank, wl.grad_dtype, acc, j > 0, wl.loss_scale)
             oracle.shard_step(micro[-1], wl.rank, wl.grad_dtype, wl.param_dtype, master, m, v,
                               acc_in=acc, threads=threads, **kw)
         return time.perf_counter() - t0
 
-    probe = min(wl.n, 1 << 21)
-    dt = timed(probe, 2) / 2
-    # host memory bound on the sample: ~6 GB of generated inputs and state
-    cap = (6 << 30) // (2 * wl.world * wl.accum + 30)
+    probe = min(L, 1 << 21)
+    dt = timed([inputs(starts[0], probe, 0)], 2, threads) / 2
     want = int(probe * target_s / max(dt, 1e-6))
-    ns = int(min(wl.n, cap, max(probe, want)))
+    ns = int(min(L, max(probe, want)))
+    if extrapolated:
+        ns = L
+        sets = [inputs(s, L, r) for r, s in enumerate(starts)]
+    else:
+        sets = [inputs(starts[0], ns, r) for r in range(min(max(1, want // ns), wl.steps))]
     reps = max(1, min(1000, int(want // ns)))
-    dt = timed(ns, reps)
-    # one thread, on a smaller sample (about a third of the time budget)
-    dt1 = timed(probe, 1, threads=1)
-    reps1 = max(1, min(100, int(target_s / 3 / max(dt1, 1e-6))))
-    dt1 = timed(probe, reps1, threads=1)
-    return dict(value=ns * reps / dt, unit="params/s", cores=threads, kind="oracle",
-                sample=f"{ns} params of the {name} rank-{wl.rank} partition (W={wl.world}, "
-                       f"{wl.accum} micro-batch(es)) x {reps} step(s), {threads} threads, "
-                       f"{dt:.1f} s",
-                value_1_thread=probe * reps1 / dt1,
-                sample_1_thread=f"{probe} params x {reps1} step(s), 1 thread, {dt1:.1f} s",
-                cpu_model=cpu_model(), host_cpus_machine=os.cpu_count(),
-                host_cpus_available=len(os.sched_getaffinity(0)))
+    dt = timed(sets, reps, threads)
+    # one thread, on a smaller sample (about a quarter of the time budget)
+    one = [inputs(starts[0], probe, 0)]
+    dt1 = timed(one, 1, 1)
+    reps1 = max(1, min(100, int(target_s / 4 / max(dt1, 1e-6))))
+    dt1 = timed(one, reps1, 1)
+    rate = ns * reps / dt
+    where = (f"{len(starts)} windows of {L} params (flat offsets {', '.join(map(str, starts))} "
+             f"of the {wl.n}-param shard)" if extrapolated else
+             f"{ns} params of the {name} rank-{wl.rank} partition")
+    out = dict(value=rate, unit="params/s", cores=threads, kind="oracle",
+               sample=f"{where} (W={wl.world}, {wl.accum} micro-batch(es)) x {reps} step(s), "
+                      f"{threads} threads, {dt:.1f} s",
+               value_1_thread=probe * reps1 / dt1,
+               sample_1_thread=f"{probe} params x {reps1} step(s), 1 thread, {dt1:.1f} s",
+               cpu_model=cpu_model(), host_cpus_machine=os.cpu_count(),
+               host_cpus_available=len(os.sched_getaffinity(0)))
+    if extrapolated:
+        out.update(extrapolated=True,
+                   extrapolated_step_s=wl.n / rate,
+                   extrapolation=f"linear: the update is elementwise, so the whole "
+                                 f"{wl.n}-param step takes n / value at the windows' rate")
+    return out
 
 
 def world_sweep(worlds, n, steps, warmup, torch):
@@ -413,7 +520,7 @@ def world_sweep(worlds, n, steps, warmup, torch):
     from sharded_mixed_precision_zs_amd import synth
 
     out = []
-    base = synth.WORKLOADS[DEFAULT_WORKLOAD]
+    base = synth.WORKLOADS["gpt2s-w8"]
     for w in worlds:
         nw = n + 4096 * w
         name = f"sweep-w{w}"
@@ -431,8 +538,8 @@ def world_sweep(worlds, n, steps, warmup, torch):
 
 def side_leg(name, fn, torch):
     """Run a leg reported beside the headline; a failure (for instance too
-    little free device memory for a 7B state) is recorded in the JSON line
-    as {"error": ...} instead of taking the headline down with it."""
+    little free device memory) is recorded in the JSON line as
+    {"error": ...} instead of taking the headline down with it."""
     try:
         return fn()
     except (RuntimeError, MemoryError, OSError, ValueError) as e:
@@ -441,24 +548,39 @@ def side_leg(name, fn, torch):
         return {"error": f"{type(e).__name__}: {e}"}
 
 
+def summary(res, wl, wire=0):
+    """The record of one workload in the JSON line."""
+    out = dict(workload=res["workload"], params_per_s=res["params_per_s"],
+               ms_per_step=res["ms_per_step"], hbm_gbps=res["hbm_gbps"],
+               hbm_pct_of_peak=100.0 * res["hbm_gbps"] / PEAK_HBM_GBPS,
+               replicas=res["replicas"], committed=res["committed"])
+    if "fused_gbps" in res:
+        out["roofline"] = roofline_of(res, wl, wire)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1,
                     help="GPUs to use; only 1 is supported (one rank's shard on one MI355X)")
-    ap.add_argument("--steps", type=int, default=320, help="timed steps of the headline workload")
+    ap.add_argument("--steps", type=int, default=20, help="timed steps of each workload")
     ap.add_argument("--warmup", type=int, default=5, help="untimed steps before the timed ones")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="headline workload (a key of synth.WORKLOADS)")
     ap.add_argument("--also", default=DEFAULT_ALSO,
-                    help="comma-separated extra workloads reported under 'other_workloads'")
-    ap.add_argument("--wire", choices=["fp32", "bf16", "fp16"], default="fp32",
-                    help="precision of the ring's partial sums (default fp32)")
+                    help="comma-separated workloads reported beside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (cpu_baseline)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host update) leg")
-    ap.add_argument("--no-copy-ceiling", action="store_true",
-                    help="skip timing the plain copies (copy_ceiling_gbps, memcpy_d2d_gbps)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy and stream-probe ceilings")
+    ap.add_argument("--ceilings", default="",
+                    help="comma-separated stream-probe names to run (default: all)")
+    ap.add_argument("--no-host-commit", action="store_true",
+                    help="skip the host-commit flow of the headline")
+    ap.add_argument("--no-side-legs", action="store_true",
+                    help="skip the bf16-wire and all-gather legs")
     ap.add_argument("--sweep-world", default="",
                     help="comma-separated W values: time the fused step at one shard size for "
                          "each and print that table as the JSON line instead")
@@ -473,8 +595,8 @@ def main():
     import torch
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
-    from sharded_mixed_precision_zs_amd import synth  # noqa: F401  (fails loudly if unbuilt)
-    from sharded_mixed_precision_zs_amd import zeroshard  # noqa: F401
+    from sharded_mixed_precision_zs_amd import synth
+    from sharded_mixed_precision_zs_amd import zeroshard  # noqa: F401  (fails loudly if unbuilt)
 
     if args.sweep_world:
         worlds = [int(x) for x in args.sweep_world.split(",") if x]
@@ -482,67 +604,69 @@ def main():
         print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "sweep": sweep}))
         return
-    copies = {} if args.no_copy_ceiling else side_leg("copy_ceiling",
-                                                       lambda: copy_rates_gbps(torch), torch)
-    if "error" in copies:
-        copies = {}
-    ceiling = copies.get("ceiling")
-    if copies:
-        log(f"plain copy ceiling {ceiling:.0f} GB/s; runtime memcpy {copies['memcpy']:.0f} GB/s")
-    wire = {"fp32": 0, "bf16": 1, "fp16": 2}[args.wire]
-    main_res = run_workload(args.workload, args.steps, args.warmup, torch, wire)
-    log(json.dumps(main_res))
-    host_res = run_workload(args.workload, args.steps, args.warmup, torch, wire,
-                            device_commit=False)
-    log(json.dumps(host_res))
-    # the beyond-core legs on the same workload: the fused step with bf16
-    # partial sums on the wire, and the ring all-gather of the parameters
-    wire_bf16 = None
-    if args.wire == "fp32":
-        r = side_leg("wire_bf16", lambda: run_workload(args.workload, max(3, args.steps // 2), 2,
-                                                        torch, 1), torch)
-        log(json.dumps(r))
-        wire_bf16 = r if "error" in r else dict(
-            workload=args.workload, ms_per_step=r["ms_per_step"],
-            params_per_s=r["params_per_s"], fused_kernel_ms=r["fused_kernel_ms"],
-            fused_gbps=r["fused_gbps"], roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS)
-    all_gather = []
-    for name in dict.fromkeys([args.workload, ALL_GATHER_LARGE]):
-        r = side_leg(f"all_gather {name}", lambda: run_all_gather(name, 10, torch), torch)
-        log(json.dumps(r))
-        all_gather.append(r if "error" not in r else dict(workload=name, error=r["error"]))
-    # the host-side legs run before the large workloads, which churn
-    # hundreds of GB of device memory
+    K, Wm = args.steps, args.warmup
+    also = [x for x in args.also.split(",") if x and x != args.workload]
+    # host-side legs first: they measured slower after the large workloads'
+    # hundreds of GB of device allocations
     offload = None
     if not args.no_offload:
-        offload = side_leg("offload", lambda: run_offload(args.workload, max(10, args.steps // 2),
-                                                          2, torch), torch)
+        offload = side_leg("offload", lambda: run_offload(HOST_LEG_WORKLOAD, max(10, K), 2, torch),
+                           torch)
         log(json.dumps(offload))
     cpu = None if args.no_cpu_baseline else side_leg("cpu_baseline",
                                                      lambda: cpu_baseline(args.workload), torch)
-    others = []
-    for name in [x for x in args.also.split(",") if x and x != args.workload]:
-        r = side_leg(name, lambda: run_workload(name, max(3, args.steps // 2), 2, torch, wire),
-                     torch)
+    log(f"cpu_baseline: {json.dumps(cpu)}")
+    copies, ceilings = {}, {}
+    if not args.no_ceilings:
+        copies = side_leg("copy_ceiling", lambda: copy_rates_gbps(torch), torch)
+        names = set(x for x in args.ceilings.split(",") if x) or None
+        ceilings = side_leg("stream_ceilings", lambda: stream_ceilings(torch, names=names), torch)
+    copy_ceiling = copies.get("ceiling")
+    # the workloads beside the headline, smallest memory first
+    others, roofs = [], {}
+    for name in also:
+        wl = synth.WORKLOADS[name]
+        k = max(K, 200) if wl.n < (1 << 20) else K
+        r = side_leg(name, lambda: run_workload(name, k, 2, torch), torch)
         log(json.dumps(r))
         if "error" in r:
             others.append(dict(workload=name, error=r["error"]))
             continue
-        others.append(dict(workload=name, params_per_s=r["params_per_s"],
-                           ms_per_step=r["ms_per_step"], hbm_gbps=r["hbm_gbps"],
-                           fused_kernel_ms=r["fused_kernel_ms"], fused_gbps=r["fused_gbps"],
-                           roofline_frac=r["fused_gbps"] / PEAK_HBM_GBPS))
+        rec = summary(r, wl)
+        others.append(rec)
+        roofs[name] = rec["roofline"]
+    wire_bf16, all_gather = None, []
+    if not args.no_side_legs:
+        if WIRE_WORKLOAD in synth.WORKLOADS:
+            wl = synth.WORKLOADS[WIRE_WORKLOAD]
+            r = side_leg("wire_bf16", lambda: run_workload(WIRE_WORKLOAD, K, 2, torch, wire=1),
+                         torch)
+            log(json.dumps(r))
+            wire_bf16 = r if "error" in r else summary(r, wl, wire=1)
+        for name in ALL_GATHER_WORKLOADS:
+            r = side_leg(f"all_gather {name}", lambda: run_all_gather(name, 10, torch), torch)
+            log(json.dumps(r))
+            all_gather.append(r if "error" not in r else dict(workload=name, error=r["error"]))
+    # the headline: device commit, then host commit, on fresh buffers each
+    main_res = run_workload(args.workload, K, Wm, torch)
+    log(json.dumps(main_res))
+    host_res = None
+    if not args.no_host_commit:
+        host_res = side_leg("host_commit", lambda: run_workload(args.workload, K, 2, torch,
+                                                                device_commit=False), torch)
+        log(json.dumps(host_res))
 
-    from sharded_mixed_precision_zs_amd import synth as s
-    wl = s.WORKLOADS[args.workload]
-    traffic = recorded_traffic(args.workload)
+    wl = synth.WORKLOADS[args.workload]
+    head = summary(main_res, wl)
+    roofs[args.workload] = head["roofline"]
+    mix = "step_mix_w1" if wl.world == 1 else "step_mix_w64" if wl.world == 64 else None
     out = {
         "metric": METRIC,
         "value": main_res["params_per_s"],
         "unit": "params/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": Wm,
         "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -553,27 +677,24 @@ def main():
                    "phi": wl.phi, "world": wl.world, "rank": wl.rank, "shard_params": wl.n,
                    "grad_dtype": "bf16" if wl.grad_dtype == 0 else "fp16",
                    "param_dtype": "bf16" if wl.param_dtype == 0 else "fp16",
-                   "micro_batches": wl.accum, "replicas": main_res["replicas"],
-                   "wire": args.wire},
+                   "micro_batches": wl.accum, "replicas": main_res["replicas"], "wire": "fp32"},
         "hbm_gbps": main_res["hbm_gbps"],
         "hbm_pct_of_peak": 100.0 * main_res["hbm_gbps"] / PEAK_HBM_GBPS,
-        "copy_ceiling_gbps": ceiling,
+        "copy_ceiling_gbps": copy_ceiling,
         "memcpy_d2d_gbps": copies.get("memcpy"),
-        "hbm_pct_of_copy_ceiling": 100.0 * main_res["hbm_gbps"] / ceiling if ceiling else None,
-        "roofline": {"bound": "hbm", "achieved": main_res["fused_gbps"],
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": main_res["fused_gbps"] / PEAK_HBM_GBPS,
-                     "traffic": traffic,
-                     "kernel": "zs::fused_kernel", "kernel_ms": main_res["fused_kernel_ms"],
-                     "kernel_ms_median": main_res["kernel_ms_median"],
-                     "kernel_samples": main_res["kernel_samples"],
-                     "event_every": main_res["event_every"],
-                     "algorithmic_bytes_per_launch": main_res["fused_bytes"]},
+        "hbm_pct_of_copy_ceiling": (100.0 * main_res["hbm_gbps"] / copy_ceiling
+                                    if copy_ceiling else None),
+        "hbm_pct_of_step_mix_ceiling": (100.0 * main_res["fused_gbps"] / ceilings[mix]["gbps"]
+                                        if mix and mix in ceilings else None),
+        "roofline": head["roofline"],
+        "roofline_by_workload": roofs,
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
         "other_workloads": others,
-        "host_commit": {"ms_per_step": host_res["ms_per_step"],
-                        "params_per_s": host_res["params_per_s"],
-                        "fused_kernel_ms": host_res["fused_kernel_ms"]},
+        "host_commit": (None if host_res is None else host_res if "error" in host_res else
+                        dict(ms_per_step=host_res["ms_per_step"],
+                             params_per_s=host_res["params_per_s"],
+                             fused_kernel_ms=host_res.get("fused_kernel_ms"))),
         "offload": offload,
         "wire_bf16": wire_bf16,
         "all_gather": all_gather,

@@ -171,9 +171,16 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
                    uint64_t offset, uint64_t n, const uint32_t *overflow_flag,
                    void *stream);
 
-/* One whole shard step in a single pass over HBM: reduce-scatter average
- * (with optional accumulated micro-batches), unscale, overflow check, AdamW
- * and cast, all with the arithmetic of the calls above, element for element.
+/* One whole shard step in a single pass over HBM: the owner's sequence of
+ * [Notes] 三 (ZeRO-1: reduce the gradient partition this rank owns, convert
+ * to fp32, update the fp32 optimizer state and master weights, refresh the
+ * 16-bit parameters for the all-gather) as [L7] "ZeRO Stage 2" and
+ * [Intro] 一.3 item (12) run it with the gradient sharded too, plus the
+ * loss-scaling check of [Intro] 一.3 items (1) and (3) and the
+ * micro-batch accumulation of [L7] "Gradient Accumulation": reduce-scatter
+ * average (with optional accumulated micro-batches), unscale, overflow
+ * check, AdamW and cast, with the arithmetic of the calls above, element
+ * for element.
  * The update is written out of place, to an output set that must not
  * overlap the input set (ZS_ERR_ALIAS), so a step whose flag turns out set
  * leaves the input set untouched: the caller reads the flag, then either
@@ -235,7 +242,9 @@ int zs_cpu_step(float *master, float *m, float *v, const float *grad_part, uint6
                 const zs_adamw_hparams *hp, void *params16, int param_dtype, int threads,
                 uint32_t *overflow);
 
-/* Pass 2 of zs_cpu_step alone, for a caller that has already established
+/* The update half of the ZeRO-Offload step ([Intro] 一.3 item (16): the
+ * optimizer update runs on the CPU where the states live) without its
+ * check: pass 2 of zs_cpu_step alone, for a caller that has already established
  * that no grad_part[i] / loss_scale is non-finite, e.g. with
  * zs_check_overflow on the device before the copy (which lets the update
  * start on the first pieces of the gradient while the rest is still in
@@ -364,8 +373,11 @@ typedef struct {
   float last_alpha, last_bc2;
 } zs_device_scaler;
 
-/* Host image of a device scaler that continues from the host scaler `s`
- * (beta powers formed by step_t + 1 repeated binary64 multiplications).
+/* Host image of a device scaler ([Intro] 一.3 items (1) and (3): the
+ * dynamic loss scale and its skip rule; the bias-correction powers of the
+ * AdamW update that [Notes] 三 runs on the owner's fp32 state) that
+ * continues from the host scaler `s` (beta powers formed by step_t + 1
+ * repeated binary64 multiplications).
  * Errors: ZS_ERR_INVALID_ARG for NULL pointers, a scale that is not
  * finite and > 0, or a beta outside [0, 1). */
 int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
@@ -394,8 +406,9 @@ int zs_device_scaler_make(const zs_loss_scaler *s, float beta1, float beta2,
  * ev_start / ev_stop: NULL, or hipEvent_t handles recorded immediately
  * before and after the fused kernel. Calls that share a dev must be ordered
  * (one stream). Errors: as zs_step_fused (ZS_ERR_INVALID_ARG also for a
- * NULL or not 8-byte-aligned dev, ZS_ERR_ALIAS also for a dev inside an
- * output buffer); argument errors return before anything
+ * NULL or not 8-byte-aligned dev, ZS_ERR_ALIAS also for a dev that
+ * overlaps an output buffer, master_in, m_in, v_in, acc_in or a worker's
+ * gradient); argument errors return before anything
  * is enqueued. ZS_ERR_HIP from the second launch leaves the fused pass
  * enqueued without its commit: dev->epoch has not advanced, and the caller
  * must not swap the sets (rerunning the step is safe: the fused pass does

@@ -554,6 +554,18 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     if (dev && overlaps(outs[i], out_bytes[i], dev, sizeof(zs_device_scaler)))
       return fail(ZS_ERR_ALIAS, "zs_step_device: an output overlaps the device scaler%s");
   }
+  /* The fused pass and the commit kernel write the device scaler while
+   * other blocks still read the input set; a scaler inside an input would
+   * corrupt the set a skipped step restores from. */
+  if (dev) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(dev, sizeof(zs_device_scaler), ins[j], b4))
+        return fail(ZS_ERR_ALIAS, "zs_step_device: the device scaler overlaps an input%s");
+    for (uint32_t w = 0; w < a->world; ++w)
+      if (overlaps(dev, sizeof(zs_device_scaler), p.g.p[w], b2))
+        return fail(ZS_ERR_ALIAS,
+                    "zs_step_device: the device scaler overlaps a gradient buffer%s");
+  }
 
   p.world = a->world;
   p.n = n;

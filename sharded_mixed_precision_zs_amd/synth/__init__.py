@@ -216,7 +216,6 @@ def _dev_lib():
         return _dev
     if not os.path.exists(DEV_LIB):
         raise RuntimeError(f"device generator not built: {DEV_LIB} (run __graft_entry__.build())")
-    import torch  # noqa: F401  (first: the library then shares torch's HIP runtime)
     lib = C.CDLL(DEV_LIB)
     lib.zsg_dev_fill_normal_f32.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, C.c_float,
                                             C.c_void_p, C.c_void_p]

@@ -64,23 +64,12 @@ class zs_device_scaler(C.Structure):
                 ("last_alpha", C.c_float), ("last_bc2", C.c_float)]
 
 
-def _runtime_first():
-    """Import torch before the library is loaded. The library asks for
-    libamdhip64.so.7, which the copy of the HIP runtime that torch ships and
-    loads answers to, so with torch imported first the library shares
-    torch's runtime, streams and allocations. Loaded first, the library's
-    search path would bring in the system runtime, and torch, which asks
-    for its copy under another file name, would then load a second runtime
-    beside it: launches from the library fail and torch's own calls can
-    crash."""
-    import torch  # noqa: F401
-
-
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libzeroshard is not built ({LIB_PATH}); "
                           "run __graft_entry__.build() -- there is no fallback path")
-    _runtime_first()
+    # the library maps torch's HIP runtime whatever the import order (see
+    # build.py), so it shares torch's streams and allocations
     lib = C.CDLL(LIB_PATH)
     vp, u32, u64, f32, i32 = C.c_void_p, C.c_uint32, C.c_uint64, C.c_float, C.c_int
     sig = {

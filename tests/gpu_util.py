@@ -97,3 +97,32 @@ def assert_ulp16(got, want, dtype, max_ulp, what):
         raise AssertionError(f"{what}: {int((d > max_ulp).sum())} beyond {max_ulp} ulp; "
                              f"e.g. {got[~gn][i]:#06x} vs {want[~wn][i]:#06x}")
     return int((d != 0).sum())
+
+
+def oracle_offload_update(master, m, v, grad, loss_scale, lr, beta1, beta2, eps, weight_decay,
+                          t, param_dtype):
+    """What the oracle computes for one ZeRO-Offload update of an averaged,
+    still loss-scaled fp32 gradient partition: the overflow flag of the
+    unscaled gradient; on a clean step the AdamW update of copies of
+    (master, m, v) and the 16-bit cast of the new master; on a skipped step
+    the inputs unchanged and no parameters (None)."""
+    import oracle
+    flag = oracle.check_overflow(grad, loss_scale)
+    state = [np.array(x, F32, copy=True) for x in (master, m, v)]
+    if flag:
+        return flag, state, None
+    oracle.adamw(*state, grad, loss_scale, lr, beta1, beta2, eps, weight_decay, t)
+    return flag, state, oracle.float_to_half(state[0], param_dtype)
+
+
+def assert_offload_matches_oracle(host_state, params_bits, want, param_dtype, what):
+    """host_state (master, m, v as numpy) and the device parameters against
+    oracle_offload_update's result, at the parity bar (fp32 within 1e-6
+    relative, 16-bit within 1 ulp); returns the elements not bit-identical."""
+    flag, state, params = want
+    nonbit = 0
+    for got, ref, name in zip(host_state, state, ("master", "m", "v")):
+        nonbit += assert_rel(got, ref, 1e-6, f"{what} {name} vs oracle")
+    if params is not None:
+        nonbit += assert_ulp16(params_bits, params, param_dtype, 1, f"{what} params vs oracle")
+    return nonbit

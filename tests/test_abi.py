@@ -269,6 +269,17 @@ def test_device_step_rejects_bad_arguments(zs):
     good, keep4 = _fused_args(zs)
     inside = C.c_void_p(good.m_out + 64)          # the scaler inside an output
     assert lib.zs_step_device(C.byref(good), inside, None, None, None) == zs.ZS_ERR_ALIAS
+    # the scaler inside an input: master_in, m_in, v_in, acc_in or a gradient
+    for field, offset in (("master_in", 0), ("m_in", 3992), ("v_in", 16)):
+        inside = C.c_void_p(getattr(good, field) + offset)
+        assert lib.zs_step_device(C.byref(good), inside, None, None, None) == \
+            zs.ZS_ERR_ALIAS, field
+    acc, keep5 = _fused_args(zs, acc_in=FAKE + 0x1800000)
+    inside = C.c_void_p(FAKE + 0x1800000 + 8)
+    assert lib.zs_step_device(C.byref(acc), inside, None, None, None) == zs.ZS_ERR_ALIAS
+    for g in (FAKE, FAKE + 0x100000 + 1992):       # each worker's 2 n bytes
+        assert lib.zs_step_device(C.byref(good), C.c_void_p(g), None, None, None) == \
+            zs.ZS_ERR_ALIAS
 
 
 def test_huge_sizes_are_refused_before_any_arithmetic(zs):

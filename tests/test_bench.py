@@ -38,14 +38,15 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic("gpt2s-w8") is None
 
 
-@pytest.mark.parametrize("step_bytes,want", [(1, 8), (1 << 20, 8), (200 << 20, 6),
-                                             (653308992, 2), (1 << 30, 1), (18 << 30, 1)])
+@pytest.mark.parametrize("step_bytes,want", [(1, 128), (1 << 20, 128), (11_184_832, 96),
+                                             (200 << 20, 6), (653308992, 2), (1 << 30, 1),
+                                             (18 << 30, 1)])
 def test_replicas_cover_a_gigabyte(step_bytes, want):
     """Copies cycled per step: enough that the working set reaches 1 GB
-    (past the 256 MB last-level cache), at most 8, at least 1."""
+    (past the 256 MB last-level cache), at most 128, at least 1."""
     got = bench.replicas_for(None, step_bytes)
     assert got == want
-    assert got == 8 or got * step_bytes >= 1 << 30
+    assert got == 128 or got * step_bytes >= 1 << 30
 
 
 def test_pad_elems_rounds_rows_to_256_bytes():
@@ -62,3 +63,29 @@ def test_cpu_baseline_record_on_the_smallest_workload():
     assert 1 <= r["cores"] <= 16
     assert r["sample"].startswith("349526 params of the mlp9-w3 rank-0 partition")
     assert r["host_cpus_available"] >= 1
+
+
+def test_cpu_sample_of_the_7b_state_is_three_windows():
+    """The 7B state does not fit host memory: the oracle runs on windows of
+    2^26 parameters at the head, the middle and the tail of the shard."""
+    from sharded_mixed_precision_zs_amd import synth
+    wl = synth.WORKLOADS["7b-full-w1"]
+    starts, L = bench.cpu_windows(wl, (6 << 30) // 32)
+    assert L == 1 << 26
+    assert starts[0] == 0 and starts[-1] == wl.n - L and len(starts) == 3
+    assert all(0 <= s and s + L <= wl.n for s in starts)
+    small = synth.WORKLOADS["mlp9-w3"]
+    assert bench.cpu_windows(small, 1 << 30) == ([0], small.n)
+
+
+def test_fused_instance_names_match_the_kernel_template():
+    from sharded_mixed_precision_zs_amd import synth
+    W = synth.WORKLOADS
+    assert bench.fused_instance(W["7b-full-w1"]) == \
+        "zs::fused_kernel<8, 1, false, false, 0, 0, 0>"
+    assert bench.fused_instance(W["7p5b-shard-w64"]) == \
+        "zs::fused_kernel<8, 2, true, false, 0, 0, 0>"
+    assert bench.fused_instance(W["1p3b-w4-acc4-fp16"]) == \
+        "zs::fused_kernel<8, 2, true, true, 1, 1, 0>"
+    assert bench.fused_bytes_per_param(64, 1) == (140, 14)
+    assert bench.fused_bytes_per_param(4, 4) == (24, 14)

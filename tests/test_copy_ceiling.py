@@ -53,3 +53,91 @@ def test_copy_is_exact(copylib, nbytes):
     out = dst.cpu().numpy()
     assert np.array_equal(out[:nbytes], src.cpu().numpy())
     assert not out[nbytes:].any()
+
+
+def _probe_fn(copylib):
+    f = copylib.zs_stream_probe
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_uint32, C.c_void_p, C.c_uint32,
+                  C.c_void_p, C.c_uint64, C.c_uint32, C.c_uint32, C.c_void_p, C.c_uint32,
+                  C.c_void_p]
+    return f
+
+
+def _ptrs(addrs):
+    return (C.c_void_p * max(1, len(addrs)))(*addrs)
+
+
+def test_probe_refuses_before_any_launch(copylib):
+    """Stream counts, vector widths, caps, alignment, ragged sizes and
+    overlapping outputs are refused with 1 before any HIP call."""
+    f = _probe_fn(copylib)
+    A = 0x7F0000000000
+    n = 4096
+    g = _ptrs([A + k * 0x100000 for k in range(3)])
+    i3 = _ptrs([A + 0x1000000 + k * 0x100000 for k in range(3)])
+    o3 = _ptrs([A + 0x2000000 + k * 0x100000 for k in range(3)])
+    sink = A + 0x3000000
+    ok = dict(in16=g, n_in16=3, in32=i3, n_in32=3, out32=o3, n_out32=3, out16=A + 0x4000000,
+              n=n, vecs=2, cap=0, sink=sink, magic=1)
+
+    def call(**over):
+        a = dict(ok, **over)
+        return f(a["in16"], a["n_in16"], a["in32"], a["n_in32"], a["out32"], a["n_out32"],
+                 a["out16"], a["n"], a["vecs"], a["cap"], a["sink"], a["magic"], None)
+
+    assert call(n_in16=65) == 1
+    assert call(n_in32=2) == 1
+    assert call(n_out32=2) == 1
+    assert call(vecs=3) == 1
+    assert call(cap=9) == 1
+    assert call(sink=None) == 1
+    assert call(sink=sink + 2) == 1
+    assert call(n=n + 2048) == 1                 # not a multiple of the 4096-element tile
+    assert call(out16=A + 0x4000008) == 1        # misaligned output
+    assert call(out16=A + 0x1000000 + 64) == 1   # output on an fp32 input
+    assert call(out16=o3[1] + 16) == 1           # output on another output
+    assert call(out16=sink - 16) == 1            # output on the sink
+    assert call(in16=_ptrs([A, 0, A + 0x200000]), n_in16=3) == 1
+    assert call(n=0) == 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("w,nin,nout,p16,vecs", [(3, 3, 3, True, 2), (1, 3, 3, True, 1),
+                                                  (9, 0, 1, False, 2), (64, 0, 0, True, 2),
+                                                  (0, 1, 1, False, 1), (0, 0, 3, True, 1),
+                                                  (17, 3, 1, True, 2)])
+def test_probe_moves_what_it_states(copylib, w, nin, nout, p16, vecs):
+    """Each output word is the documented fold of the inputs, so every
+    stream the probe states is really read and written."""
+    import torch
+    f = _probe_fn(copylib)
+    tile = 2048 * vecs
+    n = 3 * tile
+    rng = np.random.default_rng(w * 100 + nin * 10 + nout)
+    g = [torch.from_numpy(rng.integers(0, 2 ** 16, n, dtype=np.uint16).view(np.int16)).cuda()
+         for _ in range(w)]
+    i32 = [torch.from_numpy(rng.integers(0, 2 ** 32, n, dtype=np.uint32).view(np.int32)).cuda()
+           for _ in range(nin)]
+    o32 = [torch.zeros(n, dtype=torch.int32, device="cuda") for _ in range(nout)]
+    o16 = torch.zeros(n, dtype=torch.int16, device="cuda") if p16 else None
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    rc = f(_ptrs([t.data_ptr() for t in g]), w, _ptrs([t.data_ptr() for t in i32]), nin,
+           _ptrs([t.data_ptr() for t in o32]), nout, o16.data_ptr() if p16 else None, n, vecs,
+           0, sink.data_ptr(), 0x12345678, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, copylib.zs_copy_last_error().decode()
+    torch.cuda.synchronize()
+    words = [t.cpu().numpy().view(np.uint32).reshape(-1, 4) for t in g]   # one row per vector
+    fold = np.zeros((n // 8, 4), np.uint32)
+    for x in words:
+        fold += x
+    ins = [t.cpu().numpy().view(np.uint32).reshape(-1, 2, 4) for t in i32]
+    for k in range(nout):
+        got = o32[k].cpu().numpy().view(np.uint32).reshape(-1, 2, 4)
+        want = (ins[k] ^ fold[:, None, :]) if k < nin else np.repeat(fold[:, None, :], 2, 1)
+        assert np.array_equal(got, want), f"fp32 output {k}"
+    if p16:
+        rest = fold.copy()
+        for k in range(nout, nin):
+            rest ^= ins[k][:, 0, :] ^ ins[k][:, 1, :]
+        assert np.array_equal(o16.cpu().numpy().view(np.uint32).reshape(-1, 4), rest)

@@ -18,8 +18,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (F32, announce, assert_bits_equal, assert_rel, assert_ulp16, down16,
-                      down32, up16, up32)
+from gpu_util import (F32, announce, assert_bits_equal, assert_offload_matches_oracle,
+                      assert_rel, assert_ulp16, down16, down32, oracle_offload_update, up16,
+                      up32)
 
 pytestmark = pytest.mark.gpu
 
@@ -222,10 +223,11 @@ def test_all_gather_random_configuration(zs, case):
 @pytest.mark.parametrize("case", range(40))
 def test_offload_step_random_configuration(zs, case):
     """zs_offload_step (GPU check, gradient in pieces, host update per piece,
-    parameters back per piece) against zs_cpu_step on the same random
-    gradient: random size, piece count, thread count, AdamW settings, loss
-    scale and parameter dtype, sometimes a non-finite value (then nothing is
-    written)."""
+    parameters back per piece) against the oracle's check, AdamW update and
+    cast on the same random gradient -- and, beside it, against zs_cpu_step
+    (the host update without the pipeline): random size, piece count,
+    thread count, AdamW settings, loss scale and parameter dtype, sometimes
+    a non-finite value (then nothing is written)."""
     rng = np.random.default_rng(21000 + case)
     c = _draw(rng)
     n, pdt = c["n"], c["pdt"]
@@ -254,10 +256,17 @@ def test_offload_step_random_configuration(zs, case):
                             torch.zeros(1, dtype=torch.int32, pin_memory=True), DT[pdt], threads,
                             pieces)
     torch.cuda.synchronize()
-    assert ok == (ref_flag == 0) == (not c["inject"])
-    for got, want, what in zip(host, ref, ("master", "m", "v")):
-        assert_bits_equal(got.numpy(), want, f"#{case} {what}")
-    assert np.array_equal(down16(params_dev), ref_p)
+    want = oracle_offload_update(*state, a, c["scale"], c["lr"], c["beta1"], c["beta2"],
+                                 c["eps"], c["weight_decay"], c["t"], pdt)
+    assert ok == (want[0] == 0) == (ref_flag == 0) == (not c["inject"])
+    got_p = down16(params_dev)
+    assert assert_offload_matches_oracle([x.numpy() for x in host], got_p, want, pdt,
+                                         f"#{case}") == 0
+    if not ok:
+        assert np.all(got_p == 7), "a skipped step writes no parameters"
+    for got, ref_x, what in zip(host, ref, ("master", "m", "v")):
+        assert_bits_equal(got.numpy(), ref_x, f"#{case} {what} vs zs_cpu_step")
+    assert np.array_equal(got_p, ref_p)
 
 
 @pytest.mark.parametrize("case", range(100))

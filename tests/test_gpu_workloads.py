@@ -16,13 +16,24 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import F32, announce, assert_bits_equal, assert_rel, assert_ulp16, down16, down32
+from gpu_util import (F32, announce, assert_bits_equal, assert_offload_matches_oracle,
+                      assert_rel, assert_ulp16, down16, down32, oracle_offload_update)
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
 WINDOW = 1 << 16
+# Window sizes of the large workloads: as large as the host-side generation
+# and oracle allow within seconds per step (64 workers' gradients are
+# generated per element of the 7.5B shard's windows).
+WINDOW_7P5B = 1 << 21
+WINDOW_7B = 1 << 22
+WINDOW_1P3B = 1 << 20
+# Element offsets where 32-bit address arithmetic would wrap in the 7e9-
+# element arrays: fp32 byte offsets 2^31 .. 2^34 (elements 2^29 .. 2^32),
+# 16-bit byte offsets 2^31 .. 2^33 and element indices 2^31, 2^32.
+BOUNDARIES_7B = (1 << 29, 1 << 30, 1 << 31, 1 << 32)
 
 
 @pytest.fixture(scope="module")
@@ -33,14 +44,17 @@ def env(hip_built):
     return zeroshard, synth, shard
 
 
-def _windows(n, count, seed):
-    if n <= 4 * WINDOW:
+def _windows(n, count, seed, window=WINDOW, straddle=()):
+    """Head, tail, middle and seeded random windows of `window` elements,
+    plus one window centred on each offset in `straddle`."""
+    if n <= 4 * window:
         return [(0, n)]
     rng = np.random.default_rng(seed)
-    starts = {0, n - WINDOW, (n // 2) - WINDOW // 2}
-    while len(starts) < count:
-        starts.add(int(rng.integers(0, n - WINDOW)))
-    return [(s, WINDOW) for s in sorted(starts)]
+    starts = {0, n - window, (n // 2) - window // 2}
+    starts |= {b - window // 2 for b in straddle if window // 2 <= b <= n - window // 2}
+    while len(starts) < count + len(straddle):
+        starts.add(int(rng.integers(0, n - window)))
+    return [(s, window) for s in sorted(starts)]
 
 
 def run_workload(env, name, windows=None, gather_full=False, device_commit=False, wl=None):
@@ -156,21 +170,26 @@ def test_gpt2s_w8_full(env):
 def test_7p5b_shard_w64_windows(env, device_commit):
     zs, synth, shard = env
     wl = synth.WORKLOADS["7p5b-shard-w64"]
-    run_workload(env, wl.name, windows=_windows(wl.n, 8, 2), device_commit=device_commit)
+    run_workload(env, wl.name, windows=_windows(wl.n, 8, 2, WINDOW_7P5B),
+                 device_commit=device_commit)
 
 
 @pytest.mark.parametrize("device_commit", [False, True])
 def test_7b_full_w1_windows(env, device_commit):
     zs, synth, shard = env
     wl = synth.WORKLOADS["7b-full-w1"]
-    run_workload(env, wl.name, windows=_windows(wl.n, 8, 3), device_commit=device_commit)
+    wins = _windows(wl.n, 8, 3, WINDOW_7B, straddle=BOUNDARIES_7B)
+    for b in BOUNDARIES_7B:
+        assert any(s < b < s + L for s, L in wins), b
+    run_workload(env, wl.name, windows=wins, device_commit=device_commit)
 
 
 @pytest.mark.parametrize("device_commit", [False, True])
 def test_1p3b_w4_acc4_fp16_windows(env, device_commit):
     zs, synth, shard = env
     wl = synth.WORKLOADS["1p3b-w4-acc4-fp16"]
-    st = run_workload(env, wl.name, windows=_windows(wl.n, 6, 4), device_commit=device_commit)
+    st = run_workload(env, wl.name, windows=_windows(wl.n, 6, 4, WINDOW_1P3B),
+                      device_commit=device_commit)
     # two injected steps skipped: 2^16 -> 2^15 -> 2^14, eight steps committed
     assert st.loss_scale == 2.0 ** 14 and st.t == 8
 
@@ -247,8 +266,10 @@ def test_checkpoint_resume_is_bit_identical(env, tmp_path, device_commit):
 
 @pytest.mark.parametrize("name,phi", [("gpt2s-w8", 8 * 250_003), ("1p3b-w4-acc4-fp16", 4 * 200_001)])
 def test_offload_equals_fused(env, name, phi):
-    """The ZeRO-Offload variant (reduce on the GPU, update on the host) and
-    the fused GPU step produce the same bits, skipped steps included."""
+    """The ZeRO-Offload variant (reduce on the GPU, update on the host)
+    follows the oracle step by step over the whole partition (its host state
+    and device parameters after every step, skipped steps included), and
+    the fused GPU step produces the same bits."""
     zs, synth, shard = env
     import dataclasses
     wl = dataclasses.replace(synth.WORKLOADS[name], phi=phi, name=name + "-offload",
@@ -266,19 +287,42 @@ def test_offload_equals_fused(env, name, phi):
     off.v.copy_(gpu.v.cpu())
     grads = torch.empty((W, -(-n // 128) * 128), dtype=torch.int16, device="cuda")
     g = [grads[k, :n] for k in range(W)]
+    hs = list(synth.host_state(wl, 0, n))          # the oracle's state
+    hscaler = oracle.Scaler(wl.loss_scale, wl.scale_interval if wl.dynamic_scale else 10 ** 9)
+    skipped = 0
     for step in range(1, wl.steps + 1):
-        announce(f"offload vs fused {name} step {step}")
-        assert gpu.loss_scale == off.loss_scale
+        announce(f"offload vs oracle and fused {name} step {step}")
+        assert gpu.loss_scale == off.loss_scale == hscaler.scale
+        scale = hscaler.scale
+        acc = np.empty(n, F32) if A > 1 else None
         for j in range(A):
             for k in range(W):
-                synth.dev_grad(wl, k, step, j, 0, g[k], scale=gpu.loss_scale)
+                synth.dev_grad(wl, k, step, j, 0, g[k], scale=scale)
+            parts = [synth.host_grad(wl, k, step, j, 0, n, scale=scale) for k in range(W)]
             if j < A - 1:
                 gpu.reduce_micro(g, first=(j == 0))
                 off.reduce_micro(g, first=(j == 0))
+                oracle.reduce_avg(parts, 0, wl.grad_dtype, acc, j > 0, scale)
             else:
                 ok1 = gpu.step(g, acc_in=gpu.acc if A > 1 else None)
                 ok2 = off.step(g, first=(A == 1))
-                assert ok1 == ok2
+                f, mo, mmo, vo, po = oracle.shard_step(
+                    parts, 0, wl.grad_dtype, wl.param_dtype, *hs, lr=wl.lr, beta1=wl.beta1,
+                    beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay, loss_scale=scale,
+                    step_t=hscaler.t + 1, acc_in=acc, threads=8)
+                assert ok1 == ok2 == (f == 0)
+        hscaler.update(f)
+        skipped += f
+        if f == 0:
+            hs = [mo, mmo, vo]
+        torch.cuda.synchronize()
+        nonbit = assert_offload_matches_oracle(
+            [off.master.numpy(), off.m.numpy(), off.v.numpy()],
+            down16(off.params.view(torch.int16)), (f, hs, po if f == 0 else None),
+            wl.param_dtype, f"{name} step {step}")
+        assert nonbit == 0, f"{name} step {step}: {nonbit} elements not bit-identical"
+    assert (off.t, off.loss_scale) == (hscaler.t, hscaler.scale)
+    assert skipped == len(wl.inject_steps)
     torch.cuda.synchronize()
     for x, y in ((gpu.master, off.master), (gpu.m, off.m), (gpu.v, off.v)):
         assert_bits_equal(down32(x), y.numpy(), f"{name} offload state")
@@ -291,10 +335,11 @@ def test_offload_equals_fused(env, name, phi):
 def test_offload_step_equals_cpu_step(env, n, pieces, threads):
     """zs_offload_step (GPU check, gradient in pieces, host update as the
     pieces land, parameters copied back per piece) leaves the host state and
-    the device parameters exactly as zs_cpu_step on the same gradient, for
-    ragged sizes, more pieces than elements per thread, and any thread
-    count; a gradient with one non-finite value is skipped with nothing
-    written; the call runs on a side stream."""
+    the device parameters as the oracle's check, AdamW update and cast of
+    the same gradient -- and exactly as zs_cpu_step -- for ragged sizes,
+    more pieces than elements per thread, and any thread count; a gradient
+    with one non-finite value is skipped with nothing written; the call
+    runs on a side stream."""
     zs, synth, shard = env
     rng = np.random.default_rng(n + pieces)
     grad = (rng.standard_normal(n) * 3e-3 * 1024).astype(F32)
@@ -319,9 +364,13 @@ def test_offload_step_equals_cpu_step(env, n, pieces, threads):
                             flag_dev, flag_host, zs.ZS_BF16, threads, pieces, stream=side)
     side.synchronize()
     assert ok and int(flag_host[0]) == 0
-    for got, want, what in zip(host, ref, ("master", "m", "v")):
-        assert_bits_equal(got.numpy(), want, f"offload step {what}")
     p = down16(params_dev.view(torch.int16))
+    want = oracle_offload_update(*state, grad, 1024.0, 1e-3, 0.9, 0.999, 1e-8, 0.01, 3, "bf16")
+    assert want[0] == 0
+    assert assert_offload_matches_oracle([x.numpy() for x in host], p[8:8 + n], want, "bf16",
+                                         "offload step") == 0
+    for got, ref_x, what in zip(host, ref, ("master", "m", "v")):
+        assert_bits_equal(got.numpy(), ref_x, f"offload step {what} vs zs_cpu_step")
     assert np.array_equal(p[8:8 + n], ref_p) and np.all(p[:8] == 7) and np.all(p[8 + n:] == 7)
     # a non-finite gradient value: skipped, nothing written
     bad = grad.copy()
@@ -335,6 +384,10 @@ def test_offload_step_equals_cpu_step(env, n, pieces, threads):
                             flag_dev, flag_host, zs.ZS_BF16, threads, pieces, stream=side)
     side.synchronize()
     assert not ok and int(flag_host[0]) == 1
-    for got, want in zip(host, before):
-        assert_bits_equal(got.numpy(), want, "skipped offload step")
+    want = oracle_offload_update(*before, bad, 1024.0, 1e-3, 0.9, 0.999, 1e-8, 0.01, 3, "bf16")
+    assert want[0] == 1
+    assert assert_offload_matches_oracle([x.numpy() for x in host], None, want, "bf16",
+                                         "skipped offload step") == 0
+    for got, ref_x in zip(host, before):
+        assert_bits_equal(got.numpy(), ref_x, "skipped offload step")
     assert np.all(down16(params_dev.view(torch.int16))[8:8 + n] == 3)
