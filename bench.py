@@ -536,6 +536,127 @@ def world_sweep(worlds, n, steps, warmup, torch):
     return out
 
 
+# The variant sweep: per workload, (variant id, residency cap, persistent
+# blocks per CU). Ids 0 and 5 are the production shapes (libzsvariants).
+VARIANT_SWEEP = {
+    "7b-full-w1": [(0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
+                   (4, 2, 2)],
+    "gpt2s-w8": [(5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
+                 (9, 3, 0), (10, 3, 3), (11, 3, 0)],
+    "7p5b-shard-w64": [(5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0), (9, 0, 0),
+                       (10, 0, 5), (11, 0, 0)],
+}
+VARIANT_N_MAX = 1 << 30   # W = 1: the first 2^30 parameters of the 7B state (3 sets fit HBM)
+
+
+def _variantlib():
+    import ctypes as C
+    from sharded_mixed_precision_zs_amd import build as pkg_build
+    if not os.path.exists(pkg_build.VARIANTS):
+        raise RuntimeError(f"{pkg_build.VARIANTS} is not built: run the package build first")
+    lib = C.CDLL(pkg_build.VARIANTS)
+    lib.zs_variant_name.restype = C.c_char_p
+    lib.zs_variant_name.argtypes = [C.c_int]
+    lib.zs_variant_tile.argtypes = [C.c_int]
+    lib.zs_variant_multi.argtypes = [C.c_int]
+    lib.zs_variant_last_error.restype = C.c_char_p
+    lib.zs_variant_launch.restype = C.c_int
+    lib.zs_variant_launch.argtypes = [C.c_int, C.c_void_p, C.c_uint32, C.c_uint32, C.c_void_p]
+    return lib
+
+
+def variant_sweep(name, plan, reps, torch, rounds=3):
+    """Time libzeroshard's fused step (zs_step_fused) and the variants of
+    `plan` on one workload, interleaved over `rounds`, after checking that
+    each variant writes the production kernel's bits. The shard is cut to a
+    multiple of every variant's tile (and to VARIANT_N_MAX parameters)."""
+    import ctypes as C
+
+    from sharded_mixed_precision_zs_amd import synth
+    from sharded_mixed_precision_zs_amd import zeroshard as zs
+
+    lib = _variantlib()
+    wl = synth.WORKLOADS[name]
+    W = wl.world
+    tile = max(lib.zs_variant_tile(v) for v, _, _ in plan)
+    n = min(wl.n, VARIANT_N_MAX) // tile * tile
+    bytes_per = 2 * W + 12 + 14
+    R = replicas_for(wl, bytes_per * n)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    reps_sets = []
+    for r in range(R):
+        grads = torch.empty((W, pad_elems(n)), dtype=torch.int16, device="cuda")
+        views = [grads[k, :n] for k in range(W)]
+        for k in range(W):
+            synth.dev_grad(wl, k, 1 + r, 0, wl.offset, views[k], scale=wl.loss_scale)
+        sin = [torch.empty(n, **f32) for _ in range(3)]
+        synth.dev_state(wl, wl.offset, *sin)
+        sout = [torch.empty(n, **f32) for _ in range(3)]
+        par = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        hp = zs.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, wl.loss_scale, 1)
+        args = zs.StepArgs(views, 0, n, *sin, *sout, par, 0, flag, hp,
+                           grad_dtype=wl.grad_dtype, param_dtype=wl.param_dtype)
+        # StepArgs keeps raw addresses only: the replica holds its tensors
+        reps_sets.append((args, sout, par, (grads, views, sin, flag)))
+    torch.cuda.synchronize()
+
+    def prod(i):
+        zs.zs_step_fused(reps_sets[i % R][0])
+
+    def variant(v, cap, per):
+        def go(i):
+            a = reps_sets[i % R][0]
+            rc = lib.zs_variant_launch(v, C.addressof(a.args), cap, per,
+                                       torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"zs_variant_launch({v}) returned {rc}: "
+                                   f"{lib.zs_variant_last_error().decode()}")
+        return go
+
+    # bits: production into replica 0's outputs, saved; each variant must match
+    prod(0)
+    torch.cuda.synchronize()
+    _, sout0, par0, _ = reps_sets[0]
+    ref = [x.clone() for x in sout0] + [par0.clone()]
+    for v, cap, per in plan:
+        for x in sout0 + [par0]:
+            x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).fill_(-1)
+        variant(v, cap, per)(0)
+        torch.cuda.synchronize()
+        for what, x, y in zip(("master", "m", "v", "params"), sout0 + [par0], ref):
+            xi = x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32)
+            yi = y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32)
+            if not torch.equal(xi, yi):
+                bad = torch.nonzero(xi != yi).flatten()
+                i = int(bad[0])
+                raise RuntimeError(f"variant {v} ({lib.zs_variant_name(v).decode()}) differs from "
+                                   f"the production kernel: {bad.numel()} {what} elements, first "
+                                   f"at {i}: {int(xi[i])} vs {int(yi[i])}")
+    del ref
+    configs = [("libzeroshard zs_step_fused", None, None, None, prod)]
+    configs += [(lib.zs_variant_name(v).decode(), v, cap, per, variant(v, cap, per))
+                for v, cap, per in plan]
+    times = {i: [] for i in range(len(configs))}
+    for _ in range(rounds):
+        for i, (_, _, _, _, fn) in enumerate(configs):
+            ms = _time_calls(torch, lambda it=iter(range(10 ** 9)): fn(next(it)), reps)
+            times[i].append(ms)
+    base = sum(times[0]) / rounds
+    out = []
+    for i, (label, v, cap, per, _) in enumerate(configs):
+        ms = sum(times[i]) / rounds
+        out.append(dict(config=label, variant=v, blocks_per_cu=cap, persistent_per_cu=per or None,
+                        ms=ms, ms_rounds=times[i], gbps=bytes_per * n / (ms * 1e-3) / 1e9,
+                        vs_production=base / ms, bit_exact=True))
+        log(f"variants {name}: {label} cap={cap} persist={per}: {ms:.4f} ms "
+            f"({out[-1]['gbps']:.0f} GB/s, x{base / ms:.4f})")
+    del reps_sets
+    torch.cuda.empty_cache()
+    return dict(workload=name, n=n, world=W, replicas=R, bytes_per_param=bytes_per,
+                reps_per_round=reps, rounds=rounds, results=out)
+
+
 def side_leg(name, fn, torch):
     """Run a leg reported beside the headline; a failure (for instance too
     little free device memory) is recorded in the JSON line as
@@ -586,6 +707,10 @@ def main():
                          "each and print that table as the JSON line instead")
     ap.add_argument("--sweep-n", type=int, default=1 << 25,
                     help="shard size of the --sweep-world runs")
+    ap.add_argument("--sweep-variants", default="",
+                    help="comma-separated workloads (of " + ", ".join(VARIANT_SWEEP) + "): time "
+                         "the fused kernel's shapes of libzsvariants against libzeroshard's and "
+                         "print that table as the JSON line instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: the shard step takes one "
@@ -603,6 +728,12 @@ def main():
         sweep = world_sweep(worlds, args.sweep_n, args.steps, args.warmup, torch)
         print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "sweep": sweep}))
+        return
+    if args.sweep_variants:
+        res = [variant_sweep(w, VARIANT_SWEEP[w], max(4, args.steps), torch)
+               for w in args.sweep_variants.split(",") if w]
+        print(json.dumps({"metric": "fused step kernel shapes, ms per launch", "unit": "ms",
+                          "sweeps": res}))
         return
     K, Wm = args.steps, args.warmup
     also = [x for x in args.also.split(",") if x and x != args.workload]

@@ -7,6 +7,9 @@
   libzscopy.so           the plain copy and the stream probes the benchmark
                          times as HBM ceilings (HIP, gfx950; measurement
                          only) <- csrc/copy_ceiling.hip
+  libzsvariants.so       shapes of the fused kernel the benchmark times
+                         against libzeroshard's (HIP, gfx950; measurement
+                         only) <- csrc/fused_variants.hip
 
 Every call compiles from source. The libraries stay in the source tree so a
 snapshot of the tree carries them to the GPU host.
@@ -23,6 +26,7 @@ SYNTH = os.path.join(PKG, "synth")
 SYNTH_DEV = os.path.join(SYNTH, "libzssynth_dev.so")
 SYNTH_HOST = os.path.join(SYNTH, "libzssynth_host.so")
 COPY = os.path.join(PKG, "libzscopy.so")
+VARIANTS = os.path.join(PKG, "libzsvariants.so")
 
 ARCH = os.environ.get("ZS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -124,9 +128,14 @@ def build_copy(verbose=False):
     return COPY
 
 
+def build_variants(verbose=False):
+    _hip_lib(os.path.join(PKG, "csrc", "fused_variants.hip"), VARIANTS, verbose)
+    return VARIANTS
+
+
 def build_all(verbose=False):
     return [build_zeroshard(verbose), build_synth_dev(verbose), build_synth_host(verbose),
-            build_copy(verbose)]
+            build_copy(verbose), build_variants(verbose)]
 
 
 if __name__ == "__main__":

@@ -1,0 +1,280 @@
+/*
+ * fused_variants.hip -- libzsvariants: shapes of the fused shard-step kernel
+ * that the benchmark times against the one libzeroshard launches, to show
+ * what each of its launch choices is worth. Measurement only: the library
+ * reuses the per-element arithmetic of zs_kernels.h unchanged, so every
+ * variant must produce the production kernel's bits (the benchmark checks
+ * that before it times anything); only the order and shape of the memory
+ * accesses differ. Nothing in libzeroshard calls it.
+ *
+ * The knobs, each a template parameter of one kernel:
+ *   U      vectors of 8 elements per thread (a block's tile is 2048 U);
+ *   MULTI  W > 1: gradients summed first, then the fp32 state loaded;
+ *          W = 1: the state loaded first, then the one gradient;
+ *   SF     (W > 1 only) the state loaded before the gradient sum instead;
+ *   B      gradient vectors loaded ahead of the in-order adds;
+ *   NTL    gradient loads marked non-temporal;
+ *   NTS    stores marked non-temporal;
+ *   PER    persistent blocks that walk tiles with a grid stride.
+ * The launch adds a residency cap (blocks per CU, through unused dynamic
+ * LDS) and, for persistent grids, the blocks per CU of the grid.
+ * Supported arguments: bf16 gradients and parameters, fp32 partial sums, no
+ * accumulated micro-batch, the flag on the host path, every operand 16-byte
+ * aligned, and n a multiple of the variant's tile.
+ */
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+
+#include "zeroshard.h"
+#include "zs_kernels.h"
+#include "zs_host_setup.h"
+
+namespace {
+
+using namespace zs;
+
+template <bool NT>
+__device__ __forceinline__ void store_f32x8(float *p, const float (&x)[8]) {
+  if constexpr (NT) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f4 *>(p));
+    __builtin_nontemporal_store(f4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f4 *>(p + 4));
+  } else {
+    stf<8>(p, x);
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_bf16x8(uint16_t *p, const float (&x)[8]) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(u32x4{pack2<ZS_BF16>(x[0], x[1]), pack2<ZS_BF16>(x[2], x[3]),
+                                      pack2<ZS_BF16>(x[4], x[5]), pack2<ZS_BF16>(x[6], x[7])},
+                                reinterpret_cast<u32x4 *>(p));
+  } else {
+    st16<8, ZS_BF16>(p, x);
+  }
+}
+
+/* The ring-order sum of fused_kernel (worker p[0] first, the owner last),
+ * with B loads in flight and the load cache policy as knobs. */
+template <int U, int B, bool NTL>
+__device__ __forceinline__ void ring_sum_v(const GradPtrs &g, uint32_t world,
+                                           const uint64_t (&i0)[U], float (&s)[U][8]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) set_up<8, ZS_BF16, ZS_WIRE_FP32>(s[u], ld16<8, NTL>(g.p[0] + i0[u]));
+  uint32_t j = 1;
+  for (; j + B <= world; j += B) {
+    Raw16<8> r[B][U];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[b][u] = ld16<8, NTL>(g.p[j + b] + i0[u]);
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int u = 0; u < U; ++u) add_wire<8, ZS_BF16, ZS_WIRE_FP32>(s[u], r[b][u]);
+  }
+  for (; j < world; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u) add_wire<8, ZS_BF16, ZS_WIRE_FP32>(s[u], ld16<8, NTL>(g.p[j] + i0[u]));
+}
+
+template <int U, bool MULTI, bool SF, int B, bool NTL, bool NTS>
+__device__ __forceinline__ bool variant_tile(const FusedArgs &p, uint64_t base) {
+  uint64_t i0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * 8;
+  float th[U][8], m[U][8], v[U][8], s[U][8];
+  auto load_state = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ldf<8>(p.master_in + i0[u], th[u]);
+      ldf<8>(p.m_in + i0[u], m[u]);
+      ldf<8>(p.v_in + i0[u], v[u]);
+    }
+  };
+  if constexpr (MULTI && !SF) {
+    ring_sum_v<U, B, NTL>(p.g, p.world, i0, s);
+    load_state();
+  } else {
+    load_state();
+    ring_sum_v<U, B, NTL>(p.g, MULTI ? p.world : 1, i0, s);
+  }
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = unscale(average(s[u][e], p.k), p.k);
+      bad |= !__builtin_isfinite(g);
+      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, p.h);
+    }
+    store_f32x8<NTS>(p.master_out + i0[u], th[u]);
+    store_f32x8<NTS>(p.m_out + i0[u], m[u]);
+    store_f32x8<NTS>(p.v_out + i0[u], v[u]);
+    store_bf16x8<NTS>(p.param_out + i0[u], th[u]);
+  }
+  return bad;
+}
+
+template <int U, bool MULTI, bool SF, int B, bool NTL, bool NTS, bool PER>
+__global__ __launch_bounds__(kBlock) void variant_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)kBlock * U * 8;
+  const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
+  bool bad = false;
+  if constexpr (PER) {
+    for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x)
+      bad |= variant_tile<U, MULTI, SF, B, NTL, NTS>(p, t * tile);
+  } else if (blockIdx.x < tiles) {
+    bad = variant_tile<U, MULTI, SF, B, NTL, NTS>(p, (uint64_t)blockIdx.x * tile);
+  }
+  flag_or(p.flag, bad);
+}
+
+struct Variant {
+  const char *name;
+  const void *fn;
+  int u;
+  bool multi;
+  bool persistent;
+};
+
+template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER>
+constexpr Variant mk(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&variant_kernel<U, M, SF, B, NTL, NTS, PER>),
+                 U, M, PER};
+}
+
+/* Entries 0 and 5 are libzeroshard's own shapes for W = 1 and W > 1. */
+const Variant kVariants[] = {
+    mk<1, false, false, 8, true, false, false>("w1: 1 vector/thread, nt gradient loads"),
+    mk<2, false, false, 8, true, false, false>("w1: 2 vectors/thread"),
+    mk<1, false, false, 8, false, false, false>("w1: plain gradient loads"),
+    mk<1, false, false, 8, true, true, false>("w1: nt stores"),
+    mk<1, false, false, 8, true, false, true>("w1: persistent grid"),
+    mk<2, true, false, 8, true, false, false>("wN: 2 vectors/thread, 8 loads ahead, nt loads"),
+    mk<2, true, false, 4, true, false, false>("wN: 4 loads ahead"),
+    mk<1, true, false, 8, true, false, false>("wN: 1 vector/thread"),
+    mk<2, true, false, 8, false, false, false>("wN: plain gradient loads"),
+    mk<2, true, false, 8, true, true, false>("wN: nt stores"),
+    mk<2, true, false, 8, true, false, true>("wN: persistent grid"),
+    mk<2, true, true, 8, true, false, false>("wN: state loaded before the sum"),
+};
+constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
+
+thread_local char g_verr[256] = "";
+
+int vfail(const char *msg) {
+  snprintf(g_verr, sizeof g_verr, "%s", msg);
+  return ZS_ERR_INVALID_ARG;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p % 16) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+/* Number of variants; ids are 0 .. count-1. */
+int zs_variant_count(void) { return kCount; }
+
+/* Static description of variant `id` (NULL for an id out of range). */
+const char *zs_variant_name(int id) { return id >= 0 && id < kCount ? kVariants[id].name : nullptr; }
+
+/* Elements per block tile of variant `id` (0 for an id out of range). */
+int zs_variant_tile(int id) { return id >= 0 && id < kCount ? kBlock * 8 * kVariants[id].u : 0; }
+
+/* 1 if variant `id` is for W > 1, 0 if for W = 1, -1 for an id out of range. */
+int zs_variant_multi(int id) { return id >= 0 && id < kCount ? (kVariants[id].multi ? 1 : 0) : -1; }
+
+/* Detail of this thread's last refusal ("" after a launch). */
+const char *zs_variant_last_error(void) { return g_verr; }
+
+/* One launch of variant `id` on the arguments of zs_step_fused (same
+ * meaning; the flag is OR-ed into a->overflow_flag), on `stream`.
+ *   blocks_per_cu: residency cap, 0 = none, 1..8;
+ *   persist_per_cu: blocks per CU of a persistent variant's grid (1..8;
+ *                   ignored by the others).
+ * Returns ZS_OK when enqueued; ZS_ERR_INVALID_ARG, before any launch, for an
+ * id out of range, a world that does not suit the variant, a dtype, wire or
+ * accumulated input it does not support, a null or unaligned pointer, n not
+ * a multiple of its tile, or a cap out of range; ZS_ERR_HIP when the launch
+ * fails. Asynchronous; nothing is allocated. */
+int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
+                      uint32_t persist_per_cu, void *stream) {
+  if (id < 0 || id >= kCount) return vfail("variant id out of range");
+  const Variant &v = kVariants[id];
+  if (!a || !a->worker_grads || !a->master_in || !a->m_in || !a->v_in || !a->master_out ||
+      !a->m_out || !a->v_out || !a->gather_buf || !a->overflow_flag)
+    return vfail("null argument");
+  if (a->world == 0 || a->world > ZS_MAX_WORLD || a->rank >= a->world)
+    return vfail("need 0 < world <= 64 and rank < world");
+  if (v.multi != (a->world > 1)) return vfail("variant does not suit this world size");
+  if (a->grad_dtype != ZS_BF16 || a->param_dtype != ZS_BF16 || a->wire_dtype != ZS_WIRE_FP32 ||
+      a->acc_in)
+    return vfail("variants take bf16 gradients and parameters, fp32 sums, no acc_in");
+  if (blocks_per_cu > 8 || (v.persistent && (persist_per_cu < 1 || persist_per_cu > 8)))
+    return vfail("cap or persistent blocks per CU out of range");
+  const uint64_t tile = (uint64_t)kBlock * 8 * v.u;
+  if (a->n == 0 || a->n % tile != 0 || a->n / tile > 0x7fffffffull)
+    return vfail("n must be a positive multiple of the variant's tile");
+  FusedArgs p;
+  p.world = a->world;
+  p.wire = ZS_WIRE_FP32;
+  p.n = a->n;
+  for (uint32_t j = 0; j < a->world; ++j) {
+    const void *g = a->worker_grads[(a->rank + 1 + j) % a->world];
+    if (!g || !aligned16(g)) return vfail("null or unaligned gradient buffer");
+    p.g.p[j] = static_cast<const uint16_t *>(g);
+  }
+  for (uint32_t j = a->world; j < ZS_MAX_WORLD; ++j) p.g.p[j] = nullptr;
+  p.acc_in = nullptr;
+  p.master_in = a->master_in;
+  p.m_in = a->m_in;
+  p.v_in = a->v_in;
+  p.master_out = a->master_out;
+  p.m_out = a->m_out;
+  p.v_out = a->v_out;
+  p.param_out = static_cast<uint16_t *>(a->gather_buf) + a->gather_offset;
+  p.flag = a->overflow_flag;
+  p.dev = nullptr;
+  p.lr = a->hp.lr;
+  const void *ptrs[] = {p.master_in, p.m_in, p.v_in, p.master_out, p.m_out, p.v_out, p.param_out};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return vfail("operands must be 16-byte aligned");
+  if (!zs_host::make_scales(a->world, a->hp.loss_scale, &p.k)) return vfail("bad loss scale");
+  if (!zs_host::make_adam(&a->hp, &p.h)) return vfail("step_t must be >= 1");
+  int dev = 0, cus = 0, lds_per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess)
+    return ZS_ERR_HIP;
+  size_t lds = 0;
+  if (blocks_per_cu) {
+    const int bytes = (lds_per_cu / (int)blocks_per_cu - 1024) / 256 * 256;
+    lds = bytes > 0 ? (size_t)bytes : 0;
+  }
+  if (lds > 65536 &&
+      hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_per_cu) != hipSuccess)
+    return ZS_ERR_HIP;
+  const uint64_t tiles = a->n / tile;
+  uint64_t grid = tiles;
+  if (v.persistent) {
+    const uint64_t want = (uint64_t)cus * persist_per_cu;
+    grid = want < tiles ? want : tiles;
+  }
+  void *args[] = {&p};
+  const hipError_t e = hipLaunchKernel(v.fn, dim3((unsigned)grid), dim3(kBlock), args, lds,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    snprintf(g_verr, sizeof g_verr, "launch failed: %s", hipGetErrorString(e));
+    return ZS_ERR_HIP;
+  }
+  g_verr[0] = 0;
+  return ZS_OK;
+}
+
+}  // extern "C"

@@ -22,6 +22,7 @@
 #include "zs_aux_kernels.h"
 #include "zs_hparams.h"
 #include "zs_host_powers.h"
+#include "zs_host_setup.h"
 #include "zs_offload_pieces.h"
 
 
@@ -60,46 +61,8 @@ bool valid_wire(int w) { return w == ZS_WIRE_FP32 || w == ZS_WIRE_BF16 || w == Z
 /* zs_step_commit polls the stream for errors this often while it waits. */
 constexpr int kQueryMicros = 1000;
 
-/* Exact power of two with a normal reciprocal: then x * (1/p) == x / p. */
-bool exact_pow2(float p, float *inv) {
-  if (!(p > 0.0f) || !isfinite(p)) return false;
-  int e;
-  float m = frexpf(p, &e);         /* p = m * 2^e, m in [0.5, 1) */
-  if (m != 0.5f) return false;
-  int k = e - 1;                   /* p = 2^k */
-  if (k < -126 || k > 126) return false;
-  *inv = ldexpf(1.0f, -k);
-  return true;
-}
-
-bool make_scales(uint32_t world, float loss_scale, Scales *k) {
-  if (!(loss_scale > 0.0f) || !isfinite(loss_scale)) return false;
-  k->wf = (float)world;
-  k->w_pow2 = exact_pow2(k->wf, &k->inv_w) ? 1 : 0;
-  if (!k->w_pow2) k->inv_w = 0.0f;
-  k->sf = loss_scale;
-  k->s_pow2 = exact_pow2(loss_scale, &k->inv_s) ? 1 : 0;
-  if (!k->s_pow2) k->inv_s = 0.0f;
-  return true;
-}
-
-/* Per-step scalars in double, rounded once to fp32. beta^t is formed by t
- * repeated multiplications (continued from the previous call when t grows). */
-bool make_adam(const zs_adamw_hparams *hp, AdamK *k) {
-  if (hp->step_t == 0) return false;
-  double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
-  double b1t, b2t;
-  zs_host::beta_powers(hp->beta1, hp->beta2, hp->step_t, &b1t, &b2t);
-  k->alpha = (float)(lr / (1.0 - b1t));
-  k->b2 = (float)sqrt(1.0 - b2t);
-  k->delta = (float)(1.0 - lr * wd);
-  k->c1 = (float)(1.0 - b1);
-  k->c2 = (float)(1.0 - b2);
-  k->beta1 = hp->beta1;
-  k->beta2 = hp->beta2;
-  k->eps = hp->eps;
-  return true;
-}
+using zs_host::make_adam;
+using zs_host::make_scales;
 
 /* ------------------------------------------------------------------------
  * Residency and tile of the fused kernel. With writes mixed into the read

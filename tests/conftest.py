@@ -35,7 +35,8 @@ _ensure_host_built()
 def hip_built():
     """The HIP libraries (built here, from source, only if missing)."""
     from sharded_mixed_precision_zs_amd import build as pkg_build
-    if not all(os.path.exists(p) for p in (pkg_build.LIB, pkg_build.SYNTH_DEV, pkg_build.COPY)):
+    if not all(os.path.exists(p) for p in (pkg_build.LIB, pkg_build.SYNTH_DEV, pkg_build.COPY,
+                                           pkg_build.VARIANTS)):
         pkg_build.build_all()
     return pkg_build
 

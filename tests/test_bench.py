@@ -89,3 +89,17 @@ def test_fused_instance_names_match_the_kernel_template():
         "zs::fused_kernel<8, 2, true, true, 1, 1, 0>"
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
     assert bench.fused_bytes_per_param(4, 4) == (24, 14)
+
+
+def test_variant_sweep_plans_fit_their_workloads(hip_built):
+    """Every variant a sweep plan names suits its workload's world size, and
+    each plan starts with the production shape at libzeroshard's own cap."""
+    from sharded_mixed_precision_zs_amd import synth
+    lib = bench._variantlib()
+    caps = {1: 2, 8: 3, 64: 0}
+    for name, plan in bench.VARIANT_SWEEP.items():
+        W = synth.WORKLOADS[name].world
+        for v, cap, per in plan:
+            assert lib.zs_variant_multi(v) == (1 if W > 1 else 0), (name, v)
+            assert 0 <= cap <= 8 and 0 <= per <= 8
+        assert plan[0] == ((0 if W == 1 else 5), caps[W], 0), name

@@ -51,14 +51,14 @@ def _assert_one_runtime(maps):
         assert os.path.realpath(maps[key][0]).startswith(_torch_lib_dir()), maps
 
 
-@pytest.mark.parametrize("which", ["LIB", "COPY", "SYNTH_DEV"])
+@pytest.mark.parametrize("which", ["LIB", "COPY", "SYNTH_DEV", "VARIANTS"])
 def test_library_loaded_before_torch_shares_its_runtime(hip_built, which):
     """Raw ctypes load first, torch second: still one runtime, torch's."""
     path = getattr(hip_built, which)
     _assert_one_runtime(_mapped(f"ctypes.CDLL({path!r})\nimport torch"))
 
 
-@pytest.mark.parametrize("which", ["LIB", "COPY", "SYNTH_DEV"])
+@pytest.mark.parametrize("which", ["LIB", "COPY", "SYNTH_DEV", "VARIANTS"])
 def test_library_loaded_after_torch_shares_its_runtime(hip_built, which):
     path = getattr(hip_built, which)
     _assert_one_runtime(_mapped(f"import torch\nctypes.CDLL({path!r})"))
