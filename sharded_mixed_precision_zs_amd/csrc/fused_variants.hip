@@ -18,6 +18,9 @@
  *   PER    persistent blocks that walk tiles with a grid stride.
  * The launch adds a residency cap (blocks per CU, through unused dynamic
  * LDS) and, for persistent grids, the blocks per CU of the grid.
+ * A second kernel splits the waves of a block by role (split_kernel below):
+ * loader waves load, sum and update and leave the new state in LDS; storer
+ * waves drain it to HBM.
  * Supported arguments: bf16 gradients and parameters, fp32 partial sums, no
  * accumulated micro-batch, the flag on the host path, every operand 16-byte
  * aligned, and n a multiple of the variant's tile.
@@ -133,18 +136,106 @@ __global__ __launch_bounds__(kBlock) void variant_kernel(FusedArgs p) {
   flag_or(p.flag, bad);
 }
 
+/* ------------------------------------------------------------------------
+ * Loader/storer split. NL loader waves each take one 8-element vector per
+ * lane of a tile of NL * 512 elements: they load, sum and update it exactly
+ * as variant_tile does and leave the new master, m and v in an LDS slot. NS
+ * storer waves drain the previous tile's slot to HBM, casting the 16-bit
+ * parameters from the stored master. Loaders never issue a global store, so
+ * none of their loads waits behind the completion of a store (loads and
+ * stores share one in-order memory counter per wave on this family); the
+ * storers' stores complete in the background. Two slots alternate; every
+ * wave of the block passes one barrier per tile (LDS-only fences, so no
+ * wave waits there for its global memory operations), and the loop runs
+ * one extra iteration to drain the last slot. The grid is persistent; every
+ * wave of a block runs the same number of iterations.
+ * ---------------------------------------------------------------------- */
+
+template <int NL>
+constexpr int split_tile() { return NL * 64 * 8; }
+
+template <int NL, int NS, bool MULTI, int B>
+__global__ __launch_bounds__((NL + NS) * 64) void split_kernel(FusedArgs p) {
+  constexpr int kTile = split_tile<NL>();
+  extern __shared__ float lds[];  /* [2 slots][master, m, v][kTile] */
+  const uint64_t tiles = p.n / kTile;
+  const uint64_t G = gridDim.x;
+  const uint64_t mine = blockIdx.x < tiles ? (tiles - blockIdx.x + G - 1) / G : 0;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63u);
+  bool bad = false;
+  for (uint64_t it = 0; it <= mine; ++it) {
+    float *fill = lds + (it & 1) * 3 * kTile;          /* tile it          */
+    float *drain = lds + ((it + 1) & 1) * 3 * kTile;   /* tile it - 1      */
+    if (wave < NL) {
+      if (it < mine) {
+        const int local = (wave * 64 + lane) * 8;
+        const uint64_t i0[1] = {(blockIdx.x + it * G) * (uint64_t)kTile + (uint64_t)local};
+        float th[8], m[8], v[8], s[1][8];
+        if constexpr (MULTI) {
+          ring_sum_v<1, B, true>(p.g, p.world, i0, s);
+          ldf<8>(p.master_in + i0[0], th);
+          ldf<8>(p.m_in + i0[0], m);
+          ldf<8>(p.v_in + i0[0], v);
+        } else {
+          ldf<8>(p.master_in + i0[0], th);
+          ldf<8>(p.m_in + i0[0], m);
+          ldf<8>(p.v_in + i0[0], v);
+          ring_sum_v<1, B, true>(p.g, 1, i0, s);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float g = unscale(average(s[0][e], p.k), p.k);
+          bad |= !__builtin_isfinite(g);
+          th[e] = adamw_elem(th[e], m[e], v[e], g, p.h);
+        }
+        stf<8>(fill + local, th);
+        stf<8>(fill + kTile + local, m);
+        stf<8>(fill + 2 * kTile + local, v);
+      }
+    } else if (it > 0) {
+      const uint64_t base = (blockIdx.x + (it - 1) * G) * (uint64_t)kTile;
+      const int sw = wave - NL;
+#pragma unroll
+      for (int j = 0; j < NL / NS; ++j) {
+        const int local = ((j * NS + sw) * 64 + lane) * 8;
+        float x[8];
+        ldf<8>(drain + local, x);
+        stf<8>(p.master_out + base + local, x);
+        st16<8, ZS_BF16>(p.param_out + base + local, x);
+        ldf<8>(drain + kTile + local, x);
+        stf<8>(p.m_out + base + local, x);
+        ldf<8>(drain + 2 * kTile + local, x);
+        stf<8>(p.v_out + base + local, x);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
+  flag_or(p.flag, bad);
+}
+
 struct Variant {
   const char *name;
   const void *fn;
-  int u;
+  int tile;        /* elements per block tile                        */
   bool multi;
   bool persistent;
+  int block;       /* threads per block                              */
+  int lds;         /* dynamic LDS the kernel uses (0: none)          */
 };
 
 template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER>
 constexpr Variant mk(const char *name) {
   return Variant{name, reinterpret_cast<const void *>(&variant_kernel<U, M, SF, B, NTL, NTS, PER>),
-                 U, M, PER};
+                 kBlock * 8 * U, M, PER, kBlock, 0};
+}
+
+template <int NL, int NS, bool M, int B>
+constexpr Variant mk_split(const char *name) {
+  static_assert(NL % NS == 0, "each storer wave drains NL / NS vectors per lane");
+  return Variant{name, reinterpret_cast<const void *>(&split_kernel<NL, NS, M, B>),
+                 split_tile<NL>(), M, true, (NL + NS) * 64, 2 * 3 * split_tile<NL>() * 4};
 }
 
 /* Entries 0 and 5 are libzeroshard's own shapes for W = 1 and W > 1. */
@@ -161,6 +252,13 @@ const Variant kVariants[] = {
     mk<2, true, false, 8, true, true, false>("wN: nt stores"),
     mk<2, true, false, 8, true, false, true>("wN: persistent grid"),
     mk<2, true, true, 8, true, false, false>("wN: state loaded before the sum"),
+    mk_split<4, 1, false, 8>("w1: split, 4 loader + 1 storer waves"),
+    mk_split<4, 2, false, 8>("w1: split, 4 loader + 2 storer waves"),
+    mk_split<8, 2, false, 8>("w1: split, 8 loader + 2 storer waves"),
+    mk_split<4, 1, true, 8>("wN: split, 4 loader + 1 storer waves"),
+    mk_split<4, 2, true, 8>("wN: split, 4 loader + 2 storer waves"),
+    mk_split<8, 2, true, 8>("wN: split, 8 loader + 2 storer waves"),
+    mk_split<4, 1, true, 16>("wN: split, 4 loader + 1 storer waves, 16 loads ahead"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 
@@ -184,7 +282,7 @@ int zs_variant_count(void) { return kCount; }
 const char *zs_variant_name(int id) { return id >= 0 && id < kCount ? kVariants[id].name : nullptr; }
 
 /* Elements per block tile of variant `id` (0 for an id out of range). */
-int zs_variant_tile(int id) { return id >= 0 && id < kCount ? kBlock * 8 * kVariants[id].u : 0; }
+int zs_variant_tile(int id) { return id >= 0 && id < kCount ? kVariants[id].tile : 0; }
 
 /* 1 if variant `id` is for W > 1, 0 if for W = 1, -1 for an id out of range. */
 int zs_variant_multi(int id) { return id >= 0 && id < kCount ? (kVariants[id].multi ? 1 : 0) : -1; }
@@ -217,7 +315,7 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
     return vfail("variants take bf16 gradients and parameters, fp32 sums, no acc_in");
   if (blocks_per_cu > 8 || (v.persistent && (persist_per_cu < 1 || persist_per_cu > 8)))
     return vfail("cap or persistent blocks per CU out of range");
-  const uint64_t tile = (uint64_t)kBlock * 8 * v.u;
+  const uint64_t tile = (uint64_t)v.tile;
   if (a->n == 0 || a->n % tile != 0 || a->n / tile > 0x7fffffffull)
     return vfail("n must be a positive multiple of the variant's tile");
   FusedArgs p;
@@ -252,11 +350,12 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
       hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
           hipSuccess)
     return ZS_ERR_HIP;
-  size_t lds = 0;
+  size_t lds = (size_t)v.lds;
   if (blocks_per_cu) {
     const int bytes = (lds_per_cu / (int)blocks_per_cu - 1024) / 256 * 256;
-    lds = bytes > 0 ? (size_t)bytes : 0;
+    if (bytes > v.lds) lds = (size_t)bytes;
   }
+  if (lds > (size_t)lds_per_cu) return vfail("the variant's LDS exceeds the CU's");
   if (lds > 65536 &&
       hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_per_cu) != hipSuccess)
     return ZS_ERR_HIP;
@@ -267,8 +366,8 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
     grid = want < tiles ? want : tiles;
   }
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(v.fn, dim3((unsigned)grid), dim3(kBlock), args, lds,
-                                       static_cast<hipStream_t>(stream));
+  const hipError_t e = hipLaunchKernel(v.fn, dim3((unsigned)grid), dim3((unsigned)v.block), args,
+                                       lds, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     snprintf(g_verr, sizeof g_verr, "launch failed: %s", hipGetErrorString(e));
     return ZS_ERR_HIP;

@@ -55,6 +55,8 @@ def test_catalogue(vlib):
     assert vlib.zs_variant_name(count) is None and vlib.zs_variant_name(-1) is None
     assert [vlib.zs_variant_multi(i) for i in (0, 5)] == [0, 1]
     assert vlib.zs_variant_tile(0) == 2048 and vlib.zs_variant_tile(5) == 4096
+    splits = [i for i in range(count) if "split" in names[i]]
+    assert splits and all(vlib.zs_variant_tile(i) in (2048, 4096) for i in splits)
     assert vlib.zs_variant_tile(count) == 0 and vlib.zs_variant_multi(count) == -1
 
 
@@ -81,10 +83,12 @@ def test_refusals_before_any_launch(vlib, zs):
 @pytest.mark.parametrize("world", [1, 5])
 def test_every_variant_computes_the_step(vlib, zs, world):
     """Each variant of the world's family writes the oracle's state and
-    parameters bit for bit, at every residency cap it is timed with."""
+    parameters bit for bit, at several residency caps; the persistent and
+    split variants walk several tiles per block (n is 600 of the smaller
+    tiles, against a grid of at most 2 blocks per CU)."""
     import torch
     rng = np.random.default_rng(world)
-    n = 3 * 4096
+    n = 600 * 2048
     g16 = [((rng.standard_normal(n) * 1e-3).astype(F32).view(np.uint32) >> 16).astype(np.uint16)
            for _ in range(world)]
     master = (rng.standard_normal(n) * 0.02).astype(F32)
