@@ -544,7 +544,8 @@ VARIANT_SWEEP = {
     "gpt2s-w8": [(5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
                  (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3)],
     "7p5b-shard-w64": [(5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0), (9, 0, 0),
-                       (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1), (18, 0, 3)],
+                       (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1), (18, 0, 3),
+                       (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2)],
 }
 VARIANT_N_MAX = 1 << 30   # W = 1: the first 2^30 parameters of the 7B state (3 sets fit HBM)
 
@@ -657,6 +658,69 @@ def variant_sweep(name, plan, reps, torch, rounds=3):
                 reps_per_round=reps, rounds=rounds, results=out)
 
 
+def phase_sweep(torch, reps=10, rounds=2):
+    """Reads and writes of the 7.5B shard's step separated in time, with the
+    stream probe: per chunk of the shard, a read-only probe kernel (the 64
+    gradient and 3 state streams) then a write-only one (the 3 fp32 and the
+    16-bit output streams), back to back on one stream, for 1 to 64 chunks;
+    beside them the mixed probe and the read-only and write-only passes over
+    the whole shard. What a kernel that kept a chunk's outputs on chip until
+    the chunk's reads were done could at best reach, by chunk count."""
+    import ctypes as C
+    lib = _copylib()
+    n, W = N_W64, 64
+    g = torch.empty((W, n), dtype=torch.int16, device="cuda").random_()
+    ins = [torch.empty(n, dtype=torch.int32, device="cuda").random_() for _ in range(3)]
+    outs = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(3)]
+    o16 = torch.empty(n, dtype=torch.int16, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+
+    def ptrs(ts, off, es):
+        return (C.c_void_p * 64)(*[t.data_ptr() + off * es for t in ts])
+
+    def probe(c0, cn, reads, writes):
+        rc = lib.zs_stream_probe(ptrs([g[k] for k in range(W)] if reads else [], c0, 2),
+                                 W if reads else 0, ptrs(ins if reads else [], c0, 4),
+                                 3 if reads else 0, ptrs(outs if writes else [], c0, 4),
+                                 3 if writes else 0, o16.data_ptr() + 2 * c0 if writes else None,
+                                 cn, 2, 0, sink.data_ptr(), 0x6D2B79F5,
+                                 torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"zs_stream_probe returned {rc}")
+
+    def chunked(chunks, phased, reads=True, writes=True):
+        size = -(-n // chunks // 4096) * 4096
+        c0 = 0
+        while c0 < n:
+            cn = min(size, n - c0)
+            if phased:
+                probe(c0, cn, True, False)
+                probe(c0, cn, False, True)
+            else:
+                probe(c0, cn, reads, writes)
+            c0 += cn
+
+    legs = [("mixed, whole shard", lambda: chunked(1, False)),
+            ("reads only, whole shard", lambda: chunked(1, False, writes=False)),
+            ("writes only, whole shard", lambda: chunked(1, False, reads=False))]
+    legs += [(f"phased, {k} chunk(s)", (lambda k=k: chunked(k, True))) for k in (1, 2, 4, 8, 16, 64)]
+    times = {name: [] for name, _ in legs}
+    for _ in range(rounds):
+        for name, fn in legs:
+            times[name].append(_time_calls(torch, fn, reps))
+    per_param = {"reads only, whole shard": 140, "writes only, whole shard": 14}
+    out = []
+    for name, t in times.items():
+        ms = sum(t) / len(t)
+        b = per_param.get(name, 154)
+        out.append(dict(leg=name, ms=ms, ms_rounds=t, bytes_per_param=b,
+                        gbps=b * n / (ms * 1e-3) / 1e9))
+        log(f"phases: {name}: {ms:.4f} ms ({out[-1]['gbps']:.0f} GB/s)")
+    del g, ins, outs, o16
+    torch.cuda.empty_cache()
+    return dict(n=n, world=W, bytes_per_param=154, reps=reps, rounds=rounds, legs=out)
+
+
 def side_leg(name, fn, torch):
     """Run a leg reported beside the headline; a failure (for instance too
     little free device memory) is recorded in the JSON line as
@@ -694,7 +758,7 @@ def main():
                     help="skip timing the CPU oracle (cpu_baseline)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host update) leg")
-    ap.add_argument("--no-ceilings", action="store_true",
+    ap.add_argument("--no-ceilings", "--no-copy-ceiling", dest="no_ceilings", action="store_true",
                     help="skip the copy and stream-probe ceilings")
     ap.add_argument("--ceilings", default="",
                     help="comma-separated stream-probe names to run (default: all)")
@@ -707,6 +771,9 @@ def main():
                          "each and print that table as the JSON line instead")
     ap.add_argument("--sweep-n", type=int, default=1 << 25,
                     help="shard size of the --sweep-world runs")
+    ap.add_argument("--sweep-phases", action="store_true",
+                    help="time the 7.5B shard's reads and writes separated in time (stream "
+                         "probe, 1 to 64 chunks) and print that table as the JSON line instead")
     ap.add_argument("--sweep-variants", default="",
                     help="comma-separated workloads (of " + ", ".join(VARIANT_SWEEP) + "): time "
                          "the fused kernel's shapes of libzsvariants against libzeroshard's and "
@@ -728,6 +795,10 @@ def main():
         sweep = world_sweep(worlds, args.sweep_n, args.steps, args.warmup, torch)
         print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "sweep": sweep}))
+        return
+    if args.sweep_phases:
+        print(json.dumps({"metric": "7.5B-shard step mix, reads and writes separated in time",
+                          "unit": "ms", "phases": phase_sweep(torch)}))
         return
     if args.sweep_variants:
         res = [variant_sweep(w, VARIANT_SWEEP[w], max(4, args.steps), torch)

@@ -20,11 +20,13 @@
  * LDS) and, for persistent grids, the blocks per CU of the grid.
  * A second kernel splits the waves of a block by role (split_kernel below):
  * loader waves load, sum and update and leave the new state in LDS; storer
- * waves drain it to HBM.
+ * waves drain it to HBM. A third separates reads from writes in time across
+ * the whole chip (phased_kernel below).
  * Supported arguments: bf16 gradients and parameters, fp32 partial sums, no
  * accumulated micro-batch, the flag on the host path, every operand 16-byte
  * aligned, and n a multiple of the variant's tile.
  */
+#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -215,20 +217,115 @@ __global__ __launch_bounds__((NL + NS) * 64) void split_kernel(FusedArgs p) {
   flag_or(p.flag, bad);
 }
 
+/* ------------------------------------------------------------------------
+ * Reads and writes in separate phases, chip-wide. A cooperative grid (every
+ * block resident) walks the shard in chunks of gridDim.x * kPhBlock * V
+ * vectors; in a chunk each thread first loads, sums and updates V vectors
+ * of its block's region -- RV of them kept in registers, LV in its own LDS
+ * words -- while no wave of the grid stores; then, after a grid-wide sync,
+ * every thread stores its V vectors' state and parameters. SYNCS = 2 adds a
+ * second sync after the stores, so that no block reads the next chunk while
+ * another still writes. Vector v of thread t covers elements
+ * base + (v * kPhBlock + t) * 8 of the block's region; vectors past n are
+ * skipped (the host checks n % 8 == 0), every thread passes every sync.
+ * ---------------------------------------------------------------------- */
+
+constexpr int kPhBlock = 512;
+
+template <int RV, int LV, int B, int SYNCS>
+__global__ __launch_bounds__(kPhBlock) void phased_kernel(FusedArgs p) {
+  constexpr int V = RV + LV;
+  extern __shared__ float lds[];  /* [LV][master, m, v][kPhBlock * 8] */
+  namespace cg = cooperative_groups;
+  cg::grid_group grid = cg::this_grid();
+  const uint64_t per_block = (uint64_t)kPhBlock * 8 * V;
+  const uint64_t chunk = per_block * gridDim.x;
+  const uint64_t chunks = (p.n + chunk - 1) / chunk;
+  float res[RV > 0 ? RV : 1][3][8];
+  bool bad = false;
+  for (uint64_t c = 0; c < chunks; ++c) {
+    const uint64_t base = c * chunk + (uint64_t)blockIdx.x * per_block;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const uint64_t i0[1] = {base + ((uint64_t)v * kPhBlock + threadIdx.x) * 8};
+      if (i0[0] < p.n) {
+        float th[8], m[8], w[8], s[1][8];
+        ring_sum_v<1, B, true>(p.g, p.world, i0, s);
+        ldf<8>(p.master_in + i0[0], th);
+        ldf<8>(p.m_in + i0[0], m);
+        ldf<8>(p.v_in + i0[0], w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float g = unscale(average(s[0][e], p.k), p.k);
+          bad |= !__builtin_isfinite(g);
+          th[e] = adamw_elem(th[e], m[e], w[e], g, p.h);
+        }
+        if (v < RV) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            res[v < RV ? v : 0][0][e] = th[e];
+            res[v < RV ? v : 0][1][e] = m[e];
+            res[v < RV ? v : 0][2][e] = w[e];
+          }
+        } else {
+          float *own = lds + (v - RV) * 3 * kPhBlock * 8 + threadIdx.x * 8;
+          stf<8>(own, th);
+          stf<8>(own + kPhBlock * 8, m);
+          stf<8>(own + 2 * kPhBlock * 8, w);
+        }
+      }
+    }
+    grid.sync();
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const uint64_t i = base + ((uint64_t)v * kPhBlock + threadIdx.x) * 8;
+      if (i < p.n) {
+        float th[8], m[8], w[8];
+        if (v < RV) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            th[e] = res[v < RV ? v : 0][0][e];
+            m[e] = res[v < RV ? v : 0][1][e];
+            w[e] = res[v < RV ? v : 0][2][e];
+          }
+        } else {
+          const float *own = lds + (v - RV) * 3 * kPhBlock * 8 + threadIdx.x * 8;
+          ldf<8>(own, th);
+          ldf<8>(own + kPhBlock * 8, m);
+          ldf<8>(own + 2 * kPhBlock * 8, w);
+        }
+        stf<8>(p.master_out + i, th);
+        st16<8, ZS_BF16>(p.param_out + i, th);
+        stf<8>(p.m_out + i, m);
+        stf<8>(p.v_out + i, w);
+      }
+    }
+    if constexpr (SYNCS == 2) grid.sync();
+  }
+  flag_or(p.flag, bad);
+}
+
 struct Variant {
   const char *name;
   const void *fn;
-  int tile;        /* elements per block tile                        */
+  int tile;        /* elements per block tile (n must be a multiple)  */
   bool multi;
   bool persistent;
   int block;       /* threads per block                              */
   int lds;         /* dynamic LDS the kernel uses (0: none)          */
+  bool cooperative = false;  /* launched cooperatively (grid sync)   */
 };
 
 template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER>
 constexpr Variant mk(const char *name) {
   return Variant{name, reinterpret_cast<const void *>(&variant_kernel<U, M, SF, B, NTL, NTS, PER>),
                  kBlock * 8 * U, M, PER, kBlock, 0};
+}
+
+template <int RV, int LV, int B, int SYNCS>
+constexpr Variant mk_phased(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&phased_kernel<RV, LV, B, SYNCS>), 8, true,
+                 true, kPhBlock, LV * 3 * kPhBlock * 8 * 4, true};
 }
 
 template <int NL, int NS, bool M, int B>
@@ -259,6 +356,10 @@ const Variant kVariants[] = {
     mk_split<4, 2, true, 8>("wN: split, 4 loader + 2 storer waves"),
     mk_split<8, 2, true, 8>("wN: split, 8 loader + 2 storer waves"),
     mk_split<4, 1, true, 16>("wN: split, 4 loader + 1 storer waves, 16 loads ahead"),
+    mk_phased<2, 1, 8, 1>("wN: phased, 3 vectors/thread (2 in registers), 1 sync per chunk"),
+    mk_phased<2, 1, 8, 2>("wN: phased, 3 vectors/thread (2 in registers), 2 syncs per chunk"),
+    mk_phased<3, 1, 8, 1>("wN: phased, 4 vectors/thread (3 in registers), 1 sync per chunk"),
+    mk_phased<1, 1, 8, 1>("wN: phased, 2 vectors/thread (1 in registers), 1 sync per chunk"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 
@@ -366,8 +467,14 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
     grid = want < tiles ? want : tiles;
   }
   void *args[] = {&p};
-  const hipError_t e = hipLaunchKernel(v.fn, dim3((unsigned)grid), dim3((unsigned)v.block), args,
-                                       lds, static_cast<hipStream_t>(stream));
+  /* a cooperative launch is refused, not run, unless every block of its
+   * grid can be resident at once */
+  const hipError_t e =
+      v.cooperative
+          ? hipLaunchCooperativeKernel(v.fn, dim3((unsigned)grid), dim3((unsigned)v.block), args,
+                                       (unsigned)lds, static_cast<hipStream_t>(stream))
+          : hipLaunchKernel(v.fn, dim3((unsigned)grid), dim3((unsigned)v.block), args, lds,
+                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     snprintf(g_verr, sizeof g_verr, "launch failed: %s", hipGetErrorString(e));
     return ZS_ERR_HIP;

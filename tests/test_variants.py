@@ -103,6 +103,8 @@ def test_every_variant_computes_the_step(vlib, zs, world):
     for vid in range(vlib.zs_variant_count()):
         if vlib.zs_variant_multi(vid) != (1 if world > 1 else 0):
             continue
+        if "phased" in vlib.zs_variant_name(vid).decode():
+            continue  # test_phased_variants_walk_several_chunks
         for cap in (0, 2, 5):
             dout = [torch.full((n,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
             par = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
@@ -118,3 +120,41 @@ def test_every_variant_computes_the_step(vlib, zs, world):
             for got, want, name in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
                 assert_bits_equal(down32(got), want, f"{what} {name}")
             assert np.array_equal(down16(par), po), what
+
+
+@pytest.mark.gpu
+def test_phased_variants_walk_several_chunks(vlib, zs):
+    """The phase-separated variants (cooperative grid, reads and writes in
+    separate chunk-wide phases) write the oracle's bits over a shard of two
+    to three chunks, the last one partial, at one block per CU."""
+    import torch
+    world, n = 6, 2200 * 2048
+    rng = np.random.default_rng(77)
+    g16 = [((rng.standard_normal(n) * 1e-3).astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+           for _ in range(world)]
+    master = (rng.standard_normal(n) * 0.02).astype(F32)
+    m = (rng.standard_normal(n) * 1e-4).astype(F32)
+    v = rng.uniform(0, 1e-6, n).astype(F32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    f, mo, mmo, vo, po = oracle.shard_step(g16, 2, "bf16", "bf16", master, m, v, loss_scale=8.0,
+                                           step_t=5, threads=8, **hp)
+    grads = [up16(g, "bf16") for g in g16]
+    din = [up32(x) for x in (master, m, v)]
+    phased = [i for i in range(vlib.zs_variant_count())
+              if "phased" in vlib.zs_variant_name(i).decode()]
+    assert phased
+    for vid in phased:
+        dout = [torch.full((n,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+        par = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        args = zs.StepArgs(grads, 2, n, *din, *dout, par, 0, flag,
+                           zs.hparams(**hp, loss_scale=8.0, step_t=5))
+        rc = vlib.zs_variant_launch(vid, C.addressof(args.args), 0, 1,
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, vlib.zs_variant_last_error().decode()
+        torch.cuda.synchronize()
+        what = f"variant {vid} ({vlib.zs_variant_name(vid).decode()})"
+        assert int(flag.item()) == f == 0, what
+        for got, want, name in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
+            assert_bits_equal(down32(got), want, f"{what} {name}")
+        assert np.array_equal(down16(par), po), what
