@@ -24,7 +24,8 @@ committed rocprofv3 request-counter passes (profiles/fused_step_traffic.md),
 when they were taken on the current kernel source. `ceilings` are the rates
 of libzscopy's measurement kernels in the same run: a plain copy, read-only
 and write-only streams, and the step's own mix of streams with no arithmetic
-(the stream probe). `cpu_baseline` times the CPU oracle on a bounded sample of
+(the stream probe); `read_write_harmonic_gbps` combines the headline step's
+read-only and write-only stream rates at its read:write bytes. `cpu_baseline` times the CPU oracle on a bounded sample of
 the headline workload on this host's cores.
 
 Beside the headline: the step with its decision on the host (`host_commit`),
@@ -861,7 +862,13 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     head = summary(main_res, wl)
     roofs[args.workload] = head["roofline"]
-    mix = "step_mix_w1" if wl.world == 1 else "step_mix_w64" if wl.world == 64 else None
+    # the headline mix's own streams alone: read-only and write-only probe
+    # rates, and their harmonic combination at the step's read:write bytes
+    alone = {1: ("read_only_w1_streams", "write_only_w1_streams")}.get(wl.world)
+    harmonic = None
+    if alone and all(k in ceilings for k in alone):
+        rd, wr = fused_bytes_per_param(wl.world, wl.accum)
+        harmonic = (rd + wr) / (rd / ceilings[alone[0]]["gbps"] + wr / ceilings[alone[1]]["gbps"])
     out = {
         "metric": METRIC,
         "value": main_res["params_per_s"],
@@ -886,8 +893,9 @@ def main():
         "memcpy_d2d_gbps": copies.get("memcpy"),
         "hbm_pct_of_copy_ceiling": (100.0 * main_res["hbm_gbps"] / copy_ceiling
                                     if copy_ceiling else None),
-        "hbm_pct_of_step_mix_ceiling": (100.0 * main_res["fused_gbps"] / ceilings[mix]["gbps"]
-                                        if mix and mix in ceilings else None),
+        "read_write_harmonic_gbps": harmonic,
+        "fused_pct_of_read_write_harmonic": (100.0 * main_res["fused_gbps"] / harmonic
+                                             if harmonic else None),
         "roofline": head["roofline"],
         "roofline_by_workload": roofs,
         "ceilings": ceilings,
