@@ -25,12 +25,14 @@
  * Conventions for every entry point
  *   - Device pointers are HIP device (HBM) addresses the caller allocated;
  *     the library never allocates or frees device memory and never keeps a
- *     pointer after the call returns. Work is enqueued on `stream` (a
- *     hipStream_t; NULL = the null stream) and completes asynchronously;
- *     kernel faults surface at the caller's next synchronization. These
- *     calls wait by contract: zs_step_commit (for its flag), zs_offload_step
- *     (for its flag and the gradient pieces), and zs_cpu_step and
- *     zs_cpu_update (host work); no other call synchronizes.
+ *     pointer after the call returns; its only device memory of its own
+ *     is the one-word static array of zs_step_commit_noalloc. Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     completes asynchronously; kernel faults surface at the caller's next
+ *     synchronization. These calls wait by contract: zs_step_commit and
+ *     zs_step_commit_noalloc (for their flag), zs_offload_step (for its flag
+ *     and the gradient pieces), and zs_cpu_step and zs_cpu_update (host
+ *     work); no other call synchronizes.
  *   - Host pointers (arrays of device pointers, hyper-parameter structs,
  *     outputs of zs_partition) are read or written during the call only.
  *   - 16-bit values are IEEE binary16 (ZS_FP16) or bfloat16 (ZS_BF16).
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ZS_ABI_VERSION 5
+#define ZS_ABI_VERSION 6
 #define ZS_MAX_WORLD 64
 
 typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
@@ -328,6 +330,28 @@ int zs_scaler_update(zs_loss_scaler *s, uint32_t overflow);
  * on any error the scaler is left unchanged. */
 int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
                    void *stream, void *ev_start, void *ev_stop, int *committed);
+
+/* zs_step_commit for callers that cannot allocate device memory (code that
+ * must not call hipMalloc, tight serving loops, harnesses that forbid it):
+ * the same step, the same kernels and the same results, with the overflow
+ * word kept in the library's own device memory instead of a->overflow_flag,
+ * which is not used and may be NULL. The caller still passes every input and
+ * output; the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine) and clears the word itself, with a one-thread kernel on
+ * `stream` before the fused kernel, so nothing needs zeroing between calls.
+ * The word is one uint32 per device, in a static device array that each
+ * device holding the library keeps until the process ends; the library
+ * resolves its address (hipGetSymbolAddress) on the first call with that
+ * device current. Its size does not depend on n, so no size is refused for
+ * it beyond what zs_step_fused refuses. Every call on one device shares that
+ * word: calls that overlap on one device (other streams or host threads)
+ * race and must be serialized by the caller. Arguments, blocking, ev_start /
+ * ev_stop and the scaler update are as for zs_step_commit. Errors: as
+ * zs_step_commit (a NULL a->overflow_flag is accepted); ZS_ERR_UNSUPPORTED
+ * for a device ordinal above 63; ZS_ERR_HIP if the address of the word
+ * cannot be resolved, before anything is enqueued. */
+int zs_step_commit_noalloc(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
+                           void *stream, void *ev_start, void *ev_stop, int *committed);
 
 /* Device-resident commit-or-skip ([Intro] 一.3 items (1) and (3): dynamic
  * loss scaling skips the update of a step whose unscaled gradient is not

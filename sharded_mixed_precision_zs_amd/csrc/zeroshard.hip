@@ -10,6 +10,7 @@
 #include <atomic>
 #include <chrono>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -25,6 +26,16 @@
 #include "zs_host_setup.h"
 #include "zs_offload_pieces.h"
 
+/* ------------------------------------------------------------------------
+ * Device memory of zs_step_commit_noalloc: the overflow word its fused pass
+ * ORs into and its readback copies to the host, so that the caller need not
+ * allocate one: one 4-byte word, held by every device the library runs on
+ * until the process ends. In host code this name is a stand-in for the
+ * variable, not a device address: host code uses only the address
+ * scratch_word() resolves for the current device.
+ * ---------------------------------------------------------------------- */
+constexpr int kScratchWords = 1;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
 
 namespace {
 
@@ -60,6 +71,34 @@ bool valid_wire(int w) { return w == ZS_WIRE_FP32 || w == ZS_WIRE_BF16 || w == Z
 
 /* zs_step_commit polls the stream for errors this often while it waits. */
 constexpr int kQueryMicros = 1000;
+
+/* The device address of `scratch` on each device ordinal, resolved the first
+ * time zs_step_commit_noalloc runs with that device current (each device
+ * holds its own copy at its own address). */
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch[kMaxScratchDevices] = {};
+
+int scratch_word(uint32_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZS_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(ZS_ERR_UNSUPPORTED, "zs_step_commit_noalloc: device ordinal above 63%s");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+      return fail(ZS_ERR_HIP, "zs_step_commit_noalloc: hipGetSymbolAddress failed: %s",
+                  hipGetErrorString(e));
+    if (!ptr || (uintptr_t)ptr % 256 != 0)
+      return fail(ZS_ERR_HIP, "zs_step_commit_noalloc: bad device address of its scratch%s");
+    g_scratch[dev] = static_cast<uint32_t *>(ptr);
+  }
+  *out = g_scratch[dev];
+  return ZS_OK;
+}
 
 using zs_host::make_adam;
 using zs_host::make_scales;
@@ -465,8 +504,12 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
  * immediately before and after the kernel launch; with `dev`, the scale,
  * bias corrections and flag of the device-resident flow (a->hp.loss_scale,
  * a->hp.step_t and a->overflow_flag unused). */
+/* clear_first: NULL, or a device word that a one-thread kernel zeroes on
+ * `stream` after every check has passed and before the fused kernel (and
+ * ev_start), so a refused call enqueues nothing. */
 static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_start,
-                           hipEvent_t ev_stop, zs_device_scaler *dev) {
+                           hipEvent_t ev_stop, zs_device_scaler *dev,
+                           uint32_t *clear_first = nullptr) {
   if (!a) return fail(ZS_ERR_INVALID_ARG, "null args%s");
   if (!a->worker_grads || !a->master_in || !a->m_in || !a->v_in || !a->master_out ||
       !a->m_out || !a->v_out || !a->gather_buf || (!a->overflow_flag && !dev))
@@ -578,6 +621,11 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     case 2: ZS_LAUNCH_FUSED(2, G, P); break; \
     default: ZS_LAUNCH_FUSED(1, G, P); break; \
   }
+  if (clear_first) {
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, s, clear_first);
+    int rc = launch_result();
+    if (rc != ZS_OK) return rc;
+  }
   if (ev_start) {
     hipError_t e = hipEventRecord(ev_start, s);
     if (e != hipSuccess) return fail(ZS_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
@@ -601,6 +649,55 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     if (e != hipSuccess) return fail(ZS_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
   }
   return launched;
+}
+
+/* The commit-or-skip step of zs_step_commit and zs_step_commit_noalloc:
+ * the fused pass with `flag` (device memory; zeroed first on the stream when
+ * clear is true) as its overflow word, the word's readback to host_flag, and
+ * the scaler rule. */
+static int step_commit_impl(const zs_step_args *a, uint32_t *flag, bool clear,
+                            zs_loss_scaler *scaler, uint32_t *host_flag, hipStream_t s,
+                            hipEvent_t ev_start, hipEvent_t ev_stop, int *committed) {
+  if (!(scaler->scale > 0.0f) || !isfinite(scaler->scale))
+    return fail(ZS_ERR_INVALID_ARG, "scaler->scale must be finite and > 0%s");
+  if (scaler->step_t >= 0xffffffffull)
+    return fail(ZS_ERR_UNSUPPORTED, "step count exceeds 32 bits%s");
+  zs_step_args local = *a;
+  local.hp.loss_scale = scaler->scale;
+  local.hp.step_t = (uint32_t)(scaler->step_t + 1);
+  local.overflow_flag = flag;
+  int rc = step_fused_impl(&local, s, ev_start, ev_stop, nullptr, clear ? flag : nullptr);
+  if (rc != ZS_OK) return rc;
+  if (a->n == 0) {
+    *committed = 1;
+    return zs_scaler_update(scaler, 0);
+  }
+  /* The flag is only ever 0 or 1, so a sentinel in host memory shows when
+   * the 4-byte copy (stream-ordered after the kernel) has landed: the call
+   * spins on that word, which returns sooner than a blocking stream
+   * synchronization, and queries the stream once per kQueryMicros so that
+   * a failed stream ends the wait with an error instead of a hang. */
+  volatile uint32_t *hf = host_flag;
+  const uint32_t kSentinel = 0xffffffffu;
+  *hf = kSentinel;
+  hipError_t e = hipMemcpyAsync(host_flag, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return fail(ZS_ERR_HIP, "flag readback failed: %s", hipGetErrorString(e));
+  auto last = std::chrono::steady_clock::now();
+  const auto every = std::chrono::microseconds(kQueryMicros);
+  for (uint32_t spins = 1; *hf == kSentinel; ++spins) {
+    if ((spins & 1023u) != 0) continue;
+    auto now = std::chrono::steady_clock::now();
+    if (now - last < every) continue;
+    last = now;
+    hipError_t q = hipStreamQuery(s);
+    if (q == hipErrorNotReady) continue;
+    if (q != hipSuccess)
+      return fail(ZS_ERR_HIP, "stream failed before the flag arrived: %s", hipGetErrorString(q));
+    if (*hf == kSentinel) return fail(ZS_ERR_HIP, "flag readback did not arrive%s");
+  }
+  uint32_t got = *hf;
+  *committed = got == 0;
+  return zs_scaler_update(scaler, got);
 }
 
 int zs_step_fused(const zs_step_args *a, void *stream) {
@@ -683,48 +780,21 @@ int zs_step_commit(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host
                    void *stream, void *ev_start, void *ev_stop, int *committed) {
   if (!a || !scaler || !host_flag || !committed)
     return fail(ZS_ERR_INVALID_ARG, "null args, scaler, host_flag or committed%s");
-  if (!(scaler->scale > 0.0f) || !isfinite(scaler->scale))
-    return fail(ZS_ERR_INVALID_ARG, "scaler->scale must be finite and > 0%s");
-  if (scaler->step_t >= 0xffffffffull)
-    return fail(ZS_ERR_UNSUPPORTED, "step count exceeds 32 bits%s");
-  zs_step_args local = *a;
-  local.hp.loss_scale = scaler->scale;
-  local.hp.step_t = (uint32_t)(scaler->step_t + 1);
-  int rc = step_fused_impl(&local, stream, static_cast<hipEvent_t>(ev_start),
-                           static_cast<hipEvent_t>(ev_stop), nullptr);
+  return step_commit_impl(a, a->overflow_flag, false, scaler, host_flag,
+                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
+                          static_cast<hipEvent_t>(ev_stop), committed);
+}
+
+int zs_step_commit_noalloc(const zs_step_args *a, zs_loss_scaler *scaler, uint32_t *host_flag,
+                           void *stream, void *ev_start, void *ev_stop, int *committed) {
+  if (!a || !scaler || !host_flag || !committed)
+    return fail(ZS_ERR_INVALID_ARG, "null args, scaler, host_flag or committed%s");
+  uint32_t *word = nullptr;
+  int rc = scratch_word(&word);
   if (rc != ZS_OK) return rc;
-  if (a->n == 0) {
-    *committed = 1;
-    return zs_scaler_update(scaler, 0);
-  }
-  /* The flag is only ever 0 or 1, so a sentinel in host memory shows when
-   * the 4-byte copy (stream-ordered after the kernel) has landed: the call
-   * spins on that word, which returns sooner than a blocking stream
-   * synchronization, and queries the stream once per kQueryMicros so that
-   * a failed stream ends the wait with an error instead of a hang. */
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  volatile uint32_t *hf = host_flag;
-  const uint32_t kSentinel = 0xffffffffu;
-  *hf = kSentinel;
-  hipError_t e = hipMemcpyAsync(host_flag, a->overflow_flag, sizeof(uint32_t),
-                                hipMemcpyDeviceToHost, s);
-  if (e != hipSuccess) return fail(ZS_ERR_HIP, "flag readback failed: %s", hipGetErrorString(e));
-  auto last = std::chrono::steady_clock::now();
-  const auto every = std::chrono::microseconds(kQueryMicros);
-  for (uint32_t spins = 1; *hf == kSentinel; ++spins) {
-    if ((spins & 1023u) != 0) continue;
-    auto now = std::chrono::steady_clock::now();
-    if (now - last < every) continue;
-    last = now;
-    hipError_t q = hipStreamQuery(s);
-    if (q == hipErrorNotReady) continue;
-    if (q != hipSuccess)
-      return fail(ZS_ERR_HIP, "stream failed before the flag arrived: %s", hipGetErrorString(q));
-    if (*hf == kSentinel) return fail(ZS_ERR_HIP, "flag readback did not arrive%s");
-  }
-  uint32_t flag = *hf;
-  *committed = flag == 0;
-  return zs_scaler_update(scaler, flag);
+  return step_commit_impl(a, word, true, scaler, host_flag, static_cast<hipStream_t>(stream),
+                          static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop),
+                          committed);
 }
 
 int zs_all_gather_step(void *const *replicas, uint32_t world, uint64_t phi, uint32_t sigma,

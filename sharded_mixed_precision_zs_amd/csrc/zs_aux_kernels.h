@@ -35,6 +35,13 @@ namespace zs {
 constexpr int kCommitBlock = 1024;  /* threads per commit block     */
 constexpr int kCommitBlocks = 256;  /* at most this many blocks     */
 
+/* Zeroes one uint32 word (a vector store from lane 0). zs_step_commit_noalloc
+ * clears the overflow word it keeps in the library's device memory with it,
+ * on the step's own stream. */
+__global__ __launch_bounds__(64) void clear_word_kernel(uint32_t *word) {
+  if (threadIdx.x == 0) *word = 0u;
+}
+
 struct CommitArgs {
   zs_device_scaler *dev;
   const float *master_in, *m_in, *v_in;

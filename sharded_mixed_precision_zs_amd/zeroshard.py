@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 
 from . import build as _build
 
-ZS_ABI_VERSION = 5
+ZS_ABI_VERSION = 6
 ZS_MAX_WORLD = 64
 ZS_BF16, ZS_FP16 = 0, 1
 ZS_WIRE_FP32, ZS_WIRE_BF16, ZS_WIRE_FP16 = 0, 1, 2
@@ -86,6 +86,8 @@ def _load():
         "zs_scaler_update": ([C.POINTER(zs_loss_scaler), u32], i32),
         "zs_step_commit": ([C.POINTER(zs_step_args), C.POINTER(zs_loss_scaler), vp, vp, vp, vp,
                             C.POINTER(C.c_int)], i32),
+        "zs_step_commit_noalloc": ([C.POINTER(zs_step_args), C.POINTER(zs_loss_scaler), vp, vp,
+                                    vp, vp, C.POINTER(C.c_int)], i32),
         "zs_all_gather_step": ([C.POINTER(vp), u32, u64, u32, u32, vp], i32),
         "zs_cpu_step": ([vp, vp, vp, vp, u64, C.POINTER(zs_adamw_hparams), vp, i32, i32,
                          C.POINTER(u32)], i32),
@@ -293,6 +295,19 @@ def zs_step_commit(args, scaler: zs_loss_scaler, host_flag, stream=None, ev_star
     _check("zs_step_commit", _lib.zs_step_commit(C.byref(raw), C.byref(scaler), hf,
                                                  _stream(stream), ev_start, ev_stop,
                                                  C.byref(committed)))
+    return bool(committed.value)
+
+
+def zs_step_commit_noalloc(args, scaler: zs_loss_scaler, host_flag, stream=None, ev_start=None,
+                           ev_stop=None):
+    """zs_step_commit with the overflow word in the library's own device
+    memory (args' overflow_flag is not used). Returns committed."""
+    raw = args.args if isinstance(args, StepArgs) else args
+    hf = host_flag if isinstance(host_flag, int) else host_flag.data_ptr()
+    committed = C.c_int(0)
+    _check("zs_step_commit_noalloc",
+           _lib.zs_step_commit_noalloc(C.byref(raw), C.byref(scaler), hf, _stream(stream),
+                                       ev_start, ev_stop, C.byref(committed)))
     return bool(committed.value)
 
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(zs):
     lib = C.CDLL(zs.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 5
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 6
 
 
 def test_status_strings(zs):
