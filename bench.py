@@ -541,12 +541,16 @@ def world_sweep(worlds, n, steps, warmup, torch):
 # blocks per CU). Ids 0 and 5 are the production shapes (libzsvariants).
 VARIANT_SWEEP = {
     "7b-full-w1": [(0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
-                   (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1)],
+                   (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1),
+                   (30, 8, 0), (30, 0, 0), (31, 4, 0), (32, 1, 0), (33, 1, 0)],
     "gpt2s-w8": [(5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
-                 (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3)],
+                 (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3),
+                 (23, 3, 0), (25, 3, 0), (26, 8, 0), (27, 6, 0), (28, 2, 0), (29, 0, 0)],
     "7p5b-shard-w64": [(5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0), (9, 0, 0),
                        (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1), (18, 0, 3),
-                       (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2)],
+                       (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2),
+                       (23, 0, 0), (24, 0, 0), (25, 0, 0), (26, 0, 0), (27, 0, 0), (28, 0, 0),
+                       (29, 0, 0)],
 }
 VARIANT_N_MAX = 1 << 30   # W = 1: the first 2^30 parameters of the 7B state (3 sets fit HBM)
 

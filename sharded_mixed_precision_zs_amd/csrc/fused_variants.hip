@@ -15,7 +15,8 @@
  *   B      gradient vectors loaded ahead of the in-order adds;
  *   NTL    gradient loads marked non-temporal;
  *   NTS    stores marked non-temporal;
- *   PER    persistent blocks that walk tiles with a grid stride.
+ *   PER    persistent blocks that walk tiles with a grid stride;
+ *   T      threads per block (256 in libzeroshard).
  * The launch adds a residency cap (blocks per CU, through unused dynamic
  * LDS) and, for persistent grids, the blocks per CU of the grid.
  * A second kernel splits the waves of a block by role (split_kernel below):
@@ -86,11 +87,11 @@ __device__ __forceinline__ void ring_sum_v(const GradPtrs &g, uint32_t world,
     for (int u = 0; u < U; ++u) add_wire<8, ZS_BF16, ZS_WIRE_FP32>(s[u], ld16<8, NTL>(g.p[j] + i0[u]));
 }
 
-template <int U, bool MULTI, bool SF, int B, bool NTL, bool NTS>
+template <int T, int U, bool MULTI, bool SF, int B, bool NTL, bool NTS>
 __device__ __forceinline__ bool variant_tile(const FusedArgs &p, uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * 8;
+  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * T + threadIdx.x) * 8;
   float th[U][8], m[U][8], v[U][8], s[U][8];
   auto load_state = [&]() {
 #pragma unroll
@@ -124,16 +125,16 @@ __device__ __forceinline__ bool variant_tile(const FusedArgs &p, uint64_t base) 
   return bad;
 }
 
-template <int U, bool MULTI, bool SF, int B, bool NTL, bool NTS, bool PER>
-__global__ __launch_bounds__(kBlock) void variant_kernel(FusedArgs p) {
-  const uint64_t tile = (uint64_t)kBlock * U * 8;
+template <int T, int U, bool MULTI, bool SF, int B, bool NTL, bool NTS, bool PER>
+__global__ __launch_bounds__(T) void variant_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)T * U * 8;
   const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
   bool bad = false;
   if constexpr (PER) {
     for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x)
-      bad |= variant_tile<U, MULTI, SF, B, NTL, NTS>(p, t * tile);
+      bad |= variant_tile<T, U, MULTI, SF, B, NTL, NTS>(p, t * tile);
   } else if (blockIdx.x < tiles) {
-    bad = variant_tile<U, MULTI, SF, B, NTL, NTS>(p, (uint64_t)blockIdx.x * tile);
+    bad = variant_tile<T, U, MULTI, SF, B, NTL, NTS>(p, (uint64_t)blockIdx.x * tile);
   }
   flag_or(p.flag, bad);
 }
@@ -316,10 +317,11 @@ struct Variant {
   bool cooperative = false;  /* launched cooperatively (grid sync)   */
 };
 
-template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER>
+template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER, int T = kBlock>
 constexpr Variant mk(const char *name) {
-  return Variant{name, reinterpret_cast<const void *>(&variant_kernel<U, M, SF, B, NTL, NTS, PER>),
-                 kBlock * 8 * U, M, PER, kBlock, 0};
+  return Variant{name,
+                 reinterpret_cast<const void *>(&variant_kernel<T, U, M, SF, B, NTL, NTS, PER>),
+                 T * 8 * U, M, PER, T, 0};
 }
 
 template <int RV, int LV, int B, int SYNCS>
@@ -360,6 +362,17 @@ const Variant kVariants[] = {
     mk_phased<2, 1, 8, 2>("wN: phased, 3 vectors/thread (2 in registers), 2 syncs per chunk"),
     mk_phased<3, 1, 8, 1>("wN: phased, 4 vectors/thread (3 in registers), 1 sync per chunk"),
     mk_phased<1, 1, 8, 1>("wN: phased, 2 vectors/thread (1 in registers), 1 sync per chunk"),
+    mk<4, true, false, 8, true, false, false>("wN: 4 vectors/thread"),
+    mk<4, true, false, 4, true, false, false>("wN: 4 vectors/thread, 4 loads ahead"),
+    mk<2, true, false, 16, true, false, false>("wN: 16 loads ahead"),
+    mk<2, true, false, 8, true, false, false, 64>("wN: 64-thread blocks"),
+    mk<2, true, false, 8, true, false, false, 128>("wN: 128-thread blocks"),
+    mk<2, true, false, 8, true, false, false, 512>("wN: 512-thread blocks"),
+    mk<2, true, false, 8, true, false, false, 1024>("wN: 1024-thread blocks"),
+    mk<1, false, false, 8, true, false, false, 64>("w1: 64-thread blocks"),
+    mk<1, false, false, 8, true, false, false, 128>("w1: 128-thread blocks"),
+    mk<1, false, false, 8, true, false, false, 512>("w1: 512-thread blocks"),
+    mk<1, false, false, 8, true, false, false, 1024>("w1: 1024-thread blocks"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 
@@ -393,7 +406,7 @@ const char *zs_variant_last_error(void) { return g_verr; }
 
 /* One launch of variant `id` on the arguments of zs_step_fused (same
  * meaning; the flag is OR-ed into a->overflow_flag), on `stream`.
- *   blocks_per_cu: residency cap, 0 = none, 1..8;
+ *   blocks_per_cu: residency cap, 0 = none, 1..32;
  *   persist_per_cu: blocks per CU of a persistent variant's grid (1..8;
  *                   ignored by the others).
  * Returns ZS_OK when enqueued; ZS_ERR_INVALID_ARG, before any launch, for an
@@ -414,7 +427,7 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
   if (a->grad_dtype != ZS_BF16 || a->param_dtype != ZS_BF16 || a->wire_dtype != ZS_WIRE_FP32 ||
       a->acc_in)
     return vfail("variants take bf16 gradients and parameters, fp32 sums, no acc_in");
-  if (blocks_per_cu > 8 || (v.persistent && (persist_per_cu < 1 || persist_per_cu > 8)))
+  if (blocks_per_cu > 32 || (v.persistent && (persist_per_cu < 1 || persist_per_cu > 8)))
     return vfail("cap or persistent blocks per CU out of range");
   const uint64_t tile = (uint64_t)v.tile;
   if (a->n == 0 || a->n % tile != 0 || a->n / tile > 0x7fffffffull)
@@ -453,7 +466,12 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
     return ZS_ERR_HIP;
   size_t lds = (size_t)v.lds;
   if (blocks_per_cu) {
-    const int bytes = (lds_per_cu / (int)blocks_per_cu - 1024) / 256 * 256;
+    /* up to 8: the production launch's rule; above 8 the largest multiple
+     * of 1 KB with which exactly `blocks_per_cu` blocks fit a CU */
+    int bytes = blocks_per_cu <= 8 ? (lds_per_cu / (int)blocks_per_cu - 1024) / 256 * 256
+                                   : lds_per_cu / (int)blocks_per_cu / 1024 * 1024;
+    if (blocks_per_cu > 8 && (int)(blocks_per_cu + 1) * bytes <= lds_per_cu)
+      return vfail("no LDS size caps residency at that many blocks per CU");
     if (bytes > v.lds) lds = (size_t)bytes;
   }
   if (lds > (size_t)lds_per_cu) return vfail("the variant's LDS exceeds the CU's");

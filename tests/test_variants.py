@@ -73,7 +73,7 @@ def test_refusals_before_any_launch(vlib, zs):
                        ("master_out", None), ("m_in", FAKE + 0x40000004)):
         d, k4 = _args(zs, 4, 4096, **{field: val})
         assert vlib.zs_variant_launch(5, C.addressof(d), 0, 0, None) == E, field
-    assert vlib.zs_variant_launch(5, C.addressof(b), 9, 0, None) == E        # cap out of range
+    assert vlib.zs_variant_launch(5, C.addressof(b), 33, 0, None) == E       # cap out of range
     assert vlib.zs_variant_launch(10, C.addressof(b), 0, 0, None) == E       # persistent, no grid
     assert vlib.zs_variant_launch(5, None, 0, 0, None) == E
     assert vlib.zs_variant_last_error().decode()
