@@ -184,6 +184,55 @@ def test_7b_full_w1_windows(env, device_commit):
     run_workload(env, wl.name, windows=wins, device_commit=device_commit)
 
 
+FLAG_CHUNK = 1 << 28
+
+
+def _oracle_flag_over(gview, wl, scale):
+    """The oracle's overflow flag (ring sum, average, unscale, check) over a
+    whole single-worker gradient on the device, streamed to the host in
+    chunks of FLAG_CHUNK elements."""
+    n = gview.numel()
+    out = np.empty(FLAG_CHUNK, F32)
+    flag = 0
+    for c0 in range(0, n, FLAG_CHUNK):
+        c1 = min(n, c0 + FLAG_CHUNK)
+        bits = gview[c0:c1].cpu().numpy().view(np.uint16)
+        flag |= oracle.reduce_avg([bits], 0, wl.grad_dtype, out[:c1 - c0], False, scale)
+    return flag
+
+
+def test_7b_flag_covers_the_whole_gradient(env):
+    """The fused step's overflow flag at the 7B workload's full size equals
+    the oracle's check of all 7e9 gradient elements (streamed to the host),
+    and one +inf planted past element 2^32 is found: that step is skipped and
+    the kept set is left as it was."""
+    zs, synth, shard = env
+    wl = synth.WORKLOADS["7b-full-w1"]
+    n, off = wl.n, wl.offset
+    torch.cuda.empty_cache()
+    st = shard.ShardState(n, 1, wl.rank, off, off + n, wl.param_dtype, wl.grad_dtype,
+                          shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay),
+                          wl.loss_scale)
+    synth.dev_state(wl, off, st.master, st.m, st.v)
+    g = torch.empty(n, dtype=torch.int16, device="cuda")
+    synth.dev_grad(wl, 0, 1, 0, off, g, scale=wl.loss_scale)
+    announce("7b whole-gradient flag: clean step")
+    assert st.step([g]) and st.last_flag == 0
+    announce("7b whole-gradient flag: oracle over all elements")
+    assert _oracle_flag_over(g, wl, wl.loss_scale) == 0
+    p = (1 << 32) + 12_345
+    g[p] = 0x7F80  # bf16 +inf
+    kept = st.master[p - 64:p + 64].clone()
+    announce("7b whole-gradient flag: +inf past element 2^32")
+    assert not st.step([g]) and st.last_flag == 1
+    c0 = p // FLAG_CHUNK * FLAG_CHUNK
+    assert _oracle_flag_over(g[c0:c0 + FLAG_CHUNK], wl, wl.loss_scale) == 1
+    assert torch.equal(st.master[p - 64:p + 64], kept)
+    assert st.t == 1 and int(st.scaler.skipped) == 1
+    del st, g
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("device_commit", [False, True])
 def test_1p3b_w4_acc4_fp16_windows(env, device_commit):
     zs, synth, shard = env
