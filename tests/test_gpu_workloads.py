@@ -201,6 +201,49 @@ def _oracle_flag_over(gview, wl, scale):
     return flag
 
 
+def test_7p5b_flag_covers_the_whole_partition(env):
+    """The 7.5B shard's flag (64 workers) at full size against the oracle's
+    ring sum, average, unscale and check of every element of the partition,
+    the 64 gradients streamed to the host in chunks; then one NaN planted in
+    the last worker's last element is found and the step skipped."""
+    zs, synth, shard = env
+    wl = synth.WORKLOADS["7p5b-shard-w64"]
+    n, off, W = wl.n, wl.offset, wl.world
+    torch.cuda.empty_cache()
+    st = shard.ShardState(n, W, wl.rank, off, off + n, wl.param_dtype, wl.grad_dtype,
+                          shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay),
+                          wl.loss_scale)
+    synth.dev_state(wl, off, st.master, st.m, st.v)
+    row = -(-n // 128) * 128
+    grads = torch.empty((W, row), dtype=torch.int16, device="cuda")
+    gv = [grads[k, :n] for k in range(W)]
+    for k in range(W):
+        synth.dev_grad(wl, k, 1, 0, off, gv[k], scale=wl.loss_scale)
+    announce("7.5B whole-partition flag: clean step")
+    assert st.step(gv) and st.last_flag == 0
+    announce("7.5B whole-partition flag: oracle over all elements")
+    chunk = 1 << 24
+    out = np.empty(chunk, F32)
+    flag = 0
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        parts = [g[c0:c1].cpu().numpy().view(np.uint16) for g in gv]
+        flag |= oracle.reduce_avg(parts, wl.rank, wl.grad_dtype, out[:c1 - c0], False,
+                                  wl.loss_scale)
+    assert flag == 0
+    gv[W - 1][n - 1] = 0x7FC0  # bf16 quiet NaN
+    kept = st.v[n - 256:].clone()
+    announce("7.5B whole-partition flag: NaN in the last element")
+    assert not st.step(gv) and st.last_flag == 1
+    parts = [g[n - 4096:].cpu().numpy().view(np.uint16) for g in gv]
+    assert oracle.reduce_avg(parts, wl.rank, wl.grad_dtype, np.empty(4096, F32), False,
+                             wl.loss_scale) == 1
+    assert torch.equal(st.v[n - 256:], kept)
+    assert st.t == 1 and int(st.scaler.skipped) == 1
+    del st, grads, gv
+    torch.cuda.empty_cache()
+
+
 def test_7b_flag_covers_the_whole_gradient(env):
     """The fused step's overflow flag at the 7B workload's full size equals
     the oracle's check of all 7e9 gradient elements (streamed to the host),
