@@ -88,12 +88,21 @@ def fused_bytes_per_param(world, accum):
     return 2 * world + 12 + (4 if accum > 1 else 0), 14
 
 
+def shape_of(world):
+    """The fused kernel's access shape for 16-byte-aligned operands
+    (zs::kShape*): 16 loads ahead and non-temporal stores (2) from 16
+    workers on, 8 loads ahead and non-temporal stores (3) below."""
+    return 2 if world >= 16 else 3
+
+
 def fused_instance(wl, wire=0):
     """Template instance of zs::fused_kernel that a 16-byte-aligned shard of
-    this workload launches (the name rocprofv3 shows)."""
+    this workload launches (the name rocprofv3 shows): 4-element vectors,
+    four per thread when W > 1 and two when W = 1."""
     multi = wl.world > 1
-    return (f"zs::fused_kernel<8, {2 if multi else 1}, {str(multi).lower()}, "
-            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}>")
+    return (f"zs::fused_kernel<4, {4 if multi else 2}, {str(multi).lower()}, "
+            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, "
+            f"{shape_of(wl.world)}>")
 
 
 def timing_events(torch, count):
@@ -540,15 +549,18 @@ def world_sweep(worlds, n, steps, warmup, torch):
 # The variant sweep: per workload, (variant id, residency cap, persistent
 # blocks per CU). Ids 0 and 5 are the production shapes (libzsvariants).
 VARIANT_SWEEP = {
-    "7b-full-w1": [(0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
+    "7b-full-w1": [(43, 2, 0), (43, 3, 0), (43, 0, 0), (42, 2, 0),
+                   (0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
                    (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1),
                    (30, 8, 0), (30, 0, 0), (31, 4, 0), (32, 1, 0), (33, 1, 0)],
-    "gpt2s-w8": [(5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
+    "gpt2s-w8": [(41, 3, 0), (41, 0, 0), (40, 3, 0), (38, 3, 0),
+                 (5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
                  (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3),
                  (23, 3, 0), (25, 3, 0), (26, 8, 0), (27, 6, 0), (28, 2, 0), (29, 0, 0)],
-    "7p5b-shard-w64": [(5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0), (9, 0, 0),
-                       (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1), (18, 0, 3),
-                       (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2),
+    "7p5b-shard-w64": [(40, 0, 0), (41, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0),
+                       (5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0),
+                       (9, 0, 0), (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1),
+                       (18, 0, 3), (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2),
                        (23, 0, 0), (24, 0, 0), (25, 0, 0), (26, 0, 0), (27, 0, 0), (28, 0, 0),
                        (29, 0, 0)],
 }

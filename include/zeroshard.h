@@ -37,8 +37,9 @@
  *     outputs of zs_partition) are read or written during the call only.
  *   - 16-bit values are IEEE binary16 (ZS_FP16) or bfloat16 (ZS_BF16).
  *   - Any element offset is accepted; 16-byte-aligned operands take the
- *     widest (8-element) vector path, others a narrower one of the same
- *     kernel.
+ *     widest vector path (8 elements; 4 in zs_step_fused and its variants,
+ *     whose non-temporal stores then cover whole lines), others a narrower
+ *     one of the same kernel.
  *   - n == 0 is a no-op that returns ZS_OK; element counts and offsets
  *     above 2^48 return ZS_ERR_UNSUPPORTED before anything is enqueued.
  *   - Status codes: ZS_OK on success; ZS_ERR_INVALID_ARG (null pointer,

@@ -16,7 +16,9 @@
  *   NTL    gradient loads marked non-temporal;
  *   NTS    stores marked non-temporal;
  *   PER    persistent blocks that walk tiles with a grid stride;
- *   T      threads per block (256 in libzeroshard).
+ *   T      threads per block (256 in libzeroshard);
+ *   TB     the workers after the last full batch summed in batches of 8,
+ *          4, 2 and 1 rather than one load at a time.
  * The launch adds a residency cap (blocks per CU, through unused dynamic
  * LDS) and, for persistent grids, the blocks per CU of the grid.
  * A second kernel splits the waves of a block by role (split_kernel below):
@@ -63,31 +65,47 @@ __device__ __forceinline__ void store_bf16x8(uint16_t *p, const float (&x)[8]) {
   }
 }
 
-/* The ring-order sum of fused_kernel (worker p[0] first, the owner last),
- * with B loads in flight and the load cache policy as knobs. */
+/* One batch of B workers' loads, all issued before the in-order adds. */
 template <int U, int B, bool NTL>
+__device__ __forceinline__ void sum_batch_v(const GradPtrs &g, uint32_t j,
+                                            const uint64_t (&i0)[U], float (&s)[U][8]) {
+  Raw16<8> r[B][U];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[b][u] = ld16<8, NTL>(g.p[j + b] + i0[u]);
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int u = 0; u < U; ++u) add_wire<8, ZS_BF16, ZS_WIRE_FP32>(s[u], r[b][u]);
+}
+
+/* The ring-order sum of fused_kernel (worker p[0] first, the owner last),
+ * with B loads in flight and the load cache policy as knobs. TB: the
+ * workers left after the last full batch are summed in batches of 8, 4, 2
+ * and 1 (same order of adds) instead of one load and wait at a time. */
+template <int U, int B, bool NTL, bool TB = false>
 __device__ __forceinline__ void ring_sum_v(const GradPtrs &g, uint32_t world,
                                            const uint64_t (&i0)[U], float (&s)[U][8]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) set_up<8, ZS_BF16, ZS_WIRE_FP32>(s[u], ld16<8, NTL>(g.p[0] + i0[u]));
   uint32_t j = 1;
-  for (; j + B <= world; j += B) {
-    Raw16<8> r[B][U];
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int u = 0; u < U; ++u) r[b][u] = ld16<8, NTL>(g.p[j + b] + i0[u]);
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int u = 0; u < U; ++u) add_wire<8, ZS_BF16, ZS_WIRE_FP32>(s[u], r[b][u]);
+  for (; j + B <= world; j += B) sum_batch_v<U, B, NTL>(g, j, i0, s);
+  if constexpr (TB) {
+    if constexpr (B > 8) {
+      if (j + 8 <= world) { sum_batch_v<U, 8, NTL>(g, j, i0, s); j += 8; }
+    }
+    if constexpr (B > 4) {
+      if (j + 4 <= world) { sum_batch_v<U, 4, NTL>(g, j, i0, s); j += 4; }
+    }
+    if (j + 2 <= world) { sum_batch_v<U, 2, NTL>(g, j, i0, s); j += 2; }
   }
   for (; j < world; ++j)
 #pragma unroll
     for (int u = 0; u < U; ++u) add_wire<8, ZS_BF16, ZS_WIRE_FP32>(s[u], ld16<8, NTL>(g.p[j] + i0[u]));
 }
 
-template <int T, int U, bool MULTI, bool SF, int B, bool NTL, bool NTS>
+template <int T, int U, bool MULTI, bool SF, int B, bool NTL, bool NTS, bool TB>
 __device__ __forceinline__ bool variant_tile(const FusedArgs &p, uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
@@ -102,11 +120,11 @@ __device__ __forceinline__ bool variant_tile(const FusedArgs &p, uint64_t base) 
     }
   };
   if constexpr (MULTI && !SF) {
-    ring_sum_v<U, B, NTL>(p.g, p.world, i0, s);
+    ring_sum_v<U, B, NTL, TB>(p.g, p.world, i0, s);
     load_state();
   } else {
     load_state();
-    ring_sum_v<U, B, NTL>(p.g, MULTI ? p.world : 1, i0, s);
+    ring_sum_v<U, B, NTL, TB>(p.g, MULTI ? p.world : 1, i0, s);
   }
   bool bad = false;
 #pragma unroll
@@ -125,17 +143,34 @@ __device__ __forceinline__ bool variant_tile(const FusedArgs &p, uint64_t base) 
   return bad;
 }
 
-template <int T, int U, bool MULTI, bool SF, int B, bool NTL, bool NTS, bool PER>
+template <int T, int U, bool MULTI, bool SF, int B, bool NTL, bool NTS, bool PER, bool TB>
 __global__ __launch_bounds__(T) void variant_kernel(FusedArgs p) {
   const uint64_t tile = (uint64_t)T * U * 8;
   const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
   bool bad = false;
   if constexpr (PER) {
     for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x)
-      bad |= variant_tile<T, U, MULTI, SF, B, NTL, NTS>(p, t * tile);
+      bad |= variant_tile<T, U, MULTI, SF, B, NTL, NTS, TB>(p, t * tile);
   } else if (blockIdx.x < tiles) {
-    bad = variant_tile<T, U, MULTI, SF, B, NTL, NTS>(p, (uint64_t)blockIdx.x * tile);
+    bad = variant_tile<T, U, MULTI, SF, B, NTL, NTS, TB>(p, (uint64_t)blockIdx.x * tile);
   }
+  flag_or(p.flag, bad);
+}
+
+/* The production tile (zs::fused_tile) with 4-element vectors, four per
+ * thread: lane t of a block owns elements 4t .. 4t+3 of each 1024-element
+ * group, so every fp32 load and store instruction of a wave covers 1 KB of
+ * whole lines (with 8-element vectors a lane's 32 bytes take two 16-byte
+ * stores, and each 64-byte line is half-written by two instructions), and
+ * gradient loads and parameter stores are 8 bytes per lane. */
+template <int SHAPE>
+__global__ __launch_bounds__(kBlock) void g4_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)kBlock * 4 * 4;
+  const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
+  bool bad = false;
+  if (blockIdx.x < tiles)
+    bad = fused_tile<4, 4, true, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>(
+        p, p.k, p.h, (uint64_t)blockIdx.x * tile);
   flag_or(p.flag, bad);
 }
 
@@ -317,11 +352,37 @@ struct Variant {
   bool cooperative = false;  /* launched cooperatively (grid sync)   */
 };
 
-template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER, int T = kBlock>
+template <int U, bool M, bool SF, int B, bool NTL, bool NTS, bool PER, int T = kBlock,
+          bool TB = false>
 constexpr Variant mk(const char *name) {
   return Variant{name,
-                 reinterpret_cast<const void *>(&variant_kernel<T, U, M, SF, B, NTL, NTS, PER>),
+                 reinterpret_cast<const void *>(&variant_kernel<T, U, M, SF, B, NTL, NTS, PER, TB>),
                  T * 8 * U, M, PER, T, 0};
+}
+
+/* The same for a single worker: 4-element vectors, two per thread (the
+ * W = 1 kernel's 2048-element tile); SHAPE picks the store policy. */
+template <int SHAPE>
+__global__ __launch_bounds__(kBlock) void g4w1_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)kBlock * 4 * 2;
+  const uint64_t tiles = p.n / tile;
+  bool bad = false;
+  if (blockIdx.x < tiles)
+    bad = fused_tile<4, 2, false, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>(
+        p, p.k, p.h, (uint64_t)blockIdx.x * tile);
+  flag_or(p.flag, bad);
+}
+
+template <int SHAPE>
+constexpr Variant mk_g4w1(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&g4w1_kernel<SHAPE>), kBlock * 4 * 2, false,
+                 false, kBlock, 0};
+}
+
+template <int SHAPE>
+constexpr Variant mk_g4(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&g4_kernel<SHAPE>), kBlock * 4 * 4, true,
+                 false, kBlock, 0};
 }
 
 template <int RV, int LV, int B, int SYNCS>
@@ -337,7 +398,9 @@ constexpr Variant mk_split(const char *name) {
                  split_tile<NL>(), M, true, (NL + NS) * 64, 2 * 3 * split_tile<NL>() * 4};
 }
 
-/* Entries 0 and 5 are libzeroshard's own shapes for W = 1 and W > 1. */
+/* libzeroshard's own shapes, for 16-byte-aligned operands: entry 43 for
+ * W = 1, entry 41 for W = 2 to 15 and entry 40 for W >= 16. Entries 0 and 5
+ * are the shapes it launched before (8-element vectors, plain stores). */
 const Variant kVariants[] = {
     mk<1, false, false, 8, true, false, false>("w1: 1 vector/thread, nt gradient loads"),
     mk<2, false, false, 8, true, false, false>("w1: 2 vectors/thread"),
@@ -373,6 +436,18 @@ const Variant kVariants[] = {
     mk<1, false, false, 8, true, false, false, 128>("w1: 128-thread blocks"),
     mk<1, false, false, 8, true, false, false, 512>("w1: 512-thread blocks"),
     mk<1, false, false, 8, true, false, false, 1024>("w1: 1024-thread blocks"),
+    mk<2, true, false, 16, true, true, false>("wN: 16 loads ahead, nt stores"),
+    mk<2, true, false, 8, true, false, false, kBlock, true>("wN: remainder in batches"),
+    mk<2, true, false, 16, true, false, false, kBlock, true>(
+        "wN: 16 loads ahead, remainder in batches"),
+    mk<2, true, false, 16, true, true, false, kBlock, true>(
+        "wN: 16 loads ahead, remainder in batches, nt stores"),
+    mk_g4<kShapeB8>("wN: 4-element lane groups, 8 loads ahead"),
+    mk_g4<kShapeB16>("wN: 4-element lane groups, 16 loads ahead"),
+    mk_g4<kShapeB16Nt>("wN: 4-element lane groups, 16 loads ahead, nt stores"),
+    mk_g4<kShapeB8Nt>("wN: 4-element lane groups, 8 loads ahead, nt stores"),
+    mk_g4w1<kShapeB8>("w1: 4-element lane groups"),
+    mk_g4w1<kShapeB8Nt>("w1: 4-element lane groups, nt stores"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

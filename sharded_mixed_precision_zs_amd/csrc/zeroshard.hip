@@ -151,8 +151,20 @@ int env_blocks_per_cu() {
   return v;
 }
 
-/* Vectors per thread of the fused kernel: kTileVecs, but one when W = 1. */
-constexpr int fused_tile_vecs(bool multi) { return multi ? kTileVecs : 1; }
+/* Vector width, vectors per thread and access shape of the fused kernel.
+ * Operands aligned for 4-element vectors or wider take 4-element vectors:
+ * four per thread when W > 1, two when W = 1 (4096- and 2048-element
+ * tiles), stored non-temporally, with the sum loading 16 workers ahead
+ * from W = 16 on. Narrower vectors (unaligned operands) keep two per thread
+ * (one when W = 1) and plain stores. Chosen on MI355X by interleaved timing
+ * against the alternatives, all computing the same bits. */
+constexpr int fused_vec_of(int aligned_vec) { return aligned_vec >= 4 ? 4 : aligned_vec; }
+constexpr int fused_tile_vecs(int vec, bool multi) {
+  return vec == 4 ? (multi ? 4 : 2) : (multi ? 2 : 1);
+}
+constexpr int fused_shape(int vec, uint32_t world) {
+  return vec < 4 ? kShapeB8 : world >= 16 ? kShapeB16Nt : kShapeB8Nt;
+}
 
 /* Dynamic LDS bytes that cap the fused kernel's residency (0: no cap). */
 size_t fused_lds_bytes(uint32_t world) {
@@ -168,7 +180,7 @@ size_t fused_lds_bytes(uint32_t world) {
 /* Launch of one fused-kernel instance with `lds` bytes of (unused) dynamic
  * LDS; above the default 64 KB limit the instance's limit is raised once
  * per device (a bit per device id; ids past 63 raise it at every launch). */
-template <int V, int U, bool L, bool A, int G, int P, int W>
+template <int V, int U, bool L, bool A, int G, int P, int W, int F>
 void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedArgs &p) {
   if (lds > 65536) {
     static std::atomic<uint64_t> raised{0};
@@ -177,13 +189,13 @@ void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedA
     const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;
     if (!bit || !(raised.load(std::memory_order_relaxed) & bit)) {
       /* a refusal surfaces as the launch's error */
-      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W, F>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)device_lds().lds_per_cu) == hipSuccess)
         raised.fetch_or(bit, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W, F>), grid, block, lds, s, p);
 }
 
 /* Widest vector width every operand's alignment allows: 16-bit operands
@@ -590,36 +602,43 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   p16[a->world] = param_out;
   const void *f32[] = {a->master_in, a->m_in, a->v_in, a->master_out, a->m_out,
                        a->v_out, a->acc_in ? a->acc_in : a->master_in};
-  int vec = pick_vec(p16, (int)a->world + 1, f32, 7);
-  const int per_thread = vec * fused_tile_vecs(a->world > 1);
+  const int vec = fused_vec_of(pick_vec(p16, (int)a->world + 1, f32, 7));
+  const bool multi = a->world > 1, acc = a->acc_in != nullptr;
+  const int per_thread = vec * fused_tile_vecs(vec, multi);
   if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
-  const int mode = (a->world > 1 ? 1 : 0) | (a->acc_in ? 2 : 0);
+  const int shape = fused_shape(vec, a->world);
   const size_t lds = fused_lds_bytes(a->world);
-#define ZS_FUSED_KW(V, L, A, G, P, W) \
-  launch_fused<V, fused_tile_vecs(L), L, A, G, P, W>(grid, block, lds, s, p)
-#define ZS_FUSED_K(V, L, A, G, P)                                             \
-  do {                                                                        \
-    if (p.wire == ZS_WIRE_BF16) ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_BF16);     \
-    else if (p.wire == ZS_WIRE_FP16) ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_FP16); \
-    else ZS_FUSED_KW(V, L, A, G, P, ZS_WIRE_FP32);                            \
+#define ZS_KF(V, L, A, G, P, W, S) \
+  launch_fused<V, fused_tile_vecs(V, L), L, A, G, P, W, S>(grid, block, lds, s, p)
+#define ZS_K4(V, A, G, P, W)                                             \
+  do {                                                                   \
+    if (!multi) ZS_KF(4, false, A, G, P, W, kShapeB8Nt);                 \
+    else if (shape == kShapeB16Nt) ZS_KF(4, true, A, G, P, W, kShapeB16Nt); \
+    else ZS_KF(4, true, A, G, P, W, kShapeB8Nt);                         \
   } while (0)
-#define ZS_LAUNCH_FUSED(V, G, P)                          \
+#define ZS_KNARROW(V, A, G, P, W)                         \
   do {                                                    \
-    switch (mode) {                                       \
-      case 0: ZS_FUSED_K(V, false, false, G, P); break;   \
-      case 1: ZS_FUSED_K(V, true, false, G, P); break;    \
-      case 2: ZS_FUSED_K(V, false, true, G, P); break;    \
-      default: ZS_FUSED_K(V, true, true, G, P); break;    \
-    }                                                     \
+    if (!multi) ZS_KF(V, false, A, G, P, W, kShapeB8);    \
+    else ZS_KF(V, true, A, G, P, W, kShapeB8);            \
   } while (0)
-#define ZS_FUSED_VEC(G, P)                  \
-  switch (vec) {                            \
-    case 8: ZS_LAUNCH_FUSED(8, G, P); break; \
-    case 4: ZS_LAUNCH_FUSED(4, G, P); break; \
-    case 2: ZS_LAUNCH_FUSED(2, G, P); break; \
-    default: ZS_LAUNCH_FUSED(1, G, P); break; \
+#define ZS_KWIRE(KM, V, A, G, P)                                   \
+  do {                                                             \
+    if (p.wire == ZS_WIRE_BF16) KM(V, A, G, P, ZS_WIRE_BF16);      \
+    else if (p.wire == ZS_WIRE_FP16) KM(V, A, G, P, ZS_WIRE_FP16); \
+    else KM(V, A, G, P, ZS_WIRE_FP32);                             \
+  } while (0)
+#define ZS_KACC(KM, V, G, P)                        \
+  do {                                              \
+    if (acc) ZS_KWIRE(KM, V, true, G, P);           \
+    else ZS_KWIRE(KM, V, false, G, P);              \
+  } while (0)
+#define ZS_FUSED_VEC(G, P)                              \
+  switch (vec) {                                        \
+    case 4: ZS_KACC(ZS_K4, 4, G, P); break;             \
+    case 2: ZS_KACC(ZS_KNARROW, 2, G, P); break;        \
+    default: ZS_KACC(ZS_KNARROW, 1, G, P); break;       \
   }
   if (clear_first) {
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, s, clear_first);
@@ -640,9 +659,11 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     ZS_FUSED_VEC(ZS_FP16, ZS_BF16)
   }
 #undef ZS_FUSED_VEC
-#undef ZS_LAUNCH_FUSED
-#undef ZS_FUSED_K
-#undef ZS_FUSED_KW
+#undef ZS_KACC
+#undef ZS_KWIRE
+#undef ZS_KNARROW
+#undef ZS_K4
+#undef ZS_KF
   int launched = launch_result();
   if (launched == ZS_OK && ev_stop) {
     hipError_t e = hipEventRecord(ev_stop, s);

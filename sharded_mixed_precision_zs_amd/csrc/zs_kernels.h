@@ -37,6 +37,28 @@ namespace zs {
 constexpr int kBlock = 256;     /* threads per workgroup (4 waves of 64)   */
 constexpr int kLoadBatch = 8;   /* gradient vectors in flight per thread   */
 
+/* Access shape of the fused kernel (template parameter SHAPE): how many
+ * workers' gradient loads the sum issues ahead of its adds, and whether the
+ * new state and parameters are stored non-temporally.
+ *   kShapeB8     kLoadBatch ahead, plain stores;
+ *   kShapeB16    16 ahead, plain stores;
+ *   kShapeB16Nt  16 ahead, non-temporal stores;
+ *   kShapeB8Nt   kLoadBatch ahead, non-temporal stores.
+ * Non-temporal stores pay only when a wave's store covers whole lines: with
+ * 4-element vectors a wave's 16-byte fp32 stores span 1 KB of contiguous
+ * lines, while with 8-element vectors a lane's 32 bytes take two stores and
+ * each 64-byte line is half-written by two instructions, which then leave
+ * the L2 as separate writes (14 % more write bytes at W = 64, measured).
+ * The library launches kShapeB8Nt (W < 16) and kShapeB16Nt (W >= 16) on
+ * 4-element vectors, and kShapeB8 on the narrower vectors of unaligned
+ * operands. */
+constexpr int kShapeB8 = 0, kShapeB16 = 1, kShapeB16Nt = 2, kShapeB8Nt = 3;
+
+constexpr int shape_batch(int shape) {
+  return shape == kShapeB8 || shape == kShapeB8Nt ? kLoadBatch : 16;
+}
+constexpr bool shape_nt_stores(int shape) { return shape == kShapeB16Nt || shape == kShapeB8Nt; }
+
 /* ------------------------------------------------------------------------
  * Per-element arithmetic. Each line is written exactly in the order the
  * header documents; with contraction off, each operator rounds once.
@@ -214,6 +236,27 @@ __device__ __forceinline__ void stf(float *__restrict__ p, const float (&x)[VEC]
   }
 }
 
+/* stf / st16 with the stores marked non-temporal when NT: the new state
+ * and parameters are not read again by this step. */
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int VEC, bool NT>
+__device__ __forceinline__ void stf_p(float *__restrict__ p, const float (&x)[VEC]) {
+  if constexpr (!NT) {
+    stf<VEC>(p, x);
+  } else if constexpr (VEC == 8) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4 *>(p + 4));
+  } else if constexpr (VEC == 4) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(p));
+  } else if constexpr (VEC == 2) {
+    __builtin_nontemporal_store(f32x2{x[0], x[1]}, reinterpret_cast<f32x2 *>(p));
+  } else {
+    __builtin_nontemporal_store(x[0], p);
+  }
+}
+
 template <int VEC, int DT>
 __device__ __forceinline__ void st16(uint16_t *__restrict__ p, const float (&x)[VEC]) {
   if constexpr (VEC == 8) {
@@ -227,6 +270,24 @@ __device__ __forceinline__ void st16(uint16_t *__restrict__ p, const float (&x)[
     *reinterpret_cast<uint32_t *>(p) = pack2<DT>(x[0], x[1]);
   } else {
     *p = pack1<DT>(x[0]);
+  }
+}
+
+template <int VEC, int DT, bool NT>
+__device__ __forceinline__ void st16_p(uint16_t *__restrict__ p, const float (&x)[VEC]) {
+  if constexpr (!NT) {
+    st16<VEC, DT>(p, x);
+  } else if constexpr (VEC == 8) {
+    __builtin_nontemporal_store(u32x4{pack2<DT>(x[0], x[1]), pack2<DT>(x[2], x[3]),
+                                      pack2<DT>(x[4], x[5]), pack2<DT>(x[6], x[7])},
+                                reinterpret_cast<u32x4 *>(p));
+  } else if constexpr (VEC == 4) {
+    __builtin_nontemporal_store(u32x2{pack2<DT>(x[0], x[1]), pack2<DT>(x[2], x[3])},
+                                reinterpret_cast<u32x2 *>(p));
+  } else if constexpr (VEC == 2) {
+    __builtin_nontemporal_store(pack2<DT>(x[0], x[1]), reinterpret_cast<uint32_t *>(p));
+  } else {
+    __builtin_nontemporal_store(pack1<DT>(x[0]), p);
   }
 }
 
@@ -295,22 +356,22 @@ __device__ __forceinline__ void ring_sum(const GradPtrs &g, uint32_t world, int 
 }
 
 /* The same ring-order sum for U vectors per thread. Loads are issued
- * worker-major (all U vectors of one worker back to back, kLoadBatch
- * workers ahead of the adds) and marked non-temporal. */
-template <int VEC, int U, int DT, int WIRE>
+ * worker-major (all U vectors of one worker back to back, B workers ahead
+ * of the adds) and marked non-temporal. */
+template <int VEC, int U, int DT, int WIRE, int B = kLoadBatch>
 __device__ __forceinline__ void ring_sum_uw(const GradPtrs &g, uint32_t world,
                                             const uint64_t (&i0)[U], float (&s)[U][VEC]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) set_up<VEC, DT, WIRE>(s[u], ld16<VEC, true>(g.p[0] + i0[u]));
   uint32_t j = 1;
-  for (; j + kLoadBatch <= world; j += kLoadBatch) {
-    Raw16<VEC> r[kLoadBatch][U];
+  for (; j + B <= world; j += B) {
+    Raw16<VEC> r[B][U];
 #pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b)
+    for (int b = 0; b < B; ++b)
 #pragma unroll
       for (int u = 0; u < U; ++u) r[b][u] = ld16<VEC, true>(g.p[j + b] + i0[u]);
 #pragma unroll
-    for (int b = 0; b < kLoadBatch; ++b)
+    for (int b = 0; b < B; ++b)
 #pragma unroll
       for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], r[b][u]);
   }
@@ -535,10 +596,12 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, 
  * the gradient sum: on MI355X that order streamed 5-10 % faster than
  * loading the state first, registers to spare or not. With a single worker
  * (W = 1) there is no sum, one gradient load, and the state loads go
- * first. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
+ * first. SHAPE (kShape*) sets the sum's load batch and the store policy. */
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE>
 __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk, const AdamK &h,
                                            uint64_t base) {
+  constexpr int B = shape_batch(SHAPE);
+  constexpr bool NTS = shape_nt_stores(SHAPE);
   uint64_t i0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
@@ -553,11 +616,11 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
     }
   };
   if constexpr (MULTI) {
-    ring_sum_uw<VEC, U, GDT, WIRE>(p.g, p.world, i0, s);
+    ring_sum_uw<VEC, U, GDT, WIRE, B>(p.g, p.world, i0, s);
     load_state();
   } else {
     load_state();
-    ring_sum_uw<VEC, U, GDT, WIRE>(p.g, 1, i0, s);  /* one worker: no loop runs */
+    ring_sum_uw<VEC, U, GDT, WIRE, B>(p.g, 1, i0, s);  /* one worker: no loop runs */
   }
   bool bad = false;
 #pragma unroll
@@ -570,10 +633,10 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
       bad |= !__builtin_isfinite(g);
       th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, h);
     }
-    stf<VEC>(p.master_out + i0[u], th[u]);
-    stf<VEC>(p.m_out + i0[u], m[u]);
-    stf<VEC>(p.v_out + i0[u], v[u]);
-    st16<VEC, PDT>(p.param_out + i0[u], th[u]);
+    stf_p<VEC, NTS>(p.master_out + i0[u], th[u]);
+    stf_p<VEC, NTS>(p.m_out + i0[u], m[u]);
+    stf_p<VEC, NTS>(p.v_out + i0[u], v[u]);
+    st16_p<VEC, PDT, NTS>(p.param_out + i0[u], th[u]);
   }
   return bad;
 }
@@ -616,7 +679,7 @@ __device__ __forceinline__ void flag_epoch_mark(uint64_t *flag_epoch, uint64_t v
 /* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
  * added before the unscale; a separate instance so the common case carries
  * no registers for it. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE>
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE>
 __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   const uint64_t tile = (uint64_t)kBlock * U * VEC;
   const uint64_t full = p.n / tile;  /* blocks past `full` cover the tail */
@@ -625,7 +688,8 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
   uint64_t epoch = 0;
   bool bad = p.dev ? !dev_step_consts(p, sk, h, epoch) : false;
   if (blockIdx.x < full) {
-    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE>(p, sk, h, (uint64_t)blockIdx.x * tile);
+    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE, SHAPE>(p, sk, h,
+                                                                 (uint64_t)blockIdx.x * tile);
   } else {
     /* ragged end: one element per thread, spread over enough blocks that
      * no thread walks a chain of them */

@@ -80,7 +80,7 @@ def test_refusals_before_any_launch(vlib, zs):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("world", [1, 5])
+@pytest.mark.parametrize("world", [1, 5, 14, 39])
 def test_every_variant_computes_the_step(vlib, zs, world):
     """Each variant of the world's family writes the oracle's state and
     parameters bit for bit, at several residency caps; the persistent and
