@@ -360,23 +360,42 @@ constexpr Variant mk(const char *name) {
                  T * 8 * U, M, PER, T, 0};
 }
 
-/* The same for a single worker: 4-element vectors, two per thread (the
- * W = 1 kernel's 2048-element tile); SHAPE picks the store policy. */
-template <int SHAPE>
+/* The same for a single worker: U 4-element vectors per thread (two in
+ * the production W = 1 kernel, a 2048-element tile); SHAPE picks the
+ * store policy. */
+template <int U, int SHAPE>
 __global__ __launch_bounds__(kBlock) void g4w1_kernel(FusedArgs p) {
-  const uint64_t tile = (uint64_t)kBlock * 4 * 2;
+  const uint64_t tile = (uint64_t)kBlock * 4 * U;
   const uint64_t tiles = p.n / tile;
   bool bad = false;
   if (blockIdx.x < tiles)
-    bad = fused_tile<4, 2, false, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>(
+    bad = fused_tile<4, U, false, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>(
         p, p.k, p.h, (uint64_t)blockIdx.x * tile);
   flag_or(p.flag, bad);
 }
 
-template <int SHAPE>
+template <int SHAPE, int U = 2>
 constexpr Variant mk_g4w1(const char *name) {
-  return Variant{name, reinterpret_cast<const void *>(&g4w1_kernel<SHAPE>), kBlock * 4 * 2, false,
-                 false, kBlock, 0};
+  return Variant{name, reinterpret_cast<const void *>(&g4w1_kernel<U, SHAPE>), kBlock * 4 * U,
+                 false, false, kBlock, 0};
+}
+
+/* W > 1 with U 4-element vectors per thread (four in production). */
+template <int U, int SHAPE>
+__global__ __launch_bounds__(kBlock) void g4u_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)kBlock * 4 * U;
+  const uint64_t tiles = p.n / tile;
+  bool bad = false;
+  if (blockIdx.x < tiles)
+    bad = fused_tile<4, U, true, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>(
+        p, p.k, p.h, (uint64_t)blockIdx.x * tile);
+  flag_or(p.flag, bad);
+}
+
+template <int U, int SHAPE>
+constexpr Variant mk_g4u(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&g4u_kernel<U, SHAPE>), kBlock * 4 * U,
+                 true, false, kBlock, 0};
 }
 
 template <int SHAPE>
@@ -448,6 +467,11 @@ const Variant kVariants[] = {
     mk_g4<kShapeB8Nt>("wN: 4-element lane groups, 8 loads ahead, nt stores"),
     mk_g4w1<kShapeB8>("w1: 4-element lane groups"),
     mk_g4w1<kShapeB8Nt>("w1: 4-element lane groups, nt stores"),
+    mk_g4w1<kShapeB8Nt, 1>("w1: 4-element lane groups, 1 vector/thread, nt stores"),
+    mk_g4w1<kShapeB8Nt, 4>("w1: 4-element lane groups, 4 vectors/thread, nt stores"),
+    mk_g4u<2, kShapeB8Nt>("wN: 4-element lane groups, 2 vectors/thread, nt stores"),
+    mk_g4u<8, kShapeB8Nt>("wN: 4-element lane groups, 8 vectors/thread, nt stores"),
+    mk_g4u<2, kShapeB16Nt>("wN: 4-element lane groups, 2 vectors/thread, 16 ahead, nt stores"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

@@ -135,11 +135,12 @@ __global__ __launch_bounds__(kBlock) void gather_step_kernel(GatherArgs a) {
   const uint64_t i0 = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * VEC;
   if (i0 >= len) return;
   if (VEC > 1 && i0 + VEC <= len) {
+    /* 16 bytes per lane, lane-contiguous: a wave stores 1 KB of whole lines,
+     * non-temporally (the next step reads them at most once) */
     Raw16<VEC> v = ld16<VEC, true>(src + i0);
-    if constexpr (VEC == 8) {
-      u32x4 w = {v.w[0], v.w[1], v.w[2], v.w[3]};
-      *reinterpret_cast<u32x4 *>(dst + i0) = w;
-    }
+    if constexpr (VEC == 8)
+      __builtin_nontemporal_store(u32x4{v.w[0], v.w[1], v.w[2], v.w[3]},
+                                  reinterpret_cast<u32x4 *>(dst + i0));
   } else {
     for (uint64_t i = i0; i < len && i < i0 + VEC; ++i) dst[i] = src[i];
   }

@@ -432,7 +432,7 @@ __device__ __forceinline__ bool reduce_vec(const ReduceArgs &a, const Scales &k,
   return bad;
 }
 
-template <int VEC, int U, int DT, int WIRE>
+template <int VEC, int U, int DT, int WIRE, bool NTS>
 __device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, const Scales &k, uint64_t base) {
   uint64_t i0[U];
 #pragma unroll
@@ -451,18 +451,20 @@ __device__ __forceinline__ bool reduce_tile(const ReduceArgs &a, const Scales &k
       s[u][e] = v;
       bad |= !__builtin_isfinite(unscale(v, k));
     }
-    stf<VEC>(a.out + i0[u], s[u]);
+    stf_p<VEC, NTS>(a.out + i0[u], s[u]);
   }
   return bad;
 }
 
-template <int VEC, int U, int DT, int WIRE>
+/* NTS: the fp32 partition is stored non-temporally (whole lines with
+ * 4-element vectors); the launch uses it when nothing is accumulated. */
+template <int VEC, int U, int DT, int WIRE, bool NTS>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
   const uint64_t tile = (uint64_t)kBlock * U * VEC;
   const uint64_t full = a.n / tile;  /* blocks past `full` cover the tail */
   bool bad = false;
   if (blockIdx.x < full) {
-    bad = reduce_tile<VEC, U, DT, WIRE>(a, a.k, (uint64_t)blockIdx.x * tile);
+    bad = reduce_tile<VEC, U, DT, WIRE, NTS>(a, a.k, (uint64_t)blockIdx.x * tile);
   } else {
     uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * kBlock + threadIdx.x;
     if (i < a.n) bad = reduce_vec<1, DT>(a, a.k, i);
