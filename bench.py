@@ -90,9 +90,9 @@ def fused_bytes_per_param(world, accum):
 
 def shape_of(world):
     """The fused kernel's access shape for 16-byte-aligned operands
-    (zs::kShape*): 16 loads ahead and non-temporal stores (2) from 16
-    workers on, 8 loads ahead and non-temporal stores (3) below."""
-    return 2 if world >= 16 else 3
+    (zs::kShape*): non-temporal state loads and stores, with 16 loads ahead
+    (4) from 16 workers on and 8 (5) below."""
+    return 4 if world >= 16 else 5
 
 
 def fused_instance(wl, wire=0):
@@ -549,15 +549,17 @@ def world_sweep(worlds, n, steps, warmup, torch):
 # The variant sweep: per workload, (variant id, residency cap, persistent
 # blocks per CU). Ids 0 and 5 are the production shapes (libzsvariants).
 VARIANT_SWEEP = {
-    "7b-full-w1": [(43, 2, 0), (43, 3, 0), (43, 0, 0), (42, 2, 0),
+    "7b-full-w1": [(49, 2, 0), (49, 3, 0), (43, 2, 0), (42, 2, 0), (44, 4, 0), (45, 2, 0),
                    (0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
                    (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1),
                    (30, 8, 0), (30, 0, 0), (31, 4, 0), (32, 1, 0), (33, 1, 0)],
-    "gpt2s-w8": [(41, 3, 0), (41, 0, 0), (40, 3, 0), (38, 3, 0),
+    "gpt2s-w8": [(50, 3, 0), (50, 0, 0), (41, 3, 0), (51, 3, 0), (38, 3, 0), (46, 6, 0),
+                 (47, 3, 0),
                  (5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
                  (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3),
                  (23, 3, 0), (25, 3, 0), (26, 8, 0), (27, 6, 0), (28, 2, 0), (29, 0, 0)],
-    "7p5b-shard-w64": [(40, 0, 0), (41, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0),
+    "7p5b-shard-w64": [(51, 0, 0), (50, 0, 0), (40, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0),
+                       (47, 0, 0), (48, 0, 0),
                        (5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0),
                        (9, 0, 0), (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1),
                        (18, 0, 3), (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2),

@@ -417,9 +417,10 @@ constexpr Variant mk_split(const char *name) {
                  split_tile<NL>(), M, true, (NL + NS) * 64, 2 * 3 * split_tile<NL>() * 4};
 }
 
-/* libzeroshard's own shapes, for 16-byte-aligned operands: entry 43 for
- * W = 1, entry 41 for W = 2 to 15 and entry 40 for W >= 16. Entries 0 and 5
- * are the shapes it launched before (8-element vectors, plain stores). */
+/* libzeroshard's own shapes, for 16-byte-aligned operands: entry 49 for
+ * W = 1, entry 50 for W = 2 to 15 and entry 51 for W >= 16. Entries 0 and 5
+ * are the shapes it launched before (8-element vectors, plain stores), and
+ * 43, 41 and 40 the same lane groups with plain state loads. */
 const Variant kVariants[] = {
     mk<1, false, false, 8, true, false, false>("w1: 1 vector/thread, nt gradient loads"),
     mk<2, false, false, 8, true, false, false>("w1: 2 vectors/thread"),
@@ -472,6 +473,9 @@ const Variant kVariants[] = {
     mk_g4u<2, kShapeB8Nt>("wN: 4-element lane groups, 2 vectors/thread, nt stores"),
     mk_g4u<8, kShapeB8Nt>("wN: 4-element lane groups, 8 vectors/thread, nt stores"),
     mk_g4u<2, kShapeB16Nt>("wN: 4-element lane groups, 2 vectors/thread, 16 ahead, nt stores"),
+    mk_g4w1<kShapeB8NtL>("w1: 4-element lane groups, nt stores, nt state loads"),
+    mk_g4<kShapeB8NtL>("wN: 4-element lane groups, 8 loads ahead, nt stores, nt state loads"),
+    mk_g4<kShapeB16NtL>("wN: 4-element lane groups, 16 loads ahead, nt stores, nt state loads"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

@@ -154,8 +154,8 @@ int env_blocks_per_cu() {
 /* Vector width, vectors per thread and access shape of the fused kernel.
  * Operands aligned for 4-element vectors or wider take 4-element vectors:
  * four per thread when W > 1, two when W = 1 (4096- and 2048-element
- * tiles), stored non-temporally, with the sum loading 16 workers ahead
- * from W = 16 on. Narrower vectors (unaligned operands) keep two per thread
+ * tiles), the fp32 state loaded and the results stored non-temporally,
+ * with the sum loading 16 workers ahead from W = 16 on. Narrower vectors (unaligned operands) keep two per thread
  * (one when W = 1) and plain stores. Chosen on MI355X by interleaved timing
  * against the alternatives, all computing the same bits. */
 constexpr int fused_vec_of(int aligned_vec) { return aligned_vec >= 4 ? 4 : aligned_vec; }
@@ -163,7 +163,7 @@ constexpr int fused_tile_vecs(int vec, bool multi) {
   return vec == 4 ? (multi ? 4 : 2) : (multi ? 2 : 1);
 }
 constexpr int fused_shape(int vec, uint32_t world) {
-  return vec < 4 ? kShapeB8 : world >= 16 ? kShapeB16Nt : kShapeB8Nt;
+  return vec < 4 ? kShapeB8 : world >= 16 ? kShapeB16NtL : kShapeB8NtL;
 }
 
 /* Dynamic LDS bytes that cap the fused kernel's residency (0: no cap). */
@@ -620,11 +620,11 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   const size_t lds = fused_lds_bytes(a->world);
 #define ZS_KF(V, L, A, G, P, W, S) \
   launch_fused<V, fused_tile_vecs(V, L), L, A, G, P, W, S>(grid, block, lds, s, p)
-#define ZS_K4(V, A, G, P, W)                                             \
-  do {                                                                   \
-    if (!multi) ZS_KF(4, false, A, G, P, W, kShapeB8Nt);                 \
-    else if (shape == kShapeB16Nt) ZS_KF(4, true, A, G, P, W, kShapeB16Nt); \
-    else ZS_KF(4, true, A, G, P, W, kShapeB8Nt);                         \
+#define ZS_K4(V, A, G, P, W)                                                 \
+  do {                                                                       \
+    if (!multi) ZS_KF(4, false, A, G, P, W, kShapeB8NtL);                    \
+    else if (shape == kShapeB16NtL) ZS_KF(4, true, A, G, P, W, kShapeB16NtL); \
+    else ZS_KF(4, true, A, G, P, W, kShapeB8NtL);                            \
   } while (0)
 #define ZS_KNARROW(V, A, G, P, W)                         \
   do {                                                    \

@@ -49,15 +49,21 @@ constexpr int kLoadBatch = 8;   /* gradient vectors in flight per thread   */
  * lines, while with 8-element vectors a lane's 32 bytes take two stores and
  * each 64-byte line is half-written by two instructions, which then leave
  * the L2 as separate writes (14 % more write bytes at W = 64, measured).
- * The library launches kShapeB8Nt (W < 16) and kShapeB16Nt (W >= 16) on
- * 4-element vectors, and kShapeB8 on the narrower vectors of unaligned
+ * The library launches kShapeB8NtL (W < 16) and kShapeB16NtL (W >= 16)
+ * on 4-element vectors, and kShapeB8 on the narrower vectors of unaligned
  * operands. */
 constexpr int kShapeB8 = 0, kShapeB16 = 1, kShapeB16Nt = 2, kShapeB8Nt = 3;
+/* as kShapeB16Nt / kShapeB8Nt, with the fp32 state (and the accumulated
+ * gradient) also loaded non-temporally: read once per step, like the
+ * gradients (+1 to 1.8 % at W = 1 and W = 8 against plain state loads,
+ * neutral at W = 64) */
+constexpr int kShapeB16NtL = 4, kShapeB8NtL = 5;
 
 constexpr int shape_batch(int shape) {
-  return shape == kShapeB8 || shape == kShapeB8Nt ? kLoadBatch : 16;
+  return shape == kShapeB8 || shape == kShapeB8Nt || shape == kShapeB8NtL ? kLoadBatch : 16;
 }
-constexpr bool shape_nt_stores(int shape) { return shape == kShapeB16Nt || shape == kShapeB8Nt; }
+constexpr bool shape_nt_stores(int shape) { return shape >= kShapeB16Nt; }
+constexpr bool shape_nt_loads(int shape) { return shape >= kShapeB16NtL; }
 
 /* ------------------------------------------------------------------------
  * Per-element arithmetic. Each line is written exactly in the order the
@@ -219,6 +225,21 @@ __device__ __forceinline__ void ldf(const float *__restrict__ p, float (&x)[VEC]
     x[0] = a.x; x[1] = a.y;
   } else {
     x[0] = *p;
+  }
+}
+
+/* ldf with the loads marked non-temporal when NT (VEC 4 or 8) */
+template <int VEC, bool NT>
+__device__ __forceinline__ void ldf_p(const float *__restrict__ p, float (&x)[VEC]) {
+  if constexpr (!NT || (VEC != 4 && VEC != 8)) {
+    ldf<VEC>(p, x);
+  } else {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h) {
+      f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p) + h);
+      x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
+    }
   }
 }
 
@@ -604,6 +625,7 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
                                            uint64_t base) {
   constexpr int B = shape_batch(SHAPE);
   constexpr bool NTS = shape_nt_stores(SHAPE);
+  constexpr bool NTL = shape_nt_loads(SHAPE);
   uint64_t i0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
@@ -611,10 +633,10 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
   auto load_state = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      ldf<VEC>(p.master_in + i0[u], th[u]);
-      ldf<VEC>(p.m_in + i0[u], m[u]);
-      ldf<VEC>(p.v_in + i0[u], v[u]);
-      if constexpr (ACC) ldf<VEC>(p.acc_in + i0[u], acc[u]);
+      ldf_p<VEC, NTL>(p.master_in + i0[u], th[u]);
+      ldf_p<VEC, NTL>(p.m_in + i0[u], m[u]);
+      ldf_p<VEC, NTL>(p.v_in + i0[u], v[u]);
+      if constexpr (ACC) ldf_p<VEC, NTL>(p.acc_in + i0[u], acc[u]);
     }
   };
   if constexpr (MULTI) {

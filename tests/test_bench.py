@@ -82,12 +82,12 @@ def test_fused_instance_names_match_the_kernel_template():
     from sharded_mixed_precision_zs_amd import synth
     W = synth.WORKLOADS
     assert bench.fused_instance(W["7b-full-w1"]) == \
-        "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 3>"
+        "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 5>"
     assert bench.fused_instance(W["7p5b-shard-w64"]) == \
-        "zs::fused_kernel<4, 4, true, false, 0, 0, 0, 2>"
+        "zs::fused_kernel<4, 4, true, false, 0, 0, 0, 4>"
     assert bench.fused_instance(W["1p3b-w4-acc4-fp16"]) == \
-        "zs::fused_kernel<4, 4, true, true, 1, 1, 0, 3>"
-    assert [bench.shape_of(w) for w in (1, 2, 15, 16, 64)] == [3, 3, 3, 2, 2]
+        "zs::fused_kernel<4, 4, true, true, 1, 1, 0, 5>"
+    assert [bench.shape_of(w) for w in (1, 2, 15, 16, 64)] == [5, 5, 5, 4, 4]
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
     assert bench.fused_bytes_per_param(4, 4) == (24, 14)
 
@@ -98,14 +98,15 @@ def test_variant_sweep_plans_fit_their_workloads(hip_built):
     from sharded_mixed_precision_zs_amd import synth
     lib = bench._variantlib()
     caps = {1: 2, 8: 3, 64: 0}
-    production = {1: 43, 8: 41, 64: 40}  # the shapes zs_step_fused launches at these W
+    production = {1: 49, 8: 50, 64: 51}  # the shapes zs_step_fused launches at these W
     for name, plan in bench.VARIANT_SWEEP.items():
         W = synth.WORKLOADS[name].world
         for v, cap, per in plan:
             assert lib.zs_variant_multi(v) == (1 if W > 1 else 0), (name, v)
             assert 0 <= cap <= 32 and 0 <= per <= 8
         assert plan[0] == (production[W], caps[W], 0), name
-    assert lib.zs_variant_name(40).decode() == \
-        "wN: 4-element lane groups, 16 loads ahead, nt stores"
-    assert lib.zs_variant_name(41).decode() == "wN: 4-element lane groups, 8 loads ahead, nt stores"
-    assert lib.zs_variant_name(43).decode() == "w1: 4-element lane groups, nt stores"
+    assert lib.zs_variant_name(49).decode() == "w1: 4-element lane groups, nt stores, nt state loads"
+    assert lib.zs_variant_name(50).decode() == \
+        "wN: 4-element lane groups, 8 loads ahead, nt stores, nt state loads"
+    assert lib.zs_variant_name(51).decode() == \
+        "wN: 4-element lane groups, 16 loads ahead, nt stores, nt state loads"
