@@ -69,16 +69,20 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(workload):
+def recorded_traffic(workload, kernel=None):
     """HBM bytes per fused launch of `workload` from the committed rocprofv3
-    request-counter summary, if it was taken on the current kernel source;
-    else None."""
+    request-counter summary, if it was taken on the current kernel source
+    and (when `kernel` is given) on that kernel instance; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     if not m or m.group(1) != kernel_source_hash():
         return None
+    if kernel is not None:
+        row = re.search(rf"^\| `([^`]+)` \({re.escape(workload)}\) \|", text, re.M)
+        if not row or row.group(1) != kernel:
+            return None
     m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
 
@@ -88,21 +92,33 @@ def fused_bytes_per_param(world, accum):
     return 2 * world + 12 + (4 if accum > 1 else 0), 14
 
 
-def shape_of(world):
-    """The fused kernel's access shape for 16-byte-aligned operands
-    (zs::kShape*): non-temporal state loads and stores, with 16 loads ahead
-    (4) from 16 workers on and 8 (5) below."""
-    return 4 if world >= 16 else 5
+FUSED_MANY_TILES = 20000   # 2048-element tiles
+
+
+def fused_shape(world, n):
+    """(vectors per thread, zs::kShape* access shape, blocks per CU; 0 = no
+    cap) of the fused kernel that zs_step_fused launches for a
+    16-byte-aligned shard of n parameters over `world` workers: non-temporal
+    state loads and stores in 4-element vectors, 16 loads ahead (4) or 8
+    (5), the tile depth and residency following W and the shard's size."""
+    if world == 1:
+        return 2, 5, 2
+    if world == 2:
+        return 4, 5, 3
+    many = n // 2048 >= FUSED_MANY_TILES
+    if world <= 12:
+        return 2, 5, 3 if many else 4
+    if world <= 16:
+        return (2, 5, 3) if many else (4, 4 if world == 16 else 5, 0)
+    return 1, 4, 6
 
 
 def fused_instance(wl, wire=0):
     """Template instance of zs::fused_kernel that a 16-byte-aligned shard of
-    this workload launches (the name rocprofv3 shows): 4-element vectors,
-    four per thread when W > 1 and two when W = 1."""
-    multi = wl.world > 1
-    return (f"zs::fused_kernel<4, {4 if multi else 2}, {str(multi).lower()}, "
-            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, "
-            f"{shape_of(wl.world)}>")
+    this workload launches (the name rocprofv3 shows)."""
+    u, shape, _ = fused_shape(wl.world, wl.n)
+    return (f"zs::fused_kernel<4, {u}, {str(wl.world > 1).lower()}, "
+            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, {shape}>")
 
 
 def timing_events(torch, count):
@@ -332,7 +348,7 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_p
 
 def roofline_of(res, wl, wire=0):
     """The roofline object of one workload's fused kernel."""
-    traffic = recorded_traffic(res["workload"]) if wire == 0 else None
+    traffic = recorded_traffic(res["workload"], fused_instance(wl, wire)) if wire == 0 else None
     rd, wr = fused_bytes_per_param(wl.world, wl.accum)
     return {"bound": "hbm", "achieved": res["fused_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": res["fused_gbps"] / PEAK_HBM_GBPS, "traffic": traffic,
@@ -553,13 +569,13 @@ VARIANT_SWEEP = {
                    (0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
                    (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1),
                    (30, 8, 0), (30, 0, 0), (31, 4, 0), (32, 1, 0), (33, 1, 0)],
-    "gpt2s-w8": [(50, 3, 0), (50, 0, 0), (41, 3, 0), (51, 3, 0), (38, 3, 0), (46, 6, 0),
-                 (47, 3, 0),
+    "gpt2s-w8": [(53, 4, 0), (53, 3, 0), (52, 0, 0), (50, 3, 0), (50, 0, 0), (41, 3, 0),
+                 (51, 3, 0), (38, 3, 0), (46, 6, 0), (47, 3, 0),
                  (5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
                  (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3),
                  (23, 3, 0), (25, 3, 0), (26, 8, 0), (27, 6, 0), (28, 2, 0), (29, 0, 0)],
-    "7p5b-shard-w64": [(51, 0, 0), (50, 0, 0), (40, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0),
-                       (47, 0, 0), (48, 0, 0),
+    "7p5b-shard-w64": [(55, 6, 0), (55, 0, 0), (56, 3, 0), (53, 3, 0), (51, 0, 0), (50, 0, 0),
+                       (40, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0), (47, 0, 0), (48, 0, 0),
                        (5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0),
                        (9, 0, 0), (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1),
                        (18, 0, 3), (19, 0, 2), (20, 0, 2), (21, 0, 1), (22, 0, 2),

@@ -380,7 +380,8 @@ constexpr Variant mk_g4w1(const char *name) {
                  false, false, kBlock, 0};
 }
 
-/* W > 1 with U 4-element vectors per thread (four in production). */
+/* W > 1 with U 4-element vectors per thread (one, two or four in
+ * production, by W and the shard's size). */
 template <int U, int SHAPE>
 __global__ __launch_bounds__(kBlock) void g4u_kernel(FusedArgs p) {
   const uint64_t tile = (uint64_t)kBlock * 4 * U;
@@ -418,9 +419,12 @@ constexpr Variant mk_split(const char *name) {
 }
 
 /* libzeroshard's own shapes, for 16-byte-aligned operands: entry 49 for
- * W = 1, entry 50 for W = 2 to 15 and entry 51 for W >= 16. Entries 0 and 5
- * are the shapes it launched before (8-element vectors, plain stores), and
- * 43, 41 and 40 the same lane groups with plain state loads. */
+ * W = 1; entry 50 for W = 2 (and W = 13 to 15 on shards under 20 K
+ * 2048-element tiles) and 51 for W = 16 on such shards; entry 53 for W = 3
+ * to 12, and W = 13 to 16 on larger shards; entry 55 from W = 17 on.
+ * Entries 50 and 51 were its shapes for all of W > 1 before the tile depth
+ * followed W; entries 0 and 5 are older ones (8-element vectors, plain
+ * stores), and 43, 41 and 40 the lane groups with plain state loads. */
 const Variant kVariants[] = {
     mk<1, false, false, 8, true, false, false>("w1: 1 vector/thread, nt gradient loads"),
     mk<2, false, false, 8, true, false, false>("w1: 2 vectors/thread"),
@@ -476,6 +480,11 @@ const Variant kVariants[] = {
     mk_g4w1<kShapeB8NtL>("w1: 4-element lane groups, nt stores, nt state loads"),
     mk_g4<kShapeB8NtL>("wN: 4-element lane groups, 8 loads ahead, nt stores, nt state loads"),
     mk_g4<kShapeB16NtL>("wN: 4-element lane groups, 16 loads ahead, nt stores, nt state loads"),
+    mk_g4u<1, kShapeB8NtL>("wN: 4-element lane groups, 1 vector/thread, nt loads and stores"),
+    mk_g4u<2, kShapeB8NtL>("wN: 4-element lane groups, 2 vectors/thread, nt loads and stores"),
+    mk_g4w1<kShapeB8NtL, 1>("w1: 4-element lane groups, 1 vector/thread, nt loads and stores"),
+    mk_g4u<1, kShapeB16NtL>("wN: 4-element lane groups, 1 vector/thread, 16 ahead, nt loads and stores"),
+    mk_g4u<2, kShapeB16NtL>("wN: 4-element lane groups, 2 vectors/thread, 16 ahead, nt loads and stores"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

@@ -104,21 +104,28 @@ using zs_host::make_adam;
 using zs_host::make_scales;
 
 /* ------------------------------------------------------------------------
- * Residency and tile of the fused kernel. With writes mixed into the read
- * stream, HBM delivered more on MI355X when fewer blocks per CU were in
- * flight (fewer DRAM rows in contention). Interleaved A/B runs on one GPU,
- * shards of 15 M to 1 G parameters:
- *   - W = 2 to 8: 3 blocks (12 waves) per CU, against the register-limited
- *     5 to 6, measured +2.7 to +4.6 %;
- *   - W = 1: one vector per thread (2048-element tiles) and 2 blocks per CU
- *     beat that by a further 2.7 to 6 % in every variant tried (bf16 and
- *     fp16, with and without an accumulated gradient); with W = 2 to 16
- *     the same shape lost up to 18 %;
- *   - W = 16 to 64: no cap was reliably better than none (-1.3 to +2 %),
- *     so larger W runs uncapped.
- * The cap is dynamic LDS that the kernel never touches: LDS per CU / cap,
- * less 1 KB. ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..8 = that many blocks)
- * overrides the cap, for measurements.
+ * Tile and residency of the fused kernel. Each thread owns U 4-element
+ * vectors of a tile (1024 * U elements per block) and the blocks per CU are
+ * capped with dynamic LDS that the kernel never touches (LDS per CU / cap,
+ * less 1 KB). With W gradient and three state streams read while four
+ * streams are written, HBM delivered more on MI355X with fewer bytes in
+ * flight per CU than the registers allow; how many fewer depends on W and,
+ * for W = 3 to 16, on the shard's size. Interleaved timings on one GPU
+ * against the alternatives (all computing the same bits), shards of 0.35 M
+ * to 7 G parameters, three GPUs:
+ *   - W = 1: U = 2, 2 blocks per CU.
+ *   - W = 2: U = 4, 3 blocks per CU (U = 2 within 0.5 %).
+ *   - W = 3 to 16 with 20 K 2048-element tiles or more: U = 2, 3 blocks
+ *     per CU, +2 to +7 % over U = 4 at 3 blocks (or uncapped from W = 9).
+ *   - W = 3 to 12 below that: U = 2, 4 blocks per CU, +2.5 to +18 % (3
+ *     blocks lost 2 % at W = 8 and 15.6 M parameters); W = 13 to 16 below
+ *     it keep U = 4 uncapped (U = 2 lost 4 % at W = 16 and 15.6 M).
+ *   - W = 17 to 64: U = 1 with the sum loading 16 workers ahead, 6 blocks
+ *     per CU, +1 to +8 % over U = 4 uncapped.
+ * Operands aligned for 2- or 1-element vectors only keep the shapes they
+ * had before: U = 2 (1 when W = 1), plain stores, 2, 3 or no cap.
+ * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..8 = that many blocks) overrides
+ * the cap, for measurements.
  * ---------------------------------------------------------------------- */
 
 struct DeviceLds {
@@ -151,25 +158,35 @@ int env_blocks_per_cu() {
   return v;
 }
 
-/* Vector width, vectors per thread and access shape of the fused kernel.
- * Operands aligned for 4-element vectors or wider take 4-element vectors:
- * four per thread when W > 1, two when W = 1 (4096- and 2048-element
- * tiles), the fp32 state loaded and the results stored non-temporally,
- * with the sum loading 16 workers ahead from W = 16 on. Narrower vectors (unaligned operands) keep two per thread
- * (one when W = 1) and plain stores. Chosen on MI355X by interleaved timing
- * against the alternatives, all computing the same bits. */
+/* Vector width, vectors per thread, access shape (zs::kShape*) and blocks
+ * per CU (0: no cap) of the fused kernel for `vec`-aligned operands. */
 constexpr int fused_vec_of(int aligned_vec) { return aligned_vec >= 4 ? 4 : aligned_vec; }
-constexpr int fused_tile_vecs(int vec, bool multi) {
-  return vec == 4 ? (multi ? 4 : 2) : (multi ? 2 : 1);
-}
-constexpr int fused_shape(int vec, uint32_t world) {
-  return vec < 4 ? kShapeB8 : world >= 16 ? kShapeB16NtL : kShapeB8NtL;
+constexpr uint64_t kFusedManyTiles = 20000; /* 2048-element tiles */
+
+struct FusedShape {
+  int tile_vecs;
+  int access;
+  int cap;
+};
+
+FusedShape fused_shape(int vec, uint32_t world, uint64_t n) {
+  if (vec < 4) return {world > 1 ? 2 : 1, kShapeB8, world == 1 ? 2 : world <= 8 ? 3 : 0};
+  if (world == 1) return {2, kShapeB8NtL, 2};
+  if (world == 2) return {4, kShapeB8NtL, 3};
+  const bool many = n / 2048 >= kFusedManyTiles;
+  if (world <= 12) return {2, kShapeB8NtL, many ? 3 : 4};
+  if (world <= 16) {
+    if (many) return {2, kShapeB8NtL, 3};
+    return {4, world == 16 ? kShapeB16NtL : kShapeB8NtL, 0};
+  }
+  return {1, kShapeB16NtL, 6};
 }
 
-/* Dynamic LDS bytes that cap the fused kernel's residency (0: no cap). */
-size_t fused_lds_bytes(uint32_t world) {
-  int cap = env_blocks_per_cu();
-  if (cap < 0) cap = world == 1 ? 2 : world <= 8 ? 3 : 0;
+/* Dynamic LDS bytes that hold the fused kernel to `cap` blocks per CU (0:
+ * no cap), or to ZS_FUSED_BLOCKS_PER_CU when that is set. */
+size_t fused_lds_bytes(int cap) {
+  const int forced = env_blocks_per_cu();
+  if (forced >= 0) cap = forced;
   if (cap == 0) return 0;
   const DeviceLds d = device_lds();
   if (d.lds_per_cu <= 0) return 0;
@@ -612,24 +629,26 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
                        a->v_out, a->acc_in ? a->acc_in : a->master_in};
   const int vec = fused_vec_of(pick_vec(p16, (int)a->world + 1, f32, 7));
   const bool multi = a->world > 1, acc = a->acc_in != nullptr;
-  const int per_thread = vec * fused_tile_vecs(vec, multi);
+  const FusedShape fs = fused_shape(vec, a->world, n);
+  const int per_thread = vec * fs.tile_vecs;
   if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
-  const int shape = fused_shape(vec, a->world);
-  const size_t lds = fused_lds_bytes(a->world);
-#define ZS_KF(V, L, A, G, P, W, S) \
-  launch_fused<V, fused_tile_vecs(V, L), L, A, G, P, W, S>(grid, block, lds, s, p)
-#define ZS_K4(V, A, G, P, W)                                                 \
-  do {                                                                       \
-    if (!multi) ZS_KF(4, false, A, G, P, W, kShapeB8NtL);                    \
-    else if (shape == kShapeB16NtL) ZS_KF(4, true, A, G, P, W, kShapeB16NtL); \
-    else ZS_KF(4, true, A, G, P, W, kShapeB8NtL);                            \
+  const size_t lds = fused_lds_bytes(fs.cap);
+#define ZS_KF(V, U, L, A, G, P, W, S) \
+  launch_fused<V, U, L, A, G, P, W, S>(grid, block, lds, s, p)
+#define ZS_K4(V, A, G, P, W)                                                         \
+  do {                                                                               \
+    if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL);                         \
+    else if (fs.tile_vecs == 1) ZS_KF(4, 1, true, A, G, P, W, kShapeB16NtL);         \
+    else if (fs.tile_vecs == 2) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL);          \
+    else if (fs.access == kShapeB16NtL) ZS_KF(4, 4, true, A, G, P, W, kShapeB16NtL); \
+    else ZS_KF(4, 4, true, A, G, P, W, kShapeB8NtL);                                 \
   } while (0)
-#define ZS_KNARROW(V, A, G, P, W)                         \
-  do {                                                    \
-    if (!multi) ZS_KF(V, false, A, G, P, W, kShapeB8);    \
-    else ZS_KF(V, true, A, G, P, W, kShapeB8);            \
+#define ZS_KNARROW(V, A, G, P, W)                           \
+  do {                                                      \
+    if (!multi) ZS_KF(V, 1, false, A, G, P, W, kShapeB8);   \
+    else ZS_KF(V, 2, true, A, G, P, W, kShapeB8);           \
   } while (0)
 #define ZS_KWIRE(KM, V, A, G, P)                                   \
   do {                                                             \

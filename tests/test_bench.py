@@ -3,6 +3,7 @@ traffic figure that follows the kernel source, the shard replicas that keep
 a step's inputs out of the last-level cache, and the CPU-baseline record."""
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -32,6 +33,11 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     got = bench.recorded_traffic("gpt2s-w8")
     assert got is not None and got > 0
     assert bench.recorded_traffic("no-such-workload") is None
+    # only for the instance the row was taken on
+    row = re.search(r"^\| `([^`]+)` \(gpt2s-w8\) \|", text, re.M)
+    assert row is not None
+    assert bench.recorded_traffic("gpt2s-w8", row.group(1)) == got
+    assert bench.recorded_traffic("gpt2s-w8", "zs::fused_kernel<no such instance>") is None
     other = tmp_path / "zs_kernels.h"
     other.write_text("// a different kernel source\n")
     monkeypatch.setattr(bench, "KERNEL_SRC", str(other))
@@ -84,10 +90,16 @@ def test_fused_instance_names_match_the_kernel_template():
     assert bench.fused_instance(W["7b-full-w1"]) == \
         "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 5>"
     assert bench.fused_instance(W["7p5b-shard-w64"]) == \
-        "zs::fused_kernel<4, 4, true, false, 0, 0, 0, 4>"
+        "zs::fused_kernel<4, 1, true, false, 0, 0, 0, 4>"
     assert bench.fused_instance(W["1p3b-w4-acc4-fp16"]) == \
-        "zs::fused_kernel<4, 4, true, true, 1, 1, 0, 5>"
-    assert [bench.shape_of(w) for w in (1, 2, 15, 16, 64)] == [5, 5, 5, 4, 4]
+        "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5>"
+    assert bench.fused_instance(W["gpt2s-w8"]) == \
+        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5>"
+    big, small = 40_960_000, 40_959_999  # 20 000 tiles of 2048 and one element short
+    assert [bench.fused_shape(w, big) for w in (1, 2, 3, 12, 13, 16, 17, 64)] == \
+        [(2, 5, 2), (4, 5, 3), (2, 5, 3), (2, 5, 3), (2, 5, 3), (2, 5, 3), (1, 4, 6), (1, 4, 6)]
+    assert [bench.fused_shape(w, small) for w in (1, 2, 3, 12, 13, 16, 17, 64)] == \
+        [(2, 5, 2), (4, 5, 3), (2, 5, 4), (2, 5, 4), (4, 5, 0), (4, 4, 0), (1, 4, 6), (1, 4, 6)]
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
     assert bench.fused_bytes_per_param(4, 4) == (24, 14)
 
@@ -97,16 +109,17 @@ def test_variant_sweep_plans_fit_their_workloads(hip_built):
     each plan starts with the production shape at libzeroshard's own cap."""
     from sharded_mixed_precision_zs_amd import synth
     lib = bench._variantlib()
-    caps = {1: 2, 8: 3, 64: 0}
-    production = {1: 49, 8: 50, 64: 51}  # the shapes zs_step_fused launches at these W
+    # the shapes zs_step_fused launches for these workloads, at its own caps
+    production = {"7b-full-w1": (49, 2), "gpt2s-w8": (53, 4), "7p5b-shard-w64": (55, 6)}
     for name, plan in bench.VARIANT_SWEEP.items():
         W = synth.WORKLOADS[name].world
         for v, cap, per in plan:
             assert lib.zs_variant_multi(v) == (1 if W > 1 else 0), (name, v)
             assert 0 <= cap <= 32 and 0 <= per <= 8
-        assert plan[0] == (production[W], caps[W], 0), name
+        assert plan[0] == (*production[name], 0), name
     assert lib.zs_variant_name(49).decode() == "w1: 4-element lane groups, nt stores, nt state loads"
-    assert lib.zs_variant_name(50).decode() == \
-        "wN: 4-element lane groups, 8 loads ahead, nt stores, nt state loads"
-    assert lib.zs_variant_name(51).decode() == \
-        "wN: 4-element lane groups, 16 loads ahead, nt stores, nt state loads"
+    assert lib.zs_variant_name(53).decode() == \
+        "wN: 4-element lane groups, 2 vectors/thread, nt loads and stores"
+    assert lib.zs_variant_name(55).decode() == \
+        "wN: 4-element lane groups, 1 vector/thread, 16 ahead, nt loads and stores"
+    assert [lib.zs_variant_tile(v) for v in (49, 53, 55)] == [2048, 2048, 1024]

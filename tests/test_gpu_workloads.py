@@ -166,6 +166,28 @@ def test_gpt2s_w8_full(env):
     run_workload(env, "gpt2s-w8")
 
 
+# One shard per branch of the fused kernel's launch rule, whose vectors per
+# thread, loads ahead and blocks per CU follow W and the shard's size:
+# W = 2 (four vectors, 3 blocks per CU); W = 13 and 16 under 20 000
+# 2048-element tiles (four vectors, no cap, 8 and 16 loads ahead); W = 17
+# (one vector, 16 ahead, 6 blocks per CU); W = 3 and 16 at 20 000 tiles and
+# a half (two vectors, 3 blocks per CU). Each n is ragged against every tile.
+TILE_RULE_CASES = [(2, 1_000_003), (13, 1_000_003), (16, 1_000_003), (17, 1_000_003),
+                   (3, 40_961_029), (16, 40_961_029)]
+
+
+@pytest.mark.parametrize("world,n", TILE_RULE_CASES)
+def test_each_launch_shape_matches_the_oracle(env, world, n):
+    zs, synth, shard = env
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], name=f"shape-w{world}-n{n}",
+                             world=world, phi=world * n, steps=2, bucket=0)
+    assert wl.n == n and wl.offset == 0
+    wins = _windows(n, 4, world) if n > 4 * WINDOW else None
+    run_workload(env, wl.name, windows=wins, wl=wl)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("device_commit", [False, True])
 def test_7p5b_shard_w64_windows(env, device_commit):
     zs, synth, shard = env
