@@ -565,16 +565,16 @@ def world_sweep(worlds, n, steps, warmup, torch):
 # The variant sweep: per workload, (variant id, residency cap, persistent
 # blocks per CU). Ids 0 and 5 are the production shapes (libzsvariants).
 VARIANT_SWEEP = {
-    "7b-full-w1": [(49, 2, 0), (49, 3, 0), (43, 2, 0), (42, 2, 0), (44, 4, 0), (45, 2, 0),
+    "7b-full-w1": [(49, 2, 0), (59, 2, 0), (49, 3, 0), (43, 2, 0), (42, 2, 0), (44, 4, 0), (45, 2, 0),
                    (0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
                    (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1),
                    (30, 8, 0), (30, 0, 0), (31, 4, 0), (32, 1, 0), (33, 1, 0)],
-    "gpt2s-w8": [(53, 4, 0), (53, 3, 0), (52, 0, 0), (50, 3, 0), (50, 0, 0), (41, 3, 0),
+    "gpt2s-w8": [(53, 4, 0), (58, 4, 0), (53, 3, 0), (52, 0, 0), (50, 3, 0), (50, 0, 0), (41, 3, 0),
                  (51, 3, 0), (38, 3, 0), (46, 6, 0), (47, 3, 0),
                  (5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
                  (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3),
                  (23, 3, 0), (25, 3, 0), (26, 8, 0), (27, 6, 0), (28, 2, 0), (29, 0, 0)],
-    "7p5b-shard-w64": [(55, 6, 0), (55, 0, 0), (56, 3, 0), (53, 3, 0), (51, 0, 0), (50, 0, 0),
+    "7p5b-shard-w64": [(55, 6, 0), (57, 6, 0), (55, 0, 0), (56, 3, 0), (53, 3, 0), (51, 0, 0), (50, 0, 0),
                        (40, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0), (47, 0, 0), (48, 0, 0),
                        (5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0),
                        (9, 0, 0), (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1),
@@ -693,6 +693,45 @@ def variant_sweep(name, plan, reps, torch, rounds=3):
                 reps_per_round=reps, rounds=rounds, results=out)
 
 
+# Shards of the tile-depth sweep: W workers over n parameters (the 7.5B
+# shard's hyper-parameters and generator), a GPT-2-sized and a 7.5B-sized n.
+SHAPE_GRID = [(W, n) for n in (15_554_976, 117_187_500) for W in (2, 3, 4, 8, 12, 16, 24, 32, 64)]
+
+
+def shape_plan(world):
+    """Alternatives to zs_step_fused's own launch at W = `world`: the previous
+    shape (four vectors per thread, 3 blocks per CU up to W = 8, uncapped
+    above, 16 loads ahead from W = 16), two vectors at 3 and 4 blocks per CU,
+    and one vector with 16 loads ahead at 6 blocks per CU."""
+    prev = (50, 3, 0) if world <= 8 else (50, 0, 0) if world < 16 else (51, 0, 0)
+    return [prev, (53, 3, 0), (53, 4, 0), (55, 6, 0)]
+
+
+def shape_sweep(torch, rounds=3):
+    """variant_sweep over SHAPE_GRID: for each shard, the launch the library
+    picks against shape_plan's alternatives, bits checked, interleaved."""
+    import dataclasses
+
+    from sharded_mixed_precision_zs_amd import synth
+
+    base = synth.WORKLOADS["7p5b-shard-w64"]
+    out = []
+    for W, n in SHAPE_GRID:
+        name = f"shape-w{W}-n{n}"
+        synth.WORKLOADS[name] = dataclasses.replace(
+            base, name=name, world=W, phi=W * n,
+            description=f"{W} workers' bf16 gradients over a {n}-parameter shard")
+        try:
+            reps = max(4, min(100, int(2e10 / ((2 * W + 26) * n))))
+            r = variant_sweep(name, shape_plan(W), reps, torch, rounds=rounds)
+        finally:
+            del synth.WORKLOADS[name]
+        u, shape, cap = fused_shape(W, r["n"])
+        r["production"] = {"vectors_per_thread": u, "access_shape": shape, "blocks_per_cu": cap}
+        out.append(r)
+    return out
+
+
 def phase_sweep(torch, reps=10, rounds=2):
     """Reads and writes of the 7.5B shard's step separated in time, with the
     stream probe: per chunk of the shard, a read-only probe kernel (the 64
@@ -809,6 +848,10 @@ def main():
     ap.add_argument("--sweep-phases", action="store_true",
                     help="time the 7.5B shard's reads and writes separated in time (stream "
                          "probe, 1 to 64 chunks) and print that table as the JSON line instead")
+    ap.add_argument("--sweep-shapes", action="store_true",
+                    help="time the fused step's tile depths and residency caps against "
+                         "libzeroshard's own launch over a grid of W and shard sizes and print "
+                         "that table as the JSON line instead")
     ap.add_argument("--sweep-variants", default="",
                     help="comma-separated workloads (of " + ", ".join(VARIANT_SWEEP) + "): time "
                          "the fused kernel's shapes of libzsvariants against libzeroshard's and "
@@ -834,6 +877,10 @@ def main():
     if args.sweep_phases:
         print(json.dumps({"metric": "7.5B-shard step mix, reads and writes separated in time",
                           "unit": "ms", "phases": phase_sweep(torch)}))
+        return
+    if args.sweep_shapes:
+        print(json.dumps({"metric": "fused step tile depth and residency by W and shard size, "
+                          "ms per launch", "unit": "ms", "sweeps": shape_sweep(torch)}))
         return
     if args.sweep_variants:
         res = [variant_sweep(w, VARIANT_SWEEP[w], max(4, args.steps), torch)

@@ -418,6 +418,18 @@ constexpr Variant mk_split(const char *name) {
                  split_tile<NL>(), M, true, (NL + NS) * 64, 2 * 3 * split_tile<NL>() * 4};
 }
 
+/* libzeroshard's fused_kernel itself (with its ragged-tail and device
+ * scale paths), launched through this library's launcher: against the
+ * g4 kernels of the same shape it separates the cost of those paths from
+ * that of the launch. */
+template <int U, bool M, int SHAPE>
+constexpr Variant mk_prod(const char *name) {
+  return Variant{name,
+                 reinterpret_cast<const void *>(
+                     &fused_kernel<4, U, M, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>),
+                 kBlock * 4 * U, M, false, kBlock, 0};
+}
+
 /* libzeroshard's own shapes, for 16-byte-aligned operands: entry 49 for
  * W = 1; entry 50 for W = 2 (and W = 13 to 15 on shards under 20 K
  * 2048-element tiles) and 51 for W = 16 on such shards; entry 53 for W = 3
@@ -485,6 +497,9 @@ const Variant kVariants[] = {
     mk_g4w1<kShapeB8NtL, 1>("w1: 4-element lane groups, 1 vector/thread, nt loads and stores"),
     mk_g4u<1, kShapeB16NtL>("wN: 4-element lane groups, 1 vector/thread, 16 ahead, nt loads and stores"),
     mk_g4u<2, kShapeB16NtL>("wN: 4-element lane groups, 2 vectors/thread, 16 ahead, nt loads and stores"),
+    mk_prod<1, true, kShapeB16NtL>("wN: libzeroshard's kernel, 1 vector/thread, 16 ahead"),
+    mk_prod<2, true, kShapeB8NtL>("wN: libzeroshard's kernel, 2 vectors/thread, 8 ahead"),
+    mk_prod<2, false, kShapeB8NtL>("w1: libzeroshard's kernel, 2 vectors/thread"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

@@ -123,3 +123,17 @@ def test_variant_sweep_plans_fit_their_workloads(hip_built):
     assert lib.zs_variant_name(55).decode() == \
         "wN: 4-element lane groups, 1 vector/thread, 16 ahead, nt loads and stores"
     assert [lib.zs_variant_tile(v) for v in (49, 53, 55)] == [2048, 2048, 1024]
+
+
+def test_shape_sweep_plans_fit_their_shards(hip_built):
+    """Every shard of the tile-depth sweep has W > 1, and every alternative
+    it times is a multi-worker variant with a cap the launch accepts."""
+    lib = bench._variantlib()
+    assert len(bench.SHAPE_GRID) == len(set(bench.SHAPE_GRID))
+    for W, n in bench.SHAPE_GRID:
+        assert W > 1 and n > 0
+        for v, cap, per in bench.shape_plan(W):
+            assert lib.zs_variant_multi(v) == 1, (W, v)
+            assert 0 <= cap <= 8 and per == 0
+    assert bench.shape_plan(8)[0] == (50, 3, 0) and bench.shape_plan(12)[0] == (50, 0, 0)
+    assert bench.shape_plan(64)[0] == (51, 0, 0)
