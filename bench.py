@@ -96,29 +96,31 @@ FUSED_MANY_TILES = 20000   # 2048-element tiles
 
 
 def fused_shape(world, n):
-    """(vectors per thread, zs::kShape* access shape, blocks per CU; 0 = no
-    cap) of the fused kernel that zs_step_fused launches for a
-    16-byte-aligned shard of n parameters over `world` workers: non-temporal
-    state loads and stores in 4-element vectors, 16 loads ahead (4) or 8
-    (5), the tile depth and residency following W and the shard's size."""
+    """(threads per block, vectors per thread, zs::kShape* access shape,
+    blocks per CU; 0 = no cap) of the fused kernel that zs_step_fused
+    launches for a 16-byte-aligned shard of n parameters over `world`
+    workers: 4-element vectors, non-temporal state loads and stores;
+    one-wave blocks at W = 2 and from W = 17 on, 256-thread blocks
+    otherwise, the tile depth and cap following W and, for W = 3 to 16,
+    the shard's size."""
     if world == 1:
-        return 2, 5, 2
+        return 256, 2, 5, 2
     if world == 2:
-        return 4, 5, 3
+        return 64, 1, 5, 16
+    if world >= 17:
+        return 64, 2, 5, 12
     many = n // 2048 >= FUSED_MANY_TILES
-    if world <= 12:
-        return 2, 5, 3 if many else 4
-    if world <= 16:
-        return (2, 5, 3) if many else (4, 4 if world == 16 else 5, 0)
-    return 1, 4, 6
+    if world <= 12 or many:
+        return 256, 2, 5, 3 if many else 4
+    return 256, 4, 4 if world == 16 else 5, 0
 
 
 def fused_instance(wl, wire=0):
     """Template instance of zs::fused_kernel that a 16-byte-aligned shard of
     this workload launches (the name rocprofv3 shows)."""
-    u, shape, _ = fused_shape(wl.world, wl.n)
+    t, u, shape, _ = fused_shape(wl.world, wl.n)
     return (f"zs::fused_kernel<4, {u}, {str(wl.world > 1).lower()}, "
-            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, {shape}>")
+            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, {shape}, {t}>")
 
 
 def timing_events(torch, count):
@@ -145,6 +147,11 @@ def _copylib():
     lib.zs_copy_ceiling.restype = C.c_int
     lib.zs_copy_ceiling.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]
     lib.zs_copy_last_error.restype = C.c_char_p
+    lib.zs_copy_shape.restype = C.c_int
+    lib.zs_copy_shape.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_uint64, C.c_uint32,
+                                  C.c_void_p]
+    lib.zs_copy_shape_name.restype = C.c_char_p
+    lib.zs_copy_shape_tile_bytes.restype = C.c_uint64
     lib.zs_stream_probe.restype = C.c_int
     lib.zs_stream_probe.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_uint32, C.c_void_p,
                                     C.c_uint32, C.c_void_p, C.c_uint64, C.c_uint32, C.c_uint32,
@@ -188,6 +195,56 @@ def copy_rates_gbps(torch, gib=4, reps=10):
     del a, b
     torch.cuda.empty_cache()
     return rates
+
+
+COPY_SWEEP_CAPS = (0, 2, 4)            # one tile per block: residency caps (0: none)
+COPY_SWEEP_PERSISTENT = (2, 4, 8)      # persistent grids: blocks per CU
+
+
+def copy_shape_sweep(torch, gib=4, reps=10, rounds=3):
+    """Read + write rate of every copy shape of libzscopy over `gib` GiB,
+    interleaved over `rounds`: shapes with one tile per block at each cap
+    of COPY_SWEEP_CAPS, persistent shapes at each grid of
+    COPY_SWEEP_PERSISTENT. Bytes are checked once per configuration."""
+    lib = _copylib()
+    nbytes = gib << 30
+    a = torch.randint(-(1 << 31), 1 << 31, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    configs = []
+    for i in range(lib.zs_copy_shape_count()):
+        name = lib.zs_copy_shape_name(i).decode()
+        for k in (COPY_SWEEP_PERSISTENT if "persistent" in name else COPY_SWEEP_CAPS):
+            configs.append((i, name, k))
+
+    def runner(i, k):
+        def go():
+            rc = lib.zs_copy_shape(i, a.data_ptr(), b.data_ptr(), nbytes, k,
+                                   torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"zs_copy_shape({i}) returned {rc}: "
+                                   f"{lib.zs_copy_last_error().decode()}")
+        return go
+
+    for i, name, k in configs:
+        b.zero_()
+        runner(i, k)()
+        torch.cuda.synchronize()
+        if not torch.equal(a, b):
+            raise RuntimeError(f"copy shape {name} (blocks per CU {k}) did not copy exactly")
+    times = {c: [] for c in range(len(configs))}
+    for _ in range(rounds):
+        for c, (i, _, k) in enumerate(configs):
+            times[c].append(_time_calls(torch, runner(i, k), reps))
+    out = []
+    for c, (i, name, k) in enumerate(configs):
+        ms = sum(times[c]) / rounds
+        gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+        out.append(dict(shape=i, name=name, blocks_per_cu=k, ms=ms, ms_rounds=times[c],
+                        gbps=gbps, frac_of_peak=gbps / PEAK_HBM_GBPS))
+        log(f"copy shape {name} k={k}: {ms:.4f} ms ({gbps:.0f} GB/s)")
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(bytes_each_way=nbytes, reps_per_round=reps, rounds=rounds, results=out)
 
 
 # (name, 16-bit input streams, fp32 inputs, fp32 outputs, 16-bit output,
@@ -569,12 +626,13 @@ VARIANT_SWEEP = {
                    (0, 2, 0), (0, 3, 0), (0, 4, 0), (0, 0, 0), (1, 2, 0), (2, 2, 0), (3, 2, 0),
                    (4, 2, 2), (12, 0, 3), (13, 0, 3), (14, 0, 1),
                    (30, 8, 0), (30, 0, 0), (31, 4, 0), (32, 1, 0), (33, 1, 0)],
-    "gpt2s-w8": [(53, 4, 0), (58, 4, 0), (53, 3, 0), (52, 0, 0), (50, 3, 0), (50, 0, 0), (41, 3, 0),
+    "gpt2s-w8": [(53, 4, 0), (58, 4, 0), (64, 16, 0), (70, 16, 0), (53, 3, 0), (52, 0, 0), (50, 3, 0), (50, 0, 0), (41, 3, 0),
                  (51, 3, 0), (38, 3, 0), (46, 6, 0), (47, 3, 0),
                  (5, 3, 0), (5, 0, 0), (5, 2, 0), (5, 4, 0), (6, 3, 0), (7, 3, 0), (8, 3, 0),
                  (9, 3, 0), (10, 3, 3), (11, 3, 0), (15, 0, 3), (16, 0, 3),
                  (23, 3, 0), (25, 3, 0), (26, 8, 0), (27, 6, 0), (28, 2, 0), (29, 0, 0)],
-    "7p5b-shard-w64": [(55, 6, 0), (57, 6, 0), (55, 0, 0), (56, 3, 0), (53, 3, 0), (51, 0, 0), (50, 0, 0),
+    "7p5b-shard-w64": [(64, 12, 0), (70, 12, 0), (64, 8, 0), (64, 16, 0), (55, 6, 0), (57, 6, 0),
+                       (55, 0, 0), (56, 3, 0), (53, 3, 0), (51, 0, 0), (50, 0, 0),
                        (40, 0, 0), (39, 0, 0), (38, 0, 0), (34, 0, 0), (47, 0, 0), (48, 0, 0),
                        (5, 0, 0), (5, 5, 0), (5, 3, 0), (6, 0, 0), (7, 0, 0), (8, 0, 0),
                        (9, 0, 0), (10, 0, 5), (11, 0, 0), (15, 0, 3), (16, 0, 3), (17, 0, 1),
@@ -699,12 +757,16 @@ SHAPE_GRID = [(W, n) for n in (15_554_976, 117_187_500) for W in (2, 3, 4, 8, 12
 
 
 def shape_plan(world):
-    """Alternatives to zs_step_fused's own launch at W = `world`: the previous
-    shape (four vectors per thread, 3 blocks per CU up to W = 8, uncapped
-    above, 16 loads ahead from W = 16), two vectors at 3 and 4 blocks per CU,
-    and one vector with 16 loads ahead at 6 blocks per CU."""
+    """Alternatives to zs_step_fused's own launch at W = `world`, all with
+    4-element vectors and non-temporal state loads and stores: four vectors
+    per thread in 256-thread blocks (3 per CU to W = 8, uncapped above, 16
+    loads ahead from W = 16); two vectors in 256-thread blocks at 3 and 4
+    per CU; one vector, 16 ahead, 256-thread blocks at 6 per CU; and in
+    one-wave blocks, one vector at 16 per CU and two vectors at 8, 12 and
+    16 per CU."""
     prev = (50, 3, 0) if world <= 8 else (50, 0, 0) if world < 16 else (51, 0, 0)
-    return [prev, (53, 3, 0), (53, 4, 0), (55, 6, 0)]
+    return [prev, (53, 3, 0), (53, 4, 0), (55, 6, 0), (66, 16, 0), (64, 8, 0), (64, 12, 0),
+            (64, 16, 0)]
 
 
 def shape_sweep(torch, rounds=3):
@@ -726,8 +788,9 @@ def shape_sweep(torch, rounds=3):
             r = variant_sweep(name, shape_plan(W), reps, torch, rounds=rounds)
         finally:
             del synth.WORKLOADS[name]
-        u, shape, cap = fused_shape(W, r["n"])
-        r["production"] = {"vectors_per_thread": u, "access_shape": shape, "blocks_per_cu": cap}
+        t, u, shape, cap = fused_shape(W, r["n"])
+        r["production"] = {"threads_per_block": t, "vectors_per_thread": u, "access_shape": shape,
+                           "blocks_per_cu": cap}
         out.append(r)
     return out
 
@@ -848,6 +911,10 @@ def main():
     ap.add_argument("--sweep-phases", action="store_true",
                     help="time the 7.5B shard's reads and writes separated in time (stream "
                          "probe, 1 to 64 chunks) and print that table as the JSON line instead")
+    ap.add_argument("--sweep-copy", action="store_true",
+                    help="time libzscopy's copy shapes (vectors per lane, non-temporal loads "
+                         "and stores, block size, persistent grids, residency caps) over 4 GiB "
+                         "and print that table as the JSON line instead")
     ap.add_argument("--sweep-shapes", action="store_true",
                     help="time the fused step's tile depths and residency caps against "
                          "libzeroshard's own launch over a grid of W and shard sizes and print "
@@ -877,6 +944,10 @@ def main():
     if args.sweep_phases:
         print(json.dumps({"metric": "7.5B-shard step mix, reads and writes separated in time",
                           "unit": "ms", "phases": phase_sweep(torch)}))
+        return
+    if args.sweep_copy:
+        print(json.dumps({"metric": "plain copy, read + write GB/s by copy shape", "unit": "GB/s",
+                          "peak": PEAK_HBM_GBPS, "copies": copy_shape_sweep(torch)}))
         return
     if args.sweep_shapes:
         print(json.dumps({"metric": "fused step tile depth and residency by W and shard size, "

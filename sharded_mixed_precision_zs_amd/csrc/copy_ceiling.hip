@@ -9,6 +9,10 @@
  * MI355X copies with 1-2 KB per wave streamed fastest (about 6.45 TB/s for
  * read plus write); wider bursts per wave and persistent grids were slower,
  * and the runtime's device-to-device memcpy reaches 4.6-5.2 TB/s.
+ * zs_copy_shape runs the same copy in the other shapes of a small catalogue
+ * (vectors per lane, vector width, non-temporal loads and stores, block
+ * size, persistent grids, residency caps), so the benchmark can show which
+ * read-plus-write rate any copy shape reaches on the part.
  *
  * zs_stream_probe: the shard step's memory-access pattern with its
  * arithmetic replaced by integer folds -- the same tile, block size,
@@ -195,6 +199,70 @@ bool span_overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
   return na && nb && a0 < b0 + nb && b0 < a0 + na;
 }
 
+/* ------------------------------------------------------------------------
+ * Copy shapes. Lane t of block b moves U vectors of VB bytes (8 or 16):
+ * vector u at vector index (b * U + u) * T + t, so each vector of a wave
+ * covers whole lines; loads and stores are optionally non-temporal.
+ * PERSIST blocks walk the tiles with a grid stride; the others take one
+ * tile each (the grid is the tile count).
+ * ---------------------------------------------------------------------- */
+using u2 = uint32_t __attribute__((ext_vector_type(2)));
+template <int VB> struct CopyVec { using T = u4; };
+template <> struct CopyVec<8> { using T = u2; };
+
+template <int T, int U, int VB, bool NTL, bool NTS, bool PERSIST>
+__global__ void __launch_bounds__(T)
+copy_shape_kernel(const void *__restrict__ src, void *__restrict__ dst, uint64_t tiles) {
+  using V = typename CopyVec<VB>::T;
+  const V *s = static_cast<const V *>(src);
+  V *d = static_cast<V *>(dst);
+  const uint64_t stride = PERSIST ? (uint64_t)gridDim.x : tiles;
+  for (uint64_t tile = blockIdx.x; tile < tiles; tile += stride) {
+    V r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t i = (tile * U + u) * T + threadIdx.x;
+      if constexpr (NTL) r[u] = __builtin_nontemporal_load(s + i);
+      else r[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t i = (tile * U + u) * T + threadIdx.x;
+      if constexpr (NTS) __builtin_nontemporal_store(r[u], d + i);
+      else d[i] = r[u];
+    }
+  }
+}
+
+struct CopyShape {
+  const char *name;
+  const void *fn;
+  int threads, vecs, vec_bytes;
+  bool persistent;
+};
+
+template <int T, int U, int VB, bool NTL, bool NTS, bool P>
+constexpr CopyShape mk_copy(const char *name) {
+  return CopyShape{name, reinterpret_cast<const void *>(&copy_shape_kernel<T, U, VB, NTL, NTS, P>),
+                   T, U, VB, P};
+}
+
+const CopyShape kCopyShapes[] = {
+    mk_copy<256, 1, 16, true, false, false>("16 B per lane, nt load, plain store (the ceiling copy)"),
+    mk_copy<256, 1, 16, false, false, false>("16 B per lane, plain load and store"),
+    mk_copy<256, 1, 16, true, true, false>("16 B per lane, nt load and store"),
+    mk_copy<256, 1, 16, false, true, false>("16 B per lane, plain load, nt store"),
+    mk_copy<256, 1, 8, true, false, false>("8 B per lane, nt load, plain store"),
+    mk_copy<256, 2, 16, true, false, false>("2 x 16 B per lane, nt load, plain store"),
+    mk_copy<256, 4, 16, true, false, false>("4 x 16 B per lane, nt load, plain store"),
+    mk_copy<256, 2, 16, true, true, false>("2 x 16 B per lane, nt load and store"),
+    mk_copy<64, 1, 16, true, false, false>("16 B per lane, 64-thread blocks"),
+    mk_copy<1024, 1, 16, true, false, false>("16 B per lane, 1024-thread blocks"),
+    mk_copy<256, 1, 16, true, false, true>("16 B per lane, persistent grid"),
+    mk_copy<256, 4, 16, true, false, true>("4 x 16 B per lane, persistent grid"),
+};
+constexpr int kCopyShapeCount = (int)(sizeof kCopyShapes / sizeof kCopyShapes[0]);
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +377,74 @@ int zs_stream_probe(const void *const *in16, uint32_t n_in16, const void *const 
                               lds_per_cu, s, a)
           : launch_probe_i<2>(n_in32, n_out32, out16 != nullptr, (unsigned)blocks, lds,
                               lds_per_cu, s, a);
+  g_copy_err = e == hipSuccess ? "" : hipGetErrorString(e);
+  return e == hipSuccess ? 0 : 4;
+}
+
+/* Number of copy shapes, and the name of shape `id` (NULL out of range). */
+int zs_copy_shape_count(void) { return kCopyShapeCount; }
+
+const char *zs_copy_shape_name(int id) {
+  return id >= 0 && id < kCopyShapeCount ? kCopyShapes[id].name : nullptr;
+}
+
+/* Elements of one tile of shape `id`, in bytes (0 out of range): `bytes`
+ * passed to zs_copy_shape must be a multiple of it. */
+uint64_t zs_copy_shape_tile_bytes(int id) {
+  if (id < 0 || id >= kCopyShapeCount) return 0;
+  const CopyShape &c = kCopyShapes[id];
+  return (uint64_t)c.threads * (uint64_t)c.vecs * (uint64_t)c.vec_bytes;
+}
+
+/* Copies `bytes` bytes from src to dst in copy shape `id` on HIP stream
+ * `stream`; asynchronous, nothing is allocated. blocks_per_cu: for a shape
+ * with one tile per block, the residency cap (0 = none, 1..8, through
+ * dynamic LDS the kernel does not touch); for a persistent shape, the
+ * blocks per CU of the grid (0 = 4). Returns 0 when enqueued; 1 (nothing
+ * enqueued, no HIP call made) for an id out of range, a null or
+ * unaligned (16-byte) pointer, bytes not a multiple of the shape's tile or
+ * too large for one grid, blocks_per_cu above 8, or buffers that overlap;
+ * 4 when the launch fails (zs_copy_last_error() has HIP's message).
+ * bytes == 0 returns 0 and does nothing. */
+int zs_copy_shape(int id, const void *src, void *dst, uint64_t bytes, uint32_t blocks_per_cu,
+                  void *stream) {
+  if (id < 0 || id >= kCopyShapeCount || blocks_per_cu > 8) return 1;
+  const CopyShape &c = kCopyShapes[id];
+  const uint64_t tile = zs_copy_shape_tile_bytes(id);
+  if (!src || !dst || (uintptr_t)src % 16 || (uintptr_t)dst % 16 || bytes % tile) return 1;
+  if (span_overlap(src, bytes, dst, bytes)) return 1;
+  const uint64_t tiles = bytes / tile;
+  if (tiles > 0x7fffffffull) return 1;
+  if (tiles == 0) return 0;
+  int dev = 0, cus = 0;
+  uint64_t grid = tiles;
+  size_t lds = 0;
+  int lds_per_cu = 0;
+  if (c.persistent) {
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      g_copy_err = "no device attributes";
+      return 4;
+    }
+    const uint64_t want = (uint64_t)cus * (blocks_per_cu ? blocks_per_cu : 4u);
+    grid = want < tiles ? want : tiles;
+  } else {
+    lds = probe_lds_bytes(blocks_per_cu, &lds_per_cu);
+    if (lds > 65536) {
+      const hipError_t e =
+          hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_per_cu);
+      if (e != hipSuccess) {
+        g_copy_err = hipGetErrorString(e);
+        return 4;
+      }
+    }
+  }
+  const void *a_src = src;
+  void *a_dst = dst;
+  uint64_t a_tiles = tiles;
+  void *argv[] = {&a_src, &a_dst, &a_tiles};
+  const hipError_t e = hipLaunchKernel(c.fn, dim3((unsigned)grid), dim3((unsigned)c.threads),
+                                       argv, lds, static_cast<hipStream_t>(stream));
   g_copy_err = e == hipSuccess ? "" : hipGetErrorString(e);
   return e == hipSuccess ? 0 : 4;
 }

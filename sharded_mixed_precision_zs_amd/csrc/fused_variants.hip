@@ -174,6 +174,60 @@ __global__ __launch_bounds__(kBlock) void g4_kernel(FusedArgs p) {
   flag_or(p.flag, bad);
 }
 
+/* The production tile with T threads per block instead of 256: lane t of
+ * a block owns elements 4t .. 4t+3 of each 4T-element group (U groups per
+ * block), the same per-element arithmetic, load batching, load order and
+ * store policy as zs::fused_tile. */
+template <int T, int U, bool MULTI, int SHAPE>
+__device__ __forceinline__ bool fused_tile_t(const FusedArgs &p, uint64_t base) {
+  constexpr int B = shape_batch(SHAPE);
+  constexpr bool NTS = shape_nt_stores(SHAPE);
+  constexpr bool NTL = shape_nt_loads(SHAPE);
+  uint64_t i0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * T + threadIdx.x) * 4;
+  float th[U][4], m[U][4], v[U][4], s[U][4];
+  auto load_state = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ldf_p<4, NTL>(p.master_in + i0[u], th[u]);
+      ldf_p<4, NTL>(p.m_in + i0[u], m[u]);
+      ldf_p<4, NTL>(p.v_in + i0[u], v[u]);
+    }
+  };
+  if constexpr (MULTI) {
+    ring_sum_uw<4, U, ZS_BF16, ZS_WIRE_FP32, B>(p.g, p.world, i0, s);
+    load_state();
+  } else {
+    load_state();
+    ring_sum_uw<4, U, ZS_BF16, ZS_WIRE_FP32, B>(p.g, 1, i0, s);
+  }
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g = unscale(average(s[u][e], p.k), p.k);
+      bad |= !__builtin_isfinite(g);
+      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, p.h);
+    }
+    stf_p<4, NTS>(p.master_out + i0[u], th[u]);
+    stf_p<4, NTS>(p.m_out + i0[u], m[u]);
+    stf_p<4, NTS>(p.v_out + i0[u], v[u]);
+    st16_p<4, ZS_BF16, NTS>(p.param_out + i0[u], th[u]);
+  }
+  return bad;
+}
+
+template <int T, int U, bool MULTI, int SHAPE>
+__global__ __launch_bounds__(T) void g4t_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)T * 4 * U;
+  const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
+  bool bad = false;
+  if (blockIdx.x < tiles) bad = fused_tile_t<T, U, MULTI, SHAPE>(p, (uint64_t)blockIdx.x * tile);
+  flag_or(p.flag, bad);
+}
+
 /* ------------------------------------------------------------------------
  * Loader/storer split. NL loader waves each take one 8-element vector per
  * lane of a tile of NL * 512 elements: they load, sum and update it exactly
@@ -418,25 +472,34 @@ constexpr Variant mk_split(const char *name) {
                  split_tile<NL>(), M, true, (NL + NS) * 64, 2 * 3 * split_tile<NL>() * 4};
 }
 
+template <int T, int U, bool M, int SHAPE>
+constexpr Variant mk_g4t(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&g4t_kernel<T, U, M, SHAPE>), T * 4 * U, M,
+                 false, T, 0};
+}
+
 /* libzeroshard's fused_kernel itself (with its ragged-tail and device
  * scale paths), launched through this library's launcher: against the
  * g4 kernels of the same shape it separates the cost of those paths from
  * that of the launch. */
-template <int U, bool M, int SHAPE>
+template <int U, bool M, int SHAPE, int T = kBlock>
 constexpr Variant mk_prod(const char *name) {
   return Variant{name,
                  reinterpret_cast<const void *>(
-                     &fused_kernel<4, U, M, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE>),
-                 kBlock * 4 * U, M, false, kBlock, 0};
+                     &fused_kernel<4, U, M, false, ZS_BF16, ZS_BF16, ZS_WIRE_FP32, SHAPE, T>),
+                 T * 4 * U, M, false, T, 0};
 }
 
 /* libzeroshard's own shapes, for 16-byte-aligned operands: entry 49 for
- * W = 1; entry 50 for W = 2 (and W = 13 to 15 on shards under 20 K
- * 2048-element tiles) and 51 for W = 16 on such shards; entry 53 for W = 3
- * to 12, and W = 13 to 16 on larger shards; entry 55 from W = 17 on.
- * Entries 50 and 51 were its shapes for all of W > 1 before the tile depth
- * followed W; entries 0 and 5 are older ones (8-element vectors, plain
- * stores), and 43, 41 and 40 the lane groups with plain state loads. */
+ * W = 1 (256-thread blocks, 2 per CU); entry 66 at 16 per CU for W = 2 and
+ * entry 64 at 12 per CU from W = 17 on (64-thread blocks; entries 71 and
+ * 70 are libzeroshard's own kernel in those shapes); for W = 3 to 16
+ * entry 53 (3 or 4 blocks per CU by shard size), or entry 50 and 51 on
+ * shards under 20 000 tiles at W = 13 to 15 and 16. Before one-wave blocks
+ * it launched entry 50 at W = 2 and 55 from W = 17; before the tile depth
+ * followed W, entries 50 and 51 for all of W > 1; entries 0 and 5 are
+ * older still (8-element vectors, plain stores), and 43, 41 and 40 the
+ * lane groups with plain state loads. */
 const Variant kVariants[] = {
     mk<1, false, false, 8, true, false, false>("w1: 1 vector/thread, nt gradient loads"),
     mk<2, false, false, 8, true, false, false>("w1: 2 vectors/thread"),
@@ -500,6 +563,18 @@ const Variant kVariants[] = {
     mk_prod<1, true, kShapeB16NtL>("wN: libzeroshard's kernel, 1 vector/thread, 16 ahead"),
     mk_prod<2, true, kShapeB8NtL>("wN: libzeroshard's kernel, 2 vectors/thread, 8 ahead"),
     mk_prod<2, false, kShapeB8NtL>("w1: libzeroshard's kernel, 2 vectors/thread"),
+    mk_g4t<64, 2, false, kShapeB8NtL>("w1: 4-element lane groups, 2 vectors/thread, 64-thread blocks"),
+    mk_g4t<128, 2, false, kShapeB8NtL>("w1: 4-element lane groups, 2 vectors/thread, 128-thread blocks"),
+    mk_g4t<64, 1, false, kShapeB8NtL>("w1: 4-element lane groups, 1 vector/thread, 64-thread blocks"),
+    mk_g4t<64, 1, true, kShapeB16NtL>("wN: 4-element lane groups, 1 vector/thread, 16 ahead, 64-thread blocks"),
+    mk_g4t<64, 2, true, kShapeB8NtL>("wN: 4-element lane groups, 2 vectors/thread, 64-thread blocks"),
+    mk_g4t<128, 2, true, kShapeB8NtL>("wN: 4-element lane groups, 2 vectors/thread, 128-thread blocks"),
+    mk_g4t<64, 1, true, kShapeB8NtL>("wN: 4-element lane groups, 1 vector/thread, 64-thread blocks"),
+    mk_g4t<64, 4, true, kShapeB8NtL>("wN: 4-element lane groups, 4 vectors/thread, 64-thread blocks"),
+    mk_g4t<64, 2, true, kShapeB16NtL>("wN: 4-element lane groups, 2 vectors/thread, 16 ahead, 64-thread blocks"),
+    mk_g4t<64, 4, false, kShapeB8NtL>("w1: 4-element lane groups, 4 vectors/thread, 64-thread blocks"),
+    mk_prod<2, true, kShapeB8NtL, 64>("wN: libzeroshard's kernel, 2 vectors/thread, 64-thread blocks"),
+    mk_prod<1, true, kShapeB8NtL, 64>("wN: libzeroshard's kernel, 1 vector/thread, 64-thread blocks"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

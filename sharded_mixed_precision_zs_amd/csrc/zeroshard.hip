@@ -104,27 +104,32 @@ using zs_host::make_adam;
 using zs_host::make_scales;
 
 /* ------------------------------------------------------------------------
- * Tile and residency of the fused kernel. Each thread owns U 4-element
- * vectors of a tile (1024 * U elements per block) and the blocks per CU are
- * capped with dynamic LDS that the kernel never touches (LDS per CU / cap,
- * less 1 KB). With W gradient and three state streams read while four
+ * Block size, tile and residency of the fused kernel. Each thread owns U
+ * 4-element vectors of a tile (T * U * 4 elements per block of T threads)
+ * and the blocks per CU are capped with dynamic LDS that the kernel never
+ * touches. With W gradient and three state streams read while four
  * streams are written, HBM delivered more on MI355X with fewer bytes in
  * flight per CU than the registers allow; how many fewer depends on W and,
- * for W = 3 to 16, on the shard's size. Interleaved timings on one GPU
- * against the alternatives (all computing the same bits), shards of 0.35 M
- * to 7 G parameters, three GPUs:
- *   - W = 1: U = 2, 2 blocks per CU.
- *   - W = 2: U = 4, 3 blocks per CU (U = 2 within 0.5 %).
- *   - W = 3 to 16 with 20 K 2048-element tiles or more: U = 2, 3 blocks
- *     per CU, +2 to +7 % over U = 4 at 3 blocks (or uncapped from W = 9).
- *   - W = 3 to 12 below that: U = 2, 4 blocks per CU, +2.5 to +18 % (3
- *     blocks lost 2 % at W = 8 and 15.6 M parameters); W = 13 to 16 below
- *     it keep U = 4 uncapped (U = 2 lost 4 % at W = 16 and 15.6 M).
- *   - W = 17 to 64: U = 1 with the sum loading 16 workers ahead, 6 blocks
- *     per CU, +1 to +8 % over U = 4 uncapped.
- * Operands aligned for 2- or 1-element vectors only keep the shapes they
- * had before: U = 2 (1 when W = 1), plain stores, 2, 3 or no cap.
- * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..8 = that many blocks) overrides
+ * for W = 3 to 16, on the shard's size; and at W = 2 and from W = 17 on,
+ * one-wave blocks (64 threads) beat 256-thread ones at the same waves per
+ * CU. Interleaved timings on one GPU against the alternatives (all
+ * computing the same bits), shards of 0.35 M to 7 G parameters:
+ *   - W = 1: 256-thread blocks, U = 2, 2 blocks (8 waves) per CU. One-wave
+ *     blocks at 8 to 16 waves per CU ran 4 to 8 % faster in some runs and
+ *     1 to 10 % slower in others, on the same GPU.
+ *   - W = 2: one-wave blocks, U = 1, 16 per CU: +7.6 to +12 % over four
+ *     vectors in 256-thread blocks at 3 per CU.
+ *   - W = 3 to 16, 256-thread blocks: U = 2 with 3 blocks per CU from
+ *     20 000 2048-element tiles on (+2 to +7 % over U = 4), 4 blocks per
+ *     CU below that for W <= 12 (+2.5 to +18 %), U = 4 uncapped below it
+ *     for W = 13 to 16 (U = 2 lost 4 % at W = 16 and 15.6 M parameters).
+ *     One-wave blocks here ranged from -3 % (small shards) to +5 %.
+ *   - W >= 17: one-wave blocks, U = 2, 12 per CU: +2 to +5 % over one
+ *     vector with 16 loads ahead in 256-thread blocks at 6 per CU.
+ * The one-wave shapes take eight workers' loads ahead of the in-order
+ * adds. Operands aligned for 2- or 1-element vectors only keep
+ * 256-thread blocks, U = 2 (1 when W = 1), plain stores and 2, 3 or no cap.
+ * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..32 = that many blocks) overrides
  * the cap, for measurements.
  * ---------------------------------------------------------------------- */
 
@@ -153,51 +158,58 @@ int env_blocks_per_cu() {
     const char *s = getenv("ZS_FUSED_BLOCKS_PER_CU");
     if (!s || !*s) return -1;
     int x = atoi(s);
-    return x < 0 || x > 8 ? -1 : x;
+    return x < 0 || x > 32 ? -1 : x;
   }();
   return v;
 }
 
-/* Vector width, vectors per thread, access shape (zs::kShape*) and blocks
- * per CU (0: no cap) of the fused kernel for `vec`-aligned operands. */
+/* Vector width, threads per block, vectors per thread, access shape
+ * (zs::kShape*) and blocks per CU (0: no cap) of the fused kernel for
+ * `vec`-aligned operands. */
 constexpr int fused_vec_of(int aligned_vec) { return aligned_vec >= 4 ? 4 : aligned_vec; }
+constexpr int kFusedWaveBlock = 64; /* one wave */
 constexpr uint64_t kFusedManyTiles = 20000; /* 2048-element tiles */
 
 struct FusedShape {
+  int threads;
   int tile_vecs;
   int access;
   int cap;
 };
 
 FusedShape fused_shape(int vec, uint32_t world, uint64_t n) {
-  if (vec < 4) return {world > 1 ? 2 : 1, kShapeB8, world == 1 ? 2 : world <= 8 ? 3 : 0};
-  if (world == 1) return {2, kShapeB8NtL, 2};
-  if (world == 2) return {4, kShapeB8NtL, 3};
+  if (vec < 4) return {kBlock, world > 1 ? 2 : 1, kShapeB8, world == 1 ? 2 : world <= 8 ? 3 : 0};
+  if (world == 1) return {kBlock, 2, kShapeB8NtL, 2};
+  if (world == 2) return {kFusedWaveBlock, 1, kShapeB8NtL, 16};
+  if (world >= 17) return {kFusedWaveBlock, 2, kShapeB8NtL, 12};
   const bool many = n / 2048 >= kFusedManyTiles;
-  if (world <= 12) return {2, kShapeB8NtL, many ? 3 : 4};
-  if (world <= 16) {
-    if (many) return {2, kShapeB8NtL, 3};
-    return {4, world == 16 ? kShapeB16NtL : kShapeB8NtL, 0};
-  }
-  return {1, kShapeB16NtL, 6};
+  if (world <= 12 || many) return {kBlock, 2, kShapeB8NtL, many ? 3 : 4};
+  return {kBlock, 4, world == 16 ? kShapeB16NtL : kShapeB8NtL, 0};
 }
 
 /* Dynamic LDS bytes that hold the fused kernel to `cap` blocks per CU (0:
- * no cap), or to ZS_FUSED_BLOCKS_PER_CU when that is set. */
+ * no cap), or to ZS_FUSED_BLOCKS_PER_CU when that is set: LDS per CU / cap
+ * less 1 KB up to 8 blocks; above that LDS per CU / cap rounded down to
+ * 1 KB, with no cap when that would let one more block fit. */
 size_t fused_lds_bytes(int cap) {
   const int forced = env_blocks_per_cu();
   if (forced >= 0) cap = forced;
   if (cap == 0) return 0;
   const DeviceLds d = device_lds();
   if (d.lds_per_cu <= 0) return 0;
-  const int bytes = (d.lds_per_cu / cap - 1024) / 256 * 256;
-  return bytes > 0 ? (size_t)bytes : 0;
+  if (cap <= 8) {
+    const int bytes = (d.lds_per_cu / cap - 1024) / 256 * 256;
+    return bytes > 0 ? (size_t)bytes : 0;
+  }
+  const int bytes = d.lds_per_cu / cap / 1024 * 1024;
+  if (bytes <= 0 || (cap + 1) * bytes <= d.lds_per_cu) return 0;
+  return (size_t)bytes;
 }
 
 /* Launch of one fused-kernel instance with `lds` bytes of (unused) dynamic
  * LDS; above the default 64 KB limit the instance's limit is raised once
  * per device (a bit per device id; ids past 63 raise it at every launch). */
-template <int V, int U, bool L, bool A, int G, int P, int W, int F>
+template <int V, int U, bool L, bool A, int G, int P, int W, int F, int T>
 void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedArgs &p) {
   if (lds > 65536) {
     static std::atomic<uint64_t> raised{0};
@@ -206,13 +218,13 @@ void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedA
     const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;
     if (!bit || !(raised.load(std::memory_order_relaxed) & bit)) {
       /* a refusal surfaces as the launch's error */
-      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W, F>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W, F, T>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)device_lds().lds_per_cu) == hipSuccess)
         raised.fetch_or(bit, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W, F>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W, F, T>), grid, block, lds, s, p);
 }
 
 /* Widest vector width every operand's alignment allows: 16-bit operands
@@ -229,16 +241,20 @@ int pick_vec(const void *const *p16, int n16, const void *const *p32, int n32) {
   return 1;
 }
 
-/* Tiled kernels: floor(n / tile) full tiles plus one block per kBlock
+/* Tiled kernels: floor(n / tile) full tiles plus one block per `threads`
  * elements of the remainder. */
-uint64_t tiled_blocks(uint64_t n, int per_thread) {
-  uint64_t tile = (uint64_t)kBlock * (uint64_t)per_thread;
-  return n / tile + ((n % tile) + kBlock - 1) / kBlock;
+uint64_t tiled_blocks(uint64_t n, int per_thread, int threads = kBlock) {
+  uint64_t tile = (uint64_t)threads * (uint64_t)per_thread;
+  return n / tile + ((n % tile) + threads - 1) / threads;
 }
 
-unsigned tiled_grid(uint64_t n, int per_thread) { return (unsigned)tiled_blocks(n, per_thread); }
+unsigned tiled_grid(uint64_t n, int per_thread, int threads = kBlock) {
+  return (unsigned)tiled_blocks(n, per_thread, threads);
+}
 
-bool tiled_ok(uint64_t n, int per_thread) { return tiled_blocks(n, per_thread) <= 0x7fffffffull; }
+bool tiled_ok(uint64_t n, int per_thread, int threads = kBlock) {
+  return tiled_blocks(n, per_thread, threads) <= 0x7fffffffull;
+}
 
 /* Blocks for n elements when every thread covers `per_thread` of them. */
 unsigned grid_for(uint64_t n, int per_thread) {
@@ -631,24 +647,28 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   const bool multi = a->world > 1, acc = a->acc_in != nullptr;
   const FusedShape fs = fused_shape(vec, a->world, n);
   const int per_thread = vec * fs.tile_vecs;
-  if (!tiled_ok(n, per_thread)) return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
+  if (!tiled_ok(n, per_thread, fs.threads))
+    return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(tiled_grid(n, per_thread)), block(kBlock);
+  dim3 grid(tiled_grid(n, per_thread, fs.threads)), block(fs.threads);
   const size_t lds = fused_lds_bytes(fs.cap);
-#define ZS_KF(V, U, L, A, G, P, W, S) \
-  launch_fused<V, U, L, A, G, P, W, S>(grid, block, lds, s, p)
-#define ZS_K4(V, A, G, P, W)                                                         \
-  do {                                                                               \
-    if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL);                         \
-    else if (fs.tile_vecs == 1) ZS_KF(4, 1, true, A, G, P, W, kShapeB16NtL);         \
-    else if (fs.tile_vecs == 2) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL);          \
-    else if (fs.access == kShapeB16NtL) ZS_KF(4, 4, true, A, G, P, W, kShapeB16NtL); \
-    else ZS_KF(4, 4, true, A, G, P, W, kShapeB8NtL);                                 \
+#define ZS_KF(V, U, L, A, G, P, W, S, T) \
+  launch_fused<V, U, L, A, G, P, W, S, T>(grid, block, lds, s, p)
+#define ZS_K4(V, A, G, P, W)                                                             \
+  do {                                                                                   \
+    if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL, kBlock);                     \
+    else if (fs.threads == kFusedWaveBlock && fs.tile_vecs == 1)                         \
+      ZS_KF(4, 1, true, A, G, P, W, kShapeB8NtL, kFusedWaveBlock);                       \
+    else if (fs.threads == kFusedWaveBlock) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL,   \
+                                                  kFusedWaveBlock);                      \
+    else if (fs.tile_vecs == 2) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL, kBlock);      \
+    else if (fs.access == kShapeB16NtL) ZS_KF(4, 4, true, A, G, P, W, kShapeB16NtL, kBlock); \
+    else ZS_KF(4, 4, true, A, G, P, W, kShapeB8NtL, kBlock);                             \
   } while (0)
-#define ZS_KNARROW(V, A, G, P, W)                           \
-  do {                                                      \
-    if (!multi) ZS_KF(V, 1, false, A, G, P, W, kShapeB8);   \
-    else ZS_KF(V, 2, true, A, G, P, W, kShapeB8);           \
+#define ZS_KNARROW(V, A, G, P, W)                                   \
+  do {                                                              \
+    if (!multi) ZS_KF(V, 1, false, A, G, P, W, kShapeB8, kBlock);   \
+    else ZS_KF(V, 2, true, A, G, P, W, kShapeB8, kBlock);           \
   } while (0)
 #define ZS_KWIRE(KM, V, A, G, P)                                   \
   do {                                                             \

@@ -619,8 +619,11 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, 
  * the gradient sum: on MI355X that order streamed 5-10 % faster than
  * loading the state first, registers to spare or not. With a single worker
  * (W = 1) there is no sum, one gradient load, and the state loads go
- * first. SHAPE (kShape*) sets the sum's load batch and the store policy. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE>
+ * first. SHAPE (kShape*) sets the sum's load batch and the store policy;
+ * T is the block's thread count (vector u of thread t starts at
+ * base + (u * T + t) * VEC). */
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE,
+          int T = kBlock>
 __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk, const AdamK &h,
                                            uint64_t base) {
   constexpr int B = shape_batch(SHAPE);
@@ -628,7 +631,7 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
   constexpr bool NTL = shape_nt_loads(SHAPE);
   uint64_t i0[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * kBlock + threadIdx.x) * VEC;
+  for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * T + threadIdx.x) * VEC;
   float th[U][VEC], m[U][VEC], v[U][VEC], acc[U][VEC], s[U][VEC];
   auto load_state = [&]() {
 #pragma unroll
@@ -702,22 +705,24 @@ __device__ __forceinline__ void flag_epoch_mark(uint64_t *flag_epoch, uint64_t v
 
 /* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
  * added before the unscale; a separate instance so the common case carries
- * no registers for it. */
-template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE>
-__global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs p) {
-  const uint64_t tile = (uint64_t)kBlock * U * VEC;
+ * no registers for it. T threads per block, tiles of T * U * VEC elements,
+ * and the ragged end in blocks of T elements. */
+template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE,
+          int T = kBlock>
+__global__ __launch_bounds__(T) void fused_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)T * U * VEC;
   const uint64_t full = p.n / tile;  /* blocks past `full` cover the tail */
   Scales sk = p.k;
   AdamK h = p.h;
   uint64_t epoch = 0;
   bool bad = p.dev ? !dev_step_consts(p, sk, h, epoch) : false;
   if (blockIdx.x < full) {
-    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE, SHAPE>(p, sk, h,
-                                                                 (uint64_t)blockIdx.x * tile);
+    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE, SHAPE, T>(p, sk, h,
+                                                                    (uint64_t)blockIdx.x * tile);
   } else {
     /* ragged end: one element per thread, spread over enough blocks that
      * no thread walks a chain of them */
-    uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * kBlock + threadIdx.x;
+    uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * T + threadIdx.x;
     if (i < p.n) bad |= fused_vec<1, GDT, PDT>(p, sk, h, i);
   }
   if (p.dev) flag_epoch_mark(&p.dev->flag_epoch, epoch + 1, bad);

@@ -88,18 +88,20 @@ def test_fused_instance_names_match_the_kernel_template():
     from sharded_mixed_precision_zs_amd import synth
     W = synth.WORKLOADS
     assert bench.fused_instance(W["7b-full-w1"]) == \
-        "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 5>"
+        "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 5, 256>"
     assert bench.fused_instance(W["7p5b-shard-w64"]) == \
-        "zs::fused_kernel<4, 1, true, false, 0, 0, 0, 4>"
+        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5, 64>"
     assert bench.fused_instance(W["1p3b-w4-acc4-fp16"]) == \
-        "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5>"
+        "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5, 256>"
     assert bench.fused_instance(W["gpt2s-w8"]) == \
-        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5>"
+        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5, 256>"
     big, small = 40_960_000, 40_959_999  # 20 000 tiles of 2048 and one element short
     assert [bench.fused_shape(w, big) for w in (1, 2, 3, 12, 13, 16, 17, 64)] == \
-        [(2, 5, 2), (4, 5, 3), (2, 5, 3), (2, 5, 3), (2, 5, 3), (2, 5, 3), (1, 4, 6), (1, 4, 6)]
+        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 3), (256, 2, 5, 3), (256, 2, 5, 3),
+         (256, 2, 5, 3), (64, 2, 5, 12), (64, 2, 5, 12)]
     assert [bench.fused_shape(w, small) for w in (1, 2, 3, 12, 13, 16, 17, 64)] == \
-        [(2, 5, 2), (4, 5, 3), (2, 5, 4), (2, 5, 4), (4, 5, 0), (4, 4, 0), (1, 4, 6), (1, 4, 6)]
+        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 4), (256, 2, 5, 4), (256, 4, 5, 0),
+         (256, 4, 4, 0), (64, 2, 5, 12), (64, 2, 5, 12)]
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
     assert bench.fused_bytes_per_param(4, 4) == (24, 14)
 
@@ -110,7 +112,7 @@ def test_variant_sweep_plans_fit_their_workloads(hip_built):
     from sharded_mixed_precision_zs_amd import synth
     lib = bench._variantlib()
     # the shapes zs_step_fused launches for these workloads, at its own caps
-    production = {"7b-full-w1": (49, 2), "gpt2s-w8": (53, 4), "7p5b-shard-w64": (55, 6)}
+    production = {"7b-full-w1": (49, 2), "gpt2s-w8": (53, 4), "7p5b-shard-w64": (64, 12)}
     for name, plan in bench.VARIANT_SWEEP.items():
         W = synth.WORKLOADS[name].world
         for v, cap, per in plan:
@@ -118,11 +120,13 @@ def test_variant_sweep_plans_fit_their_workloads(hip_built):
             assert 0 <= cap <= 32 and 0 <= per <= 8
         assert plan[0] == (*production[name], 0), name
     assert lib.zs_variant_name(49).decode() == "w1: 4-element lane groups, nt stores, nt state loads"
-    assert lib.zs_variant_name(53).decode() == \
-        "wN: 4-element lane groups, 2 vectors/thread, nt loads and stores"
-    assert lib.zs_variant_name(55).decode() == \
-        "wN: 4-element lane groups, 1 vector/thread, 16 ahead, nt loads and stores"
-    assert [lib.zs_variant_tile(v) for v in (49, 53, 55)] == [2048, 2048, 1024]
+    assert lib.zs_variant_name(64).decode() == \
+        "wN: 4-element lane groups, 2 vectors/thread, 64-thread blocks"
+    assert lib.zs_variant_name(66).decode() == \
+        "wN: 4-element lane groups, 1 vector/thread, 64-thread blocks"
+    assert lib.zs_variant_name(70).decode() == \
+        "wN: libzeroshard's kernel, 2 vectors/thread, 64-thread blocks"
+    assert [lib.zs_variant_tile(v) for v in (49, 64, 66, 70)] == [2048, 512, 256, 512]
 
 
 def test_shape_sweep_plans_fit_their_shards(hip_built):
@@ -134,6 +138,6 @@ def test_shape_sweep_plans_fit_their_shards(hip_built):
         assert W > 1 and n > 0
         for v, cap, per in bench.shape_plan(W):
             assert lib.zs_variant_multi(v) == 1, (W, v)
-            assert 0 <= cap <= 8 and per == 0
+            assert 0 <= cap <= 32 and per == 0
     assert bench.shape_plan(8)[0] == (50, 3, 0) and bench.shape_plan(12)[0] == (50, 0, 0)
     assert bench.shape_plan(64)[0] == (51, 0, 0)

@@ -18,6 +18,11 @@ def copylib(hip_built):
     lib.zs_copy_ceiling.restype = C.c_int
     lib.zs_copy_ceiling.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]
     lib.zs_copy_last_error.restype = C.c_char_p
+    lib.zs_copy_shape.restype = C.c_int
+    lib.zs_copy_shape.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_uint64, C.c_uint32,
+                                  C.c_void_p]
+    lib.zs_copy_shape_name.restype = C.c_char_p
+    lib.zs_copy_shape_tile_bytes.restype = C.c_uint64
     return lib
 
 
@@ -141,3 +146,45 @@ def test_probe_moves_what_it_states(copylib, w, nin, nout, p16, vecs):
         for k in range(nout, nin):
             rest ^= ins[k][:, 0, :] ^ ins[k][:, 1, :]
         assert np.array_equal(o16.cpu().numpy().view(np.uint32).reshape(-1, 4), rest)
+
+
+def test_copy_shapes_catalogue_and_refusals(copylib):
+    """The copy-shape catalogue names every shape and its tile; requests it
+    cannot run return 1 before any HIP call."""
+    count = copylib.zs_copy_shape_count()
+    assert count >= 10
+    names = [copylib.zs_copy_shape_name(i) for i in range(count)]
+    assert all(names) and len(set(names)) == count
+    assert copylib.zs_copy_shape_name(count) is None and copylib.zs_copy_shape_name(-1) is None
+    tiles = [copylib.zs_copy_shape_tile_bytes(i) for i in range(count)]
+    assert tiles[0] == 4096 and all(t > 0 and (1 << 32) % t == 0 for t in tiles)
+    f = copylib.zs_copy_shape
+    assert f(count, 0x1000, 0x100000, 4096, 0, None) == 1
+    assert f(-1, 0x1000, 0x100000, 4096, 0, None) == 1
+    assert f(0, 0x1000, 0x100000, 4096, 9, None) == 1
+    assert f(0, None, 0x100000, 4096, 0, None) == 1
+    assert f(0, 0x1008, 0x100000, 4096, 0, None) == 1
+    assert f(0, 0x1000, 0x100000, 4096 + 16, 0, None) == 1
+    assert f(0, 0x1000, 0x1800, 4096, 0, None) == 1
+    assert f(0, 0x1000, 0x100000, 0, 0, None) == 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cap", [0, 2])
+def test_every_copy_shape_is_exact(copylib, cap):
+    """Every shape copies every byte of a buffer a few tiles long and writes
+    nothing past it."""
+    import torch
+    count = copylib.zs_copy_shape_count()
+    nbytes = 3 * max(copylib.zs_copy_shape_tile_bytes(i) for i in range(count)) * 8
+    rng = np.random.default_rng(cap)
+    src = torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).cuda()
+    for i in range(count):
+        dst = torch.zeros(nbytes + 4096, dtype=torch.uint8, device="cuda")
+        rc = copylib.zs_copy_shape(i, src.data_ptr(), dst.data_ptr(), nbytes, cap,
+                                   torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, (i, copylib.zs_copy_last_error().decode())
+        torch.cuda.synchronize()
+        out = dst.cpu().numpy()
+        assert np.array_equal(out[:nbytes], src.cpu().numpy()), copylib.zs_copy_shape_name(i)
+        assert not out[nbytes:].any(), copylib.zs_copy_shape_name(i)

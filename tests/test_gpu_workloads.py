@@ -166,12 +166,13 @@ def test_gpt2s_w8_full(env):
     run_workload(env, "gpt2s-w8")
 
 
-# One shard per branch of the fused kernel's launch rule, whose vectors per
-# thread, loads ahead and blocks per CU follow W and the shard's size:
-# W = 2 (four vectors, 3 blocks per CU); W = 13 and 16 under 20 000
-# 2048-element tiles (four vectors, no cap, 8 and 16 loads ahead); W = 17
-# (one vector, 16 ahead, 6 blocks per CU); W = 3 and 16 at 20 000 tiles and
-# a half (two vectors, 3 blocks per CU). Each n is ragged against every tile.
+# One shard per branch of the fused kernel's launch rule (block size,
+# vectors per thread and blocks per CU follow W and, for W = 3 to 16, the
+# shard's size): W = 2 (one-wave blocks, one vector per thread); W = 13 and
+# 16 under 20 000 2048-element tiles (256-thread blocks, four vectors, no
+# cap, 8 and 16 loads ahead); W = 17 (one-wave blocks, two vectors, 12 per
+# CU); W = 3 and 16 at 20 000 tiles and a half (256-thread blocks, two
+# vectors, 3 per CU). Each n is ragged against every tile.
 TILE_RULE_CASES = [(2, 1_000_003), (13, 1_000_003), (16, 1_000_003), (17, 1_000_003),
                    (3, 40_961_029), (16, 40_961_029)]
 
