@@ -93,16 +93,24 @@ def fused_bytes_per_param(world, accum):
 
 
 FUSED_MANY_TILES = 20000   # 2048-element tiles
+# fp32 state layout of every ShardState the benchmark builds ("split": master,
+# m and v as three arrays; "grouped": one array of 1024-element groups of
+# each); --state-layout sets it
+STATE_LAYOUT = "grouped"
 
 
-def fused_shape(world, n):
+def fused_shape(world, n, state_layout="split"):
     """(threads per block, vectors per thread, zs::kShape* access shape,
     blocks per CU; 0 = no cap) of the fused kernel that zs_step_fused
     launches for a 16-byte-aligned shard of n parameters over `world`
-    workers: 4-element vectors, non-temporal state loads and stores;
-    one-wave blocks at W = 2 and from W = 17 on, 256-thread blocks
-    otherwise, the tile depth and cap following W and, for W = 3 to 16,
-    the shard's size."""
+    workers: 4-element vectors, non-temporal state loads and stores.
+    Split state: one-wave blocks at W = 2 and from W = 17 on, 256-thread
+    blocks otherwise, the tile depth and cap following W and, for W = 3 to
+    16, the shard's size. Grouped state: one-wave blocks throughout, one
+    vector per thread up to W = 3, two beyond, 16 blocks per CU up to
+    W = 16 and 12 beyond."""
+    if state_layout == "grouped":
+        return (64, 1, 5, 16) if world <= 3 else (64, 2, 5, 16 if world <= 16 else 12)
     if world == 1:
         return 256, 2, 5, 2
     if world == 2:
@@ -115,12 +123,13 @@ def fused_shape(world, n):
     return 256, 4, 4 if world == 16 else 5, 0
 
 
-def fused_instance(wl, wire=0):
+def fused_instance(wl, wire=0, state_layout="split"):
     """Template instance of zs::fused_kernel that a 16-byte-aligned shard of
     this workload launches (the name rocprofv3 shows)."""
-    t, u, shape, _ = fused_shape(wl.world, wl.n)
+    t, u, shape, _ = fused_shape(wl.world, wl.n, state_layout)
     return (f"zs::fused_kernel<4, {u}, {str(wl.world > 1).lower()}, "
-            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, {shape}, {t}>")
+            f"{str(wl.accum > 1).lower()}, {wl.grad_dtype}, {wl.param_dtype}, {wire}, {shape}, "
+            f"{t}, {str(state_layout == 'grouped').lower()}>")
 
 
 def timing_events(torch, count):
@@ -324,13 +333,15 @@ def replicas_for(wl, bytes_per_step):
     return max(1, min(128, -(-(1 << 30) // max(bytes_per_step, 1))))
 
 
-def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_pass=True):
+def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_pass=True,
+                 state_layout=None):
     """Time `steps` steps of one workload queued back to back (no events),
     then (event_pass) the fused kernel alone over another `steps` steps,
     each bracketed by HIP events."""
     from sharded_mixed_precision_zs_amd import shard, synth
 
     wl = synth.WORKLOADS[name]
+    layout = state_layout or STATE_LAYOUT
     n, W, A = wl.n, wl.world, wl.accum
     rd, wr = wl.bytes_per_param()
     frd, fwr = fused_bytes_per_param(W, A)
@@ -338,15 +349,16 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_p
     step_bytes = (rd + wr) * n
     R = replicas_for(wl, step_bytes)
     log(f"{name}: n={n} W={W} A={A} replicas={R} step bytes={step_bytes / 1e9:.3f} GB "
-        f"commit={'device' if device_commit else 'host'} wire={wire}")
+        f"commit={'device' if device_commit else 'host'} wire={wire} state={layout}")
     opt = shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay)
     reps = []
     for r in range(R):
         st = shard.ShardState(n, W, wl.rank, wl.offset, wl.offset + n, wl.param_dtype,
                               wl.grad_dtype, opt, wl.loss_scale, dynamic=wl.dynamic_scale,
                               growth_interval=wl.scale_interval, accumulate=A > 1,
-                              wire_dtype=wire, device_commit=device_commit)
-        synth.dev_state(wl, wl.offset, st.master, st.m, st.v)
+                              wire_dtype=wire, device_commit=device_commit,
+                              state_layout=layout)
+        st.fill_state(lambda first, count, *t: synth.dev_state(wl, wl.offset + first, *t))
         # one row per worker, rows padded to 256 B like separate allocations
         grads = torch.empty((A, W, pad_elems(n)), dtype=torch.int16, device="cuda")
         views = [[grads[j, k, :n] for k in range(W)] for j in range(A)]
@@ -384,7 +396,7 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_p
     committed += committed_so_far()
     ms_per_step = elapsed * 1e3 / steps
     res = dict(workload=name, commit="device" if device_commit else "host", n=n, world=W,
-               accum=A, replicas=R, wire=wire, ms_per_step=ms_per_step,
+               accum=A, replicas=R, wire=wire, state_layout=layout, ms_per_step=ms_per_step,
                params_per_s=n / (ms_per_step * 1e-3), step_bytes=step_bytes,
                hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9, committed=committed,
                fused_bytes=fused_bytes)
@@ -405,12 +417,13 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_p
 
 def roofline_of(res, wl, wire=0):
     """The roofline object of one workload's fused kernel."""
-    traffic = recorded_traffic(res["workload"], fused_instance(wl, wire)) if wire == 0 else None
+    kernel = fused_instance(wl, wire, res["state_layout"])
+    traffic = recorded_traffic(res["workload"], kernel) if wire == 0 else None
     rd, wr = fused_bytes_per_param(wl.world, wl.accum)
     return {"bound": "hbm", "achieved": res["fused_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": res["fused_gbps"] / PEAK_HBM_GBPS, "traffic": traffic,
             "traffic_over_algorithmic": traffic / res["fused_bytes"] if traffic else None,
-            "kernel": fused_instance(wl, wire), "kernel_ms": res["fused_kernel_ms"],
+            "kernel": kernel, "kernel_ms": res["fused_kernel_ms"],
             "kernel_ms_median": res["kernel_ms_median"],
             "kernel_samples": res["kernel_samples"], "event_every": 1,
             "algorithmic_bytes_per_launch": res["fused_bytes"],
@@ -882,6 +895,7 @@ def summary(res, wl, wire=0):
 
 
 def main():
+    global STATE_LAYOUT
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1,
                     help="GPUs to use; only 1 is supported (one rank's shard on one MI355X)")
@@ -891,6 +905,8 @@ def main():
                     help="headline workload (a key of synth.WORKLOADS)")
     ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="comma-separated workloads reported beside the headline")
+    ap.add_argument("--state-layout", choices=("split", "grouped"), default=STATE_LAYOUT,
+                    help="fp32 state layout of the timed shards")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (cpu_baseline)")
     ap.add_argument("--no-offload", action="store_true",
@@ -924,6 +940,7 @@ def main():
                          "the fused kernel's shapes of libzsvariants against libzeroshard's and "
                          "print that table as the JSON line instead")
     args = ap.parse_args()
+    STATE_LAYOUT = args.state_layout
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU: the shard step takes one "
                           "rank's real share on one MI355X; multi-GPU runs are not part of it"}))
@@ -1038,7 +1055,8 @@ def main():
                    "phi": wl.phi, "world": wl.world, "rank": wl.rank, "shard_params": wl.n,
                    "grad_dtype": "bf16" if wl.grad_dtype == 0 else "fp16",
                    "param_dtype": "bf16" if wl.param_dtype == 0 else "fp16",
-                   "micro_batches": wl.accum, "replicas": main_res["replicas"], "wire": "fp32"},
+                   "micro_batches": wl.accum, "replicas": main_res["replicas"], "wire": "fp32",
+                   "state_layout": main_res["state_layout"]},
         "hbm_gbps": main_res["hbm_gbps"],
         "hbm_pct_of_peak": 100.0 * main_res["hbm_gbps"] / PEAK_HBM_GBPS,
         "copy_ceiling_gbps": copy_ceiling,

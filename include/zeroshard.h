@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define ZS_ABI_VERSION 6
+#define ZS_ABI_VERSION 7
 #define ZS_MAX_WORLD 64
 
 typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
@@ -74,6 +74,22 @@ typedef enum { ZS_BF16 = 0, ZS_FP16 = 1 } zs_dtype;
  * a 16-bit dtype does ([L7] "ZeRO 与 FSDP": MixedPrecision reduce_dtype):
  *   s = R(G[r+1]);  s = R(s + G[r+s']) for s' = 2..W   (adds in fp32). */
 typedef enum { ZS_WIRE_FP32 = 0, ZS_WIRE_BF16 = 1, ZS_WIRE_FP16 = 2 } zs_wire;
+
+/* Layout of the fp32 state (master weights, m, v) that zs_step_fused and
+ * the calls built on it read and write ([Notes] 三 keeps the three as the
+ * owner's fp32 optimizer state of its partition; their layout in HBM is
+ * this library's choice). ZS_STATE_SPLIT (0, the default): three arrays of
+ * n floats (master_*, m_*, v_*). ZS_STATE_GROUPED: one buffer per set, in
+ * groups of ZS_STATE_GROUP elements; group g holds the master weights of
+ * elements [g*1024, (g+1)*1024), then their m, then their v, as three runs of
+ * 1024 floats, so element i of the master weights is at float offset
+ * 3*1024*(i/1024) + i%1024, its m 1024 floats further and its v 2048
+ * floats further. The buffer holds ceil(n/1024) whole groups
+ * (12288 bytes each); the slots past n in the last group are never read or
+ * written. On MI355X the grouped layout moves the same bytes as one stream
+ * in and one out instead of three each, and streamed faster. */
+typedef enum { ZS_STATE_SPLIT = 0, ZS_STATE_GROUPED = 1 } zs_state_layout;
+#define ZS_STATE_GROUP 1024
 
 typedef enum {
   ZS_OK = 0,
@@ -188,20 +204,29 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
  * overlap the input set (ZS_ERR_ALIAS), so a step whose flag turns out set
  * leaves the input set untouched: the caller reads the flag, then either
  * swaps the sets (flag 0) or keeps the input set (flag 1, step skipped).
- * gather_buf belongs to the output set too. */
+ * gather_buf belongs to the output set too.
+ * With state_layout ZS_STATE_GROUPED, master_in and master_out each point
+ * at a grouped state buffer of ceil(n/1024) groups (see zs_state_layout),
+ * m_in, v_in, m_out and v_out must be NULL, and every operand must be
+ * aligned for 4-element vectors (the state buffers and acc_in to 16 bytes,
+ * the gradients and this rank's gather slice to 8); otherwise
+ * ZS_ERR_INVALID_ARG (non-NULL m/v pointers, an unknown layout) or
+ * ZS_ERR_UNSUPPORTED (alignment). acc_in, the gradients and the gather
+ * buffer keep their flat layout. */
 typedef struct {
   uint32_t world, rank;
   uint64_t n;
   int32_t grad_dtype, param_dtype;
   const void *const *worker_grads; /* host array [world], as above         */
   const float *acc_in;             /* NULL, or fp32[n] summed micro-batches */
-  const float *master_in, *m_in, *v_in;  /* fp32[n], read only             */
-  float *master_out, *m_out, *v_out;     /* fp32[n], written               */
+  const float *master_in, *m_in, *v_in;  /* fp32[n] each, read only (or   */
+  float *master_out, *m_out, *v_out;     /* the grouped buffers), written  */
   void *gather_buf;                /* 16-bit flat buffer                    */
   uint64_t gather_offset;          /* element offset of this rank's slice   */
   uint32_t *overflow_flag;         /* device uint32, OR-ed                  */
   zs_adamw_hparams hp;
   int32_t wire_dtype;              /* zs_wire; 0 = fp32 partial sums        */
+  int32_t state_layout;            /* zs_state_layout; 0 = split arrays     */
 } zs_step_args;
 
 int zs_step_fused(const zs_step_args *args, void *stream);

@@ -228,6 +228,91 @@ __global__ __launch_bounds__(T) void g4t_kernel(FusedArgs p) {
   flag_or(p.flag, bad);
 }
 
+/* The production tile with the fp32 state grouped: for each 1024-element
+ * group g the master weights, m and v are stored back to back, [theta |
+ * m | v] at float offset 3072 g (master_in / master_out point at the
+ * grouped buffers; m_in, v_in, m_out and v_out are not read). Element e of
+ * a stream is at 3072 (e / 1024) + e % 1024 (+ 1024 for m, + 2048 for v):
+ * each wave's access still covers 1 KB of whole lines, and the state is
+ * one stream in and one stream out instead of three each. */
+__device__ __forceinline__ uint64_t grouped_at(uint64_t e) {
+  return (e >> 10) * 3072u + (e & 1023u);
+}
+
+template <int T, int U, bool MULTI, int SHAPE>
+__device__ __forceinline__ bool fused_tile_g(const FusedArgs &p, uint64_t base) {
+  constexpr int B = shape_batch(SHAPE);
+  constexpr bool NTS = shape_nt_stores(SHAPE);
+  constexpr bool NTL = shape_nt_loads(SHAPE);
+  uint64_t i0[U], s0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    i0[u] = base + ((uint64_t)u * T + threadIdx.x) * 4;
+    s0[u] = grouped_at(i0[u]);
+  }
+  float th[U][4], m[U][4], v[U][4], s[U][4];
+  auto load_state = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ldf_p<4, NTL>(p.master_in + s0[u], th[u]);
+      ldf_p<4, NTL>(p.master_in + s0[u] + 1024, m[u]);
+      ldf_p<4, NTL>(p.master_in + s0[u] + 2048, v[u]);
+    }
+  };
+  if constexpr (MULTI) {
+    ring_sum_uw<4, U, ZS_BF16, ZS_WIRE_FP32, B>(p.g, p.world, i0, s);
+    load_state();
+  } else {
+    load_state();
+    ring_sum_uw<4, U, ZS_BF16, ZS_WIRE_FP32, B>(p.g, 1, i0, s);
+  }
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g = unscale(average(s[u][e], p.k), p.k);
+      bad |= !__builtin_isfinite(g);
+      th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, p.h);
+    }
+    stf_p<4, NTS>(p.master_out + s0[u], th[u]);
+    stf_p<4, NTS>(p.master_out + s0[u] + 1024, m[u]);
+    stf_p<4, NTS>(p.master_out + s0[u] + 2048, v[u]);
+    st16_p<4, ZS_BF16, NTS>(p.param_out + i0[u], th[u]);
+  }
+  return bad;
+}
+
+template <int T, int U, bool MULTI, int SHAPE>
+__global__ __launch_bounds__(T) void g4g_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)T * 4 * U;
+  const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
+  bool bad = false;
+  if (blockIdx.x < tiles) bad = fused_tile_g<T, U, MULTI, SHAPE>(p, (uint64_t)blockIdx.x * tile);
+  flag_or(p.flag, bad);
+}
+
+/* The same tiles in an XCD-contiguous order. Workgroups are dispatched to
+ * the 8 XCDs round-robin, so block b runs on XCD b % 8; here XCD x takes
+ * the x-th eighth of the tiles in order (block b -> tile start(b % 8) +
+ * b / 8), a bijection on [0, tiles) for any tile count. */
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint64_t xcd_tile(uint64_t b, uint64_t tiles) {
+  const uint64_t q = tiles / kXcds, r = tiles % kXcds, x = b % kXcds;
+  return x * q + (x < r ? x : r) + b / kXcds;
+}
+
+template <int T, int U, bool MULTI, int SHAPE>
+__global__ __launch_bounds__(T) void g4x_kernel(FusedArgs p) {
+  const uint64_t tile = (uint64_t)T * 4 * U;
+  const uint64_t tiles = p.n / tile;  /* the host checked n % tile == 0 */
+  bool bad = false;
+  if (blockIdx.x < tiles)
+    bad = fused_tile_t<T, U, MULTI, SHAPE>(p, xcd_tile(blockIdx.x, tiles) * tile);
+  flag_or(p.flag, bad);
+}
+
 /* ------------------------------------------------------------------------
  * Loader/storer split. NL loader waves each take one 8-element vector per
  * lane of a tile of NL * 512 elements: they load, sum and update it exactly
@@ -478,6 +563,18 @@ constexpr Variant mk_g4t(const char *name) {
                  false, T, 0};
 }
 
+template <int T, int U, bool M, int SHAPE>
+constexpr Variant mk_g4x(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&g4x_kernel<T, U, M, SHAPE>), T * 4 * U, M,
+                 false, T, 0};
+}
+
+template <int T, int U, bool M, int SHAPE>
+constexpr Variant mk_g4g(const char *name) {
+  return Variant{name, reinterpret_cast<const void *>(&g4g_kernel<T, U, M, SHAPE>), T * 4 * U, M,
+                 false, T, 0};
+}
+
 /* libzeroshard's fused_kernel itself (with its ragged-tail and device
  * scale paths), launched through this library's launcher: against the
  * g4 kernels of the same shape it separates the cost of those paths from
@@ -575,6 +672,17 @@ const Variant kVariants[] = {
     mk_g4t<64, 4, false, kShapeB8NtL>("w1: 4-element lane groups, 4 vectors/thread, 64-thread blocks"),
     mk_prod<2, true, kShapeB8NtL, 64>("wN: libzeroshard's kernel, 2 vectors/thread, 64-thread blocks"),
     mk_prod<1, true, kShapeB8NtL, 64>("wN: libzeroshard's kernel, 1 vector/thread, 64-thread blocks"),
+    mk_g4x<256, 2, false, kShapeB8NtL>("w1: 4-element lane groups, 2 vectors/thread, XCD-contiguous tiles"),
+    mk_g4x<64, 2, false, kShapeB8NtL>("w1: 4-element lane groups, 2 vectors/thread, 64-thread blocks, XCD-contiguous tiles"),
+    mk_g4x<64, 2, true, kShapeB8NtL>("wN: 4-element lane groups, 2 vectors/thread, 64-thread blocks, XCD-contiguous tiles"),
+    mk_g4x<256, 2, true, kShapeB8NtL>("wN: 4-element lane groups, 2 vectors/thread, XCD-contiguous tiles"),
+    mk_g4g<256, 2, false, kShapeB8NtL>("w1: grouped state, 2 vectors/thread"),
+    mk_g4g<256, 1, false, kShapeB8NtL>("w1: grouped state, 1 vector/thread"),
+    mk_g4g<64, 1, false, kShapeB8NtL>("w1: grouped state, 1 vector/thread, 64-thread blocks"),
+    mk_g4g<64, 2, false, kShapeB8NtL>("w1: grouped state, 2 vectors/thread, 64-thread blocks"),
+    mk_g4g<64, 2, true, kShapeB8NtL>("wN: grouped state, 2 vectors/thread, 64-thread blocks"),
+    mk_g4g<256, 2, true, kShapeB8NtL>("wN: grouped state, 2 vectors/thread"),
+    mk_g4g<64, 1, true, kShapeB8NtL>("wN: grouped state, 1 vector/thread, 64-thread blocks"),
 };
 constexpr int kCount = (int)(sizeof kVariants / sizeof kVariants[0]);
 

@@ -187,6 +187,19 @@ FusedShape fused_shape(int vec, uint32_t world, uint64_t n) {
   return {kBlock, 4, world == 16 ? kShapeB16NtL : kShapeB8NtL, 0};
 }
 
+/* The grouped state layout always runs one-wave blocks: one vector per
+ * thread at 16 per CU up to W = 3, two at 16 per CU to W = 16 and at 12 per
+ * CU above. */
+FusedShape fused_shape_grouped(uint32_t world) {
+  if (world <= 3) return {kFusedWaveBlock, 1, kShapeB8NtL, 16};
+  return {kFusedWaveBlock, 2, kShapeB8NtL, world <= 16 ? 16 : 12};
+}
+
+/* Bytes of a grouped state buffer for n elements: whole groups. */
+uint64_t grouped_state_bytes(uint64_t n) {
+  return (n + ZS_STATE_GROUP - 1) / ZS_STATE_GROUP * (uint64_t)(3 * ZS_STATE_GROUP * 4);
+}
+
 /* Dynamic LDS bytes that hold the fused kernel to `cap` blocks per CU (0:
  * no cap), or to ZS_FUSED_BLOCKS_PER_CU when that is set: LDS per CU / cap
  * less 1 KB up to 8 blocks; above that LDS per CU / cap rounded down to
@@ -209,7 +222,7 @@ size_t fused_lds_bytes(int cap) {
 /* Launch of one fused-kernel instance with `lds` bytes of (unused) dynamic
  * LDS; above the default 64 KB limit the instance's limit is raised once
  * per device (a bit per device id; ids past 63 raise it at every launch). */
-template <int V, int U, bool L, bool A, int G, int P, int W, int F, int T>
+template <int V, int U, bool L, bool A, int G, int P, int W, int F, int T, bool GR>
 void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedArgs &p) {
   if (lds > 65536) {
     static std::atomic<uint64_t> raised{0};
@@ -218,13 +231,13 @@ void launch_fused(dim3 grid, dim3 block, size_t lds, hipStream_t s, const FusedA
     const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;
     if (!bit || !(raised.load(std::memory_order_relaxed) & bit)) {
       /* a refusal surfaces as the launch's error */
-      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W, F, T>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&fused_kernel<V, U, L, A, G, P, W, F, T, GR>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)device_lds().lds_per_cu) == hipSuccess)
         raised.fetch_or(bit, std::memory_order_relaxed);
     }
   }
-  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W, F, T>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((fused_kernel<V, U, L, A, G, P, W, F, T, GR>), grid, block, lds, s, p);
 }
 
 /* Widest vector width every operand's alignment allows: 16-bit operands
@@ -564,9 +577,17 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
                            hipEvent_t ev_stop, zs_device_scaler *dev,
                            uint32_t *clear_first = nullptr) {
   if (!a) return fail(ZS_ERR_INVALID_ARG, "null args%s");
-  if (!a->worker_grads || !a->master_in || !a->m_in || !a->v_in || !a->master_out ||
-      !a->m_out || !a->v_out || !a->gather_buf || (!a->overflow_flag && !dev))
+  if (a->state_layout != ZS_STATE_SPLIT && a->state_layout != ZS_STATE_GROUPED)
+    return fail(ZS_ERR_INVALID_ARG, "unknown state layout%s");
+  const bool grouped = a->state_layout == ZS_STATE_GROUPED;
+  if (!a->worker_grads || !a->master_in || !a->master_out || !a->gather_buf ||
+      (!a->overflow_flag && !dev))
     return fail(ZS_ERR_INVALID_ARG, "null pointer in zs_step_args%s");
+  if (grouped ? (a->m_in || a->v_in || a->m_out || a->v_out)
+              : (!a->m_in || !a->v_in || !a->m_out || !a->v_out))
+    return fail(ZS_ERR_INVALID_ARG,
+                grouped ? "grouped state: m and v pointers must be NULL%s"
+                        : "null pointer in zs_step_args%s");
   if (a->world == 0 || a->world > ZS_MAX_WORLD || a->rank >= a->world)
     return fail(ZS_ERR_INVALID_ARG, "need 0 < world <= 64 and rank < world%s");
   if (!valid_dtype(a->grad_dtype) || !valid_dtype(a->param_dtype))
@@ -595,20 +616,24 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
 
   uint16_t *param_out = static_cast<uint16_t *>(a->gather_buf) + a->gather_offset;
   /* The output set must not overlap any input (the skip relies on the
-   * input set being untouched) nor itself. */
+   * input set being untouched) nor itself. Null entries (m and v with the
+   * grouped layout, no acc_in) take no part. */
   const uint64_t b4 = 4 * n, b2 = 2 * n;
+  const uint64_t bs = grouped ? grouped_state_bytes(n) : b4; /* master_in / master_out */
   const void *outs[] = {a->master_out, a->m_out, a->v_out, param_out};
-  const uint64_t out_bytes[] = {b4, b4, b4, b2};
+  const uint64_t out_bytes[] = {bs, b4, b4, b2};
   const void *ins[] = {a->master_in, a->m_in, a->v_in, a->acc_in};
+  const uint64_t in_bytes[] = {bs, b4, b4, b4};
   for (int i = 0; i < 4; ++i) {
+    if (!outs[i]) continue;
     for (int j = 0; j < 4; ++j)
-      if (overlaps(outs[i], out_bytes[i], ins[j], b4))
+      if (ins[j] && overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
         return fail(ZS_ERR_ALIAS, "zs_step_fused: an output overlaps an input%s");
     for (uint32_t w = 0; w < a->world; ++w)
       if (overlaps(outs[i], out_bytes[i], p.g.p[w], b2))
         return fail(ZS_ERR_ALIAS, "zs_step_fused: an output overlaps a gradient buffer%s");
     for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+      if (outs[j] && overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
         return fail(ZS_ERR_ALIAS, "zs_step_fused: two outputs overlap%s");
     if (dev && overlaps(outs[i], out_bytes[i], dev, sizeof(zs_device_scaler)))
       return fail(ZS_ERR_ALIAS, "zs_step_device: an output overlaps the device scaler%s");
@@ -618,7 +643,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
    * corrupt the set a skipped step restores from. */
   if (dev) {
     for (int j = 0; j < 4; ++j)
-      if (overlaps(dev, sizeof(zs_device_scaler), ins[j], b4))
+      if (ins[j] && overlaps(dev, sizeof(zs_device_scaler), ins[j], in_bytes[j]))
         return fail(ZS_ERR_ALIAS, "zs_step_device: the device scaler overlaps an input%s");
     for (uint32_t w = 0; w < a->world; ++w)
       if (overlaps(dev, sizeof(zs_device_scaler), p.g.p[w], b2))
@@ -645,7 +670,10 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
                        a->v_out, a->acc_in ? a->acc_in : a->master_in};
   const int vec = fused_vec_of(pick_vec(p16, (int)a->world + 1, f32, 7));
   const bool multi = a->world > 1, acc = a->acc_in != nullptr;
-  const FusedShape fs = fused_shape(vec, a->world, n);
+  if (grouped && vec != 4)
+    return fail(ZS_ERR_UNSUPPORTED,
+                "grouped state needs operands aligned for 4-element vectors%s");
+  const FusedShape fs = grouped ? fused_shape_grouped(a->world) : fused_shape(vec, a->world, n);
   const int per_thread = vec * fs.tile_vecs;
   if (!tiled_ok(n, per_thread, fs.threads))
     return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");
@@ -653,10 +681,16 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   dim3 grid(tiled_grid(n, per_thread, fs.threads)), block(fs.threads);
   const size_t lds = fused_lds_bytes(fs.cap);
 #define ZS_KF(V, U, L, A, G, P, W, S, T) \
-  launch_fused<V, U, L, A, G, P, W, S, T>(grid, block, lds, s, p)
+  launch_fused<V, U, L, A, G, P, W, S, T, false>(grid, block, lds, s, p)
+#define ZS_KG(U, L, A, G, P, W) \
+  launch_fused<4, U, L, A, G, P, W, kShapeB8NtL, kFusedWaveBlock, true>(grid, block, lds, s, p)
 #define ZS_K4(V, A, G, P, W)                                                             \
   do {                                                                                   \
-    if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL, kBlock);                     \
+    if (grouped) {                                                                       \
+      if (!multi) ZS_KG(1, false, A, G, P, W);                                           \
+      else if (fs.tile_vecs == 1) ZS_KG(1, true, A, G, P, W);                            \
+      else ZS_KG(2, true, A, G, P, W);                                                   \
+    } else if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL, kBlock);              \
     else if (fs.threads == kFusedWaveBlock && fs.tile_vecs == 1)                         \
       ZS_KF(4, 1, true, A, G, P, W, kShapeB8NtL, kFusedWaveBlock);                       \
     else if (fs.threads == kFusedWaveBlock) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL,   \
@@ -710,6 +744,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
 #undef ZS_KWIRE
 #undef ZS_KNARROW
 #undef ZS_K4
+#undef ZS_KG
 #undef ZS_KF
   int launched = launch_result();
   if (launched == ZS_OK && ev_stop) {
@@ -825,8 +860,14 @@ int zs_step_device(const zs_step_args *a, zs_device_scaler *dev, void *stream, v
   const unsigned blocks =
       (unsigned)(want < 1 ? 1 : (want > (uint64_t)kCommitBlocks ? kCommitBlocks : want));
   hipStream_t s = static_cast<hipStream_t>(stream);
-#define ZS_COMMIT_K(V, P) \
-  hipLaunchKernelGGL((commit_kernel<V, P>), dim3(blocks), dim3(kCommitBlock), 0, s, c)
+  const bool grouped = a->state_layout == ZS_STATE_GROUPED;
+#define ZS_COMMIT_K(V, P)                                                                   \
+  do {                                                                                      \
+    if (grouped)                                                                            \
+      hipLaunchKernelGGL((commit_kernel<V, P, true>), dim3(blocks), dim3(kCommitBlock), 0, s, c); \
+    else                                                                                    \
+      hipLaunchKernelGGL((commit_kernel<V, P, false>), dim3(blocks), dim3(kCommitBlock), 0, s, c); \
+  } while (0)
 #define ZS_COMMIT_VEC(P)                      \
   switch (vec) {                              \
     case 8: ZS_COMMIT_K(8, P); break;         \

@@ -51,19 +51,24 @@ struct CommitArgs {
   double beta1, beta2;
 };
 
-template <int VEC, int PDT>
+/* GR: the state in the grouped layout (master_in / master_out hold it); a
+ * vector of up to 8 elements at a multiple of VEC never straddles a group. */
+template <int VEC, int PDT, bool GR = false>
 __device__ __forceinline__ void restore_vec(const CommitArgs &c, uint64_t i0) {
+  const StateAt<GR> at(i0);
+  const float *m_in = GR ? c.master_in : c.m_in, *v_in = GR ? c.master_in : c.v_in;
+  float *m_out = GR ? c.master_out : c.m_out, *v_out = GR ? c.master_out : c.v_out;
   float x[VEC];
-  ldf<VEC>(c.master_in + i0, x);
-  stf<VEC>(c.master_out + i0, x);
+  ldf<VEC>(c.master_in + at.th, x);
+  stf<VEC>(c.master_out + at.th, x);
   st16<VEC, PDT>(c.param_out + i0, x);
-  ldf<VEC>(c.m_in + i0, x);
-  stf<VEC>(c.m_out + i0, x);
-  ldf<VEC>(c.v_in + i0, x);
-  stf<VEC>(c.v_out + i0, x);
+  ldf<VEC>(m_in + at.m, x);
+  stf<VEC>(m_out + at.m, x);
+  ldf<VEC>(v_in + at.v, x);
+  stf<VEC>(v_out + at.v, x);
 }
 
-template <int VEC, int PDT>
+template <int VEC, int PDT, bool GR = false>
 __global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
   zs_device_scaler *d = c.dev;
   /* an empty partition had no fused pass (nothing to check, nothing
@@ -77,9 +82,9 @@ __global__ __launch_bounds__(kCommitBlock) void commit_kernel(CommitArgs c) {
     for (uint64_t i0 = ((uint64_t)blockIdx.x * kCommitBlock + threadIdx.x) * VEC; i0 < c.n;
          i0 += stride) {
       if (i0 + VEC <= c.n) {
-        restore_vec<VEC, PDT>(c, i0);
+        restore_vec<VEC, PDT, GR>(c, i0);
       } else {
-        for (uint64_t i = i0; i < c.n; ++i) restore_vec<1, PDT>(c, i);
+        for (uint64_t i = i0; i < c.n; ++i) restore_vec<1, PDT, GR>(c, i);
       }
     }
   }

@@ -590,13 +590,44 @@ struct FusedArgs {
   double lr;              /* for the bias correction formed on the device */
 };
 
-template <int VEC, int GDT, int PDT>
+/* Grouped state layout: for each group of kGroup elements the master
+ * weights, m and v are stored as three consecutive runs of kGroup floats,
+ * so element e of the master weights is at float offset
+ * 3 kGroup (e / kGroup) + e % kGroup, of m kGroup further and of v 2 kGroup
+ * further. One wave's 4-element vectors still cover whole lines, and the
+ * state is one stream in and one out instead of three each. */
+constexpr uint64_t kGroup = 1024;
+
+__device__ __forceinline__ uint64_t grouped_at(uint64_t e) {
+  return (e / kGroup) * (3 * kGroup) + e % kGroup;
+}
+
+/* Offsets of element e's master weight, m and v from the state base:
+ * e, and the separate m and v arrays (GR false), or the grouped layout. */
+template <bool GR>
+struct StateAt {
+  uint64_t th, m, v;
+  __device__ __forceinline__ explicit StateAt(uint64_t e) {
+    if constexpr (GR) {
+      th = grouped_at(e);
+      m = th + kGroup;
+      v = th + 2 * kGroup;
+    } else {
+      th = m = v = e;
+    }
+  }
+};
+
+template <int VEC, int GDT, int PDT, bool GR = false>
 __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, const AdamK &h,
                                           uint64_t i0) {
   float th[VEC], m[VEC], v[VEC], acc[VEC], s[VEC];
-  ldf<VEC>(p.master_in + i0, th);
-  ldf<VEC>(p.m_in + i0, m);
-  ldf<VEC>(p.v_in + i0, v);
+  const StateAt<GR> at(i0);
+  const float *m_in = GR ? p.master_in : p.m_in, *v_in = GR ? p.master_in : p.v_in;
+  float *m_out = GR ? p.master_out : p.m_out, *v_out = GR ? p.master_out : p.v_out;
+  ldf<VEC>(p.master_in + at.th, th);
+  ldf<VEC>(m_in + at.m, m);
+  ldf<VEC>(v_in + at.v, v);
   if (p.acc_in) ldf<VEC>(p.acc_in + i0, acc);
   ring_sum<VEC, GDT>(p.g, p.world, p.wire, i0, s);
   bool bad = false;
@@ -608,9 +639,9 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, 
     bad |= !__builtin_isfinite(g);
     th[e] = adamw_elem(th[e], m[e], v[e], g, h);
   }
-  stf<VEC>(p.master_out + i0, th);
-  stf<VEC>(p.m_out + i0, m);
-  stf<VEC>(p.v_out + i0, v);
+  stf<VEC>(p.master_out + at.th, th);
+  stf<VEC>(m_out + at.m, m);
+  stf<VEC>(v_out + at.v, v);
   st16<VEC, PDT>(p.param_out + i0, th);
   return bad;
 }
@@ -623,7 +654,7 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, 
  * T is the block's thread count (vector u of thread t starts at
  * base + (u * T + t) * VEC). */
 template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE,
-          int T = kBlock>
+          int T = kBlock, bool GR = false>
 __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk, const AdamK &h,
                                            uint64_t base) {
   constexpr int B = shape_batch(SHAPE);
@@ -633,12 +664,15 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
 #pragma unroll
   for (int u = 0; u < U; ++u) i0[u] = base + ((uint64_t)u * T + threadIdx.x) * VEC;
   float th[U][VEC], m[U][VEC], v[U][VEC], acc[U][VEC], s[U][VEC];
+  const float *m_in = GR ? p.master_in : p.m_in, *v_in = GR ? p.master_in : p.v_in;
+  float *m_out = GR ? p.master_out : p.m_out, *v_out = GR ? p.master_out : p.v_out;
   auto load_state = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      ldf_p<VEC, NTL>(p.master_in + i0[u], th[u]);
-      ldf_p<VEC, NTL>(p.m_in + i0[u], m[u]);
-      ldf_p<VEC, NTL>(p.v_in + i0[u], v[u]);
+      const StateAt<GR> at(i0[u]);  /* a vector never straddles a group */
+      ldf_p<VEC, NTL>(p.master_in + at.th, th[u]);
+      ldf_p<VEC, NTL>(m_in + at.m, m[u]);
+      ldf_p<VEC, NTL>(v_in + at.v, v[u]);
       if constexpr (ACC) ldf_p<VEC, NTL>(p.acc_in + i0[u], acc[u]);
     }
   };
@@ -660,9 +694,10 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
       bad |= !__builtin_isfinite(g);
       th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, h);
     }
-    stf_p<VEC, NTS>(p.master_out + i0[u], th[u]);
-    stf_p<VEC, NTS>(p.m_out + i0[u], m[u]);
-    stf_p<VEC, NTS>(p.v_out + i0[u], v[u]);
+    const StateAt<GR> at(i0[u]);
+    stf_p<VEC, NTS>(p.master_out + at.th, th[u]);
+    stf_p<VEC, NTS>(m_out + at.m, m[u]);
+    stf_p<VEC, NTS>(v_out + at.v, v[u]);
     st16_p<VEC, PDT, NTS>(p.param_out + i0[u], th[u]);
   }
   return bad;
@@ -706,9 +741,10 @@ __device__ __forceinline__ void flag_epoch_mark(uint64_t *flag_epoch, uint64_t v
 /* ACC: an accumulated fp32 gradient of earlier micro-batches (acc_in) is
  * added before the unscale; a separate instance so the common case carries
  * no registers for it. T threads per block, tiles of T * U * VEC elements,
- * and the ragged end in blocks of T elements. */
+ * and the ragged end in blocks of T elements. GR: the fp32 state in the
+ * grouped layout (master_in / master_out hold it; m and v pointers unused). */
 template <int VEC, int U, bool MULTI, bool ACC, int GDT, int PDT, int WIRE, int SHAPE,
-          int T = kBlock>
+          int T = kBlock, bool GR = false>
 __global__ __launch_bounds__(T) void fused_kernel(FusedArgs p) {
   const uint64_t tile = (uint64_t)T * U * VEC;
   const uint64_t full = p.n / tile;  /* blocks past `full` cover the tail */
@@ -717,13 +753,13 @@ __global__ __launch_bounds__(T) void fused_kernel(FusedArgs p) {
   uint64_t epoch = 0;
   bool bad = p.dev ? !dev_step_consts(p, sk, h, epoch) : false;
   if (blockIdx.x < full) {
-    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE, SHAPE, T>(p, sk, h,
-                                                                    (uint64_t)blockIdx.x * tile);
+    bad |= fused_tile<VEC, U, MULTI, ACC, GDT, PDT, WIRE, SHAPE, T, GR>(p, sk, h,
+                                                                        (uint64_t)blockIdx.x * tile);
   } else {
     /* ragged end: one element per thread, spread over enough blocks that
      * no thread walks a chain of them */
     uint64_t i = full * tile + (uint64_t)(blockIdx.x - full) * T + threadIdx.x;
-    if (i < p.n) bad |= fused_vec<1, GDT, PDT>(p, sk, h, i);
+    if (i < p.n) bad |= fused_vec<1, GDT, PDT, GR>(p, sk, h, i);
   }
   if (p.dev) flag_epoch_mark(&p.dev->flag_epoch, epoch + 1, bad);
   else flag_or(p.flag, bad);

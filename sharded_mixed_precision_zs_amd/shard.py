@@ -39,20 +39,30 @@ class AdamW:
 
 class ShardState:
     """One rank's shard: n parameters at flat offset `offset` of a model with
-    `world` data-parallel ranks; gather buffers hold `gather_len` elements."""
+    `world` data-parallel ranks; gather buffers hold `gather_len` elements.
+    state_layout: "split" (master, m and v as three arrays) or "grouped"
+    (one buffer per set in libzeroshard's grouped layout, ZS_STATE_GROUPED)."""
 
     FLAG_RING = 256  # flags zeroed in bulk, one slot per step
+    FILL_CHUNK = 1 << 26  # elements per piece when filling a grouped set
 
     def __init__(self, n, world, rank, offset, gather_len, param_dtype, grad_dtype,
                  opt: AdamW, loss_scale, dynamic=False, growth_interval=0,
                  device="cuda", accumulate=False, wire_dtype=zs.ZS_WIRE_FP32,
-                 device_commit=False):
+                 device_commit=False, state_layout="split"):
         self.n, self.world, self.rank, self.offset = n, world, rank, offset
         self.wire_dtype = wire_dtype  # precision of the ring's partial sums
         self.param_dtype, self.grad_dtype = param_dtype, grad_dtype
         self.opt = opt
+        layouts = {"split": zs.ZS_STATE_SPLIT, "grouped": zs.ZS_STATE_GROUPED}
+        if state_layout not in layouts:
+            raise ValueError(f"state_layout must be one of {sorted(layouts)}")
+        self.state_layout = layouts[state_layout]
         f32 = dict(dtype=torch.float32, device=device)
-        self.sets = [[torch.empty(n, **f32) for _ in range(3)] for _ in range(2)]
+        if self.state_layout == zs.ZS_STATE_GROUPED:
+            self.sets = [[torch.empty(zs.grouped_len(n), **f32)] for _ in range(2)]
+        else:
+            self.sets = [[torch.empty(n, **f32) for _ in range(3)] for _ in range(2)]
         pdt = torch.bfloat16 if param_dtype == zs.ZS_BF16 else torch.float16
         self.gather = [torch.zeros(gather_len, dtype=pdt, device=device) for _ in range(2)]
         self.cur = 0
@@ -76,17 +86,67 @@ class ShardState:
         self.device = device
 
     # -- state access -------------------------------------------------------
+    def _array(self, k):
+        """Array k (0 master, 1 m, 2 v) of the current set: the tensor itself
+        (split), or a (groups, 1024) strided view of the grouped buffer."""
+        x = self.sets[self.cur]
+        if self.state_layout == zs.ZS_STATE_GROUPED:
+            return x[0].view(-1, 3, zs.ZS_STATE_GROUP)[:, k, :]
+        return x[k]
+
     @property
     def master(self):
-        return self.sets[self.cur][0]
+        return self._array(0)
 
     @property
     def m(self):
-        return self.sets[self.cur][1]
+        return self._array(1)
 
     @property
     def v(self):
-        return self.sets[self.cur][2]
+        return self._array(2)
+
+    def state(self, k, first=0, count=None):
+        """Elements [first, first + count) of array k (0 master, 1 m, 2 v) of
+        the current set as a contiguous device tensor: a view with the split
+        layout, a copy of the groups it spans with the grouped one."""
+        count = self.n - first if count is None else count
+        if self.state_layout != zs.ZS_STATE_GROUPED:
+            return self.sets[self.cur][k][first:first + count]
+        G = zs.ZS_STATE_GROUP
+        g0, g1 = first // G, -(-(first + count) // G)
+        flat = self._array(k)[g0:g1].reshape(-1)
+        return flat[first - g0 * G:first - g0 * G + count]
+
+    def write_state(self, k, first, src):
+        """Copy the device tensor src into elements [first, first + len(src))
+        of array k of the current set."""
+        count = src.numel()
+        if self.state_layout != zs.ZS_STATE_GROUPED:
+            self.sets[self.cur][k][first:first + count].copy_(src)
+            return
+        G = zs.ZS_STATE_GROUP
+        g0, g1 = first // G, -(-(first + count) // G)
+        blk = self._array(k)[g0:g1]
+        flat = blk.reshape(-1).clone()
+        flat[first - g0 * G:first - g0 * G + count] = src
+        blk.copy_(flat.view(g1 - g0, G))
+
+    def fill_state(self, fill):
+        """fill(first, count, master, m, v) writes elements [first, first +
+        count) of the three arrays into the contiguous fp32 device tensors it
+        is given; this calls it once (split) or in pieces of FILL_CHUNK
+        elements (grouped) and stores the result in the current set."""
+        if self.state_layout != zs.ZS_STATE_GROUPED:
+            fill(0, self.n, *self.sets[self.cur])
+            return
+        dev = self.sets[self.cur][0].device
+        for first in range(0, self.n, self.FILL_CHUNK):
+            count = min(self.FILL_CHUNK, self.n - first)
+            tmp = [torch.empty(count, dtype=torch.float32, device=dev) for _ in range(3)]
+            fill(first, count, *tmp)
+            for k in range(3):
+                self.write_state(k, first, tmp[k])
 
     @property
     def params(self):
@@ -110,7 +170,7 @@ class ShardState:
         if self.device_commit:
             self.sync_scaler()
         sc = self.scaler
-        return {"master": self.master.cpu(), "m": self.m.cpu(), "v": self.v.cpu(),
+        return {"master": self.state(0).cpu(), "m": self.state(1).cpu(), "v": self.state(2).cpu(),
                 "params": self.params.cpu(),
                 "scaler": {"scale": float(sc.scale), "clean_steps": int(sc.clean_steps),
                            "growth_interval": int(sc.growth_interval), "dynamic": int(sc.dynamic),
@@ -120,11 +180,14 @@ class ShardState:
         """Restore a state_dict() into the current set (shapes must match;
         waits for every queued step first, on any stream)."""
         torch.cuda.synchronize(self.sets[0][0].device)
-        for dst, key in ((self.master, "master"), (self.m, "m"), (self.v, "v"),
-                         (self.params, "params")):
-            if dst.shape != sd[key].shape or dst.dtype != sd[key].dtype:
+        for key in ("master", "m", "v"):
+            if tuple(sd[key].shape) != (self.n,) or sd[key].dtype != torch.float32:
                 raise ValueError(f"state_dict[{key!r}] has the wrong shape or dtype")
-            dst.copy_(sd[key])
+        if sd["params"].shape != self.params.shape or sd["params"].dtype != self.params.dtype:
+            raise ValueError("state_dict['params'] has the wrong shape or dtype")
+        for k, key in enumerate(("master", "m", "v")):
+            self.write_state(k, 0, sd[key].to(self.sets[0][0].device))
+        self.params.copy_(sd["params"])
         for k, v in sd["scaler"].items():
             setattr(self.scaler, k, v)
         if self.device_commit:
@@ -199,11 +262,13 @@ class ShardState:
         args = self._prepared.get(key)
         if args is None:
             src, dst = self.sets[self.cur], self.sets[1 - self.cur]
+            if self.state_layout == zs.ZS_STATE_GROUPED:
+                src, dst = [src[0], None, None], [dst[0], None, None]
             args = zs.StepArgs(worker_grads, self.rank, self.n, src[0], src[1], src[2],
                                dst[0], dst[1], dst[2], self.gather[1 - self.cur], self.offset,
                                self.flags[0:1], self.hparams(), acc_in=acc_in,
                                grad_dtype=self.grad_dtype, param_dtype=self.param_dtype,
-                               wire_dtype=self.wire_dtype)
+                               wire_dtype=self.wire_dtype, state_layout=self.state_layout)
             if len(self._prepared) > 16:
                 self._prepared.clear()
             self._prepared[key] = args

@@ -15,10 +15,12 @@ from typing import Optional, Sequence
 
 from . import build as _build
 
-ZS_ABI_VERSION = 6
+ZS_ABI_VERSION = 7
 ZS_MAX_WORLD = 64
 ZS_BF16, ZS_FP16 = 0, 1
 ZS_WIRE_FP32, ZS_WIRE_BF16, ZS_WIRE_FP16 = 0, 1, 2
+ZS_STATE_SPLIT, ZS_STATE_GROUPED = 0, 1
+ZS_STATE_GROUP = 1024
 ZS_OK, ZS_ERR_INVALID_ARG, ZS_ERR_UNSUPPORTED, ZS_ERR_ALIAS, ZS_ERR_HIP = range(5)
 
 LIB_PATH = _build.LIB
@@ -45,7 +47,13 @@ class zs_step_args(C.Structure):
                 ("master_out", C.c_void_p), ("m_out", C.c_void_p), ("v_out", C.c_void_p),
                 ("gather_buf", C.c_void_p), ("gather_offset", C.c_uint64),
                 ("overflow_flag", C.c_void_p),
-                ("hp", zs_adamw_hparams), ("wire_dtype", C.c_int32)]
+                ("hp", zs_adamw_hparams), ("wire_dtype", C.c_int32),
+                ("state_layout", C.c_int32)]
+
+
+def grouped_len(n):
+    """Floats in a grouped state buffer for n elements (whole groups)."""
+    return -(-n // ZS_STATE_GROUP) * 3 * ZS_STATE_GROUP
 
 
 class zs_loss_scaler(C.Structure):
@@ -238,7 +246,9 @@ class StepArgs:
     def __init__(self, worker_grads, rank, n, master_in, m_in, v_in, master_out, m_out, v_out,
                  gather_buf, gather_offset, overflow_flag, hp: zs_adamw_hparams,
                  acc_in=None, grad_dtype=None, param_dtype=None, gather_in=None,
-                 wire_dtype=ZS_WIRE_FP32):
+                 wire_dtype=ZS_WIRE_FP32, state_layout=ZS_STATE_SPLIT):
+        """state_layout ZS_STATE_GROUPED: master_in / master_out are grouped
+        state buffers (grouped_len(n) floats); m_in, v_in, m_out, v_out None."""
         world = len(worker_grads)
         self._grads = _grad_array(worker_grads, n)
         a = zs_step_args()
@@ -247,10 +257,12 @@ class StepArgs:
         a.param_dtype = _dtype_code(gather_buf, param_dtype)
         a.worker_grads = C.cast(self._grads, C.POINTER(C.c_void_p))
         a.acc_in = _ptr(acc_in, n, 4, "acc_in")
-        a.master_in, a.m_in, a.v_in = (_ptr(master_in, n, 4, "master_in"), _ptr(m_in, n, 4, "m_in"),
+        ns = grouped_len(n) if state_layout == ZS_STATE_GROUPED else n
+        a.master_in, a.m_in, a.v_in = (_ptr(master_in, ns, 4, "master_in"), _ptr(m_in, n, 4, "m_in"),
                                        _ptr(v_in, n, 4, "v_in"))
-        a.master_out, a.m_out, a.v_out = (_ptr(master_out, n, 4, "master_out"),
+        a.master_out, a.m_out, a.v_out = (_ptr(master_out, ns, 4, "master_out"),
                                           _ptr(m_out, n, 4, "m_out"), _ptr(v_out, n, 4, "v_out"))
+        a.state_layout = state_layout
         a.gather_buf = _ptr(gather_buf, n, 2, "gather_buf", gather_offset)
         # Optional second gather buffer: with one per set, a skipped step also
         # leaves the current set's 16-bit parameters untouched.

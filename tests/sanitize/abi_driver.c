@@ -7,11 +7,17 @@
  * the pointers below are never dereferenced.
  */
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "zeroshard.h"
+
+/* the layout the Python binding mirrors */
+_Static_assert(sizeof(zs_step_args) == 152, "zs_step_args size");
+_Static_assert(offsetof(zs_step_args, wire_dtype) == 140, "wire_dtype offset");
+_Static_assert(offsetof(zs_step_args, state_layout) == 144, "state_layout offset");
 
 #define CHECK(c)                                                   \
   do {                                                             \

@@ -38,7 +38,12 @@ def test_library_exports_every_declared_symbol(zs):
     lib = C.CDLL(zs.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 6
+    assert zs.zs_abi_version() == zs.ZS_ABI_VERSION == 7
+    # the binding's zs_step_args matches the header's layout (the C driver
+    # under tests/sanitize asserts the same size and offsets at compile time)
+    assert C.sizeof(zs.zs_step_args) == 152
+    assert zs.zs_step_args.wire_dtype.offset == 140
+    assert zs.zs_step_args.state_layout.offset == 144
 
 
 def test_status_strings(zs):
@@ -174,6 +179,36 @@ def test_fused_rejects_aliasing_and_bad_arguments(zs):
     a, keep = _fused_args(zs, n=0)
     assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_OK
     assert lib.zs_step_fused(None, None) == zs.ZS_ERR_INVALID_ARG
+
+
+def test_fused_grouped_layout_rules(zs):
+    """The grouped state layout: m and v pointers must be NULL, the layout
+    code must be known, the state buffers overlap by their grouped size
+    (whole groups of 1024 elements, 12 KB each), and every operand must be
+    aligned for 4-element vectors; all refused before anything runs."""
+    lib = _raw(zs)
+    base = FAKE + 0x1000000
+    G = dict(state_layout=zs.ZS_STATE_GROUPED, m_in=None, v_in=None, m_out=None, v_out=None)
+    for field, val in (("m_in", base + 0x100000), ("v_out", base + 0x500000)):
+        a, keep = _fused_args(zs, **{**G, field: val})
+        assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_INVALID_ARG, field
+    a, keep = _fused_args(zs, state_layout=2)
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_INVALID_ARG
+    a, keep = _fused_args(zs)  # split with a NULL m_in is still refused
+    a.m_in = None
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_INVALID_ARG
+    # n = 1000: one group, 12288 bytes; 8 KB past master_in overlaps it
+    # (split arrays of 4000 bytes would not)
+    a, keep = _fused_args(zs, **G, master_out=base + 0x2000)
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS
+    a, keep = _fused_args(zs, **G, master_out=base + 0x300000, gather_buf=base + 0x2f00)
+    assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_ALIAS
+    for field, addr in (("master_in", base + 4), ("master_out", base + 0x300008),
+                        ("gather_buf", base + 0x600002)):
+        a, keep = _fused_args(zs, **{**G, field: addr})
+        assert lib.zs_step_fused(C.byref(a), None) == zs.ZS_ERR_UNSUPPORTED, field
+    assert zs.grouped_len(1) == 3072 and zs.grouped_len(1024) == 3072
+    assert zs.grouped_len(1025) == 6144 and zs.grouped_len(0) == 0
 
 
 def test_step_commit_rejects_bad_arguments(zs):

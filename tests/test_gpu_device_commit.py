@@ -37,14 +37,14 @@ def _make(env, wl, device_commit, **kw):
     st = shard.ShardState(n, wl.world, 0, 0, n, wl.param_dtype, wl.grad_dtype, opt,
                           kw.pop("loss_scale", wl.loss_scale), accumulate=wl.accum > 1,
                           device_commit=device_commit, **kw)
-    synth.dev_state(wl, 0, st.master, st.m, st.v)
+    st.fill_state(lambda first, count, *t: synth.dev_state(wl, first, *t))
     grads = torch.empty((wl.world, -(-n // 128) * 128), dtype=torch.int16, device="cuda")
     return st, [grads[k, :n] for k in range(wl.world)]
 
 
 def _same_state(a, b, what):
-    for x, y, name in ((a.master, b.master, "master"), (a.m, b.m, "m"), (a.v, b.v, "v")):
-        assert_bits_equal(down32(x), down32(y), f"{what} {name}")
+    for k, name in enumerate(("master", "m", "v")):
+        assert_bits_equal(down32(a.state(k)), down32(b.state(k)), f"{what} {name}")
     assert np.array_equal(down16(a.params.view(torch.int16)), down16(b.params.view(torch.int16))), \
         f"{what} params"
 
@@ -75,6 +75,40 @@ def test_queued_device_steps_equal_host_commit(env, wire):
     assert (d.epoch, d.flag_epoch, d.checked_epoch) == (6, 3, 5)
     assert d.scale == wl.loss_scale
     _same_state(host, dev, "queued")
+
+
+@pytest.mark.parametrize("device_commit", [False, True])
+def test_grouped_state_equals_split(env, device_commit):
+    """Six steps over a shard whose length is not a multiple of the group
+    (the third skipped for an injected inf/NaN) with the grouped state
+    layout equal the split layout bit for bit: the state, the parameters
+    and the scaler, through both commit flows, and state_dict round trips."""
+    zs, synth, shard = env
+    wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=8 * 250_003, steps=6,
+                             inject_steps=(3,), inject_rate=1e-3, name="grouped")
+    split, gs = _make(env, wl, device_commit)
+    grouped, gg = _make(env, wl, device_commit, state_layout="grouped")
+    announce(f"grouped vs split state, device commit {device_commit}")
+    _same_state(split, grouped, "initial")
+    for step in range(1, wl.steps + 1):
+        for k in range(wl.world):
+            synth.dev_grad(wl, k, step, 0, 0, gs[k], scale=wl.loss_scale)
+            synth.dev_grad(wl, k, step, 0, 0, gg[k], scale=wl.loss_scale)
+        if device_commit:
+            split.step_device(gs)
+            grouped.step_device(gg)
+        else:
+            assert split.step(gs) == grouped.step(gg)
+    if device_commit:
+        a, b = split.sync_scaler(), grouped.sync_scaler()
+        assert (a.step_t, a.skipped, a.scale) == (b.step_t, b.skipped, b.scale) == \
+            (5, 1, wl.loss_scale)
+    _same_state(split, grouped, "after six steps")
+    sd = grouped.state_dict()
+    for k, key in enumerate(("master", "m", "v")):
+        assert_bits_equal(sd[key].numpy(), down32(split.state(k)), f"state_dict {key}")
+    grouped.load_state_dict(split.state_dict())
+    _same_state(split, grouped, "after load_state_dict")
 
 
 def test_skip_restores_state_and_params(env):

@@ -252,6 +252,98 @@ def test_step_fused(zs, world, gdt, pdt):
         assert assert_ulp16(g[off:off + n], rp, pdt, 1, "params") == 0
 
 
+SENTINEL = np.uint32(0x7FC0DEAD).view(F32)  # a NaN no arithmetic produces
+
+
+def _grouped(arrs, n):
+    """master, m, v (n floats each) in the grouped state layout, the slots
+    past n in the last group holding SENTINEL."""
+    G = -(-n // 1024)
+    buf = np.full((G, 3, 1024), SENTINEL, dtype=F32)
+    for k, x in enumerate(arrs):
+        flat = np.full(G * 1024, SENTINEL, dtype=F32)
+        flat[:n] = x
+        buf[:, k, :] = flat.reshape(G, 1024)
+    return buf.ravel()
+
+
+def _ungrouped(buf, n):
+    b = buf.reshape(-1, 3, 1024)
+    return [b[:, k, :].ravel()[:n] for k in range(3)], [b[:, k, :].ravel()[n:] for k in range(3)]
+
+
+def _fused_case_grouped(zs, rng, world, rank, n, gdt, pdt, with_acc, scale=1024.0, t=3,
+                        inject=None):
+    g16 = [rand16(rng, n, 1e-3 * scale, gdt) for _ in range(world)]
+    if inject is not None:
+        w, pos, val = inject
+        g16[w][pos] = val
+    master = (rng.standard_normal(n) * 0.02).astype(F32)
+    m = (rng.standard_normal(n) * 1e-4).astype(F32)
+    v = rng.uniform(0, 1e-6, n).astype(F32)
+    acc = (rng.standard_normal(n) * scale * 1e-3).astype(F32) if with_acc else None
+    dg = [up16(g, gdt) for g in g16]
+    gin = up32(_grouped((master, m, v), n))
+    gout = up32(np.full(zs.grouped_len(n), SENTINEL, dtype=F32))
+    gather = torch.full((n + 8,), 7, dtype=torch.int16, device="cuda")
+    flag = _flag()
+    hp = zs.hparams(**HP, loss_scale=scale, step_t=t)
+    args = zs.StepArgs(dg, rank, n, gin, None, None, gout, None, None, gather, 0, flag, hp,
+                       acc_in=up32(acc) if with_acc else None, grad_dtype=DT[gdt],
+                       param_dtype=DT[pdt], state_layout=zs.ZS_STATE_GROUPED)
+    zs.zs_step_fused(args)
+    ref = oracle.shard_step(g16, rank, gdt, pdt, master, m, v, step_t=t, acc_in=acc,
+                            loss_scale=scale, threads=4, **HP)
+    return dict(flag=int(flag.item()), gout=down32(gout), gin=down32(gin), gather=down16(gather),
+                ins=(master, m, v), ref=ref, n=n)
+
+
+@pytest.mark.parametrize("world", [1, 3, 8, 17, 64])
+@pytest.mark.parametrize("gdt,pdt", [("bf16", "bf16"), ("fp16", "fp16"), ("bf16", "fp16")])
+def test_step_fused_grouped_state(zs, world, gdt, pdt):
+    """The grouped state layout writes the oracle's state and parameters bit
+    for bit, ragged shards and accumulated micro-batches included, and
+    leaves the slots past n of its last group alone."""
+    rng = np.random.default_rng(7 + world + 100 * DT[gdt] + 10 * DT[pdt])
+    for n, with_acc, rank in ((20_011, False, 0), (5003, True, world - 1), (777, False, world // 2),
+                              (8, True, 0), (3 * 1024 + 5, False, 0), (4096, True, 0)):
+        announce(f"fused grouped W={world} {gdt}/{pdt} n={n} acc={with_acc} rank={rank}")
+        r = _fused_case_grouped(zs, rng, world, rank, n, gdt, pdt, with_acc)
+        rflag, rm, rmm, rv, rp = r["ref"]
+        assert r["flag"] == rflag == 0
+        got, tails = _ungrouped(r["gout"], n)
+        for g, want, what in zip(got, (rm, rmm, rv), ("master", "m", "v")):
+            assert assert_rel(g, want, 1e-6, what) == 0
+        for tail in tails:
+            assert_bits_equal(tail, np.full(tail.size, SENTINEL, dtype=F32), "slots past n")
+        g = r["gather"]
+        assert np.all(g[n:] == 7)
+        assert assert_ulp16(g[:n], rp, pdt, 1, "params") == 0
+
+
+def test_step_fused_grouped_skip_and_alignment(zs):
+    """A skipped grouped step leaves the input buffer as it was; a grouped
+    step whose gather slice is not aligned for 4-element vectors is refused."""
+    rng = np.random.default_rng(11)
+    n = 9000
+    announce("fused grouped skip")
+    r = _fused_case_grouped(zs, rng, 4, 1, n, "fp16", "fp16", True, scale=65536.0,
+                            inject=(2, 4321, 0x7E00))
+    assert r["flag"] == r["ref"][0] == 1
+    assert_bits_equal(r["gin"], _grouped(r["ins"], n), "input set after a skipped step")
+    g16 = [rand16(rng, 64, 1.0, "bf16") for _ in range(2)]
+    gin = up32(np.zeros(zs.grouped_len(64), F32))
+    gout = up32(np.zeros(zs.grouped_len(64), F32))
+    gather = torch.zeros(80, dtype=torch.int16, device="cuda")
+    args = zs.StepArgs([up16(g, "bf16") for g in g16], 0, 64, gin, None, None, gout, None, None,
+                       gather, 1, _flag(), zs.hparams(**HP, loss_scale=1.0, step_t=1),
+                       grad_dtype=DT["bf16"], param_dtype=DT["bf16"],
+                       state_layout=zs.ZS_STATE_GROUPED)
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_step_fused(args)
+    assert e.value.status == zs.ZS_ERR_UNSUPPORTED
+
+
 def test_step_fused_skip_leaves_the_input_set(zs):
     rng = np.random.default_rng(5)
     n = 9000

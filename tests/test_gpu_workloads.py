@@ -57,23 +57,25 @@ def _windows(n, count, seed, window=WINDOW, straddle=()):
     return [(s, window) for s in sorted(starts)]
 
 
-def run_workload(env, name, windows=None, gather_full=False, device_commit=False, wl=None):
+def run_workload(env, name, windows=None, gather_full=False, device_commit=False, wl=None,
+                 state_layout="split"):
     """device_commit: steps through zs_step_device (commit or skip decided on
     the device); the host reads the device scaler back after each step only
-    to check it and to scale the next step's synthetic gradients."""
+    to check it and to scale the next step's synthetic gradients.
+    state_layout: ShardState's fp32 state layout ("split" or "grouped")."""
     zs, synth, shard = env
     wl = wl if wl is not None else synth.WORKLOADS[name]
     n, off, W, A = wl.n, wl.offset, wl.world, wl.accum
     wins = windows if windows is not None else [(0, n)]
     announce(f"workload {name}: n={n} W={W} A={A} steps={wl.steps} windows={len(wins)} "
-             f"device_commit={device_commit}")
+             f"device_commit={device_commit} state={state_layout}")
     st = shard.ShardState(n, W, wl.rank, off, (W * wl.chunk) if gather_full else off + n,
                           wl.param_dtype, wl.grad_dtype,
                           shard.AdamW(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay),
                           wl.loss_scale, dynamic=wl.dynamic_scale,
                           growth_interval=wl.scale_interval, accumulate=A > 1,
-                          device_commit=device_commit)
-    synth.dev_state(wl, off, st.master, st.m, st.v)
+                          device_commit=device_commit, state_layout=state_layout)
+    st.fill_state(lambda first, count, *t: synth.dev_state(wl, off + first, *t))
     # one row per worker, padded to 256 B like separate allocations
     row = -(-n // 128) * 128
     grads = torch.empty((W, row), dtype=torch.int16, device="cuda")
@@ -123,9 +125,8 @@ def run_workload(env, name, windows=None, gather_full=False, device_commit=False
                 # compare the current set (committed or kept) with the oracle's
                 nonbit = 0
                 for i, (s, L) in enumerate(wins):
-                    for got, want, what in ((st.master, hs[i][0], "master"),
-                                            (st.m, hs[i][1], "m"), (st.v, hs[i][2], "v")):
-                        nonbit += assert_rel(down32(got[s:s + L]), want, 1e-6,
+                    for k, what in enumerate(("master", "m", "v")):
+                        nonbit += assert_rel(down32(st.state(k, s, L)), hs[i][k], 1e-6,
                                              f"{name} step {step} {what} window {s}")
                     if rflag == 0:
                         nonbit += assert_ulp16(down16(st.params[s:s + L].view(torch.int16)),
@@ -164,6 +165,18 @@ def test_mlp9_w3_last_rank_full(env):
 
 def test_gpt2s_w8_full(env):
     run_workload(env, "gpt2s-w8")
+
+
+@pytest.mark.parametrize("device_commit", [False, True])
+def test_gpt2s_w8_full_grouped_state(env, device_commit):
+    run_workload(env, "gpt2s-w8", device_commit=device_commit, state_layout="grouped")
+
+
+def test_1p3b_w4_acc4_windows_grouped_state(env):
+    zs, synth, shard = env
+    wl = synth.WORKLOADS["1p3b-w4-acc4-fp16"]
+    run_workload(env, wl.name, windows=_windows(wl.n, 6, 4, WINDOW_1P3B), state_layout="grouped")
+    torch.cuda.empty_cache()
 
 
 # One shard per branch of the fused kernel's launch rule (block size,
@@ -205,6 +218,23 @@ def test_7b_full_w1_windows(env, device_commit):
     for b in BOUNDARIES_7B:
         assert any(s < b < s + L for s, L in wins), b
     run_workload(env, wl.name, windows=wins, device_commit=device_commit)
+
+
+def test_7p5b_shard_w64_windows_grouped_state(env):
+    zs, synth, shard = env
+    wl = synth.WORKLOADS["7p5b-shard-w64"]
+    torch.cuda.empty_cache()
+    run_workload(env, wl.name, windows=_windows(wl.n, 8, 5, WINDOW_7P5B), state_layout="grouped")
+    torch.cuda.empty_cache()
+
+
+def test_7b_full_w1_windows_grouped_state(env):
+    zs, synth, shard = env
+    wl = synth.WORKLOADS["7b-full-w1"]
+    torch.cuda.empty_cache()
+    wins = _windows(wl.n, 8, 6, WINDOW_7B, straddle=BOUNDARIES_7B)
+    run_workload(env, wl.name, windows=wins, device_commit=True, state_layout="grouped")
+    torch.cuda.empty_cache()
 
 
 FLAG_CHUNK = 1 << 28

@@ -100,25 +100,39 @@ def test_every_variant_computes_the_step(vlib, zs, world):
     assert f == 0
     grads = [up16(g, "bf16") for g in g16]
     din = [up32(x) for x in (master, m, v)]
+    # grouped layout: [master | m | v] per 1024-element group
+    din_g = up32(np.stack([x.reshape(-1, 1024) for x in (master, m, v)], axis=1).ravel())
     for vid in range(vlib.zs_variant_count()):
         if vlib.zs_variant_multi(vid) != (1 if world > 1 else 0):
             continue
-        if "phased" in vlib.zs_variant_name(vid).decode():
+        name_v = vlib.zs_variant_name(vid).decode()
+        if "phased" in name_v:
             continue  # test_phased_variants_walk_several_chunks
+        grouped = "grouped state" in name_v
         for cap in (0, 2, 5):
-            dout = [torch.full((n,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+            if grouped:
+                dout_g = torch.full((3 * n,), 7.0, dtype=torch.float32, device="cuda")
+                ins, outs = [din_g] * 3, [dout_g] * 3
+            else:
+                outs = [torch.full((n,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+                ins = din
             par = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
             flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-            args = zs.StepArgs(grads, 0, n, *din, *dout, par, 0, flag,
+            args = zs.StepArgs(grads, 0, n, *ins, *outs, par, 0, flag,
                                zs.hparams(**hp, loss_scale=1.0, step_t=3))
             rc = vlib.zs_variant_launch(vid, C.addressof(args.args), cap, 2,
                                         torch.cuda.current_stream().cuda_stream)
             assert rc == 0, vlib.zs_variant_last_error().decode()
             torch.cuda.synchronize()
-            what = f"variant {vid} ({vlib.zs_variant_name(vid).decode()}) cap {cap}"
+            what = f"variant {vid} ({name_v}) cap {cap}"
             assert int(flag.item()) == 0, what
-            for got, want, name in zip(dout, (mo, mmo, vo), ("master", "m", "v")):
-                assert_bits_equal(down32(got), want, f"{what} {name}")
+            if grouped:
+                g3 = down32(dout_g).reshape(-1, 3, 1024)
+                got3 = [g3[:, k, :].ravel() for k in range(3)]
+            else:
+                got3 = [down32(x) for x in outs]
+            for got, want, name in zip(got3, (mo, mmo, vo), ("master", "m", "v")):
+                assert_bits_equal(got, want, f"{what} {name}")
             assert np.array_equal(down16(par), po), what
 
 
