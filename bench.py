@@ -106,11 +106,18 @@ def fused_shape(world, n, state_layout="split"):
     workers: 4-element vectors, non-temporal state loads and stores.
     Split state: one-wave blocks at W = 2 and from W = 17 on, 256-thread
     blocks otherwise, the tile depth and cap following W and, for W = 3 to
-    16, the shard's size. Grouped state: one-wave blocks throughout, one
-    vector per thread up to W = 3, two beyond, 16 blocks per CU up to
-    W = 16 and 12 beyond."""
+    16, the shard's size. Grouped state: one-wave blocks throughout; one
+    vector per thread at 12 blocks per CU for W = 1 and 16 for W = 2, 3;
+    two from W = 4 on: the batched sum at 12 per CU for W = 4, the rolling
+    sum (shape 6) at 8 per CU up to W = 12 and 6 beyond."""
     if state_layout == "grouped":
-        return (64, 1, 5, 16) if world <= 3 else (64, 2, 5, 16 if world <= 16 else 12)
+        if world == 1:
+            return 64, 1, 5, 12
+        if world <= 3:
+            return 64, 1, 5, 16
+        if world == 4:
+            return 64, 2, 5, 12
+        return 64, 2, 6, 8 if world <= 12 else 6
     if world == 1:
         return 256, 2, 5, 2
     if world == 2:

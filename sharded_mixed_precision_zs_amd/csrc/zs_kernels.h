@@ -58,12 +58,19 @@ constexpr int kShapeB8 = 0, kShapeB16 = 1, kShapeB16Nt = 2, kShapeB8Nt = 3;
  * gradients (+1 to 1.8 % at W = 1 and W = 8 against plain state loads,
  * neutral at W = 64) */
 constexpr int kShapeB16NtL = 4, kShapeB8NtL = 5;
+/* kShapeR4NtL: the rolling sum (ring_sum_roll): four workers' loads ahead
+ * of the adds at all times, each refilled as soon as its worker is added,
+ * with the fp32 state loaded while the last workers are in flight;
+ * non-temporal loads and stores as kShapeB8NtL. */
+constexpr int kShapeR4NtL = 6;
 
 constexpr int shape_batch(int shape) {
-  return shape == kShapeB8 || shape == kShapeB8Nt || shape == kShapeB8NtL ? kLoadBatch : 16;
+  return shape == kShapeR4NtL ? 4
+         : shape == kShapeB8 || shape == kShapeB8Nt || shape == kShapeB8NtL ? kLoadBatch : 16;
 }
 constexpr bool shape_nt_stores(int shape) { return shape >= kShapeB16Nt; }
 constexpr bool shape_nt_loads(int shape) { return shape >= kShapeB16NtL; }
+constexpr bool shape_rolling(int shape) { return shape == kShapeR4NtL; }
 
 /* ------------------------------------------------------------------------
  * Per-element arithmetic. Each line is written exactly in the order the
@@ -401,6 +408,96 @@ __device__ __forceinline__ void ring_sum_uw(const GradPtrs &g, uint32_t world,
     for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], ld16<VEC, true>(g.p[j] + i0[u]));
 }
 
+/* The same ring-order sum as a rolling pipeline. ring_sum_uw issues a batch
+ * of B workers' loads, adds them, and only then issues the next batch, so
+ * each wave's loads drain to zero B times per W workers; here the loads of
+ * worker j + B are issued as soon as worker j has been added, so a wave
+ * keeps B * U loads in flight from its first worker to its last, and
+ * `before` (the fp32 state loads) is issued together with the last
+ * workers' loads instead of after the whole sum. The adds run in exactly
+ * ring_sum_uw's order. Only the last round is irregular: the R < B workers
+ * left after the last full refill are loaded with the state and added
+ * last; roll_dispatch picks the instance for R so that every load and wait
+ * count is fixed at compile time (the compiler's vector-memory wait counts
+ * then keep B * U - U loads outstanding at each add; with a run-time
+ * guard on the loads they would wait for everything). The scheduling
+ * barriers keep the compiler from hoisting the unpacking of a whole batch
+ * above the refill loads, which would drain the pipeline again. With
+ * W < B + 1 there is nothing to roll and the batched sum runs, followed by
+ * `before`. On MI355X, run at 6 to 8 one-wave blocks per CU (fewer bytes in
+ * flight per CU than the batched sum at 12 to 16), it streamed the step 3 to
+ * 8 % faster at W = 5 and W = 16 to 64 (one-box interleaved timings). */
+template <int VEC, int U, int DT, int WIRE, int B, int R, typename F>
+__device__ __forceinline__ void roll_last(const GradPtrs &g, uint32_t j, const uint64_t (&i0)[U],
+                                          Raw16<VEC> (&r)[B][U], float (&s)[U][VEC],
+                                          F &before) {
+  Raw16<VEC> t[R > 0 ? R : 1][U];
+#pragma unroll
+  for (int b = 0; b < R; ++b)
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[b][u] = ld16<VEC, true>(g.p[j + B + b] + i0[u]);
+  before();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], r[b][u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], t[b][u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int VEC, int U, int DT, int WIRE, int B, int R, typename F>
+__device__ __forceinline__ void roll_dispatch(const GradPtrs &g, uint32_t j, const uint64_t (&i0)[U],
+                                              Raw16<VEC> (&r)[B][U], float (&s)[U][VEC],
+                                              F &before, uint32_t left) {
+  if constexpr (R == 0) {
+    roll_last<VEC, U, DT, WIRE, B, 0>(g, j, i0, r, s, before);
+  } else {
+    if (left == (uint32_t)R) roll_last<VEC, U, DT, WIRE, B, R>(g, j, i0, r, s, before);
+    else roll_dispatch<VEC, U, DT, WIRE, B, R - 1>(g, j, i0, r, s, before, left);
+  }
+}
+
+template <int VEC, int U, int DT, int WIRE, int B, typename F>
+__device__ __forceinline__ void ring_sum_roll(const GradPtrs &g, uint32_t world,
+                                              const uint64_t (&i0)[U], float (&s)[U][VEC],
+                                              F &before) {
+  if (world < (uint32_t)B + 1) {
+    ring_sum_uw<VEC, U, DT, WIRE, B>(g, world, i0, s);
+    before();
+    return;
+  }
+  Raw16<VEC> r0[U], r[B][U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) r0[u] = ld16<VEC, true>(g.p[0] + i0[u]);
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[b][u] = ld16<VEC, true>(g.p[1 + b] + i0[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) set_up<VEC, DT, WIRE>(s[u], r0[u]);
+  /* r holds workers j .. j + B - 1; refill while a whole next round exists */
+  uint32_t j = 1;
+  for (; j + 2 * B <= world; j += B) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) add_wire<VEC, DT, WIRE>(s[u], r[b][u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[b][u] = ld16<VEC, true>(g.p[j + B + b] + i0[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  /* j + B <= world < j + 2B: world - j - B workers (0 .. B - 1) remain */
+  roll_dispatch<VEC, U, DT, WIRE, B, B - 1>(g, j, i0, r, s, before, world - j - B);
+}
+
 /* Wave-level OR of the overflow flag: one vector atomic per wave that saw a
  * non-finite value, issued by its first such lane. */
 __device__ __forceinline__ void flag_or(uint32_t *flag, bool bad) {
@@ -648,7 +745,8 @@ __device__ __forceinline__ bool fused_vec(const FusedArgs &p, const Scales &sk, 
 
 /* One tile of U vectors per thread. MULTI (W > 1) loads the state after
  * the gradient sum: on MI355X that order streamed 5-10 % faster than
- * loading the state first, registers to spare or not. With a single worker
+ * loading the state first, registers to spare or not; the rolling shape
+ * issues the state loads with the last workers' loads. With a single worker
  * (W = 1) there is no sum, one gradient load, and the state loads go
  * first. SHAPE (kShape*) sets the sum's load batch and the store policy;
  * T is the block's thread count (vector u of thread t starts at
@@ -676,7 +774,9 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
       if constexpr (ACC) ldf_p<VEC, NTL>(p.acc_in + i0[u], acc[u]);
     }
   };
-  if constexpr (MULTI) {
+  if constexpr (MULTI && shape_rolling(SHAPE)) {
+    ring_sum_roll<VEC, U, GDT, WIRE, B>(p.g, p.world, i0, s, load_state);
+  } else if constexpr (MULTI) {
     ring_sum_uw<VEC, U, GDT, WIRE, B>(p.g, p.world, i0, s);
     load_state();
   } else {

@@ -105,10 +105,12 @@ def test_fused_instance_names_match_the_kernel_template():
     assert bench.fused_instance(W["7b-full-w1"], state_layout="grouped") == \
         "zs::fused_kernel<4, 1, false, false, 0, 0, 0, 5, 64, true>"
     assert bench.fused_instance(W["7p5b-shard-w64"], state_layout="grouped") == \
-        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5, 64, true>"
-    assert [bench.fused_shape(w, big, "grouped") for w in (1, 3, 4, 16, 17, 64)] == \
-        [(64, 1, 5, 16), (64, 1, 5, 16), (64, 2, 5, 16), (64, 2, 5, 16), (64, 2, 5, 12),
-         (64, 2, 5, 12)]
+        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 6, 64, true>"
+    assert bench.fused_instance(W["1p3b-w4-acc4-fp16"], state_layout="grouped") == \
+        "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5, 64, true>"
+    assert [bench.fused_shape(w, big, "grouped") for w in (1, 3, 4, 5, 12, 13, 64)] == \
+        [(64, 1, 5, 12), (64, 1, 5, 16), (64, 2, 5, 12), (64, 2, 6, 8), (64, 2, 6, 8),
+         (64, 2, 6, 6), (64, 2, 6, 6)]
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
     assert bench.fused_bytes_per_param(4, 4) == (24, 14)
 

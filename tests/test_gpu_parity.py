@@ -273,7 +273,7 @@ def _ungrouped(buf, n):
 
 
 def _fused_case_grouped(zs, rng, world, rank, n, gdt, pdt, with_acc, scale=1024.0, t=3,
-                        inject=None):
+                        inject=None, wire=None):
     g16 = [rand16(rng, n, 1e-3 * scale, gdt) for _ in range(world)]
     if inject is not None:
         w, pos, val = inject
@@ -290,15 +290,19 @@ def _fused_case_grouped(zs, rng, world, rank, n, gdt, pdt, with_acc, scale=1024.
     hp = zs.hparams(**HP, loss_scale=scale, step_t=t)
     args = zs.StepArgs(dg, rank, n, gin, None, None, gout, None, None, gather, 0, flag, hp,
                        acc_in=up32(acc) if with_acc else None, grad_dtype=DT[gdt],
-                       param_dtype=DT[pdt], state_layout=zs.ZS_STATE_GROUPED)
+                       param_dtype=DT[pdt], state_layout=zs.ZS_STATE_GROUPED,
+                       wire_dtype=WIRE[wire] if wire else 0)
     zs.zs_step_fused(args)
     ref = oracle.shard_step(g16, rank, gdt, pdt, master, m, v, step_t=t, acc_in=acc,
-                            loss_scale=scale, threads=4, **HP)
+                            loss_scale=scale, threads=4, wire=wire, **HP)
     return dict(flag=int(flag.item()), gout=down32(gout), gin=down32(gin), gather=down16(gather),
                 ins=(master, m, v), ref=ref, n=n)
 
 
-@pytest.mark.parametrize("world", [1, 3, 8, 17, 64])
+# W = 4 takes the batched sum; from W = 5 on the rolling sum, whose last
+# round holds (W - 1) mod 4 workers: 5, 9, 13, 17 -> 0; 6, 10 -> 1; 7 -> 2;
+# 8, 64 -> 3 (and 13 and 64 run at the 6-blocks-per-CU shape, 5 to 12 at 8)
+@pytest.mark.parametrize("world", [1, 3, 4, 5, 6, 7, 8, 10, 13, 17, 64])
 @pytest.mark.parametrize("gdt,pdt", [("bf16", "bf16"), ("fp16", "fp16"), ("bf16", "fp16")])
 def test_step_fused_grouped_state(zs, world, gdt, pdt):
     """The grouped state layout writes the oracle's state and parameters bit
@@ -319,6 +323,24 @@ def test_step_fused_grouped_state(zs, world, gdt, pdt):
         g = r["gather"]
         assert np.all(g[n:] == 7)
         assert assert_ulp16(g[:n], rp, pdt, 1, "params") == 0
+
+
+@pytest.mark.parametrize("world", [4, 6, 64])
+@pytest.mark.parametrize("wire", ["bf16", "fp16"])
+def test_step_fused_grouped_wire(zs, world, wire):
+    """The grouped layout with 16-bit partial sums on the ring equals the
+    oracle's ring with the same wire rounding."""
+    gdt = "bf16" if wire == "bf16" else "fp16"
+    rng = np.random.default_rng(31 + world + 7 * WIRE[wire])
+    for n, with_acc in ((12_345, False), (4097, True)):
+        announce(f"fused grouped wire={wire} W={world} n={n} acc={with_acc}")
+        r = _fused_case_grouped(zs, rng, world, 0, n, gdt, gdt, with_acc, t=2, wire=wire)
+        rflag, rm, rmm, rv, rp = r["ref"]
+        assert r["flag"] == rflag == 0
+        got, _ = _ungrouped(r["gout"], n)
+        for g, want, what in zip(got, (rm, rmm, rv), ("master", "m", "v")):
+            assert assert_rel(g, want, 1e-6, what) == 0
+        assert assert_ulp16(r["gather"][:n], rp, gdt, 1, "params") == 0
 
 
 def test_step_fused_grouped_skip_and_alignment(zs):
