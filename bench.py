@@ -30,8 +30,9 @@ the headline workload on this host's cores.
 
 Beside the headline: the step with its decision on the host (`host_commit`),
 with bf16 partial sums on the ring (`wire_bf16`, on the W = 64 shard), the
-ZeRO-Offload variant (`offload`), and a full ring all-gather of the 16-bit
-parameters over W replicas (`all_gather`).
+W = 64 shard with libzeroshard's write windows switched off
+(`write_windows_off`), the ZeRO-Offload variant (`offload`), and a full ring
+all-gather of the 16-bit parameters over W replicas (`all_gather`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--also NAME,...] [--no-cpu-baseline] [--no-ceilings] ...
@@ -51,6 +52,7 @@ PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E peak (vendor figure)
 DEFAULT_WORKLOAD = "7b-full-w1"  # the 7B model's full state on one rank, W = 1
 DEFAULT_ALSO = "7p5b-shard-w64,1p3b-w4-acc4-fp16,gpt2s-w8,mlp9-w3"
 WIRE_WORKLOAD = "7p5b-shard-w64"       # the bf16-wire leg: the most partial sums
+WINDOW_WORKLOAD = "7p5b-shard-w64"     # the same step timed without write windows
 HOST_LEG_WORKLOAD = "gpt2s-w8"         # the ZeRO-Offload leg (host memory bound)
 ALL_GATHER_WORKLOADS = ("1p3b-w4-acc4-fp16", "gpt2s-w8")
 KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_zs_amd", "csrc", "zs_kernels.h")
@@ -99,6 +101,30 @@ FUSED_MANY_TILES = 20000   # 2048-element tiles
 STATE_LAYOUT = "grouped"
 
 
+# write windows of the grouped rolling shape (libzeroshard's policy):
+# W >= 40 and at least 8 GB of model bytes per launch, a 30.72 us period
+# with its last eighth open for stores; ZS_FUSED_WRITE_WINDOW overrides it
+WINDOW_WORLD, WINDOW_BYTES = 40, 8e9
+WINDOW_PERIOD_US, WINDOW_OPEN = 30.72, 0.125
+
+
+def write_window_of(world, n, accum=1, state_layout="grouped"):
+    """{period_us, open_fraction} of the write windows libzeroshard uses
+    for a shard of n parameters over `world` workers, or None."""
+    if state_layout != "grouped" or world < 5:
+        return None
+    env = os.environ.get("ZS_FUSED_WRITE_WINDOW", "")
+    if env == "off":
+        return None
+    if env:
+        period, frac = (float(x) for x in env.split(","))
+        return {"period_us": period, "open_fraction": frac}
+    rd, wr = fused_bytes_per_param(world, accum)
+    if world < WINDOW_WORLD or (rd + wr) * n < WINDOW_BYTES:
+        return None
+    return {"period_us": WINDOW_PERIOD_US, "open_fraction": WINDOW_OPEN}
+
+
 def fused_shape(world, n, state_layout="split"):
     """(threads per block, vectors per thread, zs::kShape* access shape,
     blocks per CU; 0 = no cap) of the fused kernel that zs_step_fused
@@ -109,7 +135,8 @@ def fused_shape(world, n, state_layout="split"):
     16, the shard's size. Grouped state: one-wave blocks throughout; one
     vector per thread at 12 blocks per CU for W = 1 and 16 for W = 2, 3;
     two from W = 4 on: the batched sum at 12 per CU for W = 4, the rolling
-    sum (shape 6) at 8 per CU up to W = 12 and 6 beyond."""
+    sum (shape 6) at 8 per CU up to W = 12 and 6 beyond, uncapped when the
+    launch takes write windows."""
     if state_layout == "grouped":
         if world == 1:
             return 64, 1, 5, 12
@@ -117,6 +144,8 @@ def fused_shape(world, n, state_layout="split"):
             return 64, 1, 5, 16
         if world == 4:
             return 64, 2, 5, 12
+        if write_window_of(world, n) is not None:
+            return 64, 2, 6, 0
         return 64, 2, 6, 8 if world <= 12 else 6
     if world == 1:
         return 256, 2, 5, 2
@@ -406,7 +435,7 @@ def run_workload(name, steps, warmup, torch, wire=0, device_commit=True, event_p
                accum=A, replicas=R, wire=wire, state_layout=layout, ms_per_step=ms_per_step,
                params_per_s=n / (ms_per_step * 1e-3), step_bytes=step_bytes,
                hbm_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9, committed=committed,
-               fused_bytes=fused_bytes)
+               fused_bytes=fused_bytes, write_window=write_window_of(W, n, A, layout))
     if event_pass:
         evs = timing_events(torch, steps)
         for i in range(steps):
@@ -890,12 +919,26 @@ def side_leg(name, fn, torch):
         return {"error": f"{type(e).__name__}: {e}"}
 
 
+def without_write_windows(fn):
+    """fn() with libzeroshard's write windows switched off."""
+    old = os.environ.get("ZS_FUSED_WRITE_WINDOW")
+    os.environ["ZS_FUSED_WRITE_WINDOW"] = "off"
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ["ZS_FUSED_WRITE_WINDOW"]
+        else:
+            os.environ["ZS_FUSED_WRITE_WINDOW"] = old
+
+
 def summary(res, wl, wire=0):
     """The record of one workload in the JSON line."""
     out = dict(workload=res["workload"], params_per_s=res["params_per_s"],
                ms_per_step=res["ms_per_step"], hbm_gbps=res["hbm_gbps"],
                hbm_pct_of_peak=100.0 * res["hbm_gbps"] / PEAK_HBM_GBPS,
-               replicas=res["replicas"], committed=res["committed"])
+               replicas=res["replicas"], committed=res["committed"],
+               write_window=res.get("write_window"))
     if "fused_gbps" in res:
         out["roofline"] = roofline_of(res, wl, wire)
     return out
@@ -1014,7 +1057,7 @@ def main():
         rec = summary(r, wl)
         others.append(rec)
         roofs[name] = rec["roofline"]
-    wire_bf16, all_gather = None, []
+    wire_bf16, all_gather, windows_off = None, [], None
     if not args.no_side_legs:
         if WIRE_WORKLOAD in synth.WORKLOADS:
             wl = synth.WORKLOADS[WIRE_WORKLOAD]
@@ -1022,6 +1065,19 @@ def main():
                          torch)
             log(json.dumps(r))
             wire_bf16 = r if "error" in r else summary(r, wl, wire=1)
+        if WINDOW_WORKLOAD in synth.WORKLOADS and roofs.get(WINDOW_WORKLOAD):
+            r = side_leg("write_windows_off", lambda: without_write_windows(
+                lambda: run_workload(WINDOW_WORKLOAD, K, 2, torch)), torch)
+            log(json.dumps(r))
+            if "error" not in r:
+                on = roofs[WINDOW_WORKLOAD]
+                windows_off = dict(workload=WINDOW_WORKLOAD, kernel_ms_on=on["kernel_ms"],
+                                   kernel_ms_off=r["fused_kernel_ms"],
+                                   gbps_on=on["achieved"], gbps_off=r["fused_gbps"],
+                                   speedup=r["fused_kernel_ms"] / on["kernel_ms"],
+                                   ms_per_step_off=r["ms_per_step"])
+            else:
+                windows_off = r
         for name in ALL_GATHER_WORKLOADS:
             r = side_leg(f"all_gather {name}", lambda: run_all_gather(name, 10, torch), torch)
             log(json.dumps(r))
@@ -1084,6 +1140,7 @@ def main():
                              fused_kernel_ms=host_res.get("fused_kernel_ms"))),
         "offload": offload,
         "wire_bf16": wire_bf16,
+        "write_windows_off": windows_off,
         "all_gather": all_gather,
     }
     print(json.dumps(out))

@@ -742,7 +742,7 @@ int zs_variant_launch(int id, const zs_step_args *a, uint32_t blocks_per_cu,
   const uint64_t tile = (uint64_t)v.tile;
   if (a->n == 0 || a->n % tile != 0 || a->n / tile > 0x7fffffffull)
     return vfail("n must be a positive multiple of the variant's tile");
-  FusedArgs p;
+  FusedArgs p{};
   p.world = a->world;
   p.wire = ZS_WIRE_FP32;
   p.n = a->n;

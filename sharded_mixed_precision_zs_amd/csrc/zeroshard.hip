@@ -205,6 +205,67 @@ FusedShape fused_shape_grouped(uint32_t world) {
   return {kFusedWaveBlock, 2, kShapeR4NtL, world <= 12 ? 8 : 6};
 }
 
+/* ------------------------------------------------------------------------
+ * Write windows (await_write_window in zs_kernels.h) for the rolling shape
+ * at W >= 40 on launches of at least 8 GB of model bytes: a period of
+ * 30.72 us with the last eighth open for stores, and no cap on blocks per
+ * CU (the registers allow 20 one-wave blocks), since waves that wait for
+ * the window still hold their slots. The launch ends up to about one
+ * period after its last loads, hence the size floor. Interleaved on one
+ * GPU against the same kernel without windows at its own best cap (6),
+ * bits equal: W = 64 (117 M parameters) 2.70-2.75 ms against 2.98-2.99
+ * (+8 to +10 %, three boxes; periods of 25.6-40.96 us with windows of 1/8
+ * to 3/16 within 1 %), W = 48 +6.5 %; W = 32 even, W = 24 and W = 16 slower
+ * (shorter tiles leave too few tiles per period in each slot), W = 1 slower
+ * at every period tried (half its bytes are writes).
+ * ZS_FUSED_WRITE_WINDOW overrides this, for measurements and tests: "off",
+ * or "<period in us>,<open fraction>" for every rolling-shape launch.
+ * ---------------------------------------------------------------------- */
+constexpr uint32_t kWindowWorld = 40;
+constexpr double kWindowBytes = 8e9;
+constexpr double kWindowPeriodUs = 30.72, kWindowOpen = 0.125;
+
+struct WriteWindow {
+  uint32_t period = 0, open_at = 0;  /* wall-clock ticks; period 0: none */
+};
+
+/* Wall-clock ticks per microsecond of the current device, 0 if unknown. */
+double wall_ticks_per_us() {
+  static thread_local int cached_dev = -1;
+  static thread_local double cached = 0.0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0.0;
+  if (dev != cached_dev) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) khz = 0;
+    cached = khz > 0 ? khz / 1000.0 : 0.0;
+    cached_dev = dev;
+  }
+  return cached;
+}
+
+WriteWindow write_window(const FusedShape &fs, uint32_t world, uint64_t n, bool acc) {
+  WriteWindow w;
+  if (fs.access != kShapeR4NtL) return w;
+  double period_us = kWindowPeriodUs, open = kWindowOpen;
+  const char *e = getenv("ZS_FUSED_WRITE_WINDOW");
+  if (e && *e) {
+    if (!strcmp(e, "off")) return w;
+    if (sscanf(e, "%lf,%lf", &period_us, &open) != 2 || !(period_us > 0.0) || !(open > 0.0) ||
+        !(open < 1.0))
+      return w;
+  } else {
+    const double bytes = (double)n * (2.0 * world + 26.0 + (acc ? 4.0 : 0.0));
+    if (world < kWindowWorld || bytes < kWindowBytes) return w;
+  }
+  const double ticks = wall_ticks_per_us() * period_us;
+  if (!(ticks >= 8.0 && ticks < 4.0e9)) return w;
+  w.period = (uint32_t)ticks;
+  const uint32_t win = (uint32_t)(w.period * open);
+  w.open_at = w.period - (win > 0 ? win : 1);
+  return w;
+}
+
 /* Bytes of a grouped state buffer for n elements: whole groups. */
 uint64_t grouped_state_bytes(uint64_t n) {
   return (n + ZS_STATE_GROUP - 1) / ZS_STATE_GROUP * (uint64_t)(3 * ZS_STATE_GROUP * 4);
@@ -605,7 +666,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   if (!valid_wire(a->wire_dtype)) return fail(ZS_ERR_INVALID_ARG, "bad wire dtype%s");
   if (too_big(a->n) || too_big(a->gather_offset))
     return fail(ZS_ERR_UNSUPPORTED, "n or gather_offset exceeds 2^48 elements%s");
-  FusedArgs p;
+  FusedArgs p{};
   p.wire = a->wire_dtype;
   zs_adamw_hparams hp = a->hp;
   if (dev) {
@@ -683,7 +744,11 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
   if (grouped && vec != 4)
     return fail(ZS_ERR_UNSUPPORTED,
                 "grouped state needs operands aligned for 4-element vectors%s");
-  const FusedShape fs = grouped ? fused_shape_grouped(a->world) : fused_shape(vec, a->world, n);
+  FusedShape fs = grouped ? fused_shape_grouped(a->world) : fused_shape(vec, a->world, n);
+  const WriteWindow win = write_window(fs, a->world, n, acc);
+  p.win_period = win.period;
+  p.win_open = win.open_at;
+  if (win.period) fs.cap = 0;
   const int per_thread = vec * fs.tile_vecs;
   if (!tiled_ok(n, per_thread, fs.threads))
     return fail(ZS_ERR_UNSUPPORTED, "n too large for one launch%s");

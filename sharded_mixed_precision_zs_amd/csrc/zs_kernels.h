@@ -685,7 +685,27 @@ struct FusedArgs {
   AdamK h;
   zs_device_scaler *dev;  /* non-null: scale, bias corrections and epoch come from it */
   double lr;              /* for the bias correction formed on the device */
+  /* write windows (rolling shape only; win_period 0: none): a wave stores
+   * only while wall_clock64() % win_period >= win_open */
+  uint32_t win_period, win_open;
 };
+
+/* Chip-wide write windows. Every wave of a launch reads the same
+ * constant-rate wall clock (wall_clock64(), hipDeviceAttributeWallClockRate
+ * ticks per second), so "the clock modulo a period lies in its last
+ * window" is a time slot that all CUs agree on without communicating. A
+ * wave that has its results waits for that slot before it stores, so the
+ * memory sees mostly reads for the rest of each period and the writes of
+ * the whole chip together in the window, instead of a thin stream of
+ * writes mixed into the reads at all times (on MI355X those mixed writes
+ * cost about three times their own bytes' time). Loads are never held.
+ * The wait ends within one period; a wave that reaches the window while it
+ * is open stores at once. Timing only: what is stored does not change. */
+__device__ __forceinline__ void await_write_window(uint32_t period, uint32_t open_at) {
+  __builtin_amdgcn_sched_barrier(0);
+  while ((uint32_t)((uint64_t)wall_clock64() % period) < open_at) __builtin_amdgcn_s_sleep(2);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 /* Grouped state layout: for each group of kGroup elements the master
  * weights, m and v are stored as three consecutive runs of kGroup floats,
@@ -784,6 +804,13 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
     ring_sum_uw<VEC, U, GDT, WIRE, B>(p.g, 1, i0, s);  /* one worker: no loop runs */
   }
   bool bad = false;
+  auto store = [&](int u) {
+    const StateAt<GR> at(i0[u]);
+    stf_p<VEC, NTS>(p.master_out + at.th, th[u]);
+    stf_p<VEC, NTS>(m_out + at.m, m[u]);
+    stf_p<VEC, NTS>(v_out + at.v, v[u]);
+    st16_p<VEC, PDT, NTS>(p.param_out + i0[u], th[u]);
+  };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -794,11 +821,12 @@ __device__ __forceinline__ bool fused_tile(const FusedArgs &p, const Scales &sk,
       bad |= !__builtin_isfinite(g);
       th[u][e] = adamw_elem(th[u][e], m[u][e], v[u][e], g, h);
     }
-    const StateAt<GR> at(i0[u]);
-    stf_p<VEC, NTS>(p.master_out + at.th, th[u]);
-    stf_p<VEC, NTS>(m_out + at.m, m[u]);
-    stf_p<VEC, NTS>(v_out + at.v, v[u]);
-    st16_p<VEC, PDT, NTS>(p.param_out + i0[u], th[u]);
+    if constexpr (!shape_rolling(SHAPE)) store(u);
+  }
+  if constexpr (shape_rolling(SHAPE)) {
+    if (p.win_period) await_write_window(p.win_period, p.win_open);
+#pragma unroll
+    for (int u = 0; u < U; ++u) store(u);
   }
   return bad;
 }

@@ -77,13 +77,18 @@ def test_queued_device_steps_equal_host_commit(env, wire):
     _same_state(host, dev, "queued")
 
 
+@pytest.mark.parametrize("windows", [None, "2.56,0.25"])
 @pytest.mark.parametrize("device_commit", [False, True])
-def test_grouped_state_equals_split(env, device_commit):
+def test_grouped_state_equals_split(env, device_commit, windows, monkeypatch):
     """Six steps over a shard whose length is not a multiple of the group
     (the third skipped for an injected inf/NaN) with the grouped state
     layout equal the split layout bit for bit: the state, the parameters
-    and the scaler, through both commit flows, and state_dict round trips."""
+    and the scaler, through both commit flows, and state_dict round trips;
+    also with the grouped step's write windows forced on (a 2.56 us period
+    with a quarter open), which only delay its stores."""
     zs, synth, shard = env
+    if windows:
+        monkeypatch.setenv("ZS_FUSED_WRITE_WINDOW", windows)
     wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=8 * 250_003, steps=6,
                              inject_steps=(3,), inject_rate=1e-3, name="grouped")
     split, gs = _make(env, wl, device_commit)

@@ -343,6 +343,25 @@ def test_step_fused_grouped_wire(zs, world, wire):
         assert assert_ulp16(r["gather"][:n], rp, gdt, 1, "params") == 0
 
 
+@pytest.mark.parametrize("world", [5, 8, 64])
+def test_step_fused_grouped_write_windows(zs, world, monkeypatch):
+    """With write windows forced on (a 2.56 us period, a quarter of it
+    open, so that even a small shard's launch spans many periods) the
+    rolling grouped step still writes the oracle's state and parameters:
+    the windows only delay the stores."""
+    monkeypatch.setenv("ZS_FUSED_WRITE_WINDOW", "2.56,0.25")
+    rng = np.random.default_rng(57 + world)
+    for n, with_acc, gdt in ((200_003, False, "bf16"), (33_333, True, "fp16")):
+        announce(f"fused grouped write windows W={world} n={n} acc={with_acc}")
+        r = _fused_case_grouped(zs, rng, world, world - 1, n, gdt, gdt, with_acc)
+        rflag, rm, rmm, rv, rp = r["ref"]
+        assert r["flag"] == rflag == 0
+        got, _ = _ungrouped(r["gout"], n)
+        for g, want, what in zip(got, (rm, rmm, rv), ("master", "m", "v")):
+            assert assert_rel(g, want, 1e-6, what) == 0
+        assert assert_ulp16(r["gather"][:n], rp, gdt, 1, "params") == 0
+
+
 def test_step_fused_grouped_skip_and_alignment(zs):
     """A skipped grouped step leaves the input buffer as it was; a grouped
     step whose gather slice is not aligned for 4-element vectors is refused."""
