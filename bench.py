@@ -102,9 +102,9 @@ STATE_LAYOUT = "grouped"
 
 
 # write windows of the grouped rolling shape (libzeroshard's policy):
-# W >= 40 and at least 8 GB of model bytes per launch, a 30.72 us period
+# W >= 40 and at least 4 GB of model bytes per launch, a 30.72 us period
 # with its last eighth open for stores; ZS_FUSED_WRITE_WINDOW overrides it
-WINDOW_WORLD, WINDOW_BYTES = 40, 8e9
+WINDOW_WORLD, WINDOW_BYTES = 40, 4e9
 WINDOW_PERIOD_US, WINDOW_OPEN = 30.72, 0.125
 
 
@@ -844,6 +844,114 @@ def shape_sweep(torch, rounds=3):
     return out
 
 
+GROUPED_WORLDS = (1, 4, 5, 8, 16, 24, 32, 36, 40, 48, 64)
+GROUPED_N = 117_187_500
+# (W, n) cases of the grouped sweep: every W of GROUPED_WORLDS on the 7.5B
+# shard's size, then smaller W = 64 shards around the write windows' floor
+GROUPED_CASES = tuple((w, GROUPED_N) for w in GROUPED_WORLDS) + \
+    tuple((64, n) for n in (10_000_000, 20_000_000, 33_816_576))
+
+
+def grouped_plan(world):
+    """(label, environment) of each launch the grouped-layout sweep times at
+    `world` workers: libzeroshard's own launch first, then the same kernel
+    with its measurement overrides (every one computes the same bits)."""
+    plan = [("production", {})]
+    if world == 1:
+        return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (8, 16, 0)]
+    if world == 4:
+        return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (8, 16)]
+    off = {"ZS_FUSED_WRITE_WINDOW": "off"}
+    plan.append(("batched sum, cap %d (the earlier launch)" % (16 if world <= 16 else 12),
+                 {"ZS_FUSED_SUM": "batched", "ZS_FUSED_BLOCKS_PER_CU": "16" if world <= 16 else "12",
+                  **off}))
+    plan += [(f"rolling sum, cap {c}, no windows", {"ZS_FUSED_BLOCKS_PER_CU": str(c), **off})
+             for c in (4, 6, 8, 12)]
+    plan.append((f"rolling sum, uncapped, windows {WINDOW_PERIOD_US} us / {WINDOW_OPEN}",
+                 {"ZS_FUSED_BLOCKS_PER_CU": "0",
+                  "ZS_FUSED_WRITE_WINDOW": f"{WINDOW_PERIOD_US},{WINDOW_OPEN}"}))
+    return plan
+
+
+def grouped_sweep(torch, cases=GROUPED_CASES, rounds=3):
+    """libzeroshard's fused step with the grouped state for each (W, n) of
+    `cases`: its own launch against the same kernel under the
+    measurement overrides of grouped_plan (cap, batched sum, write windows),
+    each launch's output checked bit for bit against the production
+    launch's, timed interleaved over `rounds`. Random inputs (bf16
+    gradients N(0, 1e-3), master N(0, 0.02), m N(0, 1e-4), v |N(0, 1e-3)|)."""
+    from sharded_mixed_precision_zs_amd import zeroshard as zs
+
+    hp = zs.hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01,
+                    loss_scale=1.0, step_t=1)
+    saved = {k: os.environ.get(k) for k in ("ZS_FUSED_BLOCKS_PER_CU", "ZS_FUSED_SUM",
+                                            "ZS_FUSED_WRITE_WINDOW")}
+
+    def setenv(env):
+        for k in saved:
+            os.environ.pop(k, None)
+        os.environ.update(env)
+
+    out = []
+    try:
+        for W, n in cases:
+            g = torch.empty((W, pad_elems(n)), dtype=torch.int16, device="cuda")
+            for k in range(W):
+                g[k, :n].view(torch.bfloat16).copy_(
+                    torch.empty(n, dtype=torch.float32, device="cuda").normal_(0, 1e-3))
+            grads = [g[k, :n].view(torch.bfloat16) for k in range(W)]
+            L = zs.grouped_len(n)
+            sin = torch.empty(L, dtype=torch.float32, device="cuda").normal_(0, 0.02)
+            sv = sin.view(-1, 3, 1024)
+            sv[:, 1, :].mul_(5e-3)
+            sv[:, 2, :].abs_().mul_(0.05)
+            sout = torch.empty_like(sin)
+            gather = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+            flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+            args = zs.StepArgs(grads, 0, n, sin, None, None, sout, None, None, gather, 0, flag,
+                               hp, state_layout=zs.ZS_STATE_GROUPED)
+            plan = grouped_plan(W)
+            ref = None
+            for label, env in plan:
+                setenv(env)
+                sout.zero_()
+                zs.zs_step_fused(args)
+                torch.cuda.synchronize()
+                got = (sout.view(torch.int32).clone(), gather.view(torch.int16).clone())
+                if ref is None:
+                    ref = got
+                elif not (torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])):
+                    raise RuntimeError(f"W={W} {label}: bits differ from the production launch")
+            del ref, got
+            reps = max(4, min(50, int(2e10 / ((2 * W + 26) * n))))
+            times = {label: [] for label, _ in plan}
+            for _ in range(rounds):
+                for label, env in plan:
+                    setenv(env)
+                    times[label].append(_time_calls(torch, lambda: zs.zs_step_fused(args), reps))
+            rows = []
+            for label, _ in plan:
+                ms = sum(times[label]) / rounds
+                gbps = (2 * W + 26) * n / (ms * 1e-3) / 1e9
+                rows.append(dict(launch=label, ms=ms, ms_rounds=times[label], gbps=gbps,
+                                 frac_of_peak=gbps / PEAK_HBM_GBPS))
+                log(f"grouped W={W} n={n} {label}: {ms:.4f} ms ({gbps:.0f} GB/s)")
+            t, u, shape, cap = fused_shape(W, n, "grouped")
+            out.append(dict(world=W, n=n, reps=reps, rounds=rounds, results=rows,
+                            production={"threads_per_block": t, "vectors_per_thread": u,
+                                        "access_shape": shape, "blocks_per_cu": cap,
+                                        "write_window": write_window_of(W, n)}))
+            del g, grads, sin, sout, gather, args
+            torch.cuda.empty_cache()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return out
+
+
 def phase_sweep(torch, reps=10, rounds=2):
     """Reads and writes of the 7.5B shard's step separated in time, with the
     stream probe: per chunk of the shard, a read-only probe kernel (the 64
@@ -981,6 +1089,12 @@ def main():
                     help="time libzscopy's copy shapes (vectors per lane, non-temporal loads "
                          "and stores, block size, persistent grids, residency caps) over 4 GiB "
                          "and print that table as the JSON line instead")
+    ap.add_argument("--sweep-grouped", action="store_true",
+                    help="time libzeroshard's grouped-state fused step against its measurement "
+                         "overrides (caps, batched sum, write windows) over W = "
+                         + ", ".join(map(str, GROUPED_WORLDS)) + " on the 7.5B shard's size and "
+                         "three smaller W = 64 shards, and print that table as the JSON line "
+                         "instead")
     ap.add_argument("--sweep-shapes", action="store_true",
                     help="time the fused step's tile depths and residency caps against "
                          "libzeroshard's own launch over a grid of W and shard sizes and print "
@@ -1015,6 +1129,10 @@ def main():
     if args.sweep_copy:
         print(json.dumps({"metric": "plain copy, read + write GB/s by copy shape", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "copies": copy_shape_sweep(torch)}))
+        return
+    if args.sweep_grouped:
+        print(json.dumps({"metric": "grouped-state fused step by launch setting, ms per launch",
+                          "unit": "ms", "sweeps": grouped_sweep(torch)}))
         return
     if args.sweep_shapes:
         print(json.dumps({"metric": "fused step tile depth and residency by W and shard size, "

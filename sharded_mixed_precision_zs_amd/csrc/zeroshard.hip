@@ -130,7 +130,7 @@ using zs_host::make_scales;
  * adds. Operands aligned for 2- or 1-element vectors only keep
  * 256-thread blocks, U = 2 (1 when W = 1), plain stores and 2, 3 or no cap.
  * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..32 = that many blocks) overrides
- * the cap, for measurements.
+ * the cap, for measurements; it is read at every launch.
  * ---------------------------------------------------------------------- */
 
 struct DeviceLds {
@@ -153,14 +153,20 @@ DeviceLds device_lds() {
   return cached;
 }
 
+/* Read at every launch, so one process can time several settings. */
 int env_blocks_per_cu() {
-  static const int v = [] {
-    const char *s = getenv("ZS_FUSED_BLOCKS_PER_CU");
-    if (!s || !*s) return -1;
-    int x = atoi(s);
-    return x < 0 || x > 32 ? -1 : x;
-  }();
-  return v;
+  const char *s = getenv("ZS_FUSED_BLOCKS_PER_CU");
+  if (!s || !*s) return -1;
+  int x = atoi(s);
+  return x < 0 || x > 32 ? -1 : x;
+}
+
+/* ZS_FUSED_SUM=batched (measurements): the grouped layout's W >= 5 shape
+ * with the batched sum (kShapeB8NtL) in place of the rolling one; the cap
+ * stays the rolling shape's unless ZS_FUSED_BLOCKS_PER_CU sets one. */
+bool env_batched_sum() {
+  const char *s = getenv("ZS_FUSED_SUM");
+  return s && !strcmp(s, "batched");
 }
 
 /* Vector width, threads per block, vectors per thread, access shape
@@ -207,22 +213,24 @@ FusedShape fused_shape_grouped(uint32_t world) {
 
 /* ------------------------------------------------------------------------
  * Write windows (await_write_window in zs_kernels.h) for the rolling shape
- * at W >= 40 on launches of at least 8 GB of model bytes: a period of
+ * at W >= 40 on launches of at least 4 GB of model bytes: a period of
  * 30.72 us with the last eighth open for stores, and no cap on blocks per
  * CU (the registers allow 20 one-wave blocks), since waves that wait for
  * the window still hold their slots. The launch ends up to about one
  * period after its last loads, hence the size floor. Interleaved on one
  * GPU against the same kernel without windows at its own best cap (6),
- * bits equal: W = 64 (117 M parameters) 2.70-2.75 ms against 2.98-2.99
- * (+8 to +10 %, three boxes; periods of 25.6-40.96 us with windows of 1/8
- * to 3/16 within 1 %), W = 48 +6.5 %; W = 32 even, W = 24 and W = 16 slower
- * (shorter tiles leave too few tiles per period in each slot), W = 1 slower
- * at every period tried (half its bytes are writes).
+ * bits equal: W = 64 on 117 M parameters 2.70-2.83 ms against 2.98-3.03
+ * (+7 to +10 %, four boxes; periods of 25.6-40.96 us with windows of 1/8
+ * to 3/16 within 1 %), on 34 M +12 %, 20 M (3.1 GB) +1 %, 10 M (1.5 GB)
+ * -8 %; W = 48 +2 to +6.5 %, W = 40 +2 % (5.3 and 10.6 GB), -3 % at 2.1 GB;
+ * W = 36 -1 %, W = 32 -4 %, W = 24 and below slower still (shorter tiles
+ * leave too few tiles per period in each slot), W = 1 slower at every
+ * period tried (half its bytes are writes).
  * ZS_FUSED_WRITE_WINDOW overrides this, for measurements and tests: "off",
  * or "<period in us>,<open fraction>" for every rolling-shape launch.
  * ---------------------------------------------------------------------- */
 constexpr uint32_t kWindowWorld = 40;
-constexpr double kWindowBytes = 8e9;
+constexpr double kWindowBytes = 4e9;
 constexpr double kWindowPeriodUs = 30.72, kWindowOpen = 0.125;
 
 struct WriteWindow {
@@ -745,6 +753,7 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     return fail(ZS_ERR_UNSUPPORTED,
                 "grouped state needs operands aligned for 4-element vectors%s");
   FusedShape fs = grouped ? fused_shape_grouped(a->world) : fused_shape(vec, a->world, n);
+  if (fs.access == kShapeR4NtL && env_batched_sum()) fs.access = kShapeB8NtL;
   const WriteWindow win = write_window(fs, a->world, n, acc);
   p.win_period = win.period;
   p.win_open = win.open_at;

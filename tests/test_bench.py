@@ -110,14 +110,15 @@ def test_fused_instance_names_match_the_kernel_template():
         "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5, 64, true>"
     assert [bench.fused_shape(w, big, "grouped") for w in (1, 3, 4, 5, 12, 13, 64)] == \
         [(64, 1, 5, 12), (64, 1, 5, 16), (64, 2, 5, 12), (64, 2, 6, 8), (64, 2, 6, 8),
-         (64, 2, 6, 6), (64, 2, 6, 6)]
-    # write windows: W >= 40 and >= 8 GB per launch (the 7.5B shard), uncapped
+         (64, 2, 6, 6), (64, 2, 6, 0)]
+    # write windows: W >= 40 and >= 4 GB per launch (the 7.5B shard), uncapped
     assert bench.fused_shape(64, W["7p5b-shard-w64"].n, "grouped") == (64, 2, 6, 0)
     assert bench.write_window_of(64, W["7p5b-shard-w64"].n) == \
         {"period_us": 30.72, "open_fraction": 0.125}
     assert bench.write_window_of(39, 10**9) is None
     assert bench.write_window_of(64, W["7p5b-shard-w64"].n, state_layout="split") is None
-    assert bench.write_window_of(64, 8 * 10**9 // 154 - 1) is None
+    assert bench.write_window_of(64, 4 * 10**9 // 154 - 1) is None
+    assert bench.write_window_of(64, 4 * 10**9 // 154 + 1) is not None
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
     assert bench.fused_bytes_per_param(4, 4) == (24, 14)
 
