@@ -212,7 +212,16 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
  * the gradients and this rank's gather slice to 8); otherwise
  * ZS_ERR_INVALID_ARG (non-NULL m/v pointers, an unknown layout) or
  * ZS_ERR_UNSUPPORTED (alignment). acc_in, the gradients and the gather
- * buffer keep their flat layout. */
+ * buffer keep their flat layout.
+ * Timing only (the values written never change): with the grouped layout
+ * at world >= 40 on launches of at least 4 GB of model bytes, each wave
+ * holds its stores until a window of the device's wall clock that every
+ * CU reads alike (the last eighth of each 30.72 us period), so the chip's
+ * writes reach memory together instead of mixed into its reads; every wait
+ * ends within one period. For measurements the environment variables
+ * ZS_FUSED_BLOCKS_PER_CU (blocks per CU, 0 = uncapped), ZS_FUSED_SUM
+ * ("batched") and ZS_FUSED_WRITE_WINDOW ("off", or "<period in us>,<open
+ * fraction>") change the launch; they are read at every call. */
 typedef struct {
   uint32_t world, rank;
   uint64_t n;
