@@ -110,8 +110,9 @@ WINDOW_PERIOD_US, WINDOW_OPEN = 30.72, 0.125
 
 def write_window_of(world, n, accum=1, state_layout="grouped"):
     """{period_us, open_fraction} of the write windows libzeroshard uses
-    for a shard of n parameters over `world` workers, or None."""
-    if state_layout != "grouped" or world < 5:
+    for a 16-byte-aligned shard of n parameters over `world` workers (either
+    state layout), or None."""
+    if world < 5:
         return None
     env = os.environ.get("ZS_FUSED_WRITE_WINDOW", "")
     if env == "off":
@@ -130,9 +131,10 @@ def fused_shape(world, n, state_layout="split"):
     blocks per CU; 0 = no cap) of the fused kernel that zs_step_fused
     launches for a 16-byte-aligned shard of n parameters over `world`
     workers: 4-element vectors, non-temporal state loads and stores.
-    Split state: one-wave blocks at W = 2 and from W = 17 on, 256-thread
-    blocks otherwise, the tile depth and cap following W and, for W = 3 to
-    16, the shard's size. Grouped state: one-wave blocks throughout; one
+    Split state: 256-thread blocks with two vectors per thread at W = 1 (2
+    per CU) and W = 3 (3 or 4 per CU by the shard's size), one-wave blocks
+    otherwise: one vector at 16 per CU for W = 2, then as the grouped state
+    from W = 4 on. Grouped state: one-wave blocks throughout; one
     vector per thread at 12 blocks per CU for W = 1 and 16 for W = 2, 3;
     two from W = 4 on: the batched sum at 12 per CU for W = 4, the rolling
     sum (shape 6) at 8 per CU up to W = 12 and 6 beyond, uncapped when the
@@ -151,12 +153,13 @@ def fused_shape(world, n, state_layout="split"):
         return 256, 2, 5, 2
     if world == 2:
         return 64, 1, 5, 16
-    if world >= 17:
+    if world == 3:
+        return 256, 2, 5, 3 if n // 2048 >= FUSED_MANY_TILES else 4
+    if world == 4:
         return 64, 2, 5, 12
-    many = n // 2048 >= FUSED_MANY_TILES
-    if world <= 12 or many:
-        return 256, 2, 5, 3 if many else 4
-    return 256, 4, 4 if world == 16 else 5, 0
+    if write_window_of(world, n) is not None:
+        return 64, 2, 6, 0
+    return 64, 2, 6, 8 if world <= 12 else 6
 
 
 def fused_instance(wl, wire=0, state_layout="split"):
@@ -852,17 +855,20 @@ GROUPED_CASES = tuple((w, GROUPED_N) for w in GROUPED_WORLDS) + \
     tuple((64, n) for n in (10_000_000, 20_000_000, 33_816_576))
 
 
-def grouped_plan(world):
-    """(label, environment) of each launch the grouped-layout sweep times at
-    `world` workers: libzeroshard's own launch first, then the same kernel
-    with its measurement overrides (every one computes the same bits)."""
+def grouped_plan(world, layout="grouped"):
+    """(label, environment) of each launch the layout sweep times at `world`
+    workers: libzeroshard's own launch first, then the same kernel with its
+    measurement overrides (every one computes the same bits)."""
     plan = [("production", {})]
+    if layout == "split" and world <= 3:
+        return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (2, 4, 8)]
     if world == 1:
         return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (8, 16, 0)]
     if world == 4:
         return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (8, 16)]
     off = {"ZS_FUSED_WRITE_WINDOW": "off"}
-    plan.append(("batched sum, cap %d (the earlier launch)" % (16 if world <= 16 else 12),
+    plan.append(("batched sum, cap %d%s" % (16 if world <= 16 else 12,
+                                            " (the earlier launch)" if layout == "grouped" else ""),
                  {"ZS_FUSED_SUM": "batched", "ZS_FUSED_BLOCKS_PER_CU": "16" if world <= 16 else "12",
                   **off}))
     plan += [(f"rolling sum, cap {c}, no windows", {"ZS_FUSED_BLOCKS_PER_CU": str(c), **off})
@@ -873,9 +879,9 @@ def grouped_plan(world):
     return plan
 
 
-def grouped_sweep(torch, cases=GROUPED_CASES, rounds=3):
-    """libzeroshard's fused step with the grouped state for each (W, n) of
-    `cases`: its own launch against the same kernel under the
+def grouped_sweep(torch, cases=GROUPED_CASES, rounds=3, layout="grouped"):
+    """libzeroshard's fused step with the grouped (or split) state for each
+    (W, n) of `cases`: its own launch against the same kernel under the
     measurement overrides of grouped_plan (cap, batched sum, write windows),
     each launch's output checked bit for bit against the production
     launch's, timed interleaved over `rounds`. Random inputs (bf16
@@ -900,17 +906,22 @@ def grouped_sweep(torch, cases=GROUPED_CASES, rounds=3):
                 g[k, :n].view(torch.bfloat16).copy_(
                     torch.empty(n, dtype=torch.float32, device="cuda").normal_(0, 1e-3))
             grads = [g[k, :n].view(torch.bfloat16) for k in range(W)]
-            L = zs.grouped_len(n)
+            grouped = layout == "grouped"
+            L = zs.grouped_len(n) if grouped else 3 * n
             sin = torch.empty(L, dtype=torch.float32, device="cuda").normal_(0, 0.02)
-            sv = sin.view(-1, 3, 1024)
-            sv[:, 1, :].mul_(5e-3)
-            sv[:, 2, :].abs_().mul_(0.05)
+            sv = sin.view(-1, 3, 1024) if grouped else sin.view(3, 1, n)
+            sv[:, 1, :].mul_(5e-3) if grouped else sv[1].mul_(5e-3)
+            sv[:, 2, :].abs_().mul_(0.05) if grouped else sv[2].abs_().mul_(0.05)
             sout = torch.empty_like(sin)
             gather = torch.empty(n, dtype=torch.bfloat16, device="cuda")
             flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-            args = zs.StepArgs(grads, 0, n, sin, None, None, sout, None, None, gather, 0, flag,
-                               hp, state_layout=zs.ZS_STATE_GROUPED)
-            plan = grouped_plan(W)
+            if grouped:
+                args = zs.StepArgs(grads, 0, n, sin, None, None, sout, None, None, gather, 0,
+                                   flag, hp, state_layout=zs.ZS_STATE_GROUPED)
+            else:
+                args = zs.StepArgs(grads, 0, n, sin[:n], sin[n:2 * n], sin[2 * n:], sout[:n],
+                                   sout[n:2 * n], sout[2 * n:], gather, 0, flag, hp)
+            plan = grouped_plan(W, layout)
             ref = None
             for label, env in plan:
                 setenv(env)
@@ -935,9 +946,10 @@ def grouped_sweep(torch, cases=GROUPED_CASES, rounds=3):
                 gbps = (2 * W + 26) * n / (ms * 1e-3) / 1e9
                 rows.append(dict(launch=label, ms=ms, ms_rounds=times[label], gbps=gbps,
                                  frac_of_peak=gbps / PEAK_HBM_GBPS))
-                log(f"grouped W={W} n={n} {label}: {ms:.4f} ms ({gbps:.0f} GB/s)")
-            t, u, shape, cap = fused_shape(W, n, "grouped")
-            out.append(dict(world=W, n=n, reps=reps, rounds=rounds, results=rows,
+                log(f"{layout} W={W} n={n} {label}: {ms:.4f} ms ({gbps:.0f} GB/s)")
+            setenv({})
+            t, u, shape, cap = fused_shape(W, n, layout)
+            out.append(dict(world=W, n=n, layout=layout, reps=reps, rounds=rounds, results=rows,
                             production={"threads_per_block": t, "vectors_per_thread": u,
                                         "access_shape": shape, "blocks_per_cu": cap,
                                         "write_window": write_window_of(W, n)}))
@@ -1095,6 +1107,8 @@ def main():
                          + ", ".join(map(str, GROUPED_WORLDS)) + " on the 7.5B shard's size and "
                          "three smaller W = 64 shards, and print that table as the JSON line "
                          "instead")
+    ap.add_argument("--sweep-split", action="store_true",
+                    help="the same sweep as --sweep-grouped with the split state layout")
     ap.add_argument("--sweep-shapes", action="store_true",
                     help="time the fused step's tile depths and residency caps against "
                          "libzeroshard's own launch over a grid of W and shard sizes and print "
@@ -1133,6 +1147,10 @@ def main():
     if args.sweep_grouped:
         print(json.dumps({"metric": "grouped-state fused step by launch setting, ms per launch",
                           "unit": "ms", "sweeps": grouped_sweep(torch)}))
+        return
+    if args.sweep_split:
+        print(json.dumps({"metric": "split-state fused step by launch setting, ms per launch",
+                          "unit": "ms", "sweeps": grouped_sweep(torch, layout="split")}))
         return
     if args.sweep_shapes:
         print(json.dumps({"metric": "fused step tile depth and residency by W and shard size, "

@@ -107,28 +107,30 @@ using zs_host::make_scales;
  * Block size, tile and residency of the fused kernel. Each thread owns U
  * 4-element vectors of a tile (T * U * 4 elements per block of T threads)
  * and the blocks per CU are capped with dynamic LDS that the kernel never
- * touches. With W gradient and three state streams read while four
- * streams are written, HBM delivered more on MI355X with fewer bytes in
- * flight per CU than the registers allow; how many fewer depends on W and,
- * for W = 3 to 16, on the shard's size; and at W = 2 and from W = 17 on,
- * one-wave blocks (64 threads) beat 256-thread ones at the same waves per
- * CU. Interleaved timings on one GPU against the alternatives (all
- * computing the same bits), shards of 0.35 M to 7 G parameters:
+ * touches. HBM delivered more on MI355X with fewer bytes in flight per CU
+ * than the registers allow, by an amount that depends on W; from W = 5 on
+ * the rolling sum (each wave streaming without draining) lets the fewest
+ * waves win. Both state layouts share the rule from W = 4 on (the grouped
+ * layout's is fused_shape_grouped below); for the split layout, interleaved
+ * timings on one GPU against the alternatives (all computing the same
+ * bits):
  *   - W = 1: 256-thread blocks, U = 2, 2 blocks (8 waves) per CU. One-wave
  *     blocks at 8 to 16 waves per CU ran 4 to 8 % faster in some runs and
  *     1 to 10 % slower in others, on the same GPU.
  *   - W = 2: one-wave blocks, U = 1, 16 per CU: +7.6 to +12 % over four
  *     vectors in 256-thread blocks at 3 per CU.
- *   - W = 3 to 16, 256-thread blocks: U = 2 with 3 blocks per CU from
- *     20 000 2048-element tiles on (+2 to +7 % over U = 4), 4 blocks per
- *     CU below that for W <= 12 (+2.5 to +18 %), U = 4 uncapped below it
- *     for W = 13 to 16 (U = 2 lost 4 % at W = 16 and 15.6 M parameters).
- *     One-wave blocks here ranged from -3 % (small shards) to +5 %.
- *   - W >= 17: one-wave blocks, U = 2, 12 per CU: +2 to +5 % over one
- *     vector with 16 loads ahead in 256-thread blocks at 6 per CU.
- * The one-wave shapes take eight workers' loads ahead of the in-order
- * adds. Operands aligned for 2- or 1-element vectors only keep
- * 256-thread blocks, U = 2 (1 when W = 1), plain stores and 2, 3 or no cap.
+ *   - W = 3: 256-thread blocks, U = 2, 3 blocks per CU from 20 000
+ *     2048-element tiles on, 4 below.
+ *   - W = 4: one-wave blocks, U = 2, the batched sum, 12 per CU.
+ *   - W >= 5: one-wave blocks, U = 2, the rolling sum, 8 per CU up to
+ *     W = 12 and 6 above (write windows as below). On 117 M parameters
+ *     against the previous split-layout launches (256-thread blocks at 3
+ *     per CU up to W = 16, batched one-wave blocks at 12 per CU above):
+ *     W = 4 +4.5 %, W = 5 +4 %, W = 8 +7 %, W = 12 +4 %, W = 16 +4 %,
+ *     W = 17 +6 %, W = 24 +3.5 %, W = 32 +2 %, W = 64 +16 % (with windows;
+ *     +6 % without); W = 8 on 15.6 M +1 %.
+ * Operands aligned for 2- or 1-element vectors only keep 256-thread
+ * blocks, U = 2 (1 when W = 1), plain stores and 2, 3 or no cap.
  * ZS_FUSED_BLOCKS_PER_CU (0 = no cap, 1..32 = that many blocks) overrides
  * the cap, for measurements; it is read at every launch.
  * ---------------------------------------------------------------------- */
@@ -187,10 +189,9 @@ FusedShape fused_shape(int vec, uint32_t world, uint64_t n) {
   if (vec < 4) return {kBlock, world > 1 ? 2 : 1, kShapeB8, world == 1 ? 2 : world <= 8 ? 3 : 0};
   if (world == 1) return {kBlock, 2, kShapeB8NtL, 2};
   if (world == 2) return {kFusedWaveBlock, 1, kShapeB8NtL, 16};
-  if (world >= 17) return {kFusedWaveBlock, 2, kShapeB8NtL, 12};
-  const bool many = n / 2048 >= kFusedManyTiles;
-  if (world <= 12 || many) return {kBlock, 2, kShapeB8NtL, many ? 3 : 4};
-  return {kBlock, 4, world == 16 ? kShapeB16NtL : kShapeB8NtL, 0};
+  if (world == 3) return {kBlock, 2, kShapeB8NtL, n / 2048 >= kFusedManyTiles ? 3 : 4};
+  if (world == 4) return {kFusedWaveBlock, 2, kShapeB8NtL, 12};
+  return {kFusedWaveBlock, 2, kShapeR4NtL, world <= 12 ? 8 : 6};
 }
 
 /* The grouped state layout runs one-wave blocks: one vector per thread at
@@ -778,11 +779,11 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
     } else if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL, kBlock);              \
     else if (fs.threads == kFusedWaveBlock && fs.tile_vecs == 1)                         \
       ZS_KF(4, 1, true, A, G, P, W, kShapeB8NtL, kFusedWaveBlock);                       \
+    else if (fs.threads == kFusedWaveBlock && fs.access == kShapeR4NtL)                  \
+      ZS_KF(4, 2, true, A, G, P, W, kShapeR4NtL, kFusedWaveBlock);                       \
     else if (fs.threads == kFusedWaveBlock) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL,   \
                                                   kFusedWaveBlock);                      \
-    else if (fs.tile_vecs == 2) ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL, kBlock);      \
-    else if (fs.access == kShapeB16NtL) ZS_KF(4, 4, true, A, G, P, W, kShapeB16NtL, kBlock); \
-    else ZS_KF(4, 4, true, A, G, P, W, kShapeB8NtL, kBlock);                             \
+    else ZS_KF(4, 2, true, A, G, P, W, kShapeB8NtL, kBlock);                             \
   } while (0)
 #define ZS_KNARROW(V, A, G, P, W)                                   \
   do {                                                              \

@@ -49,9 +49,10 @@ constexpr int kLoadBatch = 8;   /* gradient vectors in flight per thread   */
  * lines, while with 8-element vectors a lane's 32 bytes take two stores and
  * each 64-byte line is half-written by two instructions, which then leave
  * the L2 as separate writes (14 % more write bytes at W = 64, measured).
- * The library launches kShapeB8NtL (W < 16) and kShapeB16NtL (W >= 16)
- * on 4-element vectors, and kShapeB8 on the narrower vectors of unaligned
- * operands. */
+ * The library launches kShapeB8NtL (W <= 4) and kShapeR4NtL below
+ * (W >= 5) on 4-element vectors, and kShapeB8 on the narrower vectors of
+ * unaligned operands; the other shapes are kept for the measurement
+ * library's variants. */
 constexpr int kShapeB8 = 0, kShapeB16 = 1, kShapeB16Nt = 2, kShapeB8Nt = 3;
 /* as kShapeB16Nt / kShapeB8Nt, with the fp32 state (and the accumulated
  * gradient) also loaded non-temporally: read once per step, like the

@@ -90,18 +90,18 @@ def test_fused_instance_names_match_the_kernel_template():
     assert bench.fused_instance(W["7b-full-w1"]) == \
         "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 5, 256, false>"
     assert bench.fused_instance(W["7p5b-shard-w64"]) == \
-        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5, 64, false>"
+        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 6, 64, false>"
     assert bench.fused_instance(W["1p3b-w4-acc4-fp16"]) == \
-        "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5, 256, false>"
+        "zs::fused_kernel<4, 2, true, true, 1, 1, 0, 5, 64, false>"
     assert bench.fused_instance(W["gpt2s-w8"]) == \
-        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 5, 256, false>"
+        "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 6, 64, false>"
     big, small = 40_960_000, 40_959_999  # 20 000 tiles of 2048 and one element short
-    assert [bench.fused_shape(w, big) for w in (1, 2, 3, 12, 13, 16, 17, 64)] == \
-        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 3), (256, 2, 5, 3), (256, 2, 5, 3),
-         (256, 2, 5, 3), (64, 2, 5, 12), (64, 2, 5, 12)]
-    assert [bench.fused_shape(w, small) for w in (1, 2, 3, 12, 13, 16, 17, 64)] == \
-        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 4), (256, 2, 5, 4), (256, 4, 5, 0),
-         (256, 4, 4, 0), (64, 2, 5, 12), (64, 2, 5, 12)]
+    assert [bench.fused_shape(w, big) for w in (1, 2, 3, 4, 5, 12, 13, 64)] == \
+        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 3), (64, 2, 5, 12), (64, 2, 6, 8),
+         (64, 2, 6, 8), (64, 2, 6, 6), (64, 2, 6, 0)]
+    assert [bench.fused_shape(w, small) for w in (1, 2, 3, 4, 5, 12, 13, 64)] == \
+        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 4), (64, 2, 5, 12), (64, 2, 6, 8),
+         (64, 2, 6, 8), (64, 2, 6, 6), (64, 2, 6, 0)]
     assert bench.fused_instance(W["7b-full-w1"], state_layout="grouped") == \
         "zs::fused_kernel<4, 1, false, false, 0, 0, 0, 5, 64, true>"
     assert bench.fused_instance(W["7p5b-shard-w64"], state_layout="grouped") == \
@@ -116,7 +116,8 @@ def test_fused_instance_names_match_the_kernel_template():
     assert bench.write_window_of(64, W["7p5b-shard-w64"].n) == \
         {"period_us": 30.72, "open_fraction": 0.125}
     assert bench.write_window_of(39, 10**9) is None
-    assert bench.write_window_of(64, W["7p5b-shard-w64"].n, state_layout="split") is None
+    assert bench.write_window_of(64, W["7p5b-shard-w64"].n, state_layout="split") is not None
+    assert bench.fused_shape(64, W["7p5b-shard-w64"].n) == (64, 2, 6, 0)
     assert bench.write_window_of(64, 4 * 10**9 // 154 - 1) is None
     assert bench.write_window_of(64, 4 * 10**9 // 154 + 1) is not None
     assert bench.fused_bytes_per_param(64, 1) == (140, 14)
