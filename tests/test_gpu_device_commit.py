@@ -234,11 +234,16 @@ def test_empty_shard_commits(env):
     assert (d.step_t, d.skipped, d.last_flag, d.epoch) == (2, 1, 0, 3)
 
 
-def test_graph_capture_replays_match_eager(env):
+@pytest.mark.parametrize("windows", [None, "2.56,0.25"])
+def test_graph_capture_replays_match_eager(env, windows, monkeypatch):
     """Two device steps (one per direction of the ping-pong sets) captured in
     a graph; three replays, with eager work and synchronizations between
-    them, each equal to two eager steps."""
+    them, each equal to two eager steps; also with write windows forced on
+    for both the eager and the captured steps (the captured launches keep
+    the window they were recorded with)."""
     zs, synth, shard = env
+    if windows:
+        monkeypatch.setenv("ZS_FUSED_WRITE_WINDOW", windows)
     wl = dataclasses.replace(synth.WORKLOADS["gpt2s-w8"], phi=8 * 100_003, name="graph")
     eager, ge = _make(env, wl, True)
     graph, gg = _make(env, wl, True)

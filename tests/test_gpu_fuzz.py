@@ -1,7 +1,9 @@
 """Randomized GPU parity: seeded random configurations of the fused step
-(with the decision on the host and on the device), of the reduction, of the
-unfused check / update / cast chain, of the ring all-gather and of the
-pipelined offload step, each against the oracle through the C ABI.
+(with the decision on the host and on the device; with the split and the
+grouped state, the latter with write windows forced on at random), of the
+reduction, of the unfused check / update / cast chain, of the ring
+all-gather and of the pipelined offload step, each against the oracle
+through the C ABI.
 
 Every case draws the worker count (1 to 64), a ragged size, the rank, the
 gradient and parameter dtypes, the precision of the ring's partial sums,
@@ -115,6 +117,68 @@ def test_fused_step_random_configuration(zs, case):
         gb = down16(gather)
         off = c["off"]
         assert np.all(gb[:off] == 7) and np.all(gb[off + n:] == 7)
+        assert assert_ulp16(gb[off:off + n], po, pdt, 1, f"#{case} params") == 0
+
+
+SENTINEL = np.uint32(0x7FC0DEAD).view(F32)  # a NaN no arithmetic produces
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_fused_step_random_grouped(zs, case, monkeypatch):
+    """The grouped state layout (operands aligned for 4-element vectors, so
+    every W >= 5 takes the rolling sum) with write windows forced on in
+    about half the cases, against the oracle; the slots past n of the last
+    group stay untouched."""
+    rng = np.random.default_rng(7000 + case)
+    c = _draw(rng)
+    W, n, gdt, pdt = c["world"], c["n"], c["gdt"], c["pdt"]
+    off = 4 * int(rng.integers(0, 3))
+    windows = rng.random() < 0.5
+    if windows:
+        monkeypatch.setenv("ZS_FUSED_WRITE_WINDOW",
+                           f"{float(rng.choice([1.28, 2.56, 5.12]))},{float(rng.choice([0.125, 0.25]))}")
+    announce(f"fuzz fused grouped #{case}: W={W} n={n} rank={c['rank']} {gdt}/{pdt} "
+             f"wire={c['wire']} acc={c['acc']} windows={windows} inject={c['inject']}")
+    g16 = [_rand16(rng, n, 1e-3 * c["scale"], gdt) for _ in range(W)]
+    if c["inject"]:
+        bad = 0x7F80 if gdt == "bf16" else 0x7C00
+        g16[int(rng.integers(0, W))][int(rng.integers(0, n))] = bad
+    state = [(rng.standard_normal(n) * 0.02).astype(F32), (rng.standard_normal(n) * 1e-4).astype(F32),
+             rng.uniform(0, 1e-6, n).astype(F32)]
+    acc = (rng.standard_normal(n) * c["scale"] * 1e-3).astype(F32) if c["acc"] else None
+    hp = dict(lr=c["lr"], beta1=c["beta1"], beta2=c["beta2"], eps=c["eps"],
+              weight_decay=c["weight_decay"])
+    G = -(-n // 1024)
+    buf = np.full((G, 3, 1024), SENTINEL, dtype=F32)
+    for k, x in enumerate(state):
+        flat = np.full(G * 1024, SENTINEL, dtype=F32)
+        flat[:n] = x
+        buf[:, k, :] = flat.reshape(G, 1024)
+    gin = up32(buf.ravel())
+    gout = up32(np.full(G * 3072, SENTINEL, dtype=F32))
+    gather = torch.full((n + off + 8,), 7, dtype=torch.int16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    args = zs.StepArgs([up16(g, gdt) for g in g16], c["rank"], n, gin, None, None, gout, None,
+                       None, gather, off, flag,
+                       zs.hparams(**hp, loss_scale=c["scale"], step_t=c["t"]),
+                       acc_in=up32(acc) if acc is not None else None, grad_dtype=DT[gdt],
+                       param_dtype=DT[pdt], wire_dtype=WIRE_CODE[c["wire"]],
+                       state_layout=zs.ZS_STATE_GROUPED)
+    zs.zs_step_fused(args)
+    f, mo, mmo, vo, po = oracle.shard_step(g16, c["rank"], gdt, pdt, *state, step_t=c["t"],
+                                           acc_in=acc, loss_scale=c["scale"], threads=4,
+                                           wire=c["wire"], **hp)
+    assert int(flag.item()) == f == (1 if c["inject"] else 0)
+    assert_bits_equal(down32(gin), buf.ravel(), "input set untouched")
+    out = down32(gout).reshape(G, 3, 1024)
+    for k, (want, what) in enumerate(zip((mo, mmo, vo), ("master", "m", "v"))):
+        flat = out[:, k, :].ravel()
+        assert_bits_equal(flat[n:], np.full(G * 1024 - n, SENTINEL, dtype=F32), f"{what} past n")
+        if f == 0:
+            assert assert_rel(flat[:n], want, 1e-6, f"#{case} {what}") == 0
+    gb = down16(gather)
+    assert np.all(gb[:off] == 7) and np.all(gb[off + n:] == 7)
+    if f == 0:
         assert assert_ulp16(gb[off:off + n], po, pdt, 1, f"#{case} params") == 0
 
 
