@@ -876,6 +876,14 @@ def grouped_plan(world, layout="grouped"):
     plan.append((f"rolling sum, uncapped, windows {WINDOW_PERIOD_US} us / {WINDOW_OPEN}",
                  {"ZS_FUSED_BLOCKS_PER_CU": "0",
                   "ZS_FUSED_WRITE_WINDOW": f"{WINDOW_PERIOD_US},{WINDOW_OPEN}"}))
+    if world >= WINDOW_WORLD:
+        for period, share in ((20.48, 0.125), (40.96, 0.125), (30.72, 0.09375), (30.72, 0.15625)):
+            plan.append((f"rolling sum, uncapped, windows {period} us / {share}",
+                         {"ZS_FUSED_BLOCKS_PER_CU": "0",
+                          "ZS_FUSED_WRITE_WINDOW": f"{period},{share}"}))
+        plan.append((f"rolling sum, 16 per CU, windows {WINDOW_PERIOD_US} us / {WINDOW_OPEN}",
+                     {"ZS_FUSED_BLOCKS_PER_CU": "16",
+                      "ZS_FUSED_WRITE_WINDOW": f"{WINDOW_PERIOD_US},{WINDOW_OPEN}"}))
     return plan
 
 
