@@ -131,10 +131,10 @@ def fused_shape(world, n, state_layout="split"):
     blocks per CU; 0 = no cap) of the fused kernel that zs_step_fused
     launches for a 16-byte-aligned shard of n parameters over `world`
     workers: 4-element vectors, non-temporal state loads and stores.
-    Split state: 256-thread blocks with two vectors per thread at W = 1 (2
-    per CU) and W = 3 (3 or 4 per CU by the shard's size), one-wave blocks
-    otherwise: one vector at 16 per CU for W = 2, then as the grouped state
-    from W = 4 on. Grouped state: one-wave blocks throughout; one
+    Split state: 256-thread blocks with two vectors per thread at W = 3 (3
+    or 4 per CU by the shard's size), one-wave blocks otherwise: one vector
+    at 12 per CU for W = 1 and 16 for W = 2, then as the grouped state from
+    W = 4 on. Grouped state: one-wave blocks throughout; one
     vector per thread at 12 blocks per CU for W = 1 and 16 for W = 2, 3;
     two from W = 4 on: the batched sum at 12 per CU for W = 4, the rolling
     sum (shape 6) at 8 per CU up to W = 12 and 6 beyond, uncapped when the
@@ -150,7 +150,7 @@ def fused_shape(world, n, state_layout="split"):
             return 64, 2, 6, 0
         return 64, 2, 6, 8 if world <= 12 else 6
     if world == 1:
-        return 256, 2, 5, 2
+        return (256, 2, 5, 2) if os.environ.get("ZS_FUSED_W1") == "block256" else (64, 1, 5, 12)
     if world == 2:
         return 64, 1, 5, 16
     if world == 3:
@@ -850,9 +850,10 @@ def shape_sweep(torch, rounds=3):
 GROUPED_WORLDS = (1, 4, 5, 8, 16, 24, 32, 36, 40, 48, 64)
 GROUPED_N = 117_187_500
 # (W, n) cases of the grouped sweep: every W of GROUPED_WORLDS on the 7.5B
-# shard's size, then smaller W = 64 shards around the write windows' floor
+# shard's size, then smaller W = 64 shards around the write windows' floor,
+# then W = 1 on 1 G parameters (28 GB per launch)
 GROUPED_CASES = tuple((w, GROUPED_N) for w in GROUPED_WORLDS) + \
-    tuple((64, n) for n in (10_000_000, 20_000_000, 33_816_576))
+    tuple((64, n) for n in (10_000_000, 20_000_000, 33_816_576)) + ((1, 1_000_000_000),)
 
 
 def grouped_plan(world, layout="grouped"):
@@ -860,6 +861,10 @@ def grouped_plan(world, layout="grouped"):
     workers: libzeroshard's own launch first, then the same kernel with its
     measurement overrides (every one computes the same bits)."""
     plan = [("production", {})]
+    if layout == "split" and world == 1:
+        return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (8, 16)] + [
+            ("256-thread blocks, 2 vectors per thread, 2 per CU (the earlier launch)",
+             {"ZS_FUSED_W1": "block256"})]
     if layout == "split" and world <= 3:
         return plan + [(f"cap {c}", {"ZS_FUSED_BLOCKS_PER_CU": str(c)}) for c in (2, 4, 8)]
     if world == 1:
@@ -899,7 +904,7 @@ def grouped_sweep(torch, cases=GROUPED_CASES, rounds=3, layout="grouped"):
     hp = zs.hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01,
                     loss_scale=1.0, step_t=1)
     saved = {k: os.environ.get(k) for k in ("ZS_FUSED_BLOCKS_PER_CU", "ZS_FUSED_SUM",
-                                            "ZS_FUSED_WRITE_WINDOW")}
+                                            "ZS_FUSED_WRITE_WINDOW", "ZS_FUSED_W1")}
 
     def setenv(env):
         for k in saved:

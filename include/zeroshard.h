@@ -220,8 +220,9 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
  * writes reach memory together instead of mixed into its reads; every wait
  * ends within one period. For measurements the environment variables
  * ZS_FUSED_BLOCKS_PER_CU (blocks per CU, 0 = uncapped), ZS_FUSED_SUM
- * ("batched") and ZS_FUSED_WRITE_WINDOW ("off", or "<period in us>,<open
- * fraction>") change the launch; they are read at every call. */
+ * ("batched"), ZS_FUSED_W1 ("block256") and ZS_FUSED_WRITE_WINDOW ("off",
+ * or "<period in us>,<open fraction>") change the launch; they are read at
+ * every call. */
 typedef struct {
   uint32_t world, rank;
   uint64_t n;

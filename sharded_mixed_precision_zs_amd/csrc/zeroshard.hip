@@ -114,9 +114,10 @@ using zs_host::make_scales;
  * layout's is fused_shape_grouped below); for the split layout, interleaved
  * timings on one GPU against the alternatives (all computing the same
  * bits):
- *   - W = 1: 256-thread blocks, U = 2, 2 blocks (8 waves) per CU. One-wave
- *     blocks at 8 to 16 waves per CU ran 4 to 8 % faster in some runs and
- *     1 to 10 % slower in others, on the same GPU.
+ *   - W = 1: one-wave blocks, U = 1, 12 per CU (as the grouped layout):
+ *     +5 to +8 % over 256-thread blocks with U = 2 at 2 per CU on 0.5 to 2 G
+ *     parameters (three boxes); on 117 M the two traded places by box
+ *     (ZS_FUSED_W1 = block256 selects the earlier shape for measurements).
  *   - W = 2: one-wave blocks, U = 1, 16 per CU: +7.6 to +12 % over four
  *     vectors in 256-thread blocks at 3 per CU.
  *   - W = 3: 256-thread blocks, U = 2, 3 blocks per CU from 20 000
@@ -163,6 +164,13 @@ int env_blocks_per_cu() {
   return x < 0 || x > 32 ? -1 : x;
 }
 
+/* ZS_FUSED_W1=block256 (measurements): the split layout's W = 1 launch in
+ * the earlier shape (256-thread blocks, two vectors per thread, 2 per CU). */
+bool env_w1_block256() {
+  const char *s = getenv("ZS_FUSED_W1");
+  return s && !strcmp(s, "block256");
+}
+
 /* ZS_FUSED_SUM=batched (measurements): the grouped layout's W >= 5 shape
  * with the batched sum (kShapeB8NtL) in place of the rolling one; the cap
  * stays the rolling shape's unless ZS_FUSED_BLOCKS_PER_CU sets one. */
@@ -187,7 +195,9 @@ struct FusedShape {
 
 FusedShape fused_shape(int vec, uint32_t world, uint64_t n) {
   if (vec < 4) return {kBlock, world > 1 ? 2 : 1, kShapeB8, world == 1 ? 2 : world <= 8 ? 3 : 0};
-  if (world == 1) return {kBlock, 2, kShapeB8NtL, 2};
+  if (world == 1)
+    return env_w1_block256() ? FusedShape{kBlock, 2, kShapeB8NtL, 2}
+                             : FusedShape{kFusedWaveBlock, 1, kShapeB8NtL, 12};
   if (world == 2) return {kFusedWaveBlock, 1, kShapeB8NtL, 16};
   if (world == 3) return {kBlock, 2, kShapeB8NtL, n / 2048 >= kFusedManyTiles ? 3 : 4};
   if (world == 4) return {kFusedWaveBlock, 2, kShapeB8NtL, 12};
@@ -776,7 +786,9 @@ static int step_fused_impl(const zs_step_args *a, void *stream, hipEvent_t ev_st
       else if (fs.tile_vecs == 1) ZS_KG(1, true, A, G, P, W, kShapeB8NtL);               \
       else if (fs.access == kShapeR4NtL) ZS_KG(2, true, A, G, P, W, kShapeR4NtL);        \
       else ZS_KG(2, true, A, G, P, W, kShapeB8NtL);                                      \
-    } else if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL, kBlock);              \
+    } else if (!multi && fs.threads == kFusedWaveBlock)                                  \
+      ZS_KF(4, 1, false, A, G, P, W, kShapeB8NtL, kFusedWaveBlock);                      \
+    else if (!multi) ZS_KF(4, 2, false, A, G, P, W, kShapeB8NtL, kBlock);                \
     else if (fs.threads == kFusedWaveBlock && fs.tile_vecs == 1)                         \
       ZS_KF(4, 1, true, A, G, P, W, kShapeB8NtL, kFusedWaveBlock);                       \
     else if (fs.threads == kFusedWaveBlock && fs.access == kShapeR4NtL)                  \

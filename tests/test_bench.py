@@ -88,7 +88,7 @@ def test_fused_instance_names_match_the_kernel_template():
     from sharded_mixed_precision_zs_amd import synth
     W = synth.WORKLOADS
     assert bench.fused_instance(W["7b-full-w1"]) == \
-        "zs::fused_kernel<4, 2, false, false, 0, 0, 0, 5, 256, false>"
+        "zs::fused_kernel<4, 1, false, false, 0, 0, 0, 5, 64, false>"
     assert bench.fused_instance(W["7p5b-shard-w64"]) == \
         "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 6, 64, false>"
     assert bench.fused_instance(W["1p3b-w4-acc4-fp16"]) == \
@@ -97,10 +97,10 @@ def test_fused_instance_names_match_the_kernel_template():
         "zs::fused_kernel<4, 2, true, false, 0, 0, 0, 6, 64, false>"
     big, small = 40_960_000, 40_959_999  # 20 000 tiles of 2048 and one element short
     assert [bench.fused_shape(w, big) for w in (1, 2, 3, 4, 5, 12, 13, 64)] == \
-        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 3), (64, 2, 5, 12), (64, 2, 6, 8),
+        [(64, 1, 5, 12), (64, 1, 5, 16), (256, 2, 5, 3), (64, 2, 5, 12), (64, 2, 6, 8),
          (64, 2, 6, 8), (64, 2, 6, 6), (64, 2, 6, 0)]
     assert [bench.fused_shape(w, small) for w in (1, 2, 3, 4, 5, 12, 13, 64)] == \
-        [(256, 2, 5, 2), (64, 1, 5, 16), (256, 2, 5, 4), (64, 2, 5, 12), (64, 2, 6, 8),
+        [(64, 1, 5, 12), (64, 1, 5, 16), (256, 2, 5, 4), (64, 2, 5, 12), (64, 2, 6, 8),
          (64, 2, 6, 8), (64, 2, 6, 6), (64, 2, 6, 0)]
     assert bench.fused_instance(W["7b-full-w1"], state_layout="grouped") == \
         "zs::fused_kernel<4, 1, false, false, 0, 0, 0, 5, 64, true>"
