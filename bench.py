@@ -1177,16 +1177,13 @@ def main():
         return
     K, Wm = args.steps, args.warmup
     also = [x for x in args.also.split(",") if x and x != args.workload]
-    # host-side legs first: they measured slower after the large workloads'
-    # hundreds of GB of device allocations
+    # the host-side offload leg first: it measured slower after the large
+    # workloads' hundreds of GB of device allocations
     offload = None
     if not args.no_offload:
         offload = side_leg("offload", lambda: run_offload(HOST_LEG_WORKLOAD, max(10, K), 2, torch),
                            torch)
         log(json.dumps(offload))
-    cpu = None if args.no_cpu_baseline else side_leg("cpu_baseline",
-                                                     lambda: cpu_baseline(args.workload), torch)
-    log(f"cpu_baseline: {json.dumps(cpu)}")
     copies, ceilings = {}, {}
     if not args.no_ceilings:
         copies = side_leg("copy_ceiling", lambda: copy_rates_gbps(torch), torch)
@@ -1239,6 +1236,11 @@ def main():
         host_res = side_leg("host_commit", lambda: run_workload(args.workload, K, 2, torch,
                                                                 device_commit=False), torch)
         log(json.dumps(host_res))
+
+    # the CPU oracle last, so the GPU legs run back to back from the start
+    cpu = None if args.no_cpu_baseline else side_leg("cpu_baseline",
+                                                     lambda: cpu_baseline(args.workload), torch)
+    log(f"cpu_baseline: {json.dumps(cpu)}")
 
     wl = synth.WORKLOADS[args.workload]
     head = summary(main_res, wl)
