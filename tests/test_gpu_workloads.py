@@ -179,15 +179,17 @@ def test_1p3b_w4_acc4_windows_grouped_state(env):
     torch.cuda.empty_cache()
 
 
-# One shard per branch of the fused kernel's launch rule (block size,
-# vectors per thread and blocks per CU follow W and, for W = 3 to 16, the
-# shard's size): W = 2 (one-wave blocks, one vector per thread); W = 13 and
-# 16 under 20 000 2048-element tiles (256-thread blocks, four vectors, no
-# cap, 8 and 16 loads ahead); W = 17 (one-wave blocks, two vectors, 12 per
-# CU); W = 3 and 16 at 20 000 tiles and a half (256-thread blocks, two
-# vectors, 3 per CU). Each n is ragged against every tile.
-TILE_RULE_CASES = [(2, 1_000_003), (13, 1_000_003), (16, 1_000_003), (17, 1_000_003),
-                   (3, 40_961_029), (16, 40_961_029)]
+# One shard per branch of the split layout's launch rule (block size,
+# vectors per thread, sum and blocks per CU follow W, and at W = 3 the
+# shard's size): W = 1 and 2 (one-wave blocks, one vector per thread, 12
+# and 16 per CU); W = 3 under and at 20 000 2048-element tiles and a half
+# (256-thread blocks, two vectors, 4 and 3 per CU); W = 4 (one-wave blocks,
+# two vectors, the batched sum); W = 6 and 13 (the rolling sum at 8 and 6
+# per CU, tails of 1 and 0 workers); W = 40 below the write windows' size
+# floor. Each n is ragged against every tile. (The windows themselves run
+# in the 7.5B-shard tests below.)
+TILE_RULE_CASES = [(1, 1_000_003), (2, 1_000_003), (3, 1_000_003), (3, 40_961_029),
+                   (4, 1_000_003), (6, 1_000_003), (13, 1_000_003), (40, 1_000_003)]
 
 
 @pytest.mark.parametrize("world,n", TILE_RULE_CASES)
