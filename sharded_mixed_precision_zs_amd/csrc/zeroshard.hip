@@ -116,7 +116,7 @@ using zs_host::make_scales;
  * bits):
  *   - W = 1: one-wave blocks, U = 1, 12 per CU (as the grouped layout):
  *     +5 to +8 % over 256-thread blocks with U = 2 at 2 per CU on 0.5 to 2 G
- *     parameters (three boxes); on 117 M the two traded places by box
+ *     parameters (three GPUs); on 117 M the two traded places by GPU
  *     (ZS_FUSED_W1 = block256 selects the earlier shape for measurements).
  *   - W = 2: one-wave blocks, U = 1, 16 per CU: +7.6 to +12 % over four
  *     vectors in 256-thread blocks at 3 per CU.
@@ -212,9 +212,9 @@ FusedShape fused_shape(int vec, uint32_t world, uint64_t n) {
  * without draining, and fewer waves per CU streamed faster (about 24 KB of
  * loads in flight per CU). Against the previous choice (the batched sum
  * everywhere, 16 per CU up to W = 16 and 12 above), interleaved on one
- * GPU, bits equal: W = 1 +3 % (two boxes), W = 4 with fp16 gradients and
+ * GPU, bits equal: W = 1 +3 % (two GPUs), W = 4 with fp16 gradients and
  * an accumulated input +7.7 %, W = 5 +3 %, W = 8 even, W = 16 +8 %,
- * W = 24 and 32 +5 %, W = 64 +5 to +6 % (three boxes). */
+ * W = 24 and 32 +5 %, W = 64 +5 to +6 % (three GPUs). */
 FusedShape fused_shape_grouped(uint32_t world) {
   if (world == 1) return {kFusedWaveBlock, 1, kShapeB8NtL, 12};
   if (world <= 3) return {kFusedWaveBlock, 1, kShapeB8NtL, 16};
@@ -231,7 +231,7 @@ FusedShape fused_shape_grouped(uint32_t world) {
  * period after its last loads, hence the size floor. Interleaved on one
  * GPU against the same kernel without windows at its own best cap (6),
  * bits equal: W = 64 on 117 M parameters 2.70-2.83 ms against 2.98-3.03
- * (+7 to +10 %, four boxes; periods of 25.6-40.96 us with windows of 1/8
+ * (+7 to +10 %, four GPUs; periods of 25.6-40.96 us with windows of 1/8
  * to 3/16 within 1 %), on 34 M +12 %, 20 M (3.1 GB) +1 %, 10 M (1.5 GB)
  * -8 %; W = 48 +2 to +6.5 %, W = 40 +2 % (5.3 and 10.6 GB), -3 % at 2.1 GB;
  * W = 36 -1 %, W = 32 -4 %, W = 24 and below slower still (shorter tiles

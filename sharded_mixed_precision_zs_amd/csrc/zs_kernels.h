@@ -427,7 +427,7 @@ __device__ __forceinline__ void ring_sum_uw(const GradPtrs &g, uint32_t world,
  * W < B + 1 there is nothing to roll and the batched sum runs, followed by
  * `before`. On MI355X, run at 6 to 8 one-wave blocks per CU (fewer bytes in
  * flight per CU than the batched sum at 12 to 16), it streamed the step 3 to
- * 8 % faster at W = 5 and W = 16 to 64 (one-box interleaved timings). */
+ * 8 % faster at W = 5 and W = 16 to 64 (interleaved timings on one GPU). */
 template <int VEC, int U, int DT, int WIRE, int B, int R, typename F>
 __device__ __forceinline__ void roll_last(const GradPtrs &g, uint32_t j, const uint64_t (&i0)[U],
                                           Raw16<VEC> (&r)[B][U], float (&s)[U][VEC],
