@@ -24,9 +24,12 @@ committed rocprofv3 request-counter passes (profiles/fused_step_traffic.md),
 when they were taken on the current kernel source. `ceilings` are the rates
 of libzscopy's measurement kernels in the same run: a plain copy, read-only
 and write-only streams, and the step's own mix of streams with no arithmetic
-(the stream probe); `read_write_harmonic_gbps` combines the headline step's
-read-only and write-only stream rates at its read:write bytes. `cpu_baseline` times the CPU oracle on a bounded sample of
-the headline workload on this host's cores.
+(the wave probe, in the fused kernel's launch shapes).
+`read_write_harmonic_gbps` combines the headline step's read-only and
+write-only stream rates at its read:write bytes; `stream_bounds` does the
+same for the W = 64 shard and sets each fused rate against it and against
+the no-arithmetic mix. `cpu_baseline` times the CPU oracle on a bounded
+sample of the headline workload on this host's cores.
 
 Beside the headline: the step with its decision on the host (`host_commit`),
 with bf16 partial sums on the ring (`wire_bf16`, on the W = 64 shard), the
@@ -204,6 +207,10 @@ def _copylib():
     lib.zs_stream_probe.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_uint32, C.c_void_p,
                                     C.c_uint32, C.c_void_p, C.c_uint64, C.c_uint32, C.c_uint32,
                                     C.c_void_p, C.c_uint32, C.c_void_p]
+    lib.zs_wave_probe.restype = C.c_int
+    lib.zs_wave_probe.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_uint64, C.c_uint32, C.c_uint32, C.c_double, C.c_double,
+                                  C.c_void_p, C.c_uint32, C.c_void_p]
     return lib
 
 
@@ -295,65 +302,104 @@ def copy_shape_sweep(torch, gib=4, reps=10, rounds=3):
     return dict(bytes_each_way=nbytes, reps_per_round=reps, rounds=rounds, results=out)
 
 
-# (name, 16-bit input streams, fp32 inputs, fp32 outputs, 16-bit output,
-#  vectors per thread, blocks per CU (0: no cap), shard size)
+# (name, 16-bit input streams, grouped fp32 state read, state written,
+#  16-bit output, vectors per thread, blocks per CU (0: no cap), write
+#  windows, shard size): the wave probe in the fused kernel's launch shapes
+#  (W = 1: one vector per thread, 12 blocks per CU; W = 64: two, no cap and
+#  the write windows, or its best cap without them)
 N_W1 = 1 << 30                 # 1 G parameters: 28 GB for the W = 1 mix
 N_W64 = 117_186_560            # the 7.5B shard rounded down to the 4096-element tile
+WINDOW_W64 = (WINDOW_PERIOD_US, WINDOW_OPEN)
 PROBES = (
-    ("step_mix_w1", 1, 3, 3, True, 1, 2, N_W1),
-    ("read_only_w1_streams", 1, 3, 0, False, 1, 2, N_W1),
-    ("write_only_w1_streams", 0, 0, 3, True, 1, 2, N_W1),
-    ("step_mix_w64", 64, 3, 3, True, 2, 5, N_W64),
-    ("step_mix_w64_uncapped", 64, 3, 3, True, 2, 0, N_W64),
-    ("read_only_w64_streams", 64, 3, 0, False, 2, 5, N_W64),
-    ("read_only_w64_grads", 64, 0, 0, False, 2, 0, N_W64),
-    ("w64_grads_plus_param_store", 64, 0, 0, True, 2, 0, N_W64),
-    ("w64_reduce_shape", 64, 0, 1, False, 2, 0, N_W64),
+    ("step_mix_w1", 1, True, True, True, 1, 12, None, N_W1),
+    ("read_only_w1_streams", 1, True, False, False, 1, 12, None, N_W1),
+    ("write_only_w1_streams", 0, False, True, True, 1, 12, None, N_W1),
+    ("step_mix_w64", 64, True, True, True, 2, 0, WINDOW_W64, N_W64),
+    ("step_mix_w64_no_windows", 64, True, True, True, 2, 6, None, N_W64),
+    ("read_only_w64_streams", 64, True, False, False, 2, 0, None, N_W64),
+    ("read_only_w64_grads", 64, False, False, False, 2, 0, None, N_W64),
+    ("write_only_w64_streams", 0, False, True, True, 2, 0, None, N_W64),
+    ("w64_grads_plus_param_store", 64, False, False, True, 2, 0, None, N_W64),
 )
 
 
+# per shard size: the probes of its streams read alone, written alone, and
+# all of them in the fused kernel's launch shape
+BOUND_PROBES = {
+    1: ("read_only_w1_streams", "write_only_w1_streams", "step_mix_w1"),
+    64: ("read_only_w64_streams", "write_only_w64_streams", "step_mix_w64"),
+}
+
+
+def stream_bounds(ceilings, roofs):
+    """For each measured workload whose streams the probes carry (W = 1 and
+    W = 64): the time its reads alone plus its writes alone take (the two
+    phases back to back, no read/write turnaround in between) as a rate,
+    and the fused kernel's rate against that and against the probe of the
+    same mix in the same launch shape."""
+    from sharded_mixed_precision_zs_amd import synth
+    out = {}
+    for name, roof in roofs.items():
+        wl = synth.WORKLOADS.get(name)
+        names = BOUND_PROBES.get(wl.world) if wl is not None and wl.accum == 1 else None
+        if not names or not all(k in ceilings for k in names) or not roof:
+            continue
+        rd, wr = fused_bytes_per_param(wl.world, wl.accum)
+        r_alone, w_alone, mix = (ceilings[k]["gbps"] for k in names)
+        phased = (rd + wr) / (rd / r_alone + wr / w_alone)
+        out[name] = dict(read_only_gbps=r_alone, write_only_gbps=w_alone,
+                         phased_gbps=phased, phased_frac_of_peak=phased / PEAK_HBM_GBPS,
+                         no_arithmetic_mix_gbps=mix, fused_gbps=roof["achieved"],
+                         fused_pct_of_phased=100.0 * roof["achieved"] / phased,
+                         fused_pct_of_no_arithmetic_mix=100.0 * roof["achieved"] / mix,
+                         probes=list(names))
+    return out
+
+
 def stream_ceilings(torch, reps=8, names=None):
-    """Rates of the stream probe in the shapes above: for each, HBM bytes
-    per launch (2 per 16-bit stream element, 4 per fp32 stream element) over
-    the average launch time. step_mix_w1 and step_mix_w64 are the fused
-    step's own streams (W = 1 with 2 blocks per CU; W = 64 with 5, the
-    residency the register count gives the fused kernel), with integer folds
-    in place of the arithmetic."""
+    """Rates of the wave probe in the shapes above: for each, HBM bytes per
+    launch (2 per element of each 16-bit stream, 12 per element of the state
+    read or written) over the average launch time. step_mix_w1 and
+    step_mix_w64 carry the fused step's own streams in its own launch shape
+    (residency cap, write windows), with integer folds in place of the
+    arithmetic."""
     import ctypes as C
     lib = _copylib()
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
     out = {}
-    for name, w, nin, nout, p16, vecs, cap, n in PROBES:
+    for name, w, sin, sout, p16, vecs, cap, window, n in PROBES:
         if names is not None and name not in names:
             continue
         row = -(-n // 128) * 128
         g = torch.empty((max(w, 1), row), dtype=torch.int16, device="cuda").random_()
-        ins = [torch.empty(n, dtype=torch.int32, device="cuda").random_() for _ in range(nin)]
-        outs = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(nout)]
+        st_in = torch.empty(3 * n, dtype=torch.int32, device="cuda").random_() if sin else None
+        st_out = torch.empty(3 * n, dtype=torch.int32, device="cuda") if sout else None
         o16 = torch.empty(n, dtype=torch.int16, device="cuda") if p16 else None
         gp = (C.c_void_p * 64)(*[g[k].data_ptr() for k in range(w)])
-        ip = (C.c_void_p * 3)(*[t.data_ptr() for t in ins])
-        op = (C.c_void_p * 3)(*[t.data_ptr() for t in outs])
+        period, share = window or (0.0, 0.0)
 
         def launch():
-            rc = lib.zs_stream_probe(gp, w, ip, nin, op, nout,
-                                     o16.data_ptr() if p16 else None, n, vecs, cap,
-                                     sink.data_ptr(), 0x6D2B79F5,
-                                     torch.cuda.current_stream().cuda_stream)
+            rc = lib.zs_wave_probe(gp, w, st_in.data_ptr() if sin else None,
+                                   st_out.data_ptr() if sout else None,
+                                   o16.data_ptr() if p16 else None, n, vecs, cap, period, share,
+                                   sink.data_ptr(), 0x6D2B79F5,
+                                   torch.cuda.current_stream().cuda_stream)
             if rc != 0:
-                raise RuntimeError(f"zs_stream_probe({name}) returned {rc}: "
+                raise RuntimeError(f"zs_wave_probe({name}) returned {rc}: "
                                    f"{lib.zs_copy_last_error().decode()}")
 
         ms = _time_calls(torch, launch, reps)
-        rd, wr = 2 * w + 4 * nin, 4 * nout + (2 if p16 else 0)
+        rd, wr = 2 * w + (12 if sin else 0), (12 if sout else 0) + (2 if p16 else 0)
         gbps = (rd + wr) * n / (ms * 1e-3) / 1e9
         out[name] = dict(gbps=gbps, frac_of_peak=gbps / PEAK_HBM_GBPS, ms=ms, n=n,
                          read_bytes_per_param=rd, write_bytes_per_param=wr,
                          blocks_per_cu=cap or None,
-                         kernel=f"stream_probe<{vecs}, {str(w > 1).lower()}, {nin}, {nout}, "
+                         write_window=(dict(period_us=period, open_fraction=share)
+                                       if window else None),
+                         kernel=f"wave_probe<{vecs}, {str(sin).lower()}, {str(sout).lower()}, "
                                 f"{str(p16).lower()}>")
         log(f"ceiling {name}: {gbps:.0f} GB/s ({ms:.3f} ms)")
-        del g, ins, outs, o16
+        del g, st_in, st_out, o16
         torch.cuda.empty_cache()
     return out
 
@@ -1252,6 +1298,7 @@ def main():
     if alone and all(k in ceilings for k in alone):
         rd, wr = fused_bytes_per_param(wl.world, wl.accum)
         harmonic = (rd + wr) / (rd / ceilings[alone[0]]["gbps"] + wr / ceilings[alone[1]]["gbps"])
+    bounds = stream_bounds(ceilings, roofs)
     out = {
         "metric": METRIC,
         "value": main_res["params_per_s"],
@@ -1283,6 +1330,7 @@ def main():
         "roofline": head["roofline"],
         "roofline_by_workload": roofs,
         "ceilings": ceilings,
+        "stream_bounds": bounds,
         "cpu_baseline": cpu,
         "other_workloads": others,
         "host_commit": (None if host_res is None else host_res if "error" in host_res else

@@ -213,7 +213,7 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
  * ZS_ERR_INVALID_ARG (non-NULL m/v pointers, an unknown layout) or
  * ZS_ERR_UNSUPPORTED (alignment). acc_in, the gradients and the gather
  * buffer keep their flat layout.
- * Timing only (the values written never change): with the grouped layout
+ * Timing only (the values written never change): in either state layout
  * at world >= 40 on launches of at least 4 GB of model bytes, each wave
  * holds its stores until a window of the device's wall clock that every
  * CU reads alike (the last eighth of each 30.72 us period), so the chip's
@@ -221,8 +221,10 @@ int zs_cast_gather(const float *master, void *gather_buf, int param_dtype,
  * ends within one period. For measurements the environment variables
  * ZS_FUSED_BLOCKS_PER_CU (blocks per CU, 0 = uncapped), ZS_FUSED_SUM
  * ("batched"), ZS_FUSED_W1 ("block256") and ZS_FUSED_WRITE_WINDOW ("off",
- * or "<period in us>,<open fraction>") change the launch; they are read at
- * every call. */
+ * or "<period in us>,<open fraction>" for every rolling-sum launch: world
+ * >= 5 with operands aligned for 4-element vectors;
+ * periods under 64 wall-clock ticks mean no windows, and the open part is
+ * at least 16 ticks) change the launch; they are read at every call. */
 typedef struct {
   uint32_t world, rank;
   uint64_t n;

@@ -277,11 +277,13 @@ WriteWindow write_window(const FusedShape &fs, uint32_t world, uint64_t n, bool 
     const double bytes = (double)n * (2.0 * world + 26.0 + (acc ? 4.0 : 0.0));
     if (world < kWindowWorld || bytes < kWindowBytes) return w;
   }
+  /* at least 64 ticks per period and 16 open, so that a wave polling the
+   * clock between short sleeps cannot keep missing the open part */
   const double ticks = wall_ticks_per_us() * period_us;
-  if (!(ticks >= 8.0 && ticks < 4.0e9)) return w;
+  if (!(ticks >= 64.0 && ticks < 4.0e9)) return w;
   w.period = (uint32_t)ticks;
   const uint32_t win = (uint32_t)(w.period * open);
-  w.open_at = w.period - (win > 0 ? win : 1);
+  w.open_at = w.period - (win > 16 ? win : 16);
   return w;
 }
 

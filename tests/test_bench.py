@@ -159,3 +159,25 @@ def test_shape_sweep_plans_fit_their_shards(hip_built):
             assert 0 <= cap <= 32 and per == 0
     assert bench.shape_plan(8)[0] == (50, 3, 0) and bench.shape_plan(12)[0] == (50, 0, 0)
     assert bench.shape_plan(64)[0] == (51, 0, 0)
+
+
+def test_stream_bounds_combine_the_phases_at_the_step_bytes():
+    """The phased bound is the step's bytes over its reads' time alone plus
+    its writes' time alone: W = 1 reads 14 and writes 14 B per parameter, the
+    7.5B shard reads 140 and writes 14; workloads the probes do not carry
+    (other W, accumulated inputs) get none."""
+    c = {k: {"gbps": g} for k, g in [
+        ("read_only_w1_streams", 7000.0), ("write_only_w1_streams", 5000.0),
+        ("step_mix_w1", 6000.0), ("read_only_w64_streams", 7000.0),
+        ("write_only_w64_streams", 3500.0), ("step_mix_w64", 6000.0)]}
+    roofs = {"7b-full-w1": {"achieved": 5600.0}, "7p5b-shard-w64": {"achieved": 6300.0},
+             "gpt2s-w8": {"achieved": 6000.0}, "1p3b-w4-acc4-fp16": {"achieved": 6000.0}}
+    b = bench.stream_bounds(c, roofs)
+    assert set(b) == {"7b-full-w1", "7p5b-shard-w64"}
+    w1 = b["7b-full-w1"]
+    assert w1["phased_gbps"] == pytest.approx(28 / (14 / 7000 + 14 / 5000))
+    assert w1["fused_pct_of_phased"] == pytest.approx(100 * 5600 / w1["phased_gbps"])
+    assert w1["fused_pct_of_no_arithmetic_mix"] == pytest.approx(100 * 5600 / 6000)
+    w64 = b["7p5b-shard-w64"]
+    assert w64["phased_gbps"] == pytest.approx(154 / (140 / 7000 + 14 / 3500))
+    assert bench.stream_bounds({}, roofs) == {}

@@ -188,3 +188,114 @@ def test_every_copy_shape_is_exact(copylib, cap):
         out = dst.cpu().numpy()
         assert np.array_equal(out[:nbytes], src.cpu().numpy()), copylib.zs_copy_shape_name(i)
         assert not out[nbytes:].any(), copylib.zs_copy_shape_name(i)
+
+
+def _wave_fn(copylib):
+    f = copylib.zs_wave_probe
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint64,
+                  C.c_uint32, C.c_uint32, C.c_double, C.c_double, C.c_void_p, C.c_uint32,
+                  C.c_void_p]
+    return f
+
+
+def test_wave_probe_refuses_before_any_launch(copylib):
+    """Stream counts, vector widths, caps, windows, alignment, sizes that are
+    not whole 1024-element groups and overlapping outputs are refused with 1
+    before any HIP call; a request with no stream at all too."""
+    f = _wave_fn(copylib)
+    A = 0x7F0000000000
+    n = 4096
+    g = _ptrs([A + k * 0x100000 for k in range(3)])
+    ok = dict(in16=g, n_in16=3, sin=A + 0x1000000, sout=A + 0x2000000, out16=A + 0x3000000,
+              n=n, vecs=2, cap=0, period=0.0, open=0.0, sink=A + 0x4000000, magic=1)
+
+    def call(**over):
+        a = dict(ok, **over)
+        return f(a["in16"], a["n_in16"], a["sin"], a["sout"], a["out16"], a["n"], a["vecs"],
+                 a["cap"], a["period"], a["open"], a["sink"], a["magic"], None)
+
+    assert call(n_in16=65) == 1
+    assert call(in16=None) == 1
+    assert call(n_in16=0, sin=None, sout=None, out16=None) == 1
+    assert call(vecs=3) == 1 and call(vecs=0) == 1
+    assert call(cap=33) == 1
+    assert call(sink=None) == 1 and call(sink=A + 0x4000002) == 1
+    assert call(n=n + 512) == 1                  # not whole 1024-element groups
+    assert call(period=-1.0, open=0.1) == 1
+    assert call(period=30.0, open=0.0) == 1 and call(period=30.0, open=1.0) == 1
+    assert call(period=2e6, open=0.5) == 1
+    assert call(sin=A + 0x1000008) == 1          # misaligned state
+    assert call(out16=A + 0x3000008) == 1        # misaligned output
+    assert call(sout=A + 0x1000000 + 12 * n - 16) == 1   # state out on state in
+    assert call(out16=A + 0x2000000 + 12 * n - 16) == 1  # 16-bit out on state out
+    assert call(out16=g[2] + 2 * n - 16) == 1    # 16-bit out on a gradient stream
+    assert call(out16=A + 0x4000000 - 16) == 1   # output on the sink
+    assert call(in16=_ptrs([A, 0, A + 0x200000]), n_in16=3) == 1
+    assert call(n=0) == 0
+    assert call(n=0, period=30.72, open=0.125) == 0
+
+
+def _wave_expected(gw, sin, sout, p16, magic, n):
+    """The wave probe's documented outputs, word by word: one row per
+    4-element vector (two 32-bit words of a 16-bit stream, four of a state
+    array)."""
+    q = np.arange(n // 4, dtype=np.uint64)
+    s = np.zeros((n // 4, 2), np.uint32)
+    for x in gw:   # fold = rotl(fold, 1) + the stream's words, in stream order
+        s = ((s << np.uint32(1)) | (s >> np.uint32(31))) + x.view(np.uint32).reshape(-1, 2)
+    base = s ^ np.stack([(4 * q).astype(np.uint32), np.full(n // 4, magic, np.uint32)], 1)
+    b4 = np.concatenate([base, base], 1)
+    state = None
+    if sin is not None:
+        # grouped: [group][array][1024] -> per vector, per array, four words
+        state = sin.view(np.uint32).reshape(-1, 3, 256, 4).transpose(0, 2, 1, 3).reshape(-1, 3, 4)
+    want_state = None
+    if sout:
+        want_state = (state ^ b4[:, None, :]) if state is not None else np.repeat(b4[:, None, :], 3, 1)
+    rest = base.copy()
+    if state is not None and not sout:
+        for j in range(3):
+            rest ^= np.stack([state[:, j, 0] ^ state[:, j, 2], state[:, j, 1] ^ state[:, j, 3]], 1)
+    return want_state, (rest if p16 else None)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("w,sin,sout,p16,vecs,window", [
+    (1, True, True, True, 1, None), (0, False, True, True, 1, None),
+    (1, True, False, False, 1, None), (3, True, True, True, 2, None),
+    (4, True, False, True, 2, None), (5, True, True, True, 2, None),
+    (6, True, True, False, 2, None), (7, False, False, True, 2, None),
+    (8, True, True, True, 2, None), (13, True, True, True, 1, None),
+    (64, True, True, True, 2, None), (64, True, True, True, 2, (2.56, 0.25)),
+    (9, True, True, True, 2, (5.12, 0.125))])
+def test_wave_probe_moves_what_it_states(copylib, w, sin, sout, p16, vecs, window):
+    """Every output word is the documented fold of the inputs, for every
+    count of streams left after the rolling sum's last full round and with
+    write windows, so every stream the probe states is really read and
+    written where it says."""
+    import torch
+    f = _wave_fn(copylib)
+    n = 3 * 4096
+    magic = 0x9E3779B9
+    rng = np.random.default_rng(1000 + w * 10 + vecs)
+    gw = [rng.integers(0, 2 ** 16, n, dtype=np.uint16) for _ in range(w)]
+    g = [torch.from_numpy(x.view(np.int16)).cuda() for x in gw]
+    sin_h = rng.integers(0, 2 ** 32, 3 * n, dtype=np.uint32) if sin else None
+    sin_d = torch.from_numpy(sin_h.view(np.int32)).cuda() if sin else None
+    sout_d = torch.zeros(3 * n, dtype=torch.int32, device="cuda") if sout else None
+    o16 = torch.zeros(n, dtype=torch.int16, device="cuda") if p16 else None
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    per, op = window or (0.0, 0.0)
+    rc = f(_ptrs([t.data_ptr() for t in g]), w, sin_d.data_ptr() if sin else None,
+           sout_d.data_ptr() if sout else None, o16.data_ptr() if p16 else None, n, vecs, 0,
+           per, op, sink.data_ptr(), magic, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, copylib.zs_copy_last_error().decode()
+    torch.cuda.synchronize()
+    want_state, want16 = _wave_expected(gw, sin_h, sout, p16, magic, n)
+    if sout:
+        got = sout_d.cpu().numpy().view(np.uint32).reshape(-1, 3, 256, 4)
+        got = got.transpose(0, 2, 1, 3).reshape(-1, 3, 4)
+        assert np.array_equal(got, want_state)
+    if p16:
+        assert np.array_equal(o16.cpu().numpy().view(np.uint32).reshape(-1, 2), want16)
