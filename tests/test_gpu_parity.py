@@ -343,16 +343,19 @@ def test_step_fused_grouped_wire(zs, world, wire):
         assert assert_ulp16(r["gather"][:n], rp, gdt, 1, "params") == 0
 
 
-@pytest.mark.parametrize("world", [5, 8, 64])
-def test_step_fused_grouped_write_windows(zs, world, monkeypatch):
+@pytest.mark.parametrize("world,window", [(5, "2.56,0.25"), (8, "2.56,0.25"), (64, "2.56,0.25"),
+                                          (8, "30.72,0.001"), (8, "0.2,0.5")])
+def test_step_fused_grouped_write_windows(zs, world, window, monkeypatch):
     """With write windows forced on (a 2.56 us period, a quarter of it
-    open, so that even a small shard's launch spans many periods) the
-    rolling grouped step still writes the oracle's state and parameters:
-    the windows only delay the stores."""
-    monkeypatch.setenv("ZS_FUSED_WRITE_WINDOW", "2.56,0.25")
+    open, so that even a small shard's launch spans many periods; or the
+    production period with an open part below the 16-tick floor, which the
+    library widens; or a period under the 64-tick floor, which means no
+    windows) the rolling grouped step still writes the oracle's state and
+    parameters: the windows only delay the stores."""
+    monkeypatch.setenv("ZS_FUSED_WRITE_WINDOW", window)
     rng = np.random.default_rng(57 + world)
     for n, with_acc, gdt in ((200_003, False, "bf16"), (33_333, True, "fp16")):
-        announce(f"fused grouped write windows W={world} n={n} acc={with_acc}")
+        announce(f"fused grouped write windows {window} W={world} n={n} acc={with_acc}")
         r = _fused_case_grouped(zs, rng, world, world - 1, n, gdt, gdt, with_acc)
         rflag, rm, rmm, rv, rp = r["ref"]
         assert r["flag"] == rflag == 0
