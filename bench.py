@@ -404,6 +404,57 @@ def stream_ceilings(torch, reps=8, names=None):
     return out
 
 
+# (W, shard size, vectors per thread, caps): the wave probe's step mixes
+PROBE_SWEEP = ((64, N_W64, 2, (0, 4, 6, 8, 12, 16)), (1, N_W1 // 2, 1, (0, 8, 12, 16)))
+
+
+def probe_sweep(torch, rounds=3, reps=6):
+    """The wave probe's W = 64 and W = 1 step mixes (all streams read and
+    written, no arithmetic) at each residency cap, with and without the
+    write windows the library uses at W = 64, interleaved over `rounds`."""
+    import ctypes as C
+    lib = _copylib()
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    cases, keep = [], []
+    for w, n, vecs, caps in PROBE_SWEEP:
+        g = torch.empty((w, -(-n // 128) * 128), dtype=torch.int16, device="cuda").random_()
+        si = torch.empty(3 * n, dtype=torch.int32, device="cuda").random_()
+        so = torch.empty(3 * n, dtype=torch.int32, device="cuda")
+        o16 = torch.empty(n, dtype=torch.int16, device="cuda")
+        gp = (C.c_void_p * 64)(*[g[k].data_ptr() for k in range(w)])
+        keep.append((g, si, so, o16, gp))
+        for cap in caps:
+            for win in (None, WINDOW_W64):
+                def launch(w=w, n=n, vecs=vecs, cap=cap, win=win, b=keep[-1]):
+                    period, share = win or (0.0, 0.0)
+                    rc = lib.zs_wave_probe(b[4], w, b[1].data_ptr(), b[2].data_ptr(),
+                                           b[3].data_ptr(), n, vecs, cap, period, share,
+                                           sink.data_ptr(), 0x6D2B79F5,
+                                           torch.cuda.current_stream().cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"zs_wave_probe returned {rc}: "
+                                           f"{lib.zs_copy_last_error().decode()}")
+                cases.append(dict(world=w, n=n, vecs_per_thread=vecs, blocks_per_cu=cap or None,
+                                  write_window=(dict(period_us=win[0], open_fraction=win[1])
+                                                if win else None), fn=launch))
+    times = [[] for _ in cases]
+    for _ in range(rounds):
+        for c, case in enumerate(cases):
+            times[c].append(_time_calls(torch, case["fn"], reps))
+    out = []
+    for c, case in enumerate(cases):
+        ms = sum(times[c]) / rounds
+        gbps = (2 * case["world"] + 26) * case["n"] / (ms * 1e-3) / 1e9
+        rec = {k: v for k, v in case.items() if k != "fn"}
+        rec.update(ms=ms, ms_rounds=times[c], gbps=gbps, frac_of_peak=gbps / PEAK_HBM_GBPS)
+        out.append(rec)
+        log(f"probe W={case['world']} cap={case['blocks_per_cu']} "
+            f"windows={'on' if case['write_window'] else 'off'}: {ms:.3f} ms ({gbps:.0f} GB/s)")
+    del keep
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---- the shard step ------------------------------------------------------------
 
 def pad_elems(n, align_bytes=256):
@@ -1153,6 +1204,9 @@ def main():
                          "each and print that table as the JSON line instead")
     ap.add_argument("--sweep-n", type=int, default=1 << 25,
                     help="shard size of the --sweep-world runs")
+    ap.add_argument("--sweep-probe", action="store_true",
+                    help="the wave probe's W = 64 and W = 1 step mixes by residency cap, with "
+                         "and without write windows")
     ap.add_argument("--sweep-phases", action="store_true",
                     help="time the 7.5B shard's reads and writes separated in time (stream "
                          "probe, 1 to 64 chunks) and print that table as the JSON line instead")
@@ -1194,6 +1248,10 @@ def main():
         sweep = world_sweep(worlds, args.sweep_n, args.steps, args.warmup, torch)
         print(json.dumps({"metric": "fused step HBM GB/s by worker count", "unit": "GB/s",
                           "peak": PEAK_HBM_GBPS, "sweep": sweep}))
+        return
+    if args.sweep_probe:
+        print(json.dumps({"metric": "wave-probe step mix GB/s by residency cap and write windows",
+                          "unit": "GB/s", "peak": PEAK_HBM_GBPS, "probe": probe_sweep(torch)}))
         return
     if args.sweep_phases:
         print(json.dumps({"metric": "7.5B-shard step mix, reads and writes separated in time",
