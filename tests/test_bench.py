@@ -181,3 +181,16 @@ def test_stream_bounds_combine_the_phases_at_the_step_bytes():
     w64 = b["7p5b-shard-w64"]
     assert w64["phased_gbps"] == pytest.approx(154 / (140 / 7000 + 14 / 3500))
     assert bench.stream_bounds({}, roofs) == {}
+
+
+def test_wave_probe_plans_fit_the_probe():
+    """Every shard the wave probe is asked to stream is whole 1024-element
+    groups (its grouped state) and whole tiles, with at most 64 gradient
+    streams, 1 or 2 vectors per thread and caps the library accepts."""
+    plans = [(w, n, vecs, (cap,)) for _, w, _, _, _, vecs, cap, _, n in bench.PROBES]
+    plans += list(bench.PROBE_SWEEP)
+    for w, n, vecs, caps in plans:
+        assert 0 <= w <= 64 and vecs in (1, 2)
+        assert n % 1024 == 0 and n % (256 * vecs) == 0
+        assert all(0 <= c <= 32 for c in caps)
+    assert bench.WINDOW_W64 == (bench.WINDOW_PERIOD_US, bench.WINDOW_OPEN)
